@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the CacheGen KV-cache codec on one MI355X.
+
+One step = the whole hot path on one batch of synthetic KV already resident
+in HBM: cg_to_bytes (quantise, histogram + CDF, range-encode, blob) followed
+by cg_from_bytes (length scan, range-decode + dequantise) of that blob.
+
+Default workload: Llama-3.1-8B-shaped long context, 32 layers x 8 KV heads x
+128 = 1024 channels x 32768 tokens of bf16 (4 GiB of raw K+V), default
+per-layer bins, seeded AR(1) generator with 1% outlier channels x20.
+
+Prints ONE JSON line. ``value`` is the round-trip throughput: raw KV bytes /
+(encode time + decode time). Encode and decode GB/s, the compression ratio,
+per-stage times, the roofline of the dominant kernel (timed live with HIP
+events on the stream the library launches on) and the CPU oracle timed on a
+bounded sample are reported beside it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "encode & decode GB/s of raw bf16 KV on 1 MI355X (32L×1024ch) + compression ratio"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD public spec
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama31_8b_t32k")
+    ap.add_argument("--stage-reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-layers", type=int, default=4)
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_events(fn, reps, torch):
+    """Average milliseconds of fn() over reps, HIP events on the current stream."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def cpu_baseline(w, layers):
+    """The oracle (scalar C, one thread) on layers [0, layers) of the workload."""
+    import oracle
+    from kv_cache_compression_layer_amd.synth import generate_kv
+
+    kv = generate_kv(layers, w.ntokens, w.nheads, w.head_size, rho=w.rho, innovations=w.innovations,
+                     outlier_frac=w.outlier_frac, outlier_scale=w.outlier_scale, seed=w.seed + 500)
+    bk, bv = oracle.default_bins(w.nlayers)
+    bk, bv = bk[:layers], bv[:layers]
+    t0 = time.perf_counter()
+    blob = oracle.to_bytes(kv, bk, bv)
+    t1 = time.perf_counter()
+    oracle.from_bytes(blob)
+    t2 = time.perf_counter()
+    raw = kv.nbytes
+    return {
+        "value": raw / (t2 - t0) / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"layers 0-{layers - 1} of {w.name} ({layers}x2x{w.ntokens}x{w.nheads}x{w.head_size} bf16, "
+                  f"{raw / 2**20:.0f} MiB; same generator, seed {w.seed + 500}, bins of those layers); "
+                  f"to_bytes then from_bytes, single thread",
+        "encode_GBps": raw / (t1 - t0) / 1e9,
+        "decode_GBps": raw / (t2 - t1) / 1e9,
+        "seconds": t2 - t0,
+        "cpu": platform.processor() or platform.machine(),
+        "nproc": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this codec runs on one GPU; multi-GPU runs are not part of this "
+                                   "build (see DESIGN.md for how the work would shard)",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_compression_layer_amd import cachegen as cgb
+    from kv_cache_compression_layer_amd.synth import WORKLOADS, generate_workload
+
+    w = WORKLOADS[args.workload]
+    L, T, H, D = w.nlayers, w.ntokens, w.nheads, w.head_size
+    C = H * D
+    N = 2 * L * T * C
+    raw = 2 * N
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"generating {w.name} {w.shape}")
+    t0 = time.perf_counter()
+    kv_np = generate_workload(w)
+    log(f"generated in {time.perf_counter() - t0:.1f}s")
+    kv = torch.from_numpy(kv_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    del kv_np
+
+    desc = cgb.Desc.for_kv(tuple(kv.shape))
+    A = desc.alphabet
+    blob = torch.empty(cgb.cg_blob_bound(desc), dtype=torch.uint8, device=dev)
+    size_dev = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_enc = cgb.alloc_workspace(desc, cgb.CG_OP_TO_BYTES, dev)
+    ws_dec = cgb.alloc_workspace(desc, cgb.CG_OP_FROM_BYTES, dev)
+    kv_out = torch.empty_like(kv)
+
+    def encode():
+        cgb.cg_to_bytes(desc, kv, blob, size_dev, ws_enc)
+
+    encode()
+    cgb.check_status(ws_enc, what="cg_to_bytes")
+    blob_size = int(size_dev.item())
+
+    def decode():
+        cgb.cg_from_bytes(desc, blob, blob_size, kv_out, ws_dec)
+
+    decode()
+    cgb.check_status(ws_dec, what="cg_from_bytes")
+    info, _, _ = cgb.peek(blob[:blob_size])
+    payload_bytes = blob_size - info["off_payload"]
+
+    log(f"warmup {args.warmup}, steps {args.steps}")
+    for _ in range(args.warmup):
+        encode()
+        decode()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        ev[3 * i].record()
+        encode()
+        ev[3 * i + 1].record()
+        decode()
+        ev[3 * i + 2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    enc_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)) / args.steps
+    dec_ms = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)) / args.steps
+    cgb.check_status(ws_dec, what="cg_from_bytes")
+    step_ms = enc_ms + dec_ms
+    log(f"encode {enc_ms:.3f} ms, decode {dec_ms:.3f} ms, wall/step {1e3 * wall / args.steps:.3f} ms")
+
+    # Stage entry points, each timed on its own (same inputs, same stream).
+    sym = torch.empty(N, dtype=torch.uint8, device=dev)
+    scale = torch.empty(2 * L * T, dtype=torch.int16, device=dev)
+    cdf = torch.empty(2 * L * C * (A + 1), dtype=torch.int32, device=dev)
+    payload = torch.empty(max(payload_bytes, 1) + 1024, dtype=torch.uint8, device=dev)
+    lengths = torch.empty(desc.nstreams, dtype=torch.int16, device=dev)
+    chunk_off = torch.empty(desc.nchunks + 1, dtype=torch.int64, device=dev)
+    ws_q = cgb.alloc_workspace(desc, cgb.CG_OP_QUANTIZE, dev)
+    ws_c = cgb.alloc_workspace(desc, cgb.CG_OP_BUILD_CDF, dev)
+    ws_e = cgb.alloc_workspace(desc, cgb.CG_OP_ENCODE, dev)
+    ws_d = cgb.alloc_workspace(desc, cgb.CG_OP_DECODE, dev)
+    sym2 = torch.empty_like(sym)
+    kv_out2 = torch.empty_like(kv)
+    stage_fns = {
+        "quantize": lambda: cgb.cg_quantize(desc, kv, sym, scale, ws_q),
+        "build_cdf": lambda: cgb.cg_build_cdf(desc, sym, cdf, ws_c),
+        "encode": lambda: cgb.cg_encode(desc, sym, cdf, payload, lengths, chunk_off, ws_e),
+        "decode": lambda: cgb.cg_decode(desc, payload, payload_bytes, lengths, chunk_off, cdf, sym2, ws_d),
+        "dequantize": lambda: cgb.cg_dequantize(desc, sym2, scale, kv_out2),
+    }
+    stages_ms = {}
+    for name, fn in stage_fns.items():
+        fn()
+        stages_ms[name] = time_events(fn, args.stage_reps, torch)
+    for ws in (ws_q, ws_c, ws_e, ws_d):
+        cgb.check_status(ws, what="stage calls")
+    stages_ms["from_bytes"] = dec_ms
+    log(f"stages (ms): {json.dumps({k: round(v, 4) for k, v in stages_ms.items()})}")
+
+    # Algorithmic HBM bytes of the main kernel behind each entry point.
+    nstreams = desc.nstreams
+    len_bytes = 2 * nstreams
+    alg_bytes = {
+        # k_quantize: read bf16 KV, write u8 symbols and bf16 scales.
+        "quantize": 2 * N + N + 4 * L * T,
+        # k_histogram + k_cdf: read symbols, write int32 tables.
+        "build_cdf": N + 4 * 2 * L * C * (A + 1),
+        # k_encode: read symbols and tables, write payload, lengths, offsets.
+        "encode": N + 4 * 2 * L * C * (A + 1) + payload_bytes + len_bytes + 8 * (desc.nchunks + 1),
+        # k_decode (stage): read payload, lengths, tables; write symbols.
+        "decode": payload_bytes + len_bytes + 4 * 2 * L * C * (A + 1) + N,
+        # k_dequantize: read symbols + scales, write bf16.
+        "dequantize": N + 4 * L * T + 2 * N,
+        # k_lenscan + k_decode fused: read the blob, write bf16 KV.
+        "from_bytes": blob_size + 2 * N,
+    }
+    kernel_of = {"quantize": "k_quantize_vec", "build_cdf": "k_histogram", "encode": "k_encode",
+                 "decode": "k_decode<5,false>", "dequantize": "k_dequantize",
+                 "from_bytes": "k_decode<5,true>"}
+    path_stages = ["quantize", "build_cdf", "encode", "from_bytes"]
+    dom = max(path_stages, key=lambda k: stages_ms[k])
+    achieved = alg_bytes[dom] / (stages_ms[dom] * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm",
+        "achieved": achieved,
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": achieved / HBM_PEAK_GBPS,
+        "traffic": None,
+        "kernel": kernel_of[dom],
+        "entry_point": f"cg_{dom}" if dom != "from_bytes" else "cg_from_bytes",
+        "algorithmic_bytes": alg_bytes[dom],
+        "avg_ms": stages_ms[dom],
+    }
+
+    enc_GBps = raw / (enc_ms * 1e-3) / 1e9
+    dec_GBps = raw / (dec_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": raw / (step_ms * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "io_dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: bf16 KV [L,2,T,H,D]=[{L},2,{T},{H},{D}], default per-layer bins "
+                        f"(K 32/16, V 32/16), AR(1) rho={w.rho} {w.innovations}, "
+                        f"{w.outlier_frac:.0%} outlier channels x{w.outlier_scale:g}, seed {w.seed}",
+            "raw_bytes": raw,
+            "chunk_tokens": 256,
+            "alphabet": A,
+        },
+        "encode_GBps": enc_GBps,
+        "decode_GBps": dec_GBps,
+        "encode_ms": enc_ms,
+        "decode_ms": dec_ms,
+        "compression_ratio": raw / blob_size,
+        "payload_ratio": raw / payload_bytes,
+        "blob_bytes": blob_size,
+        "encode_hbm_frac": (raw + blob_size) / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "decode_hbm_frac": (raw + blob_size) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "stages_ms": stages_ms,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+
+    del sym, sym2, kv_out2, payload
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_sample_layers} layers")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_layers)
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * cachegen.h -- C ABI of libcachegen_mi355x.so, the CacheGen KV-cache codec
+ * for AMD Instinct MI355X (gfx950), in hand-written HIP.
+ *
+ * The codec follows the LMCache CacheGen page
+ *   "LMCache 中的 KV Cache 压缩：CacheGen 编解码原理、配置方式与源码解析"
+ *   (0539edu.com/news/4720135), cited below as [P2 sN] for its section N:
+ *   s1 QuantizationSpec (per-layer bins), s2 quantisation, s3 CDF estimation
+ *   and normalisation, s4 arithmetic coding and the GPU kernels, s5 decoding
+ *   and dequantisation.
+ *
+ * Conventions
+ * -----------
+ * - Every entry point returns CG_OK (0) or a negative CG_E_* code. Argument,
+ *   shape and capacity checks happen on the host before anything is
+ *   launched; on such an error nothing is launched.
+ * - Pointers marked "device" are HIP device pointers. The caller allocates
+ *   and owns every buffer, including the workspace `ws`; the library never
+ *   allocates, frees or keeps state between calls, so concurrent calls on
+ *   different streams with different workspaces are safe.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *   device work is enqueued asynchronously on it, in order.
+ * - Conditions only the device can see (NaN/Inf input, a corrupt stream,
+ *   a payload beyond capacity) are recorded in a status word at the start of
+ *   `ws`; cg_read_status() waits for the stream and returns them as a code.
+ *   Each device entry point clears that word first.
+ * - Layouts are C order. bf16 tensors hold raw bf16 bit patterns.
+ *   KV:      bf16  [nlayers, 2, ntokens, nheads, head_size]  ([P2 s2], [P2 s5])
+ *   symbols: uint8 [2, nlayers, ntokens, C]       (K before V; C = nheads*head_size)
+ *   scales:  bf16  [2, nlayers, ntokens]          (absmax over channels)
+ *   cdf:     int32 [2, nlayers, C, A+1]           (A = max of all bins)
+ *   lengths: uint16 [NC, 2*nlayers, C]            (NC = ceil(ntokens/256))
+ *   chunk_off: uint64 [NC+1]                      (payload offset of each chunk)
+ *   Streams are ordered (chunk, K|V, layer, channel); stream (j, kv, l, c)
+ *   holds the symbols of tokens [256j, min(256j+256, ntokens)) of channel c.
+ */
+#ifndef CACHEGEN_H
+#define CACHEGEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ----------------------------------------------------------------- codes */
+#define CG_OK            0
+#define CG_E_INVAL      (-1) /* null pointer, bad bins, bad op, bad sizes     */
+#define CG_E_SHAPE      (-2) /* dimensions out of range                       */
+#define CG_E_CAPACITY   (-3) /* output buffer too small                       */
+#define CG_E_CORRUPT    (-4) /* malformed blob, stream, CDF or lengths        */
+#define CG_E_NONFINITE  (-5) /* NaN or Inf in the KV input                    */
+#define CG_E_HIP        (-6) /* a HIP runtime call failed                     */
+#define CG_E_WORKSPACE  (-7) /* workspace smaller than cg_workspace_bytes()   */
+
+#define CG_CHUNK_TOKENS     256  /* tokens per coder stream ([P2 s4])        */
+#define CG_MAX_LAYERS       1024
+#define CG_MIN_BINS         4
+#define CG_MAX_BINS         128
+#define CG_MAX_STREAM_BYTES 513  /* worst-case coded size of a 256-symbol stream */
+
+/* Problem descriptor. bins_k / bins_v are HOST arrays of length nlayers
+ * holding the number of quantisation bins of each layer ([P2 s1]); each must
+ * be in [4, 128]. Valid shapes: 1 <= nlayers <= 1024, ntokens >= 1,
+ * nheads >= 1, head_size >= 1, 2*nlayers*ntokens*nheads*head_size < 2^40. */
+typedef struct cg_desc {
+    int32_t nlayers;
+    int32_t ntokens;
+    int32_t nheads;
+    int32_t head_size;
+    const uint8_t *bins_k;
+    const uint8_t *bins_v;
+} cg_desc;
+
+/* Blob layout, as written by cg_to_bytes and read by cg_blob_peek. Offsets
+ * are byte offsets from the start of the blob; every section is 64-byte
+ * aligned and the gaps are zero. Header (little-endian): "CGMX", u16
+ * version 1, u16 dtype 1 (bf16), u32 nlayers, ntokens, nheads, head_size,
+ * chunk_tokens (256), nchunks, alphabet, reserved (0), u64 blob_size, then
+ * u8 bins_k[nlayers], u8 bins_v[nlayers]. Sections: scales bf16 [2,L,T];
+ * cdf u16 [2,L,C,A] (entries 0..A-1 of each table, entry A is 2^16);
+ * chunk_off u64 [NC+1]; lengths u16 [NC,2L,C]; payload. */
+typedef struct cg_blob_info {
+    int32_t nlayers, ntokens, nheads, head_size;
+    int32_t chunk_tokens, nchunks, alphabet, reserved;
+    uint64_t blob_size;      /* 0 when unknown (cg_blob_layout)           */
+    uint64_t header_bytes;
+    uint64_t off_scales, off_cdf, off_chunk_off, off_lengths, off_payload;
+} cg_blob_info;
+
+/* Operation selector for cg_workspace_bytes. */
+enum cg_op {
+    CG_OP_QUANTIZE = 0,
+    CG_OP_BUILD_CDF = 1,
+    CG_OP_ENCODE = 2,
+    CG_OP_DECODE = 3,
+    CG_OP_DEQUANTIZE = 4,
+    CG_OP_TO_BYTES = 5,
+    CG_OP_FROM_BYTES = 6
+};
+
+/* ------------------------------------------------------- host-only calls */
+
+/* Message for a status code (static storage). */
+const char *cg_strerror(int code);
+
+/* Library ABI version (1). */
+int cg_version(void);
+
+/* Default bins ([P2 s1]): with fewer than 10 layers every K and V layer gets
+ * 32 bins; otherwise K layers 0..9 get 32 and the rest 16, V layers 0..1
+ * get 32 and the rest 16. bins_k / bins_v: host arrays of nlayers bytes. */
+int cg_default_bins(int32_t nlayers, uint8_t *bins_k, uint8_t *bins_v);
+
+/* Validates a descriptor: CG_OK, CG_E_INVAL or CG_E_SHAPE. */
+int cg_desc_check(const cg_desc *desc);
+
+/* Bytes of workspace `op` needs (>= 256), or a negative code. */
+int64_t cg_workspace_bytes(const cg_desc *desc, int op);
+
+/* Upper bound of the payload cg_encode can produce: NS * 513 bytes with
+ * NS = NC * 2 * nlayers * C streams. Negative code on a bad descriptor. */
+int64_t cg_encode_bound(const cg_desc *desc);
+
+/* Upper bound of the blob cg_to_bytes can produce. */
+int64_t cg_blob_bound(const cg_desc *desc);
+
+/* Section offsets of the blob for `desc` (blob_size set to 0). */
+int cg_blob_layout(const cg_desc *desc, cg_blob_info *out);
+
+/* Parses a blob header held in HOST memory (the first n bytes of a blob; n
+ * must cover the header, i.e. 48 + 2*nlayers bytes). Fills `out` and copies
+ * the bins into bins_k / bins_v (host arrays of bins_cap bytes). Returns
+ * CG_E_CORRUPT for a bad magic, version, dtype, shape or bins, and
+ * CG_E_CAPACITY if bins_cap < nlayers. */
+int cg_blob_peek(const void *header, size_t n, cg_blob_info *out, uint8_t *bins_k,
+                 uint8_t *bins_v, int32_t bins_cap);
+
+/* Waits for `stream`, then returns the device status recorded in `ws` by the
+ * last entry point that used it: CG_OK, CG_E_NONFINITE, CG_E_CORRUPT or
+ * CG_E_CAPACITY (CG_E_HIP if the wait or the copy fails). */
+int cg_read_status(const void *ws, void *stream);
+
+/* ------------------------------------------------------------ stage calls */
+
+/* [P2 s2] Quantise. For each (kv, layer, token) row: m = max |x| over the C
+ * channels, M = bins//2 - 1 of that layer, q = round_half_even(x*(M/m) + M)
+ * in fp32 with each operation rounded separately, clamped to [0, 2M]; a row
+ * with m = 0 gives q = M. kv: device bf16 [L,2,T,H,D]; sym: device uint8
+ * [2,L,T,C]; scale: device bf16 [2,L,T] (m, exact). NaN/Inf input records
+ * CG_E_NONFINITE. */
+int cg_quantize(const cg_desc *desc, const void *kv, uint8_t *sym, uint16_t *scale, void *ws,
+                size_t ws_bytes, void *stream);
+
+/* [P2 s3] Histogram of each (kv, layer, channel) over all ntokens tokens and
+ * its integer CDF: cdf[k] = round_half_even(cum[k] * (2^16 - A) / T) + k for
+ * k = 0..A, so cdf[0] = 0, cdf[A] = 2^16 and every symbol keeps frequency
+ * >= 1. sym: device uint8 [2,L,T,C] (every symbol < A); cdf: device int32
+ * [2,L,C,A+1]. */
+int cg_build_cdf(const cg_desc *desc, const uint8_t *sym, int32_t *cdf, void *ws,
+                 size_t ws_bytes, void *stream);
+
+/* [P2 s4] Range-code every stream (byte-wise 32-bit range coder, 16-bit
+ * tables) and concatenate them in stream order. payload: device buffer of
+ * `cap` bytes (cap >= cg_encode_bound() can never overflow; a smaller cap
+ * records CG_E_CAPACITY if exceeded); lengths: device uint16 [NC,2L,C]
+ * bytes per stream; chunk_off: device uint64 [NC+1], chunk_off[NC] is the
+ * payload size. */
+int cg_encode(const cg_desc *desc, const uint8_t *sym, const int32_t *cdf, uint8_t *payload,
+              size_t cap, uint16_t *lengths, uint64_t *chunk_off, void *ws, size_t ws_bytes,
+              void *stream);
+
+/* [P2 s5] Decode every stream: its offset is the chunk offset plus the prefix
+ * sum of the lengths before it in the chunk; symbols are found by search in
+ * the CDF. Bytes past a stream's length read as zero. payload_bytes bounds
+ * every read. A malformed stream, or chunk offsets that disagree with the
+ * lengths, record CG_E_CORRUPT. sym: device uint8 [2,L,T,C]. */
+int cg_decode(const cg_desc *desc, const uint8_t *payload, size_t payload_bytes,
+              const uint16_t *lengths, const uint64_t *chunk_off, const int32_t *cdf,
+              uint8_t *sym, void *ws, size_t ws_bytes, void *stream);
+
+/* [P2 s5] Dequantise: x = bf16_round((q - M) / M * m) with fp32 division and
+ * product. sym: device uint8 [2,L,T,C]; scale: device bf16 [2,L,T];
+ * kv_out: device bf16 [L,2,T,H,D]. */
+int cg_dequantize(const cg_desc *desc, const uint8_t *sym, const uint16_t *scale, void *kv_out,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------ whole-blob calls */
+
+/* to_bytes: the whole encode path on [L,2,T,H,D] bf16 KV, writing the blob
+ * described at cg_blob_info into `blob` (device, `cap` bytes; cap >=
+ * cg_blob_bound() can never overflow). The blob size is written to
+ * *blob_size_dev (device uint64) and into the header. */
+int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
+                uint64_t *blob_size_dev, void *ws, size_t ws_bytes, void *stream);
+
+/* from_bytes: the whole decode path. `desc` must be the one cg_blob_peek
+ * returned for this blob (bins included); blob: device; blob_size: its size
+ * in bytes; kv_out: device bf16 [L,2,T,H,D]. */
+int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,
+                  void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CACHEGEN_H */

@@ -1,0 +1,234 @@
+// Element-wise kernels of the CacheGen codec on gfx950: quantise, dequantise,
+// workspace fills and the blob header.
+//
+// Quantisation follows the LMCache CacheGen page (0539edu.com/news/4720135),
+// section 2: a symmetric per-layer quantiser whose scale is the absolute
+// maximum over the channels of a (K|V, layer, token) row. Dequantisation
+// follows section 5: t = (t - M) / M * scale, cast back to bf16.
+//
+// One wave owns one row of C channels: its loads are 16-byte vectors that
+// cover the row contiguously (64 lanes x 16 B = 1 KiB per instruction), the
+// absmax is a max over bf16 bit patterns (|x| orders like its bit pattern
+// with the sign cleared) reduced across the wave, and the row stays in
+// registers between the reduction and the quantisation.
+#include "cg_internal.hpp"
+
+namespace cg {
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t *__restrict__ p, uint32_t v, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------- quantise
+
+// Symbol of one element: q = clamp(rint(x*f + M), 0, 2M) with every fp32
+// operation rounded on its own (the library is built without contraction).
+__device__ __forceinline__ uint32_t quant1(uint32_t bits16, float f, float Mf, int twoM) {
+    float x = bf16_to_f32(bits16 & 0xFFFFu);
+    float y = __fmul_rn(x, f);
+    float z = __fadd_rn(y, Mf);
+    int q = (int)rintf(z);
+    q = min(max(q, 0), twoM);
+    return (uint32_t)q;
+}
+
+__device__ __forceinline__ uint32_t absmax_pair(uint32_t w) {
+    return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+}
+
+__device__ __forceinline__ void row_coords(int64_t row, int L, int T, int &k, int &l, int &t) {
+    const int64_t LT = (int64_t)L * T;
+    k = (int)(row / LT);
+    const int64_t rem = row - (int64_t)k * LT;
+    l = (int)(rem / T);
+    t = (int)(rem - (int64_t)l * T);
+}
+
+// NV 16-byte vectors per lane hold the row (C <= NV * 512, C % 8 == 0).
+template <int NV>
+__global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict__ kv,
+                                                      uint8_t *__restrict__ sym,
+                                                      uint16_t *__restrict__ scale,
+                                                      uint32_t *__restrict__ status, int L, int T,
+                                                      int C, MaxTable mt) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= 2LL * L * T) return;
+    int k, l, t;
+    row_coords(row, L, T, k, l, t);
+    const uint16_t *src = kv + (((int64_t)l * 2 + k) * T + t) * C;
+    uint8_t *dst = sym + row * C;
+
+    uint4 v[NV];
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c0 = (i * 64 + lane) * 8;
+        if (c0 < C) {
+            v[i] = *reinterpret_cast<const uint4 *>(src + c0);
+        } else {
+            v[i] = make_uint4(0, 0, 0, 0);
+        }
+        am = max(am, max(max(absmax_pair(v[i].x), absmax_pair(v[i].y)),
+                         max(absmax_pair(v[i].z), absmax_pair(v[i].w))));
+    }
+    am = wave_max_u32(am);
+    if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
+    const int M = mt.m[k][l];
+    const float Mf = (float)M;
+    // m == 0 gives f == 0, so every symbol is exactly M.
+    const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
+    const int twoM = 2 * M;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c0 = (i * 64 + lane) * 8;
+        if (c0 < C) {
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                lo |= quant1(w[e], f, Mf, twoM) << (16 * e);
+                lo |= quant1(w[e] >> 16, f, Mf, twoM) << (16 * e + 8);
+                hi |= quant1(w[e + 2], f, Mf, twoM) << (16 * e);
+                hi |= quant1(w[e + 2] >> 16, f, Mf, twoM) << (16 * e + 8);
+            }
+            *reinterpret_cast<uint2 *>(dst + c0) = make_uint2(lo, hi);
+        }
+    }
+    if (lane == 0) scale[row] = (uint16_t)am;
+}
+
+// Any C and alignment: two passes over the row (the second hits the cache).
+__global__ __launch_bounds__(256) void k_quantize_any(const uint16_t *__restrict__ kv,
+                                                      uint8_t *__restrict__ sym,
+                                                      uint16_t *__restrict__ scale,
+                                                      uint32_t *__restrict__ status, int L, int T,
+                                                      int C, MaxTable mt) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= 2LL * L * T) return;
+    int k, l, t;
+    row_coords(row, L, T, k, l, t);
+    const uint16_t *src = kv + (((int64_t)l * 2 + k) * T + t) * C;
+    uint8_t *dst = sym + row * C;
+    uint32_t am = 0;
+    for (int c = lane; c < C; c += 64) am = max(am, (uint32_t)src[c] & 0x7FFFu);
+    am = wave_max_u32(am);
+    if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
+    const int M = mt.m[k][l];
+    const float Mf = (float)M;
+    const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
+    for (int c = lane; c < C; c += 64) dst[c] = (uint8_t)quant1(src[c], f, Mf, 2 * M);
+    if (lane == 0) scale[row] = (uint16_t)am;
+}
+
+hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
+                           uint16_t *scale, uint32_t *status, hipStream_t s) {
+    const int64_t rows = 2LL * d.L * d.T;
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    const bool aligned = ((uintptr_t)kv % 16 == 0) && ((uintptr_t)sym % 8 == 0);
+    if (aligned && d.C % 8 == 0 && d.C <= 2048) {
+        const int nv = (d.C + 511) / 512;
+        switch (nv) {
+        case 1: hipLaunchKernelGGL(k_quantize_vec<1>, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt); break;
+        case 2: hipLaunchKernelGGL(k_quantize_vec<2>, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt); break;
+        case 3: hipLaunchKernelGGL(k_quantize_vec<3>, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt); break;
+        default: hipLaunchKernelGGL(k_quantize_vec<4>, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt); break;
+        }
+    } else {
+        hipLaunchKernelGGL(k_quantize_any, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------- dequantise
+
+// dq[q] = fl32((q - M) / M) for q in [0, 128), one table per wave in LDS.
+__device__ __forceinline__ void build_dq(float *dq, int M, int lane) {
+    const float Mf = (float)M;
+    dq[lane] = __fdiv_rn((float)(lane - M), Mf);
+    dq[lane + 64] = __fdiv_rn((float)(lane + 64 - M), Mf);
+}
+
+__global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ sym,
+                                                    const uint16_t *__restrict__ scale,
+                                                    uint16_t *__restrict__ out, int L, int T, int C,
+                                                    MaxTable mt, int vec8) {
+    __shared__ float dq_all[4][128];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wv;
+    if (row >= 2LL * L * T) return;
+    int k, l, t;
+    row_coords(row, L, T, k, l, t);
+    float *dq = dq_all[wv];
+    build_dq(dq, mt.m[k][l], lane);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const float m = bf16_to_f32(scale[row]);
+    const uint8_t *src = sym + row * C;
+    uint16_t *dst = out + (((int64_t)l * 2 + k) * T + t) * C;
+    if (vec8) {
+        for (int c0 = lane * 8; c0 < C; c0 += 512) {
+            const uint2 q = *reinterpret_cast<const uint2 *>(src + c0);
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w = e < 2 ? q.x : q.y;
+                const int sh = (e & 1) * 16;
+                const uint32_t a = f32_to_bf16_rne(__fmul_rn(dq[(w >> sh) & 0x7F], m));
+                const uint32_t b = f32_to_bf16_rne(__fmul_rn(dq[(w >> (sh + 8)) & 0x7F], m));
+                o[e] = a | (b << 16);
+            }
+            *reinterpret_cast<uint4 *>(dst + c0) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    } else {
+        for (int c = lane; c < C; c += 64)
+            dst[c] = (uint16_t)f32_to_bf16_rne(__fmul_rn(dq[src[c] & 0x7F], m));
+    }
+}
+
+hipError_t launch_dequantize(const Dims &d, const MaxTable &mt, const uint8_t *sym,
+                             const uint16_t *scale, uint16_t *kv_out, hipStream_t s) {
+    const int64_t rows = 2LL * d.L * d.T;
+    const int vec8 = (d.C % 8 == 0) && ((uintptr_t)sym % 8 == 0) && ((uintptr_t)kv_out % 16 == 0);
+    hipLaunchKernelGGL(k_dequantize, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, sym, scale,
+                       kv_out, d.L, d.T, d.C, mt, vec8);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ blob header
+
+__global__ __launch_bounds__(256) void k_blob_header(uint8_t *__restrict__ blob, HeaderBytes h,
+                                                     BlobLayout lay, uint64_t end_scales,
+                                                     uint64_t end_cdf, uint64_t end_off,
+                                                     uint64_t end_len) {
+    for (uint32_t i = threadIdx.x; i < h.n; i += blockDim.x) blob[i] = h.b[i];
+    // Zero the gaps between the end of each section and the next one.
+    const uint64_t from[4] = {end_scales, end_cdf, end_off, end_len};
+    const uint64_t to[4] = {lay.off_cdf, lay.off_chunk_off, lay.off_lengths, lay.off_payload};
+    for (int g = 0; g < 4; ++g)
+        for (uint64_t i = from[g] + threadIdx.x; i < to[g]; i += blockDim.x) blob[i] = 0;
+}
+
+hipError_t launch_blob_header(uint8_t *blob, const HeaderBytes &h, const BlobLayout &lay,
+                              const Dims &d, hipStream_t s) {
+    const uint64_t end_scales = lay.off_scales + 4ull * d.L * d.T;
+    const uint64_t end_cdf = lay.off_cdf + 4ull * d.L * d.C * d.A;
+    const uint64_t end_off = lay.off_chunk_off + 8ull * (d.NC + 1);
+    const uint64_t end_len = lay.off_lengths + 4ull * d.NC * d.L * d.C;
+    hipLaunchKernelGGL(k_blob_header, dim3(1), dim3(256), 0, s, blob, h, lay, end_scales, end_cdf,
+                       end_off, end_len);
+    return hipGetLastError();
+}
+
+}  // namespace cg

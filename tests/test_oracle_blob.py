@@ -8,38 +8,17 @@ page's pickled encoder output; it is parsed here independently with struct.
 """
 
 import math
-import struct
 
 import numpy as np
 import pytest
 
 import oracle
+from blob_format import parse
 from kv_cache_compression_layer_amd.synth import generate_kv
 
 
 def _parse(blob: bytes):
-    """Independent parse of the blob layout."""
-    magic, ver, dt, L, T, H, D, chunk, NC, A, _res, size = struct.unpack_from("<4sHH8IQ", blob, 0)
-    assert magic == b"CGMX" and ver == 1 and dt == 1 and chunk == 256
-    C = H * D
-    up = lambda x: (x + 63) // 64 * 64
-    bk = np.frombuffer(blob, np.uint8, L, 48)
-    bv = np.frombuffer(blob, np.uint8, L, 48 + L)
-    o_sc = up(48 + 2 * L)
-    o_cdf = o_sc + up(4 * L * T)
-    o_off = o_cdf + up(4 * L * C * A)
-    o_len = o_off + up(8 * (NC + 1))
-    o_pay = o_len + up(2 * NC * 2 * L * C)
-    return dict(
-        L=L, T=T, H=H, D=D, NC=NC, A=A, size=size, bins_k=bk, bins_v=bv,
-        scales=np.frombuffer(blob, "<u2", 2 * L * T, o_sc).reshape(2, L, T),
-        cdf=np.frombuffer(blob, "<u2", 2 * L * C * A, o_cdf).reshape(2, L, C, A),
-        chunk_off=np.frombuffer(blob, "<u8", NC + 1, o_off),
-        lengths=np.frombuffer(blob, "<u2", NC * 2 * L * C, o_len).reshape(NC, 2 * L, C),
-        payload=np.frombuffer(blob, np.uint8, len(blob) - o_pay, o_pay),
-        gaps=[(48 + 2 * L, o_sc), (o_sc + 4 * L * T, o_cdf), (o_cdf + 4 * L * C * A, o_off),
-              (o_off + 8 * (NC + 1), o_len), (o_len + 4 * NC * L * C, o_pay)],
-    )
+    return parse(blob)
 
 
 CASES = [

@@ -70,7 +70,8 @@ BlobLayout blob_layout(const Dims &d) {
 
 // Workspace regions (byte offsets; 0 = unused). Region 0 is the WsHeader.
 struct WsLayout {
-    uint64_t counts = 0, tile_state = 0, overflow = 0, cdf = 0, sym = 0, tile_off = 0;
+    uint64_t counts = 0, tile_sum = 0, tile_off = 0, chunk_total = 0, overflow = 0, staging = 0, cdf = 0,
+             sym = 0;
     uint64_t clear_end = kWsAlign;  // bytes from 0 that must start zeroed
     uint64_t total = kWsAlign;
 };
@@ -89,9 +90,11 @@ WsLayout ws_layout(const Dims &d, int op) {
         w.clear_end = off;
         break;
     case CG_OP_ENCODE:
-        w.tile_state = take(8ull * d.tiles);
-        w.clear_end = off;
+        w.tile_sum = take(4ull * d.tiles);
+        w.tile_off = take(8ull * d.tiles);
+        w.chunk_total = take(8ull * d.NC);
         w.overflow = take(4ull * d.tiles);
+        w.staging = take(encode_staging_bytes(d));
         break;
     case CG_OP_DECODE:
     case CG_OP_FROM_BYTES:
@@ -99,9 +102,12 @@ WsLayout ws_layout(const Dims &d, int op) {
         break;
     case CG_OP_TO_BYTES:
         w.counts = take(4ull * 2 * d.L * d.C * d.A);
-        w.tile_state = take(8ull * d.tiles);
         w.clear_end = off;
+        w.tile_sum = take(4ull * d.tiles);
+        w.tile_off = take(8ull * d.tiles);
+        w.chunk_total = take(8ull * d.NC);
         w.overflow = take(4ull * d.tiles);
+        w.staging = take(encode_staging_bytes(d));
         w.cdf = take(4ull * 2 * d.L * d.C * (d.A + 1));
         w.sym = take((uint64_t)d.N);
         break;
@@ -312,7 +318,8 @@ int cg_encode(const cg_desc *desc, const uint8_t *sym, const int32_t *cdf, uint8
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if ((rc = clear_ws(ws, w, s))) return rc;
     EncodeOut o{payload, (uint64_t)cap, lengths, chunk_off, nullptr, nullptr, 0};
-    EncodeWs ew{at<WsHeader>(ws, 0), at<uint64_t>(ws, w.tile_state), at<uint32_t>(ws, w.overflow)};
+    EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
+                at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging)};
     return hip_rc(launch_encode(d, sym, cdf, o, ew, s));
 }
 
@@ -398,7 +405,8 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
                 blob_size_dev,
                 blob + 40,
                 b.off_payload};
-    EncodeWs ew{at<WsHeader>(ws, 0), at<uint64_t>(ws, w.tile_state), at<uint32_t>(ws, w.overflow)};
+    EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
+                at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging)};
     return hip_rc(launch_encode(d, sym, cdf, o, ew, s));
 }
 

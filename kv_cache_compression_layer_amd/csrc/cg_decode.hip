@@ -11,20 +11,24 @@
 // prefix sum of the lengths before it, and checks that the chunk's lengths
 // add up to the next chunk offset.
 //
-// Pass 2 (k_decode, one wave per tile, lane = stream) copies the tile's
-// bytes (contiguous in the payload) into LDS with the 64 lanes reading
-// consecutive words, stages the 64 tables as start | freq << 16 [symbol][lane]
-// and decodes. The symbol is the largest s with r * cdf[s] <= code, found by
-// a branch-free binary search over the LDS table; comparing r * cdf[s] with
-// code is the same test as cdf[s] <= floor(code / r), so no division is
-// needed. Renormalisation is two predicated steps (the window never needs
-// more). The fused variant multiplies by the per-token scale and writes bf16
-// directly, so the symbols never reach memory.
+// Pass 2 (k_decode): one wave per group of S tiles that share 64 channels
+// (lane = channel) and differ only in the chunk, so each lane decodes S
+// streams of its channel interleaved (independent dependency chains) with
+// one table. The tiles' bytes (contiguous in the payload) are copied into LDS
+// with the 64 lanes reading consecutive words; the tables are staged as
+// start | freq << 16 [symbol][lane]. The symbol is the largest s with
+// r * cdf[s] <= code, found by a branch-free binary search over the whole
+// alphabet (depth fixed at compile time, the S searches interleaved);
+// comparing r * cdf[s] with code is the same test as cdf[s] <= floor(code / r), so no
+// division is needed. Renormalisation is two predicated steps. The fused
+// variant multiplies by the per-token scale and converts to bf16 with the
+// hardware round-to-nearest-even conversion, so the symbols never reach
+// memory.
 #include "cg_internal.hpp"
 
 namespace cg {
 
-constexpr int kStageBytes = 8192;  // LDS bytes for a tile's payload
+constexpr int kStageTile = 2048;  // LDS bytes per staged tile payload (larger tiles read global memory)
 
 // Block-wide exclusive scan of one uint32 per thread (256 threads).
 __device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t *tmp,
@@ -82,79 +86,184 @@ struct DecArgs {
     const uint16_t *scale;
     uint32_t *status;
     MaxTable mt;
-    int L, T, C, A, CB;
+    int L, T, C, A, NC, CB;
 };
 
-template <int LOGA, bool FUSED>
+// One stream's decoder state and byte source.
+struct DecStream {
+    uint32_t code, range;
+    uint32_t ptr, end;    // LDS byte address of the next byte / of the stream's end
+    uint32_t pos, len;    // the same, counted in the stream (unstaged path)
+    const uint8_t *gsrc;  // unstaged source (payload + stream offset)
+};
+
+// The per-token loop of k_decode; STAGED selects where bytes come from.
+template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED>
+__device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S], const int (&n)[S],
+                                            const int (&t0)[S], const uint32_t *tab, const float *dq,
+                                            const float *sc, const uint8_t *stage, int lane, bool active,
+                                            int slab, int kv, int l, int cb, bool &corrupt) {
+    // Next byte of a stream; bytes past its length read as zero (the staged
+    // path reads the zero byte kept after the stage instead).
+    const uint32_t zero_at = S * kStageTile;
+    auto next_byte = [&](DecStream &d) -> uint32_t {
+        uint32_t b;
+        if (STAGED) {
+            b = stage[d.ptr < d.end ? d.ptr : zero_at];
+            ++d.ptr;
+        } else {
+            b = d.pos < d.len ? (uint32_t)d.gsrc[d.pos] : 0u;
+            ++d.pos;
+        }
+        return b;
+    };
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        for (int i = 0; i < 4; ++i) st[s].code = (st[s].code << 8) | next_byte(st[s]);
+
+    // Byte address in tab of (symbol s, this lane) is s * 256 + lane * 4.
+    const uint8_t *tabb = reinterpret_cast<const uint8_t *>(tab);
+    const uint32_t lane4 = (uint32_t)lane * 4;
+    const uint32_t amax4 = ((uint32_t)a.A - 1) * 256 + lane4;
+    const int lane_c = active ? lane : 0;
+    const int nmax = n[0];
+    for (int t = 0; t < nmax; ++t) {
+        uint32_t r[S], ad[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            r[s] = st[s].range >> 16;
+            ad[s] = lane4;
+        }
+        // Interleaved branch-free binary searches over the whole alphabet,
+        // carrying the LDS address of the current symbol's entry.
+#pragma unroll
+        for (int i = LOGA - 1; i >= 0; --i) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                uint32_t cand = ad[s] + (256u << i);
+                if (CLAMP) cand = min(cand, amax4);
+                const uint32_t ec = *reinterpret_cast<const uint32_t *>(tabb + cand);
+                ad[s] = __umul24(r[s], ec & 0xFFFFu) <= st[s].code ? cand : ad[s];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            // Every stream steps every token (a finished stream keeps decoding
+            // zeros); only its output and its checks are guarded.
+            DecStream &d = st[s];
+            const bool live = t < n[s];
+            const uint32_t e = *reinterpret_cast<const uint32_t *>(tabb + ad[s]);
+            const uint32_t sy = (ad[s] - lane4) >> 8;
+            d.code -= __umul24(r[s], e & 0xFFFFu);
+            d.range = __umul24(r[s], e >> 16);
+            if (d.range < kTop) {
+                d.code = (d.code << 8) | next_byte(d);
+                d.range <<= 8;
+                if (d.range < kTop) {
+                    d.code = (d.code << 8) | next_byte(d);
+                    d.range <<= 8;
+                }
+            }
+            corrupt |= live && d.code >= d.range;
+            if (live) {
+                // Row t of this stream: a wave-uniform base plus the lane.
+                if (FUSED) {
+                    const float x = __fmul_rn(dq[sy], sc[s * kChunk + t]);
+                    const __hip_bfloat16 h = __float2bfloat16(x);
+                    uint16_t *row = a.kv + (((int64_t)l * 2 + kv) * a.T + t0[s] + t) * a.C + cb * 64;
+                    if (active) row[lane_c] = *reinterpret_cast<const uint16_t *>(&h);
+                } else {
+                    uint8_t *row = a.sym + ((int64_t)slab * a.T + t0[s] + t) * a.C + cb * 64;
+                    if (active) row[lane_c] = (uint8_t)sy;
+                }
+            }
+        }
+    }
+}
+
+template <int S, bool FUSED, int LOGA, bool CLAMP>
 __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
-    extern __shared__ uint32_t smem[];
+    // Static LDS sized by the template, so every address folds to an immediate.
+    __shared__ float dq[128];
+    __shared__ uint32_t tab[(1 << LOGA) * 64];          // [symbol][lane]
+    __shared__ __attribute__((aligned(16))) uint8_t stage[S * kStageTile + 8];  // tiles' bytes, then 8 zeros
+    __shared__ float sc[FUSED ? S * kChunk : 1];        // per-token scales
     const int lane = threadIdx.x;
     const int A = a.A;
-    uint32_t *tab = smem;                                            // [A][64]
-    uint32_t *bytes_w = tab + A * 64;                                // kStageBytes/4 words
-    float *sc = reinterpret_cast<float *>(bytes_w + kStageBytes / 4);  // [256]
-    float *dq = sc + kChunk;                                          // [128]
-    const uint8_t *bytes = reinterpret_cast<const uint8_t *>(bytes_w);
 
-    const int64_t tile = blockIdx.x;
-    const int64_t per_chunk = 2LL * a.L * a.CB;
-    const int j = (int)(tile / per_chunk);
-    const int rem = (int)(tile - (int64_t)j * per_chunk);
-    const int slab = rem / a.CB, cb = rem - slab * a.CB;
+    const int bid = blockIdx.x;
+    const int cb = bid % a.CB;
+    const int slab = (bid / a.CB) % (2 * a.L);
+    const int g = bid / (a.CB * 2 * a.L);
     const int kv = slab / a.L, l = slab - kv * a.L;
     const int c = cb * 64 + lane;
     const bool active = c < a.C;
-    const int t0 = j * kChunk;
-    const int n = min(kChunk, a.T - t0);
+    const int M = a.mt.m[kv][l];
 
-    uint32_t len = active ? a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] : 0u;
-    const uint32_t incl = wave_incl_scan_u32(len, lane);
-    uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
-    uint32_t excl = incl - len;
-    const uint64_t base = a.tile_off[tile];
-    bool corrupt = false;
-    if (base > a.payload_bytes || total > a.payload_bytes - base) {
-        corrupt = true;  // offsets point outside the payload: decode from nothing
-        len = 0;
-        excl = 0;
-        total = 0;
-    }
-
-    // Stage the tile's bytes: words from the aligned start, bounded by the payload.
-    const bool staged = total <= (uint32_t)(kStageBytes - 8);
-    const uint64_t abase = base & ~3ull;
-    const uint32_t head = (uint32_t)(base - abase);
-    if (staged && total) {
-        const uint32_t nw = (head + total + 3) >> 2;
-        for (uint32_t w = lane; w < nw; w += 64) {
-            const uint64_t g = abase + 4ull * w;
-            uint32_t v;
-            if (g + 4 <= a.payload_bytes) {
-                v = *reinterpret_cast<const uint32_t *>(a.payload + g);
-            } else {
-                v = 0;
-                for (int i = 0; i < 4; ++i)
-                    if (g + i < a.payload_bytes) v |= (uint32_t)a.payload[g + i] << (8 * i);
+    int n[S], t0[S];
+    DecStream st[S];
+    bool corrupt = false, all_staged = true;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int j = g * S + s;
+        n[s] = j < a.NC ? min(kChunk, a.T - j * kChunk) : 0;
+        t0[s] = min(j, a.NC - 1) * kChunk;
+        uint32_t len = 0, excl = 0, total = 0;
+        uint64_t base = 0;
+        if (n[s]) {
+            len = active ? a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] : 0u;
+            const uint32_t incl = wave_incl_scan_u32(len, lane);
+            total = (uint32_t)__shfl((int)incl, 63, 64);
+            excl = incl - len;
+            base = a.tile_off[((int64_t)j * 2 * a.L + slab) * a.CB + cb];
+            if (base > a.payload_bytes || total > a.payload_bytes - base) {
+                corrupt = true;  // offsets point outside the payload: decode from nothing
+                len = excl = total = 0;
+                base = 0;
             }
-            bytes_w[w] = v;
         }
+        // Stage the tile's bytes: words from the aligned start, bounded by the payload.
+        const uint64_t abase = base & ~3ull;
+        const uint32_t head = (uint32_t)(base - abase);
+        const bool staged = total + head <= (uint32_t)kStageTile;
+        all_staged &= staged;
+        if (staged && total) {
+            uint32_t *w = reinterpret_cast<uint32_t *>(stage + s * kStageTile);
+            const uint32_t nw = (head + total + 3) >> 2;
+            for (uint32_t i = lane; i < nw; i += 64) {
+                const uint64_t gaddr = abase + 4ull * i;
+                uint32_t v;
+                if (gaddr + 4 <= a.payload_bytes) {
+                    v = *reinterpret_cast<const uint32_t *>(a.payload + gaddr);
+                } else {
+                    v = 0;
+                    for (int k = 0; k < 4; ++k)
+                        if (gaddr + k < a.payload_bytes) v |= (uint32_t)a.payload[gaddr + k] << (8 * k);
+                }
+                w[i] = v;
+            }
+        }
+        st[s].len = len;
+        st[s].pos = 0;
+        st[s].ptr = s * kStageTile + head + excl;
+        st[s].end = st[s].ptr + len;
+        st[s].gsrc = a.payload + base + excl;
+        st[s].range = 0xFFFFFFFFu;
+        st[s].code = 0;
     }
 
     // Tables.
     bool bad_table = false;
     if (active) {
         const int64_t row = (int64_t)slab * a.C + c;
-        uint32_t prev = 0;
+        uint32_t prev = a.cdf32 ? (uint32_t)a.cdf32[row * (A + 1)] : (uint32_t)a.cdf16[row * A];
+        bad_table = prev != 0;
         for (int s = 0; s < A; ++s) {
             uint32_t nxt;
-            if (a.cdf32) {
-                if (s == 0) prev = (uint32_t)a.cdf32[row * (A + 1)];
+            if (a.cdf32)
                 nxt = (uint32_t)a.cdf32[row * (A + 1) + s + 1];
-            } else {
-                if (s == 0) prev = a.cdf16[row * A];
+            else
                 nxt = s + 1 < A ? (uint32_t)a.cdf16[row * A + s + 1] : kProbOne;
-            }
-            if (s == 0) bad_table |= prev != 0;
             uint32_t f = nxt - prev;
             if (nxt <= prev || nxt > kProbOne) {
                 bad_table = true;
@@ -170,72 +279,49 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
         tab[lane] = 0xFFFFu << 16;
         for (int s = 1; s < A; ++s) tab[s * 64 + lane] = (uint32_t)s | (1u << 16);
     }
+    if (lane < 8) stage[S * kStageTile + lane] = 0;  // the byte read past every stream
     if (FUSED) {
-        const uint16_t *sp = a.scale + (int64_t)slab * a.T + t0;
-        for (int t = lane; t < n; t += 64) sc[t] = bf16_to_f32(sp[t]);
-        const int M = a.mt.m[kv][l];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const uint16_t *sp = a.scale + (int64_t)slab * a.T + t0[s];
+            for (int t = lane; t < n[s]; t += 64) sc[s * kChunk + t] = bf16_to_f32(sp[t]);
+        }
         dq[lane] = __fdiv_rn((float)(lane - M), (float)M);
         dq[lane + 64] = __fdiv_rn((float)(lane + 64 - M), (float)M);
     }
     __syncthreads();
 
-    const uint8_t *gsrc = a.payload + base + excl;  // unstaged path
-    const uint32_t loff = head + excl;
-    uint32_t pos = 0;
-    auto next_byte = [&]() -> uint32_t {
-        uint32_t b = 0;
-        if (pos < len) b = staged ? (uint32_t)bytes[loff + pos] : (uint32_t)gsrc[pos];
-        ++pos;
-        return b;
-    };
-    uint32_t code = 0;
-    for (int i = 0; i < 4; ++i) code = (code << 8) | next_byte();
-    uint32_t range = 0xFFFFFFFFu;
-
-    uint8_t *sym_out = FUSED ? nullptr : a.sym + ((int64_t)slab * a.T + t0) * a.C + c;
-    uint16_t *kv_out = FUSED ? a.kv + (((int64_t)l * 2 + kv) * a.T + t0) * a.C + c : nullptr;
-    for (int t = 0; t < n; ++t) {
-        const uint32_t r = range >> 16;
-        uint32_t s = 0;
-#pragma unroll
-        for (int step = 1 << (LOGA - 1); step > 0; step >>= 1) {
-            const uint32_t cand = s + step;
-            if (cand < (uint32_t)A) {
-                const uint32_t st = tab[cand * 64 + lane] & 0xFFFFu;
-                if (__umul24(r, st) <= code) s = cand;
-            }
-        }
-        const uint32_t e = tab[s * 64 + lane];
-        code -= __umul24(r, e & 0xFFFFu);
-        range = __umul24(r, e >> 16);
-        if (range < kTop) {
-            code = (code << 8) | next_byte();
-            range <<= 8;
-            if (range < kTop) {
-                code = (code << 8) | next_byte();
-                range <<= 8;
-            }
-        }
-        corrupt |= code >= range;
-        if (active) {
-            if (FUSED) {
-                kv_out[(int64_t)t * a.C] = (uint16_t)f32_to_bf16_rne(__fmul_rn(dq[s & 0x7F], sc[t]));
-            } else {
-                sym_out[(int64_t)t * a.C] = (uint8_t)s;
-            }
-        }
-    }
+    const bool staged_wave = __ballot(!all_staged) == 0;  // wave-uniform
+    if (staged_wave)
+        decode_loop<S, FUSED, LOGA, CLAMP, true>(a, st, n, t0, tab, dq, sc, stage, lane, active, slab, kv, l,
+                                                cb, corrupt);
+    else
+        decode_loop<S, FUSED, LOGA, CLAMP, false>(a, st, n, t0, tab, dq, sc, stage, lane, active, slab, kv, l,
+                                                 cb, corrupt);
     if (__ballot(active && (corrupt || bad_table)) && lane == 0) atomicOr(a.status, kStCorrupt);
 }
 
-template <int LOGA>
-static hipError_t launch_decode_t(const Dims &d, const DecArgs &a, bool fused, hipStream_t s) {
-    const size_t lds = (size_t)d.A * 64 * 4 + kStageBytes + kChunk * 4 + 128 * 4;
-    if (fused)
-        hipLaunchKernelGGL((k_decode<LOGA, true>), dim3((unsigned)d.tiles), dim3(64), lds, s, a);
+template <int S, bool FUSED, int LOGA>
+static hipError_t launch_decode_s(const Dims &d, const DecArgs &a, hipStream_t s) {
+    static_assert(kStageTile % 4 == 0, "stage holds whole words");
+    const size_t lds = 0;  // all LDS is static
+    const int ngroups = (d.NC + S - 1) / S;
+    const dim3 grid((unsigned)((int64_t)ngroups * 2 * d.L * d.CB));
+    if (d.A == (1 << LOGA))
+        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, false>), grid, dim3(64), lds, s, a);
     else
-        hipLaunchKernelGGL((k_decode<LOGA, false>), dim3((unsigned)d.tiles), dim3(64), lds, s, a);
+        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, true>), grid, dim3(64), lds, s, a);
     return hipGetLastError();
+}
+
+template <int S, bool FUSED>
+static hipError_t launch_decode_f(const Dims &d, const DecArgs &a, hipStream_t s) {
+    if (d.A <= 4) return launch_decode_s<S, FUSED, 2>(d, a, s);
+    if (d.A <= 8) return launch_decode_s<S, FUSED, 3>(d, a, s);
+    if (d.A <= 16) return launch_decode_s<S, FUSED, 4>(d, a, s);
+    if (d.A <= 32) return launch_decode_s<S, FUSED, 5>(d, a, s);
+    if (d.A <= 64) return launch_decode_s<S, FUSED, 6>(d, a, s);
+    return launch_decode_s<S, FUSED, 7>(d, a, s);
 }
 
 hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, const DecodeOut &out,
@@ -260,11 +346,11 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     a.T = d.T;
     a.C = d.C;
     a.A = d.A;
+    a.NC = d.NC;
     a.CB = d.CB;
     const bool fused = out.kv != nullptr;
-    if (d.A <= 32) return launch_decode_t<5>(d, a, fused, s);
-    if (d.A <= 64) return launch_decode_t<6>(d, a, fused, s);
-    return launch_decode_t<7>(d, a, fused, s);
+    if (d.NC >= 2) return fused ? launch_decode_f<2, true>(d, a, s) : launch_decode_f<2, false>(d, a, s);
+    return fused ? launch_decode_f<1, true>(d, a, s) : launch_decode_f<1, false>(d, a, s);
 }
 
 }  // namespace cg

@@ -11,32 +11,44 @@
 //   finish with the smallest multiple of 2^24 that is >= low (one byte, or
 //   none if that byte is zero or the value carries into the bytes before).
 //
-// A carry out of the 32-bit window must reach the bytes already emitted. The
-// device coder never rewrites emitted bytes: it holds back the last byte and
-// the run of 0xFF bytes after it (Subbotin/Pavlov "cache + pending" form of
-// the byte range coder) and releases them once no carry can reach them. The
-// bytes produced are identical to rewriting them on a carry.
+// Three kernels:
 //
-// Work decomposition: one wave per tile of 64 streams = 64 consecutive
-// channels of one (chunk, K|V, layer); lane = stream. The tile's symbols
-// (<= 256 tokens x 64 channels) and its 64 tables (packed as
-// start | freq << 16, laid out [symbol][lane] so lookups never conflict on
-// LDS banks) are staged in LDS. Output bytes are accumulated four at a time
-// in a register and stored to LDS words [word][lane], up to kStageWords per
-// lane; longer streams are finished by a fix-up kernel.
+// k_encode: one wave per tile = 64 consecutive channels (lane = channel) of
+// one (K|V, layer) and S consecutive 256-token chunks; each lane codes the S
+// streams of its channel interleaved (independent dependency chains), with
+// one table per lane staged in LDS as start | freq << 16 laid out
+// [symbol][lane] (no bank conflicts whatever the symbols); the table is the
+// only LDS the kernel uses, which keeps many waves resident. Symbols come
+// straight from global memory (64 lanes read one 64-byte row per load) into
+// a 16-deep register ring, so the loop never waits on them. Finished bytes
+// go straight to the tile's staging slot in global memory as [byte][lane]
+// rows; the last byte and the run of 0xFF bytes after it are held back in
+// registers until no carry can reach them (the classic "cache + pending"
+// form of the byte range coder), so nothing is ever rewritten. The kernel
+// writes the stream lengths and the tile's byte total. Streams longer than
+// the slot (kStageBytes) mark the tile for k_fixup.
 //
-// Streams are concatenated in stream order. The wave scans its 64 lengths,
-// then finds the byte offset of the tile with a decoupled look-back over the
-// tiles before it (Merrill & Garland, "Single-pass Parallel Prefix Scan with
-// Decoupled Look-back", 2016); tiles take their ids from an atomic counter so
-// every tile a wave waits on belongs to a wave that is already running.
+// k_tile_scan + k_chunk_scan: exclusive scan of the tile totals in stream
+// order (per chunk, then over the chunk totals) -> tile offsets, chunk
+// offsets and the payload size.
+//
+// k_compact: one wave per tile copies its streams from the staging slot to
+// their final offsets; each lane writes consecutive payload bytes (64 bytes
+// per store instruction), finding its source stream by a search over the
+// scanned lengths.
+//
+// k_fixup: re-encodes every stream of a marked tile straight to its final
+// offset with the same held-back-byte coder.
 #include "cg_internal.hpp"
 
 namespace cg {
 
-constexpr int kStageWords = 32;  // 128 bytes of staged output per stream
+constexpr int kStageBytes = 256;  // staging slot bytes per stream (5 bits/symbol fit)
+constexpr int kRing = 16;         // symbol prefetch depth
 
-struct RcEnc {
+// ----------------------------------------------------------- fix-up coder
+
+struct RcEncHold {
     uint32_t low, range, carry, cache, nff;
     bool first;  // the held-back byte is still the leading placeholder
 
@@ -72,21 +84,15 @@ struct RcEnc {
         carry |= (uint32_t)(nl < low);
         low = nl;
         range = __umul24(r, freq);
-        // range >= 2^8 here (r >= 2^8, freq >= 1), so two shifts restore it.
-        if (range < kTop) {
+        while (range < kTop) {
             shift(out);
             range <<= 8;
-            if (range < kTop) {
-                shift(out);
-                range <<= 8;
-            }
         }
     }
 
     template <class Sink>
     __device__ __forceinline__ void flush(Sink &out) {
-        const uint64_t u = (uint64_t)low + 0xFFFFFFull;
-        uint32_t b = (uint32_t)(u >> 24);  // ceil(low / 2^24), 0..256
+        uint32_t b = (low >> 24) + ((low & 0xFFFFFFu) != 0);  // ceil(low / 2^24), 0..256
         uint32_t cc = carry;
         if (b == 256u) {  // the final value carries into the held-back bytes
             cc += 1;
@@ -99,30 +105,6 @@ struct RcEnc {
     }
 };
 
-// Byte sink into LDS words [word][lane]; bytes beyond the stage are counted
-// but dropped (the stream is then re-encoded by the fix-up kernel).
-struct LdsSink {
-    uint32_t *stage;
-    int lane;
-    uint32_t acc, n;
-    __device__ __forceinline__ void put(uint32_t b) {
-        acc = (acc >> 8) | (b << 24);  // little-endian: first byte ends in bits 0..7
-        ++n;
-        if ((n & 3u) == 0) {
-            const uint32_t w = (n >> 2) - 1;
-            if (w < (uint32_t)kStageWords) stage[w * 64 + lane] = acc;
-        }
-    }
-    __device__ __forceinline__ void finish() {
-        const uint32_t k = n & 3u;
-        if (k) {
-            const uint32_t w = n >> 2;
-            if (w < (uint32_t)kStageWords) stage[w * 64 + lane] = acc >> (8 * (4 - k));
-        }
-    }
-};
-
-// Byte sink straight to global memory, bounded by cap.
 struct GlobalSink {
     uint8_t *base;
     uint64_t off, cap;
@@ -135,242 +117,393 @@ struct GlobalSink {
     }
 };
 
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o, 64);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o, 64);
-        v += ((uint64_t)hi << 32) | lo;
-    }
-    return v;
-}
-
-constexpr uint64_t kFlagAgg = 1ull << 62;
-constexpr uint64_t kFlagIncl = 2ull << 62;
-constexpr uint64_t kValMask = (1ull << 62) - 1;
-
-// Exclusive byte offset of `tile` in stream order. Publishes the tile's
-// aggregate first, then its inclusive prefix.
-__device__ uint64_t lookback(uint64_t *state, int64_t tile, uint64_t total, int lane) {
-    if (tile == 0) {
-        if (lane == 0)
-            __hip_atomic_store(&state[0], kFlagIncl | total, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        return 0;
-    }
-    if (lane == 0)
-        __hip_atomic_store(&state[tile], kFlagAgg | total, __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    uint64_t excl = 0;
-    int64_t idx = tile - 1;
-    for (;;) {
-        const int64_t my = idx - lane;
-        const uint64_t v = my >= 0 ? __hip_atomic_load(&state[my], __ATOMIC_ACQUIRE,
-                                                       __HIP_MEMORY_SCOPE_AGENT)
-                                   : kFlagIncl;  // before tile 0: inclusive prefix 0
-        const uint32_t flag = (uint32_t)(v >> 62);
-        const uint64_t incl = __ballot(flag == 2);
-        const uint64_t none = __ballot(flag == 0);
-        const int first_incl = incl ? __ffsll((unsigned long long)incl) - 1 : 64;
-        const uint64_t need = first_incl >= 63 ? ~0ull : ((2ull << first_incl) - 1);
-        if (none & need) {  // a predecessor has not published yet
-            __builtin_amdgcn_s_sleep(1);
-            continue;
-        }
-        excl += wave_sum_u64(lane <= first_incl ? (v & kValMask) : 0);
-        if (first_incl < 64) break;
-        idx -= 64;
-    }
-    if (lane == 0)
-        __hip_atomic_store(&state[tile], kFlagIncl | (excl + total), __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    return excl;
-}
+// ------------------------------------------------------------ main coder
 
 struct EncArgs {
     const uint8_t *sym;
     const int32_t *cdf;
-    uint8_t *payload;          // start of the payload
-    uint64_t cap;
-    uint16_t *lengths;
-    uint64_t *chunk_off;
-    uint64_t *size_dev;
-    uint8_t *header_size;
-    uint64_t payload_base;
+    uint8_t *staging;          // [tiles][kStageBytes][64] bytes
+    uint32_t *tile_sum;        // [tiles]
+    uint16_t *lengths;         // [NC, 2L, C]
     WsHeader *hdr;
-    uint64_t *tile_state;
-    uint32_t *overflow_list;
+    uint32_t *overflow_list;   // [tiles]
     int L, T, C, A, NC, CB;
-    int64_t tiles;
-    int vec16;                 // symbol rows can be staged with 16-byte loads
 };
 
-__device__ __forceinline__ void tile_coords(int64_t tile, int L, int CB, int &j, int &slab,
-                                            int &cb) {
-    const int64_t per_chunk = 2LL * L * CB;
-    j = (int)(tile / per_chunk);
-    const int64_t rem = tile - (int64_t)j * per_chunk;
-    slab = (int)(rem / CB);
-    cb = (int)(rem - (int64_t)slab * CB);
+// Tile = (chunk j, slab = kv*L + l, 64-channel block cb); tile index in
+// stream order: (j * 2L + slab) * CB + cb.
+__device__ __forceinline__ int64_t tile_index(int j, int slab, int cb, int L, int CB) {
+    return ((int64_t)j * 2 * L + slab) * CB + cb;
 }
 
-// Packed table entry of symbol s: start | freq << 16 (start <= 65535 and
-// freq <= 65536 - A + 1 both fit in 16 bits).
-__device__ __forceinline__ uint32_t packed_entry(const int32_t *tab, int s) {
-    const uint32_t a = (uint32_t)tab[s], b = (uint32_t)tab[s + 1];
-    return (a & 0xFFFFu) | ((b - a) << 16);
-}
+// Range coder that writes finished bytes straight to the tile's staging
+// slot ([byte][lane], 64-byte rows). The last byte and the run of 0xFF bytes
+// after it are held back in registers until no carry can reach them, so no
+// byte is ever rewritten. pos starts at -1: the first byte released is the
+// placeholder in front of the stream and is dropped.
+struct Coder {
+    uint32_t low, range, carry, cache, nff;
+    int pos;
+    __device__ __forceinline__ void init() {
+        low = 0;
+        range = 0xFFFFFFFFu;
+        carry = 0;
+        cache = 0;
+        nff = 0;
+        pos = -1;
+    }
+    __device__ __forceinline__ void put(uint8_t *slot, int lane, uint32_t b) {
+        if ((uint32_t)pos < (uint32_t)kStageBytes) slot[pos * 64 + lane] = (uint8_t)b;
+        ++pos;
+    }
+    __device__ __forceinline__ void shift(uint8_t *slot, int lane) {
+        const uint32_t top = low >> 24;
+        if (top != 0xFFu || carry) {
+            put(slot, lane, cache + carry);
+            if (nff) {
+                const uint32_t ff = (0xFFu + carry) & 0xFFu;
+                for (; nff; --nff) put(slot, lane, ff);
+            }
+            cache = top;
+            carry = 0;
+        } else {
+            ++nff;
+        }
+        low <<= 8;
+    }
+    __device__ __forceinline__ void step(uint32_t e, uint8_t *slot, int lane) {
+        const uint32_t r = range >> 16;
+        const uint32_t nl = low + __umul24(r, e & 0xFFFFu);
+        carry += (uint32_t)(nl < low);  // at most one wrap between two shifts
+        low = nl;
+        range = __umul24(r, e >> 16);
+        // range >= 2^8 here (r >= 2^8, freq >= 1), so two shifts restore it.
+        if (range < kTop) {
+            shift(slot, lane);
+            range <<= 8;
+            if (range < kTop) {
+                shift(slot, lane);
+                range <<= 8;
+            }
+        }
+    }
+    // Final value: the smallest multiple of 2^24 >= low; returns the length.
+    __device__ __forceinline__ uint32_t flush(uint8_t *slot, int lane) {
+        uint32_t b = (low >> 24) + ((low & 0xFFFFFFu) != 0);  // 0..256
+        uint32_t cc = carry;
+        if (b == 256u) {
+            cc += 1;
+            b = 0;
+        }
+        put(slot, lane, (cache + cc) & 0xFFu);
+        const uint32_t ff = (0xFFu + cc) & 0xFFu;
+        for (; nff; --nff) put(slot, lane, ff);
+        if (b) put(slot, lane, b);
+        return (uint32_t)pos;
+    }
+};
 
+template <int S, int LOGA>
 __global__ __launch_bounds__(64) void k_encode(EncArgs a) {
-    extern __shared__ uint32_t smem[];
+    __shared__ uint32_t tab[(1 << LOGA) * 64];  // [symbol][lane]; the kernel's only LDS
     const int lane = threadIdx.x;
     const int A = a.A;
-    uint32_t *tab = smem;                                   // [A][64]
-    uint8_t *symt = reinterpret_cast<uint8_t *>(tab + A * 64);  // [256][64]
-    uint32_t *stage = reinterpret_cast<uint32_t *>(symt + kChunk * 64);  // [kStageWords][64]
 
-    int64_t tile = 0;
-    if (lane == 0) tile = atomicAdd(&a.hdr->tile_counter, 1u);
-    tile = __shfl((int)tile, 0, 64);
-    int j, slab, cb;
-    tile_coords(tile, a.L, a.CB, j, slab, cb);
+    // Block -> (chunk group g, slab, cb); all wave-uniform.
+    const int bid = blockIdx.x;
+    const int cb = bid % a.CB;
+    const int slab = (bid / a.CB) % (2 * a.L);
+    const int g = bid / (a.CB * 2 * a.L);
     const int c = cb * 64 + lane;
     const bool active = c < a.C;
-    const int t0 = j * kChunk;
-    const int n = min(kChunk, a.T - t0);
+    const int lane_off = active ? lane : (a.C - 1 - cb * 64);  // in-bounds column for idle lanes
 
-    // Tables: one per lane, packed, [symbol][lane].
-    bool bad_table = false;
-    if (active) {
-        const int32_t *src = a.cdf + ((int64_t)slab * a.C + c) * (A + 1);
-        bad_table = src[0] != 0 || src[A] != (int32_t)kProbOne;
-        for (int s = 0; s < A; ++s) {
-            const uint32_t e = packed_entry(src, s);
-            bad_table |= (e >> 16) == 0;
-            tab[s * 64 + lane] = (e >> 16) ? e : (e | (1u << 16));
+    // Row r of stream s is at rowbase[s] + r * C (uniform), plus lane_off.
+    int n[S];
+    const uint8_t *rowbase[S];
+    uint8_t *slot[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int j = g * S + s;
+        n[s] = j < a.NC ? min(kChunk, a.T - j * kChunk) : 0;
+        rowbase[s] = a.sym + ((int64_t)slab * a.T + (int64_t)min(j, a.NC - 1) * kChunk) * a.C + cb * 64;
+        slot[s] = a.staging + tile_index(min(j, a.NC - 1), slab, cb, a.L, a.CB) * (kStageBytes * 64);
+    }
+    const int nmax = n[0];  // the first chunk of a group is never the short one
+
+    // Prefetch ring: symbol of token t of stream s sits in ring[s][t % kRing]
+    // from kRing tokens before it is coded. Loads are unconditional (rows are
+    // clamped into the stream) so their waits are exact.
+    uint32_t ring[S][kRing];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int last = max(n[s] - 1, 0);
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) {
+            const uint8_t *rowp = rowbase[s] + (int64_t)min(k, last) * a.C;
+            ring[s][k] = rowp[lane_off];
         }
-    } else {
-        // Idle lanes code symbol 0 with frequency 65535: they never shift a
-        // byte out, so they do not force the wave through the slow path.
-        for (int s = 0; s < A; ++s) tab[s * 64 + lane] = 0xFFFFu << 16;
     }
 
-    // Symbols of the tile: rows t0..t0+n-1, channels cb*64..cb*64+63.
-    const uint8_t *sbase = a.sym + ((int64_t)slab * a.T + t0) * a.C + cb * 64;
-    if (a.vec16 && cb * 64 + 64 <= a.C) {
-        // 4 lanes per 64-byte row, 16 rows per instruction.
-        const int r = lane >> 2, part = lane & 3;
-        for (int t = r; t < n; t += 16)
-            *reinterpret_cast<uint4 *>(symt + t * 64 + part * 16) =
-                *reinterpret_cast<const uint4 *>(sbase + (int64_t)t * a.C + part * 16);
+    // Tables: one per lane, packed, [symbol][lane].
+    bool bad = false;
+    if (active) {
+        const int32_t *src = a.cdf + ((int64_t)slab * a.C + c) * (A + 1);
+        uint32_t prev = (uint32_t)src[0];
+        bad = prev != 0 || (uint32_t)src[A] != kProbOne;
+        for (int s = 0; s < A; ++s) {
+            const uint32_t nxt = (uint32_t)src[s + 1];
+            uint32_t f = nxt - prev;
+            if (nxt <= prev || nxt > kProbOne) {
+                bad = true;
+                f = 1;
+            }
+            tab[s * 64 + lane] = (prev & 0xFFFFu) | (f << 16);
+            prev = nxt;
+        }
     } else {
-        for (int t = 0; t < n; ++t) symt[t * 64 + lane] = active ? sbase[(int64_t)t * a.C + lane] : 0;
+        // Idle lanes code with frequency 65535 whatever their symbol: they
+        // never shift a byte out, so they do not force the wave through the
+        // slow path.
+        for (int s = 0; s < A; ++s) tab[s * 64 + lane] = 0xFFFFu << 16;
     }
     __syncthreads();
 
-    RcEnc enc;
-    enc.init();
-    LdsSink sink{stage, lane, 0u, 0u};
-    uint32_t bad_sym = 0;
-    for (int t = 0; t < n; ++t) {
-        uint32_t s = symt[t * 64 + lane];
-        bad_sym |= s >= (uint32_t)A;
-        s = min(s, (uint32_t)A - 1);
-        const uint32_t e = tab[s * 64 + lane];
-        enc.encode(e & 0xFFFFu, e >> 16, sink);
+    Coder cd[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) cd[s].init();
+    const uint32_t amax = (uint32_t)A - 1;
+    uint32_t qmax = 0;
+    // Table entry of the next token of every stream, read one step ahead.
+    uint32_t e_next[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        qmax = max(qmax, ring[s][0]);
+        e_next[s] = tab[min(ring[s][0], amax) * 64 + lane];
     }
-    enc.flush(sink);
-    sink.finish();
-    const uint32_t len = active ? sink.n : 0u;
-    if (__ballot((active && (bad_sym || bad_table))) && lane == 0) atomicOr(&a.hdr->status, kStCorrupt);
-
-    if (active) a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] = (uint16_t)len;
-    const uint32_t incl = wave_incl_scan_u32(len, lane);
-    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
-    const uint32_t excl = incl - len;
-    const uint64_t prefix = lookback(a.tile_state, tile, total, lane);
-
-    // Copy the staged bytes of each lane to its place in the payload.
-    const bool spilled = len > (uint32_t)(kStageWords * 4);
-    const uint64_t dst = prefix + excl;
-    bool over_cap = false;
-    if (!spilled) {
-        uint32_t w = 0;
-        for (uint32_t b = 0; b < len; ++b) {
-            if ((b & 3u) == 0) w = stage[(b >> 2) * 64 + lane];
-            if (dst + b < a.cap) a.payload[dst + b] = (uint8_t)(w >> (8 * (b & 3u)));
-            else over_cap = true;
+    for (int t0 = 0; t0 < nmax; t0 += kRing) {
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) {
+            const int t = t0 + k;
+            uint32_t e[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                e[s] = e_next[s];
+                // Refill the slot just consumed with token t + kRing.
+                const int last = max(n[s] - 1, 0);
+                const uint8_t *rowp = rowbase[s] + (int64_t)min(t + kRing, last) * a.C;
+                ring[s][k] = rowp[lane_off];
+                // Entry of token t + 1 (its symbol has been in the ring for a while).
+                const uint32_t q = ring[s][(k + 1) % kRing];
+                qmax = max(qmax, q);
+                e_next[s] = tab[min(q, amax) * 64 + lane];
+            }
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                if (t < n[s]) cd[s].step(e[s], slot[s], lane);
         }
     }
-    if (__ballot(spilled) && lane == 0) {
-        const uint32_t slot = atomicAdd(&a.hdr->overflow_count, 1u);
-        a.overflow_list[slot] = (uint32_t)tile;
-    }
-    if (__ballot(over_cap) && lane == 0) atomicOr(&a.hdr->status, kStCapacity);
 
-    if (lane == 0) {
-        if (slab == 0 && cb == 0) a.chunk_off[j] = prefix;
-        if (tile == a.tiles - 1) {
-            const uint64_t end = prefix + total;
-            a.chunk_off[a.NC] = end;
-            a.hdr->payload_total = end;
-            if (end > a.cap) atomicOr(&a.hdr->status, kStCapacity);
-            const uint64_t size = a.payload_base + end;
-            if (a.size_dev) *a.size_dev = size;
-            if (a.header_size)
-                for (int i = 0; i < 8; ++i) a.header_size[i] = (uint8_t)(size >> (8 * i));
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        if (n[s] == 0) continue;
+        const uint32_t len0 = cd[s].flush(slot[s], lane);
+        const uint32_t len = active ? len0 : 0u;
+        const int j = g * S + s;
+        if (active) a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] = (uint16_t)len;
+        uint32_t sum = len;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sum += (uint32_t)__shfl_xor((int)sum, o, 64);
+        const int64_t tile = tile_index(j, slab, cb, a.L, a.CB);
+        if (lane == 0) a.tile_sum[tile] = sum;
+        if (__ballot(len > (uint32_t)kStageBytes) && lane == 0)
+            a.overflow_list[atomicAdd(&a.hdr->overflow_count, 1u)] = (uint32_t)tile;
+    }
+    if (__ballot((active && (qmax > amax || bad))) && lane == 0) atomicOr(&a.hdr->status, kStCorrupt);
+}
+
+// ------------------------------------------------------------ tile scan
+
+// Pass 1: one block per chunk scans the totals of the chunk's tiles (stream
+// order) into offsets relative to the chunk and writes the chunk's total.
+__global__ __launch_bounds__(256) void k_tile_scan(const uint32_t *__restrict__ tile_sum,
+                                                   uint64_t *__restrict__ tile_off,
+                                                   uint64_t *__restrict__ chunk_total,
+                                                   int64_t tiles_per_chunk) {
+    __shared__ uint32_t wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t base = (int64_t)blockIdx.x * tiles_per_chunk;
+    uint64_t run = 0;
+    for (int64_t seg = 0; seg < tiles_per_chunk; seg += 256) {
+        const int64_t i = seg + tid;
+        const uint32_t v = i < tiles_per_chunk ? tile_sum[base + i] : 0u;
+        const uint32_t incl = wave_incl_scan_u32(v, lane);
+        if (lane == 63) wsum[wv] = incl;
+        __syncthreads();
+        uint32_t before = 0;
+        for (int k = 0; k < wv; ++k) before += wsum[k];
+        const uint32_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        if (i < tiles_per_chunk) tile_off[base + i] = run + before + incl - v;
+        run += total;
+        __syncthreads();
+    }
+    if (tid == 0) chunk_total[blockIdx.x] = run;
+}
+
+struct ChunkScanArgs {
+    const uint64_t *chunk_total;
+    uint64_t *chunk_off;
+    uint64_t *size_dev;
+    uint8_t *header_size;
+    WsHeader *hdr;
+    uint64_t payload_base;
+    uint64_t cap;
+    int NC;
+};
+
+// Pass 2: one block scans the chunk totals into chunk offsets and the size.
+__global__ __launch_bounds__(1024) void k_chunk_scan(ChunkScanArgs a) {
+    __shared__ uint64_t wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    uint64_t run = 0;
+    for (int seg = 0; seg < a.NC; seg += 1024) {
+        const int i = seg + tid;
+        const uint64_t v = i < a.NC ? a.chunk_total[i] : 0ull;
+        uint64_t incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)incl, o, 64);
+            const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(incl >> 32), o, 64);
+            if (lane >= o) incl += ((uint64_t)hi << 32) | lo;
         }
+        if (lane == 63) wsum[wv] = incl;
+        __syncthreads();
+        uint64_t before = 0, total = 0;
+        for (int k = 0; k < 16; ++k) {
+            if (k < wv) before += wsum[k];
+            total += wsum[k];
+        }
+        if (i < a.NC) a.chunk_off[i] = run + before + incl - v;
+        run += total;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        a.chunk_off[a.NC] = run;
+        a.hdr->payload_total = run;
+        if (run > a.cap) atomicOr(&a.hdr->status, kStCapacity);
+        const uint64_t size = a.payload_base + run;
+        if (a.size_dev) *a.size_dev = size;
+        if (a.header_size)
+            for (int i = 0; i < 8; ++i) a.header_size[i] = (uint8_t)(size >> (8 * i));
     }
 }
 
-// Streams longer than the LDS stage: re-encode them straight into the
-// payload at their final offsets (rare; the tile list comes from k_encode).
-__global__ __launch_bounds__(64) void k_encode_overflow(EncArgs a) {
+// ------------------------------------------------------------- compaction
+
+struct CompactArgs {
+    const uint8_t *staging;
+    const uint16_t *lengths;
+    const uint64_t *tile_off;   // relative to the chunk
+    const uint64_t *chunk_off;
+    const uint32_t *overflow_list;
+    const WsHeader *hdr;
+    uint8_t *payload;
+    uint64_t cap;
+    uint32_t *status;
+    int L, C, CB;
+    int64_t tiles_per_chunk;
+};
+
+__global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
+    __shared__ uint32_t start[65];
+    const int lane = threadIdx.x;
+    const int64_t tile = blockIdx.x;
+    const int cb = (int)(tile % a.CB);
+    const int64_t js = tile / a.CB;  // j * 2L + slab
+    const int c = cb * 64 + lane;
+    const uint32_t len = c < a.C ? a.lengths[js * a.C + c] : 0u;
+    if (__ballot(len > (uint32_t)kStageBytes)) return;  // k_fixup writes this tile
+    const uint32_t incl = wave_incl_scan_u32(len, lane);
+    start[lane + 1] = incl;
+    if (lane == 0) start[0] = 0;
+    __syncthreads();
+    const uint32_t total = start[64];
+    const uint64_t base = a.chunk_off[tile / a.tiles_per_chunk] + a.tile_off[tile];
+    const uint8_t *src = a.staging + tile * (kStageBytes * 64);
+    bool over = false;
+    for (uint32_t p = lane; p < total; p += 64) {
+        // Stream k with start[k] <= p < start[k+1].
+        uint32_t k = 0;
+#pragma unroll
+        for (int step = 32; step > 0; step >>= 1)
+            if (start[k + step] <= p) k += step;
+        const uint8_t b = src[(p - start[k]) * 64 + k];
+        if (base + p < a.cap) a.payload[base + p] = b;
+        else over = true;
+    }
+    if (__ballot(over) && lane == 0) atomicOr(a.status, kStCapacity);
+}
+
+// ----------------------------------------------------------------- fix-up
+
+struct FixupArgs {
+    const uint8_t *sym;
+    const int32_t *cdf;
+    const uint16_t *lengths;
+    const uint64_t *tile_off;   // relative to the chunk
+    const uint64_t *chunk_off;
+    const uint32_t *overflow_list;
+    WsHeader *hdr;
+    uint8_t *payload;
+    uint64_t cap;
+    int L, T, C, A, CB;
+};
+
+__global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
     const int lane = threadIdx.x;
     const uint32_t count = a.hdr->overflow_count;
     for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
         const int64_t tile = a.overflow_list[i];
-        int j, slab, cb;
-        tile_coords(tile, a.L, a.CB, j, slab, cb);
+        const int cb = (int)(tile % a.CB);
+        const int64_t js = tile / a.CB;
+        const int slab = (int)(js % (2 * a.L));
+        const int j = (int)(js / (2 * a.L));
         const int c = cb * 64 + lane;
         const bool active = c < a.C;
-        const int t0 = j * kChunk;
-        const int n = min(kChunk, a.T - t0);
-        const uint32_t len = active ? a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] : 0u;
+        const int n = min(kChunk, a.T - j * kChunk);
+        const uint32_t len = active ? a.lengths[js * a.C + c] : 0u;
         const uint32_t incl = wave_incl_scan_u32(len, lane);
-        const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
-        const uint64_t prefix = (a.tile_state[tile] & kValMask) - total;
-        if (!active || len <= (uint32_t)(kStageWords * 4)) continue;
+        if (!active) continue;
         const int32_t *tab = a.cdf + ((int64_t)slab * a.C + c) * (a.A + 1);
-        const uint8_t *sp = a.sym + ((int64_t)slab * a.T + t0) * a.C + c;
-        RcEnc enc;
+        const uint8_t *sp = a.sym + ((int64_t)slab * a.T + (int64_t)j * kChunk) * a.C + c;
+        RcEncHold enc;
         enc.init();
-        GlobalSink sink{a.payload, prefix + incl - len, a.cap, 0u, false};
+        GlobalSink sink{a.payload, a.chunk_off[j] + a.tile_off[tile] + incl - len, a.cap, 0u, false};
         for (int t = 0; t < n; ++t) {
             const uint32_t s = min((uint32_t)sp[(int64_t)t * a.C], (uint32_t)a.A - 1);
-            uint32_t e = packed_entry(tab, (int)s);
-            if ((e >> 16) == 0) e |= 1u << 16;
-            enc.encode(e & 0xFFFFu, e >> 16, sink);
+            const uint32_t lo = (uint32_t)tab[s], hi = (uint32_t)tab[s + 1];
+            const uint32_t f = hi > lo ? hi - lo : 1u;
+            enc.encode(lo & 0xFFFFu, f, sink);
         }
         enc.flush(sink);
         if (sink.overflow) atomicOr(&a.hdr->status, kStCapacity);
     }
 }
 
+// ---------------------------------------------------------------- launch
+
+size_t encode_staging_bytes(const Dims &d) { return (size_t)d.tiles * kStageBytes * 64; }
+
 hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, const EncodeOut &o,
                          const EncodeWs &w, hipStream_t s) {
+    const int S = d.NC >= 2 ? 2 : 1;
     EncArgs a;
     a.sym = sym;
     a.cdf = cdf;
-    a.payload = o.payload;
-    a.cap = o.cap;
+    a.staging = w.staging;
+    a.tile_sum = w.tile_sum;
     a.lengths = o.lengths;
-    a.chunk_off = o.chunk_off;
-    a.size_dev = o.size_dev;
-    a.header_size = o.header_size;
-    a.payload_base = o.payload_base;
     a.hdr = w.hdr;
-    a.tile_state = w.tile_state;
     a.overflow_list = w.overflow_list;
     a.L = d.L;
     a.T = d.T;
@@ -378,13 +511,72 @@ hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, 
     a.A = d.A;
     a.NC = d.NC;
     a.CB = d.CB;
-    a.tiles = d.tiles;
-    a.vec16 = (d.C % 16 == 0) && ((uintptr_t)sym % 16 == 0);
-    const size_t lds = (size_t)d.A * 64 * 4 + (size_t)kChunk * 64 + (size_t)kStageWords * 64 * 4;
-    hipLaunchKernelGGL(k_encode, dim3((unsigned)d.tiles), dim3(64), lds, s, a);
+    const int ngroups = (d.NC + S - 1) / S;
+    const unsigned blocks = (unsigned)((int64_t)ngroups * 2 * d.L * d.CB);
+    const dim3 grid(blocks), block(64);
+    if (S == 2) {
+        if (d.A <= 16) hipLaunchKernelGGL((k_encode<2, 4>), grid, block, 0, s, a);
+        else if (d.A <= 32) hipLaunchKernelGGL((k_encode<2, 5>), grid, block, 0, s, a);
+        else if (d.A <= 64) hipLaunchKernelGGL((k_encode<2, 6>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_encode<2, 7>), grid, block, 0, s, a);
+    } else {
+        if (d.A <= 16) hipLaunchKernelGGL((k_encode<1, 4>), grid, block, 0, s, a);
+        else if (d.A <= 32) hipLaunchKernelGGL((k_encode<1, 5>), grid, block, 0, s, a);
+        else if (d.A <= 64) hipLaunchKernelGGL((k_encode<1, 6>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_encode<1, 7>), grid, block, 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_encode_overflow, dim3(256), dim3(64), 0, s, a);
+
+    const int64_t tpc = 2LL * d.L * d.CB;
+    hipLaunchKernelGGL(k_tile_scan, dim3((unsigned)d.NC), dim3(256), 0, s, w.tile_sum, w.tile_off,
+                       w.chunk_total, tpc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    ChunkScanArgs sa;
+    sa.chunk_total = w.chunk_total;
+    sa.chunk_off = o.chunk_off;
+    sa.size_dev = o.size_dev;
+    sa.header_size = o.header_size;
+    sa.hdr = w.hdr;
+    sa.payload_base = o.payload_base;
+    sa.cap = o.cap;
+    sa.NC = d.NC;
+    hipLaunchKernelGGL(k_chunk_scan, dim3(1), dim3(1024), 0, s, sa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    CompactArgs ca;
+    ca.staging = w.staging;
+    ca.lengths = o.lengths;
+    ca.tile_off = w.tile_off;
+    ca.chunk_off = o.chunk_off;
+    ca.overflow_list = w.overflow_list;
+    ca.hdr = w.hdr;
+    ca.payload = o.payload;
+    ca.cap = o.cap;
+    ca.status = &w.hdr->status;
+    ca.L = d.L;
+    ca.C = d.C;
+    ca.CB = d.CB;
+    ca.tiles_per_chunk = tpc;
+    hipLaunchKernelGGL(k_compact, dim3((unsigned)d.tiles), dim3(64), 0, s, ca);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    FixupArgs fa;
+    fa.sym = sym;
+    fa.cdf = cdf;
+    fa.lengths = o.lengths;
+    fa.tile_off = w.tile_off;
+    fa.chunk_off = o.chunk_off;
+    fa.overflow_list = w.overflow_list;
+    fa.hdr = w.hdr;
+    fa.payload = o.payload;
+    fa.cap = o.cap;
+    fa.L = d.L;
+    fa.T = d.T;
+    fa.C = d.C;
+    fa.A = d.A;
+    fa.CB = d.CB;
+    hipLaunchKernelGGL(k_fixup, dim3(256), dim3(64), 0, s, fa);
     return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 // Target: gfx950 (CDNA4), wave64. Layout conventions follow include/cachegen.h.
 #pragma once
 
+#include <hip/hip_bf16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -79,9 +80,15 @@ struct EncodeOut {
 
 struct EncodeWs {
     WsHeader *hdr;
-    uint64_t *tile_state;     // [tiles] look-back words
-    uint32_t *overflow_list;  // [tiles]
+    uint32_t *tile_sum;       // [tiles] bytes of each 64-stream tile
+    uint64_t *tile_off;       // [tiles] offset of each tile within its chunk
+    uint64_t *chunk_total;    // [NC] bytes of each chunk
+    uint32_t *overflow_list;  // [tiles] tiles with a stream beyond the LDS stage
+    uint8_t *staging;         // encode_staging_bytes(d)
 };
+
+// Bytes of the staging area k_encode needs (one slot per tile).
+size_t encode_staging_bytes(const Dims &d);
 
 hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, const EncodeOut &o,
                          const EncodeWs &w, hipStream_t s);

@@ -84,3 +84,30 @@ def run_stages(kv_bits: np.ndarray, bins_k, bins_v):
         kv_out=to_np(kv_out, np.uint16).reshape(L, 2, T, C),
     )
     return out
+
+
+def run_coder(sym_np: np.ndarray, cdf_np: np.ndarray, desc):
+    """cg_encode then cg_decode on given symbols [2,L,T,C] and tables [2,L,C,A+1]."""
+    torch = torch_mod()
+    sym = to_dev(np.ascontiguousarray(sym_np, np.uint8)).reshape(-1)
+    cdf = to_dev(np.ascontiguousarray(cdf_np, np.int32)).reshape(-1)
+    payload = torch.empty(cgb.cg_encode_bound(desc), dtype=torch.uint8, device="cuda:0")
+    lengths = torch.empty(desc.nstreams, dtype=torch.int16, device="cuda:0")
+    chunk_off = torch.empty(desc.nchunks + 1, dtype=torch.int64, device="cuda:0")
+    ws = cgb.alloc_workspace(desc, cgb.CG_OP_ENCODE)
+    cgb.cg_encode(desc, sym, cdf, payload, lengths, chunk_off, ws)
+    enc_status = cgb.cg_read_status(ws)
+    nbytes = int(chunk_off[-1].item())
+    out = torch.full_like(sym, 255)
+    ws = cgb.alloc_workspace(desc, cgb.CG_OP_DECODE)
+    cgb.cg_decode(desc, payload, nbytes, lengths, chunk_off, cdf, out, ws)
+    dec_status = cgb.cg_read_status(ws)
+    NC = desc.nchunks
+    return dict(
+        encode_status=enc_status,
+        decode_status=dec_status,
+        payload=to_np(payload[:nbytes]),
+        lengths=to_np(lengths, np.uint16).reshape(NC, 2 * desc.nlayers, desc.nchannels),
+        chunk_off=to_np(chunk_off, np.uint64),
+        sym_decoded=to_np(out).reshape(sym_np.shape),
+    )

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import bf16_ulp_distance, run_stages, to_dev, to_np
+from gpu_util import bf16_ulp_distance, run_coder, run_stages, to_dev, to_np
 from kv_cache_compression_layer_amd import cachegen as cgb
 from kv_cache_compression_layer_amd.synth import WORKLOADS, generate_kv, generate_workload
 
@@ -187,3 +187,24 @@ def test_bad_arguments_launch_nothing():
     rc = cgb.lib().cg_to_bytes(desc.ptr, small.data_ptr(), small.data_ptr(), 64, small.data_ptr(),
                                small.data_ptr(), 64, None)
     assert rc in (cgb.CG_E_WORKSPACE, cgb.CG_E_INVAL)
+
+
+def test_coder_on_symbols_beyond_the_layer_range():
+    """The stage coder takes any symbol below A, also above a layer's own 2M
+    (the decoder's short search must fall back to the whole alphabet)."""
+    rng = np.random.default_rng(31)
+    L, T, H, D = 2, 600, 1, 72
+    bk = np.array([8, 32], np.uint8)
+    bv = np.array([4, 16], np.uint8)
+    desc = cgb.Desc(L, T, H, D, bk, bv)
+    A = desc.alphabet
+    sym = rng.integers(0, A, (2, L, T, H * D)).astype(np.uint8)
+    sym[:, :, :, :10] = rng.integers(0, 3, (2, L, T, 10))  # some low-entropy channels
+    cdf = oracle.build_cdf(sym, A)
+    payload, lengths, chunk_off = oracle.encode(sym, cdf)
+    g = run_coder(sym, cdf, desc)
+    assert g["encode_status"] == 0 and g["decode_status"] == 0
+    np.testing.assert_array_equal(g["lengths"], lengths)
+    np.testing.assert_array_equal(g["chunk_off"], chunk_off)
+    np.testing.assert_array_equal(g["payload"], payload)
+    np.testing.assert_array_equal(g["sym_decoded"], sym)

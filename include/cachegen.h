@@ -63,7 +63,8 @@ extern "C" {
 /* Problem descriptor. bins_k / bins_v are HOST arrays of length nlayers
  * holding the number of quantisation bins of each layer ([P2 s1]); each must
  * be in [4, 128]. Valid shapes: 1 <= nlayers <= 1024, ntokens >= 1,
- * nheads >= 1, head_size >= 1, 2*nlayers*ntokens*nheads*head_size < 2^40. */
+ * nheads >= 1, head_size >= 1, 2*nlayers*ntokens*nheads*head_size < 2^40 and
+ * ntokens*nheads*head_size < 2^31 (one (K|V, layer) slab). */
 typedef struct cg_desc {
     int32_t nlayers;
     int32_t ntokens;

@@ -46,6 +46,8 @@ int make_dims(const cg_desc *desc, Dims &d) {
     d.NS = (int64_t)d.NC * 2 * d.L * d.C;
     d.tiles = (int64_t)d.NC * 2 * d.L * d.CB;
     if (d.N >= (1LL << 40) || d.tiles >= (1LL << 31)) return CG_E_SHAPE;
+    // Kernels address one (K|V, layer) slab with 32-bit byte offsets.
+    if ((int64_t)d.T * d.C >= (1LL << 31)) return CG_E_SHAPE;
     return CG_OK;
 }
 

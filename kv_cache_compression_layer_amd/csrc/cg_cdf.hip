@@ -9,11 +9,12 @@
 //
 // Histogram: a block of 256 threads owns 256 channels of one (K|V, layer)
 // over a tile of tokens. Each thread owns one channel, so its counters need
-// no atomics: they sit in LDS as uint16 [A][256] (row s, column = thread),
-// which keeps every LDS access of a wave on distinct banks whatever the
-// symbols are. Loads are one byte per thread, 256 contiguous bytes per token
-// row. At the end of the tile the non-zero counters are added to the global
-// uint32 counts with atomics.
+// no atomics across threads: they sit in LDS as uint32 [A][256] (row s,
+// column = thread), which keeps every LDS access of a wave on distinct banks
+// whatever the symbols are; an increment is one ds_add. Loads are one byte
+// per thread, 256 contiguous bytes per token row, eight rows in flight. At
+// the end of the tile the non-zero counters are added to the global uint32
+// counts with atomics.
 #include "cg_internal.hpp"
 
 namespace cg {
@@ -22,7 +23,7 @@ __global__ __launch_bounds__(256) void k_histogram(const uint8_t *__restrict__ s
                                                    uint32_t *__restrict__ counts,
                                                    uint32_t *__restrict__ status, int L, int T,
                                                    int C, int A, int TT) {
-    extern __shared__ uint16_t hist[];  // [A][256]
+    extern __shared__ uint32_t hist[];  // [A][256]
     const int tid = threadIdx.x;
     const int slab = blockIdx.z;                 // kv * L + l
     const int c = blockIdx.y * 256 + tid;
@@ -31,23 +32,24 @@ __global__ __launch_bounds__(256) void k_histogram(const uint8_t *__restrict__ s
     for (int s = 0; s < A; ++s) hist[s * 256 + tid] = 0;
     if (c >= C) return;
     const uint8_t *p = sym + ((int64_t)slab * T + t0) * C + c;
-    bool bad = false;
+    const uint32_t amax = (uint32_t)A - 1;
+    uint32_t qmax = 0;
+    auto bump = [&](uint32_t q) {
+        qmax = max(qmax, q);
+        __hip_atomic_fetch_add(&hist[min(q, amax) * 256 + tid], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
     int t = t0;
-    for (; t + 4 <= t1; t += 4) {
-        const uint32_t s0 = p[0], s1 = p[C], s2 = p[2 * (int64_t)C], s3 = p[3 * (int64_t)C];
-        p += 4 * (int64_t)C;
-        bad |= (s0 >= (uint32_t)A) | (s1 >= (uint32_t)A) | (s2 >= (uint32_t)A) | (s3 >= (uint32_t)A);
-        hist[min(s0, (uint32_t)A - 1) * 256 + tid] += 1;
-        hist[min(s1, (uint32_t)A - 1) * 256 + tid] += 1;
-        hist[min(s2, (uint32_t)A - 1) * 256 + tid] += 1;
-        hist[min(s3, (uint32_t)A - 1) * 256 + tid] += 1;
+    for (; t + 8 <= t1; t += 8) {
+        uint32_t q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = p[(int64_t)i * C];
+        p += 8 * (int64_t)C;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bump(q[i]);
     }
-    for (; t < t1; ++t, p += C) {
-        const uint32_t s0 = p[0];
-        bad |= s0 >= (uint32_t)A;
-        hist[min(s0, (uint32_t)A - 1) * 256 + tid] += 1;
-    }
-    if (bad) atomicOr(status, kStCorrupt);
+    for (; t < t1; ++t, p += C) bump(p[0]);
+    if (qmax > amax) atomicOr(status, kStCorrupt);
     uint32_t *dst = counts + ((int64_t)slab * C + c) * A;
     for (int s = 0; s < A; ++s) {
         const uint32_t v = hist[s * 256 + tid];
@@ -57,15 +59,13 @@ __global__ __launch_bounds__(256) void k_histogram(const uint8_t *__restrict__ s
 
 hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts,
                             uint32_t *status, hipStream_t s) {
-    // Token tiles: enough blocks to fill the chip, and at most 65535 tokens
-    // per tile so the 16-bit LDS counters cannot overflow.
+    // Token tiles: enough blocks to fill the chip.
     const int cgroups = (d.C + 255) / 256;
     const int64_t slabs = 2LL * d.L;
     int TT = d.T;
-    while (TT > 65535 || (slabs * cgroups * ((d.T + TT - 1) / TT) < 2048 && TT > 512))
-        TT = (TT + 1) / 2;
+    while (slabs * cgroups * ((d.T + TT - 1) / TT) < 2048 && TT > 512) TT = (TT + 1) / 2;
     const dim3 grid((unsigned)((d.T + TT - 1) / TT), (unsigned)cgroups, (unsigned)slabs);
-    const size_t lds = (size_t)d.A * 256 * sizeof(uint16_t);
+    const size_t lds = (size_t)d.A * 256 * sizeof(uint32_t);
     hipLaunchKernelGGL(k_histogram, grid, dim3(256), lds, s, sym, counts, status, d.L, d.T, d.C,
                        d.A, TT);
     return hipGetLastError();

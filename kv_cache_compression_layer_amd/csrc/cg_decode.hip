@@ -28,7 +28,7 @@
 
 namespace cg {
 
-constexpr int kStageTile = 2048;  // LDS bytes per staged tile payload (larger tiles read global memory)
+constexpr int kStageTile = 1536;  // LDS bytes per staged tile payload (larger tiles read global memory)
 
 // Block-wide exclusive scan of one uint32 per thread (256 threads).
 __device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t *tmp,
@@ -97,47 +97,87 @@ struct DecStream {
     const uint8_t *gsrc;  // unstaged source (payload + stream offset)
 };
 
-// The per-token loop of k_decode; STAGED selects where bytes come from.
-template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED>
+// The per-token loop of k_decode.
+//
+// Latency: the first two levels of the binary search compare against CDF
+// values held in registers (the same candidates every token); the byte the
+// next renormalisation shifts in is read one renormalisation ahead; each
+// token's dequantisation and store run one token later, so their LDS reads
+// overlap the next search. A stream whose tile did not fit the LDS stage
+// reads its bytes from global memory instead (staged[s] is wave-uniform).
+template <int S, bool FUSED, int LOGA, bool CLAMP>
 __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S], const int (&n)[S],
-                                            const int (&t0)[S], const uint32_t *tab, const float *dq,
-                                            const float *sc, const uint8_t *stage, int lane, bool active,
-                                            int slab, int kv, int l, int cb, bool &corrupt) {
-    // Next byte of a stream; bytes past its length read as zero (the staged
-    // path reads the zero byte kept after the stage instead).
+                                            const bool (&staged)[S], const uint32_t (&rowoff)[S],
+                                            const uint32_t *tab, const float *dq, const uint16_t *sc,
+                                            const uint8_t *stage, __amdgpu_buffer_rsrc_t out_rsrc,
+                                            uint32_t out_voff, int lane, uint64_t &bad_mask) {
     const uint32_t zero_at = S * kStageTile;
-    auto next_byte = [&](DecStream &d) -> uint32_t {
-        uint32_t b;
-        if (STAGED) {
-            b = stage[d.ptr < d.end ? d.ptr : zero_at];
-            ++d.ptr;
-        } else {
-            b = d.pos < d.len ? (uint32_t)d.gsrc[d.pos] : 0u;
-            ++d.pos;
-        }
-        return b;
+    auto fetch = [&](int s) -> uint32_t {
+        const DecStream &d = st[s];
+        if (staged[s]) return stage[d.ptr < d.end ? d.ptr : zero_at];
+        return d.pos < d.len ? (uint32_t)d.gsrc[d.pos] : 0u;
     };
+    auto advance = [&](int s) {
+        ++st[s].ptr;
+        ++st[s].pos;
+    };
+    uint32_t nxt[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s)
-        for (int i = 0; i < 4; ++i) st[s].code = (st[s].code << 8) | next_byte(st[s]);
+    for (int s = 0; s < S; ++s) {
+        for (int i = 0; i < 4; ++i) {
+            st[s].code = (st[s].code << 8) | fetch(s);
+            advance(s);
+        }
+        nxt[s] = fetch(s);
+    }
 
     // Byte address in tab of (symbol s, this lane) is s * 256 + lane * 4.
     const uint8_t *tabb = reinterpret_cast<const uint8_t *>(tab);
     const uint32_t lane4 = (uint32_t)lane * 4;
     const uint32_t amax4 = ((uint32_t)a.A - 1) * 256 + lane4;
-    const int lane_c = active ? lane : 0;
+    constexpr uint32_t H1 = 1u << (LOGA - 1), H2 = 1u << (LOGA - 2);
+    // Candidates of the first two levels (clamped to the alphabet).
+    const uint32_t sa = CLAMP ? min(H1, (uint32_t)a.A - 1) : H1;
+    const uint32_t sb = CLAMP ? min(H2, (uint32_t)a.A - 1) : H2;
+    const uint32_t sc3 = CLAMP ? min(H1 + H2, (uint32_t)a.A - 1) : H1 + H2;
+    const uint32_t cdf_a = tab[sa * 64 + lane] & 0xFFFFu;
+    const uint32_t cdf_b = tab[sb * 64 + lane] & 0xFFFFu;
+    const uint32_t cdf_c = tab[sc3 * 64 + lane] & 0xFFFFu;
+    const uint32_t ad_a = sa * 256 + lane4, ad_b = sb * 256 + lane4, ad_c = sc3 * 256 + lane4;
     const int nmax = n[0];
+
+    // Output of the previous token, written one step late.
+    uint32_t p_sy[S], p_sc[S];
+    float p_dq[S];
+    int p_t = -1;
+    auto store = [&](int s, int t) {
+        if (t < n[s]) {
+            const uint32_t off = rowoff[s] + (uint32_t)t * (uint32_t)a.C * (FUSED ? 2u : 1u);
+            if (FUSED) {
+                const float x = __fmul_rn(p_dq[s], __uint_as_float(p_sc[s] << 16));
+                const __hip_bfloat16 h = __float2bfloat16(x);
+                __builtin_amdgcn_raw_buffer_store_b16(*reinterpret_cast<const uint16_t *>(&h), out_rsrc,
+                                                      (int)out_voff, (int)off, 0);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)p_sy[s], out_rsrc, (int)out_voff, (int)off, 0);
+            }
+        }
+    };
+
     for (int t = 0; t < nmax; ++t) {
         uint32_t r[S], ad[S];
+        // Levels 1 and 2 from registers.
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             r[s] = st[s].range >> 16;
-            ad[s] = lane4;
+            const bool hi = __umul24(r[s], cdf_a) <= st[s].code;
+            const uint32_t c2 = hi ? cdf_c : cdf_b;
+            const bool hi2 = __umul24(r[s], c2) <= st[s].code;
+            ad[s] = hi ? (hi2 ? ad_c : ad_a) : (hi2 ? ad_b : lane4);
         }
-        // Interleaved branch-free binary searches over the whole alphabet,
-        // carrying the LDS address of the current symbol's entry.
+        // Remaining levels: interleaved branch-free binary searches over LDS.
 #pragma unroll
-        for (int i = LOGA - 1; i >= 0; --i) {
+        for (int i = LOGA - 3; i >= 0; --i) {
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 uint32_t cand = ad[s] + (256u << i);
@@ -146,38 +186,43 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
                 ad[s] = __umul24(r[s], ec & 0xFFFFu) <= st[s].code ? cand : ad[s];
             }
         }
+        // The previous token's output, now that its LDS reads have landed.
+        if (p_t >= 0) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) store(s, p_t);
+        }
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             // Every stream steps every token (a finished stream keeps decoding
             // zeros); only its output and its checks are guarded.
             DecStream &d = st[s];
-            const bool live = t < n[s];
             const uint32_t e = *reinterpret_cast<const uint32_t *>(tabb + ad[s]);
             const uint32_t sy = (ad[s] - lane4) >> 8;
             d.code -= __umul24(r[s], e & 0xFFFFu);
             d.range = __umul24(r[s], e >> 16);
             if (d.range < kTop) {
-                d.code = (d.code << 8) | next_byte(d);
+                d.code = (d.code << 8) | nxt[s];
                 d.range <<= 8;
+                advance(s);
                 if (d.range < kTop) {
-                    d.code = (d.code << 8) | next_byte(d);
+                    d.code = (d.code << 8) | fetch(s);
                     d.range <<= 8;
+                    advance(s);
                 }
+                nxt[s] = fetch(s);
             }
-            corrupt |= live && d.code >= d.range;
-            if (live) {
-                // Row t of this stream: a wave-uniform base plus the lane.
-                if (FUSED) {
-                    const float x = __fmul_rn(dq[sy], sc[s * kChunk + t]);
-                    const __hip_bfloat16 h = __float2bfloat16(x);
-                    uint16_t *row = a.kv + (((int64_t)l * 2 + kv) * a.T + t0[s] + t) * a.C + cb * 64;
-                    if (active) row[lane_c] = *reinterpret_cast<const uint16_t *>(&h);
-                } else {
-                    uint8_t *row = a.sym + ((int64_t)slab * a.T + t0[s] + t) * a.C + cb * 64;
-                    if (active) row[lane_c] = (uint8_t)sy;
-                }
+            if (t < n[s]) bad_mask |= __ballot(d.code >= d.range);
+            p_sy[s] = sy;
+            if (FUSED) {
+                p_dq[s] = dq[sy];
+                p_sc[s] = sc[s * kChunk + t];
             }
         }
+        p_t = t;
+    }
+    if (p_t >= 0) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) store(s, p_t);
     }
 }
 
@@ -185,9 +230,9 @@ template <int S, bool FUSED, int LOGA, bool CLAMP>
 __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     // Static LDS sized by the template, so every address folds to an immediate.
     __shared__ float dq[128];
-    __shared__ uint32_t tab[(1 << LOGA) * 64];          // [symbol][lane]
-    __shared__ __attribute__((aligned(16))) uint8_t stage[S * kStageTile + 8];  // tiles' bytes, then 8 zeros
-    __shared__ float sc[FUSED ? S * kChunk : 1];        // per-token scales
+    __shared__ uint32_t tab[(1 << LOGA) * 64];                                   // [symbol][lane]
+    __shared__ __attribute__((aligned(16))) uint8_t stage[S * kStageTile + 8];  // tiles' bytes, then zeros
+    __shared__ uint16_t sc[FUSED ? S * kChunk : 1];                             // per-token scales (bf16)
     const int lane = threadIdx.x;
     const int A = a.A;
 
@@ -201,8 +246,9 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     const int M = a.mt.m[kv][l];
 
     int n[S], t0[S];
+    bool staged[S];
     DecStream st[S];
-    bool corrupt = false, all_staged = true;
+    bool corrupt = false;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int j = g * S + s;
@@ -225,9 +271,8 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
         // Stage the tile's bytes: words from the aligned start, bounded by the payload.
         const uint64_t abase = base & ~3ull;
         const uint32_t head = (uint32_t)(base - abase);
-        const bool staged = total + head <= (uint32_t)kStageTile;
-        all_staged &= staged;
-        if (staged && total) {
+        staged[s] = total + head <= (uint32_t)kStageTile;
+        if (staged[s] && total) {
             uint32_t *w = reinterpret_cast<uint32_t *>(stage + s * kStageTile);
             const uint32_t nw = (head + total + 3) >> 2;
             for (uint32_t i = lane; i < nw; i += 64) {
@@ -259,18 +304,18 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
         uint32_t prev = a.cdf32 ? (uint32_t)a.cdf32[row * (A + 1)] : (uint32_t)a.cdf16[row * A];
         bad_table = prev != 0;
         for (int s = 0; s < A; ++s) {
-            uint32_t nxt;
+            uint32_t nxtv;
             if (a.cdf32)
-                nxt = (uint32_t)a.cdf32[row * (A + 1) + s + 1];
+                nxtv = (uint32_t)a.cdf32[row * (A + 1) + s + 1];
             else
-                nxt = s + 1 < A ? (uint32_t)a.cdf16[row * A + s + 1] : kProbOne;
-            uint32_t f = nxt - prev;
-            if (nxt <= prev || nxt > kProbOne) {
+                nxtv = s + 1 < A ? (uint32_t)a.cdf16[row * A + s + 1] : kProbOne;
+            uint32_t f = nxtv - prev;
+            if (nxtv <= prev || nxtv > kProbOne) {
                 bad_table = true;
                 f = 1;
             }
             tab[s * 64 + lane] = (prev & 0xFFFFu) | (f << 16);
-            prev = nxt;
+            prev = nxtv;
         }
         if (a.cdf32) bad_table |= (uint32_t)a.cdf32[row * (A + 1) + A] != kProbOne;
     } else {
@@ -284,21 +329,30 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const uint16_t *sp = a.scale + (int64_t)slab * a.T + t0[s];
-            for (int t = lane; t < n[s]; t += 64) sc[s * kChunk + t] = bf16_to_f32(sp[t]);
+            for (int t = lane; t < n[s]; t += 64) sc[s * kChunk + t] = sp[t];
         }
         dq[lane] = __fdiv_rn((float)(lane - M), (float)M);
         dq[lane + 64] = __fdiv_rn((float)(lane + 64 - M), (float)M);
     }
     __syncthreads();
 
-    const bool staged_wave = __ballot(!all_staged) == 0;  // wave-uniform
-    if (staged_wave)
-        decode_loop<S, FUSED, LOGA, CLAMP, true>(a, st, n, t0, tab, dq, sc, stage, lane, active, slab, kv, l,
-                                                cb, corrupt);
-    else
-        decode_loop<S, FUSED, LOGA, CLAMP, false>(a, st, n, t0, tab, dq, sc, stage, lane, active, slab, kv, l,
-                                                 cb, corrupt);
-    if (__ballot(active && (corrupt || bad_table)) && lane == 0) atomicOr(a.status, kStCorrupt);
+    // Output rows: a buffer over this (K|V, layer) slab; the row offset is
+    // wave-uniform, the lane offset constant; idle lanes point past the end.
+    const uint32_t esz = FUSED ? 2u : 1u;
+    const uint64_t slab_elems = (uint64_t)a.T * a.C;
+    const void *obase = FUSED ? (const void *)(a.kv + ((int64_t)l * 2 + kv) * (int64_t)slab_elems)
+                              : (const void *)(a.sym + (int64_t)slab * (int64_t)slab_elems);
+    const __amdgpu_buffer_rsrc_t out_rsrc = make_rsrc(obase, (uint32_t)(slab_elems * esz));
+    const uint32_t out_voff = active ? (uint32_t)(cb * 64 + lane) * esz : 0x7FFFFFF0u;
+    uint32_t rowoff[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) rowoff[s] = (uint32_t)t0[s] * (uint32_t)a.C * esz;
+
+    uint64_t bad_mask = 0;
+    decode_loop<S, FUSED, LOGA, CLAMP>(a, st, n, staged, rowoff, tab, dq, sc, stage, out_rsrc, out_voff,
+                                       lane, bad_mask);
+    if ((__ballot(active && (corrupt || bad_table)) | (bad_mask & __ballot(active))) && lane == 0)
+        atomicOr(a.status, kStCorrupt);
 }
 
 template <int S, bool FUSED, int LOGA>

@@ -31,27 +31,42 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s) {
 
 // --------------------------------------------------------------- quantise
 
-// Symbol of one element: q = clamp(rint(x*f + M), 0, 2M) with every fp32
+// Symbol of one element: q = round_half_even(x*f + M) with every fp32
 // operation rounded on its own (the library is built without contraction).
-__device__ __forceinline__ uint32_t quant1(uint32_t bits16, float f, float Mf, int twoM) {
-    float x = bf16_to_f32(bits16 & 0xFFFFu);
-    float y = __fmul_rn(x, f);
-    float z = __fadd_rn(y, Mf);
-    int q = (int)rintf(z);
-    q = min(max(q, 0), twoM);
-    return (uint32_t)q;
+// Adding 1.5 * 2^23 to a value in [-0.5, 2^22) rounds it to an integer (half
+// to even) and leaves that integer in the low mantissa bits, so the symbol is
+// the low byte of the sum. The clamp to [0, 2M] of the definition is a no-op
+// here: |x| <= m gives |x*f| <= M(1 + 2^-23), so x*f + M lies within
+// [-M*2^-23, 2M + M*2^-23] and rounds into [0, 2M].
+__device__ __forceinline__ uint32_t quant_bits(float x, float f, float Mf) {
+    const float y = __fmul_rn(x, f);
+    const float z = __fadd_rn(y, Mf);
+    return __float_as_uint(__fadd_rn(z, 12582912.0f));  // low byte = symbol
 }
 
-__device__ __forceinline__ uint32_t absmax_pair(uint32_t w) {
-    return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+// Four bf16 values packed in two words -> four symbol bytes in one word.
+__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float f, float Mf) {
+    const uint32_t a = quant_bits(__uint_as_float(w0 << 16), f, Mf);
+    const uint32_t b = quant_bits(__uint_as_float(w0 & 0xFFFF0000u), f, Mf);
+    const uint32_t c = quant_bits(__uint_as_float(w1 << 16), f, Mf);
+    const uint32_t d = quant_bits(__uint_as_float(w1 & 0xFFFF0000u), f, Mf);
+    // Byte 0 of each: perm selects bytes of {src0, src1} (src1 = bytes 0..3).
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // [a0, b0, 0, 0]
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x04000c0cu);  // [0, 0, c0, d0]
+    return ab | cd;
 }
 
-__device__ __forceinline__ void row_coords(int64_t row, int L, int T, int &k, int &l, int &t) {
-    const int64_t LT = (int64_t)L * T;
-    k = (int)(row / LT);
-    const int64_t rem = row - (int64_t)k * LT;
-    l = (int)(rem / T);
-    t = (int)(rem - (int64_t)l * T);
+__device__ __forceinline__ uint32_t quant1(uint32_t bits16, float f, float Mf) {
+    return quant_bits(bf16_to_f32(bits16 & 0xFFFFu), f, Mf) & 0xFFu;
+}
+
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+
+// Per-half max of |bf16| bit patterns (sign cleared) with packed 16-bit max.
+__device__ __forceinline__ uint32_t absmax2(uint32_t acc, uint32_t w) {
+    ushort2_t a = __builtin_bit_cast(ushort2_t, acc);
+    ushort2_t b = __builtin_bit_cast(ushort2_t, w & 0x7FFF7FFFu);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
 }
 
 // NV 16-byte vectors per lane hold the row (C <= NV * 512, C % 8 == 0).
@@ -62,15 +77,15 @@ __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict
                                                       uint32_t *__restrict__ status, int L, int T,
                                                       int C, MaxTable mt) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= 2LL * L * T) return;
-    int k, l, t;
-    row_coords(row, L, T, k, l, t);
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int slab = blockIdx.y, k = slab / L, l = slab - k * L;  // grid: (tokens/4, 2L)
+    const int64_t row = (int64_t)slab * T + t;
     const uint16_t *src = kv + (((int64_t)l * 2 + k) * T + t) * C;
     uint8_t *dst = sym + row * C;
 
     uint4 v[NV];
-    uint32_t am = 0;
+    uint32_t am2 = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int c0 = (i * 64 + lane) * 8;
@@ -79,29 +94,21 @@ __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict
         } else {
             v[i] = make_uint4(0, 0, 0, 0);
         }
-        am = max(am, max(max(absmax_pair(v[i].x), absmax_pair(v[i].y)),
-                         max(absmax_pair(v[i].z), absmax_pair(v[i].w))));
+        am2 = absmax2(absmax2(absmax2(absmax2(am2, v[i].x), v[i].y), v[i].z), v[i].w);
     }
+    uint32_t am = max(am2 & 0xFFFFu, am2 >> 16);
     am = wave_max_u32(am);
     if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
     const int M = mt.m[k][l];
     const float Mf = (float)M;
     // m == 0 gives f == 0, so every symbol is exactly M.
     const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
-    const int twoM = 2 * M;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int c0 = (i * 64 + lane) * 8;
         if (c0 < C) {
-            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                lo |= quant1(w[e], f, Mf, twoM) << (16 * e);
-                lo |= quant1(w[e] >> 16, f, Mf, twoM) << (16 * e + 8);
-                hi |= quant1(w[e + 2], f, Mf, twoM) << (16 * e);
-                hi |= quant1(w[e + 2] >> 16, f, Mf, twoM) << (16 * e + 8);
-            }
+            const uint32_t lo = quant4(v[i].x, v[i].y, f, Mf);
+            const uint32_t hi = quant4(v[i].z, v[i].w, f, Mf);
             *reinterpret_cast<uint2 *>(dst + c0) = make_uint2(lo, hi);
         }
     }
@@ -115,10 +122,10 @@ __global__ __launch_bounds__(256) void k_quantize_any(const uint16_t *__restrict
                                                       uint32_t *__restrict__ status, int L, int T,
                                                       int C, MaxTable mt) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= 2LL * L * T) return;
-    int k, l, t;
-    row_coords(row, L, T, k, l, t);
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int slab = blockIdx.y, k = slab / L, l = slab - k * L;  // grid: (tokens/4, 2L)
+    const int64_t row = (int64_t)slab * T + t;
     const uint16_t *src = kv + (((int64_t)l * 2 + k) * T + t) * C;
     uint8_t *dst = sym + row * C;
     uint32_t am = 0;
@@ -128,14 +135,13 @@ __global__ __launch_bounds__(256) void k_quantize_any(const uint16_t *__restrict
     const int M = mt.m[k][l];
     const float Mf = (float)M;
     const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
-    for (int c = lane; c < C; c += 64) dst[c] = (uint8_t)quant1(src[c], f, Mf, 2 * M);
+    for (int c = lane; c < C; c += 64) dst[c] = (uint8_t)quant1(src[c], f, Mf);
     if (lane == 0) scale[row] = (uint16_t)am;
 }
 
 hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
                            uint16_t *scale, uint32_t *status, hipStream_t s) {
-    const int64_t rows = 2LL * d.L * d.T;
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    const dim3 grid((unsigned)((d.T + 3) / 4), (unsigned)(2 * d.L)), block(256);
     const bool aligned = ((uintptr_t)kv % 16 == 0) && ((uintptr_t)sym % 8 == 0);
     if (aligned && d.C % 8 == 0 && d.C <= 2048) {
         const int nv = (d.C + 511) / 512;
@@ -166,10 +172,10 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
                                                     MaxTable mt, int vec8) {
     __shared__ float dq_all[4][128];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wv;
-    if (row >= 2LL * L * T) return;
-    int k, l, t;
-    row_coords(row, L, T, k, l, t);
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T) return;
+    const int slab = blockIdx.y, k = slab / L, l = slab - k * L;  // grid: (tokens/4, 2L)
+    const int64_t row = (int64_t)slab * T + t;
     float *dq = dq_all[wv];
     build_dq(dq, mt.m[k][l], lane);
     __builtin_amdgcn_wave_barrier();
@@ -199,9 +205,8 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
 
 hipError_t launch_dequantize(const Dims &d, const MaxTable &mt, const uint8_t *sym,
                              const uint16_t *scale, uint16_t *kv_out, hipStream_t s) {
-    const int64_t rows = 2LL * d.L * d.T;
     const int vec8 = (d.C % 8 == 0) && ((uintptr_t)sym % 8 == 0) && ((uintptr_t)kv_out % 16 == 0);
-    hipLaunchKernelGGL(k_dequantize, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, sym, scale,
+    hipLaunchKernelGGL(k_dequantize, dim3((unsigned)((d.T + 3) / 4), (unsigned)(2 * d.L)), dim3(256), 0, s, sym, scale,
                        kv_out, d.L, d.T, d.C, mt, vec8);
     return hipGetLastError();
 }

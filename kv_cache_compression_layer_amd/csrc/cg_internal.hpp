@@ -125,6 +125,15 @@ hipError_t launch_blob_header(uint8_t *blob, const HeaderBytes &h, const BlobLay
 
 // ----------------------------------------------------------- device helpers
 
+// Buffer resource (V#) over [base, base + bytes) for raw byte-offset loads and
+// stores; word 3 is the gfx9-family value for untyped buffer access. With a
+// 32-bit row offset in an SGPR and the lane's offset in a VGPR, the access
+// needs no per-lane address arithmetic. An access whose lane offset lies
+// beyond `bytes` is dropped (stores) or reads 0 (loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }

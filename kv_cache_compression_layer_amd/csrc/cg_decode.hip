@@ -11,24 +11,24 @@
 // prefix sum of the lengths before it, and checks that the chunk's lengths
 // add up to the next chunk offset.
 //
-// Pass 2 (k_decode): one wave per group of S tiles that share 64 channels
-// (lane = channel) and differ only in the chunk, so each lane decodes S
-// streams of its channel interleaved (independent dependency chains) with
-// one table. The tiles' bytes (contiguous in the payload) are copied into LDS
-// with the 64 lanes reading consecutive words; the tables are staged as
-// start | freq << 16 [symbol][lane]. The symbol is the largest s with
-// r * cdf[s] <= code, found by a branch-free binary search over the whole
-// alphabet (depth fixed at compile time, the S searches interleaved);
-// comparing r * cdf[s] with code is the same test as cdf[s] <= floor(code / r), so no
-// division is needed. Renormalisation is two predicated steps. The fused
-// variant multiplies by the per-token scale and converts to bf16 with the
-// hardware round-to-nearest-even conversion, so the symbols never reach
-// memory.
+// Pass 2 (k_decode): a block of NW waves owns 64 channels of one (K|V,
+// layer) (lane = channel) and NW * S chunks; each wave decodes S streams per
+// lane interleaved (independent dependency chains) with the one table of its
+// channel. The waves share the tables, staged as start | freq << 16
+// [symbol][lane], and an LDS pool for their tiles' payload: every lane copies
+// its own stream there, followed by four zero bytes (the bytes past a
+// stream's end read as zero), so the byte fetch needs no bounds check. A
+// wave whose tiles do not fit the pool reads global memory instead. The
+// symbol is the largest s with r * cdf[s] <= code, found by a branch-free
+// binary search over the whole alphabet (depth fixed at compile time, the S
+// searches interleaved); comparing r * cdf[s] with code is the same test as
+// cdf[s] <= floor(code / r), so no division is needed. Renormalisation is
+// two predicated steps. The fused variant multiplies by the per-token scale
+// and converts to bf16 with the hardware round-to-nearest-even conversion,
+// so the symbols never reach memory.
 #include "cg_internal.hpp"
 
 namespace cg {
-
-constexpr int kStageTile = 1536;  // LDS bytes per staged tile payload (larger tiles read global memory)
 
 // Block-wide exclusive scan of one uint32 per thread (256 threads).
 __device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t *tmp,
@@ -89,46 +89,57 @@ struct DecArgs {
     int L, T, C, A, NC, CB;
 };
 
-// One stream's decoder state and byte source.
+// Bytes of the LDS pool a block of NW waves shares for its tiles' payload,
+// and the slack after it: a stream is never read more than 4 + 2 * 256 + 2
+// bytes past its first byte (two renormalisations per symbol at most, two
+// bytes of look-ahead), so reads of a malformed stream stay inside the
+// block's LDS.
+constexpr uint32_t kPoolPerWave = 5760;
+constexpr uint32_t kPoolSlack = 528;
+
+// One stream's decoder state. Staged streams read pool bytes at `ptr` (each
+// stream is followed by at least four zero bytes, the bytes past its end);
+// unstaged streams read global memory at gsrc[pos] while pos < len.
 struct DecStream {
     uint32_t code, range;
-    uint32_t ptr, end;    // LDS byte address of the next byte / of the stream's end
-    uint32_t pos, len;    // the same, counted in the stream (unstaged path)
-    const uint8_t *gsrc;  // unstaged source (payload + stream offset)
+    uint32_t ptr;
+    uint32_t pos, len;
+    const uint8_t *gsrc;
 };
 
 // The per-token loop of k_decode.
 //
+// The table holds 2^LOGA entries per lane; entries past the alphabet have
+// start 0xFFFF, so the search can only land on them when the symbol is the
+// last one, and one clamp at the end maps them back (CLAMP).
+//
 // Latency: the first two levels of the binary search compare against CDF
-// values held in registers (the same candidates every token); the byte the
-// next renormalisation shifts in is read one renormalisation ahead; each
-// token's dequantisation and store run one token later, so their LDS reads
-// overlap the next search. A stream whose tile did not fit the LDS stage
-// reads its bytes from global memory instead (staged[s] is wave-uniform).
-template <int S, bool FUSED, int LOGA, bool CLAMP>
+// values held in registers (the same candidates every token); the two bytes
+// the next renormalisations shift in are read ahead; each token's
+// dequantisation and store run one token later, so their LDS reads overlap
+// the next search. The per-token scale is wave-uniform: lane i of sc_v[s][k]
+// holds the scale of token 64k + i of stream s, read out with readlane.
+template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED>
 __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S], const int (&n)[S],
-                                            const bool (&staged)[S], const uint32_t (&rowoff)[S],
-                                            const uint32_t *tab, const float *dq, const uint16_t *sc,
-                                            const uint8_t *stage, __amdgpu_buffer_rsrc_t out_rsrc,
-                                            uint32_t out_voff, int lane, uint64_t &bad_mask) {
-    const uint32_t zero_at = S * kStageTile;
+                                            const uint32_t (&rowoff)[S], const uint32_t *tab,
+                                            const float *dq, uint32_t (&sc_v)[S][4], const uint8_t *pool,
+                                            __amdgpu_buffer_rsrc_t out_rsrc, uint32_t out_voff,
+                                            int lane, uint64_t &bad_mask) {
     auto fetch = [&](int s) -> uint32_t {
-        const DecStream &d = st[s];
-        if (staged[s]) return stage[d.ptr < d.end ? d.ptr : zero_at];
-        return d.pos < d.len ? (uint32_t)d.gsrc[d.pos] : 0u;
+        DecStream &d = st[s];
+        if (STAGED) return pool[d.ptr++];
+        const uint32_t v = d.pos < d.len ? (uint32_t)d.gsrc[d.pos] : 0u;
+        ++d.pos;
+        return v;
     };
-    auto advance = [&](int s) {
-        ++st[s].ptr;
-        ++st[s].pos;
-    };
-    uint32_t nxt[S];
+    uint32_t nx0[S], nx1[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        for (int i = 0; i < 4; ++i) {
-            st[s].code = (st[s].code << 8) | fetch(s);
-            advance(s);
-        }
-        nxt[s] = fetch(s);
+        for (int i = 0; i < 4; ++i) st[s].code = (st[s].code << 8) | fetch(s);
+        nx0[s] = fetch(s);
+        nx1[s] = fetch(s);
+        if (STAGED) st[s].ptr -= 2;
+        else st[s].pos -= 2;
     }
 
     // Byte address in tab of (symbol s, this lane) is s * 256 + lane * 4.
@@ -136,14 +147,9 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
     const uint32_t lane4 = (uint32_t)lane * 4;
     const uint32_t amax4 = ((uint32_t)a.A - 1) * 256 + lane4;
     constexpr uint32_t H1 = 1u << (LOGA - 1), H2 = 1u << (LOGA - 2);
-    // Candidates of the first two levels (clamped to the alphabet).
-    const uint32_t sa = CLAMP ? min(H1, (uint32_t)a.A - 1) : H1;
-    const uint32_t sb = CLAMP ? min(H2, (uint32_t)a.A - 1) : H2;
-    const uint32_t sc3 = CLAMP ? min(H1 + H2, (uint32_t)a.A - 1) : H1 + H2;
-    const uint32_t cdf_a = tab[sa * 64 + lane] & 0xFFFFu;
-    const uint32_t cdf_b = tab[sb * 64 + lane] & 0xFFFFu;
-    const uint32_t cdf_c = tab[sc3 * 64 + lane] & 0xFFFFu;
-    const uint32_t ad_a = sa * 256 + lane4, ad_b = sb * 256 + lane4, ad_c = sc3 * 256 + lane4;
+    const uint32_t cdf_a = tab[H1 * 64 + lane] & 0xFFFFu;
+    const uint32_t cdf_b = tab[H2 * 64 + lane] & 0xFFFFu;
+    const uint32_t cdf_c = tab[(H1 + H2) * 64 + lane] & 0xFFFFu;
     const int nmax = n[0];
 
     // Output of the previous token, written one step late.
@@ -165,6 +171,14 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
     };
 
     for (int t = 0; t < nmax; ++t) {
+        if (FUSED && t > 0 && (t & 63) == 0) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                sc_v[s][0] = sc_v[s][1];
+                sc_v[s][1] = sc_v[s][2];
+                sc_v[s][2] = sc_v[s][3];
+            }
+        }
         uint32_t r[S], ad[S];
         // Levels 1 and 2 from registers.
 #pragma unroll
@@ -173,15 +187,14 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
             const bool hi = __umul24(r[s], cdf_a) <= st[s].code;
             const uint32_t c2 = hi ? cdf_c : cdf_b;
             const bool hi2 = __umul24(r[s], c2) <= st[s].code;
-            ad[s] = hi ? (hi2 ? ad_c : ad_a) : (hi2 ? ad_b : lane4);
+            ad[s] = lane4 | (hi ? H1 * 256 : 0u) | (hi2 ? H2 * 256 : 0u);
         }
         // Remaining levels: interleaved branch-free binary searches over LDS.
 #pragma unroll
         for (int i = LOGA - 3; i >= 0; --i) {
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                uint32_t cand = ad[s] + (256u << i);
-                if (CLAMP) cand = min(cand, amax4);
+                const uint32_t cand = ad[s] | (256u << i);
                 const uint32_t ec = *reinterpret_cast<const uint32_t *>(tabb + cand);
                 ad[s] = __umul24(r[s], ec & 0xFFFFu) <= st[s].code ? cand : ad[s];
             }
@@ -196,26 +209,36 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
             // Every stream steps every token (a finished stream keeps decoding
             // zeros); only its output and its checks are guarded.
             DecStream &d = st[s];
+            if (CLAMP) ad[s] = min(ad[s], amax4);
             const uint32_t e = *reinterpret_cast<const uint32_t *>(tabb + ad[s]);
-            const uint32_t sy = (ad[s] - lane4) >> 8;
             d.code -= __umul24(r[s], e & 0xFFFFu);
             d.range = __umul24(r[s], e >> 16);
             if (d.range < kTop) {
-                d.code = (d.code << 8) | nxt[s];
+                d.code = (d.code << 8) | nx0[s];
                 d.range <<= 8;
-                advance(s);
+                uint32_t adv = 1;
                 if (d.range < kTop) {
-                    d.code = (d.code << 8) | fetch(s);
+                    d.code = (d.code << 8) | nx1[s];
                     d.range <<= 8;
-                    advance(s);
+                    adv = 2;
                 }
-                nxt[s] = fetch(s);
+                if (STAGED) {
+                    d.ptr += adv;
+                    nx0[s] = pool[d.ptr];
+                    nx1[s] = pool[d.ptr + 1];
+                } else {
+                    d.pos += adv;
+                    nx0[s] = d.pos < d.len ? (uint32_t)d.gsrc[d.pos] : 0u;
+                    nx1[s] = d.pos + 1 < d.len ? (uint32_t)d.gsrc[d.pos + 1] : 0u;
+                }
             }
             if (t < n[s]) bad_mask |= __ballot(d.code >= d.range);
-            p_sy[s] = sy;
             if (FUSED) {
-                p_dq[s] = dq[sy];
-                p_sc[s] = sc[s * kChunk + t];
+                p_dq[s] = *reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(dq) +
+                                                           ((ad[s] >> 6) & ~3u));
+                p_sc[s] = (uint32_t)__builtin_amdgcn_readlane((int)sc_v[s][0], t & 63);
+            } else {
+                p_sy[s] = ad[s] >> 8;
             }
         }
         p_t = t;
@@ -226,14 +249,30 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
     }
 }
 
-template <int S, bool FUSED, int LOGA, bool CLAMP>
-__global__ __launch_bounds__(64) void k_decode(DecArgs a) {
+// Reads the aligned 32-bit word at payload offset g (g % 4 == 0), with the
+// bytes at or beyond payload_bytes read as zero.
+__device__ __forceinline__ uint32_t load_word(const uint8_t *payload, uint64_t payload_bytes, uint64_t g) {
+    if (g + 4 <= payload_bytes) return *reinterpret_cast<const uint32_t *>(payload + g);
+    uint32_t v = 0;
+    for (int k = 0; k < 4; ++k)
+        if (g + k < payload_bytes) v |= (uint32_t)payload[g + k] << (8 * k);
+    return v;
+}
+
+// Block of NW waves for one (K|V, layer, 64-channel block): wave w decodes
+// the S chunks (group * NW + w) * S + s, lane = channel. The waves share the
+// channel tables, the dequantisation table and an LDS pool for the payload.
+template <int S, bool FUSED, int LOGA, bool CLAMP, int NW>
+__global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // Static LDS sized by the template, so every address folds to an immediate.
+    __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
     __shared__ float dq[128];
-    __shared__ uint32_t tab[(1 << LOGA) * 64];                                   // [symbol][lane]
-    __shared__ __attribute__((aligned(16))) uint8_t stage[S * kStageTile + 8];  // tiles' bytes, then zeros
-    __shared__ uint16_t sc[FUSED ? S * kChunk : 1];                             // per-token scales (bf16)
-    const int lane = threadIdx.x;
+    __shared__ uint32_t pool_w[(NW * kPoolPerWave + kPoolSlack) / 4];        // staged payload
+    __shared__ uint32_t need_w[NW];
+    const int lane = threadIdx.x & 63;
+    // The wave index is uniform across the wave; readfirstlane tells the compiler so,
+    // which keeps everything derived from it in scalar registers.
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int A = a.A;
 
     const int bid = blockIdx.x;
@@ -245,92 +284,117 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     const bool active = c < a.C;
     const int M = a.mt.m[kv][l];
 
+    // This wave's streams: lengths, offsets and the pool bytes they need
+    // (alignment head + bytes + four zero bytes after each of the 64 streams).
     int n[S], t0[S];
-    bool staged[S];
-    DecStream st[S];
+    uint32_t len[S], excl[S], need[S];
+    uint64_t base[S];
     bool corrupt = false;
+    uint32_t need_total = 0;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const int j = g * S + s;
+        const int j = (g * NW + wv) * S + s;
         n[s] = j < a.NC ? min(kChunk, a.T - j * kChunk) : 0;
         t0[s] = min(j, a.NC - 1) * kChunk;
-        uint32_t len = 0, excl = 0, total = 0;
-        uint64_t base = 0;
+        uint32_t total = 0;
+        len[s] = excl[s] = 0;
+        base[s] = 0;
         if (n[s]) {
-            len = active ? a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] : 0u;
-            const uint32_t incl = wave_incl_scan_u32(len, lane);
+            len[s] = active ? a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] : 0u;
+            const uint32_t incl = wave_incl_scan_u32(len[s], lane);
             total = (uint32_t)__shfl((int)incl, 63, 64);
-            excl = incl - len;
-            base = a.tile_off[((int64_t)j * 2 * a.L + slab) * a.CB + cb];
-            if (base > a.payload_bytes || total > a.payload_bytes - base) {
+            excl[s] = incl - len[s];
+            base[s] = a.tile_off[((int64_t)j * 2 * a.L + slab) * a.CB + cb];
+            if (base[s] > a.payload_bytes || total > a.payload_bytes - base[s]) {
                 corrupt = true;  // offsets point outside the payload: decode from nothing
-                len = excl = total = 0;
-                base = 0;
+                len[s] = excl[s] = total = 0;
+                base[s] = 0;
             }
         }
-        // Stage the tile's bytes: words from the aligned start, bounded by the payload.
-        const uint64_t abase = base & ~3ull;
-        const uint32_t head = (uint32_t)(base - abase);
-        staged[s] = total + head <= (uint32_t)kStageTile;
-        if (staged[s] && total) {
-            uint32_t *w = reinterpret_cast<uint32_t *>(stage + s * kStageTile);
-            const uint32_t nw = (head + total + 3) >> 2;
-            for (uint32_t i = lane; i < nw; i += 64) {
-                const uint64_t gaddr = abase + 4ull * i;
-                uint32_t v;
-                if (gaddr + 4 <= a.payload_bytes) {
-                    v = *reinterpret_cast<const uint32_t *>(a.payload + gaddr);
-                } else {
-                    v = 0;
-                    for (int k = 0; k < 4; ++k)
-                        if (gaddr + k < a.payload_bytes) v |= (uint32_t)a.payload[gaddr + k] << (8 * k);
+        need[s] = ((uint32_t)(base[s] & 3u) + total + 4u * 64u + 4u + 3u) & ~3u;
+        need_total += need[s];
+    }
+    if (lane == 0) need_w[wv] = need_total;
+    __syncthreads();
+    uint32_t woff = 0;
+    for (int i = 0; i < wv; ++i) woff += need_w[i];
+    const bool staged = woff + need_total <= (uint32_t)(NW * kPoolPerWave);
+
+    DecStream st[S];
+    uint8_t *pool = reinterpret_cast<uint8_t *>(pool_w);
+    if (staged) {
+        for (uint32_t i = lane; i < need_total / 4; i += 64) pool_w[woff / 4 + i] = 0;
+        uint32_t soff = woff;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            // LDS start of this lane's stream: congruent to its payload offset mod 4.
+            const uint64_t g0 = base[s] + excl[s];
+            const uint32_t ls = soff + (uint32_t)(base[s] & 3u) + excl[s] + 4u * (uint32_t)lane;
+            st[s].ptr = ls;
+            if (len[s]) {
+                const uint64_t gend = g0 + len[s];
+                const uint64_t ga = g0 & ~3ull, ge = (gend + 3) & ~3ull;
+                uint32_t la = ls - (uint32_t)(g0 - ga);
+#pragma unroll 4
+                for (uint64_t gw = ga; gw < ge; gw += 4, la += 4) {
+                    uint32_t v = load_word(a.payload, a.payload_bytes, gw);
+                    if (gw < g0) v &= 0xFFFFFFFFu << (8 * (uint32_t)(g0 - gw));
+                    if (gw + 4 > gend) v &= 0xFFFFFFFFu >> (8 * (uint32_t)(gw + 4 - gend));
+                    pool_w[la >> 2] = v;
                 }
-                w[i] = v;
             }
+            soff += need[s];
         }
-        st[s].len = len;
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        st[s].len = len[s];
         st[s].pos = 0;
-        st[s].ptr = s * kStageTile + head + excl;
-        st[s].end = st[s].ptr + len;
-        st[s].gsrc = a.payload + base + excl;
+        st[s].gsrc = a.payload + base[s] + excl[s];
         st[s].range = 0xFFFFFFFFu;
         st[s].code = 0;
+        if (!staged) st[s].ptr = 0;
     }
 
-    // Tables.
+    // Tables, built by the block's waves together: wave w writes symbols w,
+    // w + NW, ...; entries past the alphabet (up to 2^LOGA) have start 0xFFFF.
     bool bad_table = false;
-    if (active) {
-        const int64_t row = (int64_t)slab * a.C + c;
-        uint32_t prev = a.cdf32 ? (uint32_t)a.cdf32[row * (A + 1)] : (uint32_t)a.cdf16[row * A];
-        bad_table = prev != 0;
-        for (int s = 0; s < A; ++s) {
-            uint32_t nxtv;
-            if (a.cdf32)
-                nxtv = (uint32_t)a.cdf32[row * (A + 1) + s + 1];
-            else
-                nxtv = s + 1 < A ? (uint32_t)a.cdf16[row * A + s + 1] : kProbOne;
-            uint32_t f = nxtv - prev;
-            if (nxtv <= prev || nxtv > kProbOne) {
+    for (int s = wv; s < (1 << LOGA); s += NW) {
+        uint32_t entry = 0xFFFFu;
+        if (s < A && active) {
+            const int64_t row = (int64_t)slab * a.C + c;
+            uint32_t lo, hi;
+            if (a.cdf32) {
+                lo = (uint32_t)a.cdf32[row * (A + 1) + s];
+                hi = (uint32_t)a.cdf32[row * (A + 1) + s + 1];
+            } else {
+                lo = (uint32_t)a.cdf16[row * A + s];
+                hi = s + 1 < A ? (uint32_t)a.cdf16[row * A + s + 1] : kProbOne;
+            }
+            uint32_t f = hi - lo;
+            if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == A - 1 && hi != kProbOne)) {
                 bad_table = true;
                 f = 1;
             }
-            tab[s * 64 + lane] = (prev & 0xFFFFu) | (f << 16);
-            prev = nxtv;
+            entry = (lo & 0xFFFFu) | (f << 16);
+        } else if (s < A) {
+            // Idle lanes: code stays 0, so they always decode symbol 0, whose
+            // frequency 65535 never forces a renormalisation.
+            entry = s == 0 ? 0xFFFFu << 16 : (uint32_t)s | (1u << 16);
         }
-        if (a.cdf32) bad_table |= (uint32_t)a.cdf32[row * (A + 1) + A] != kProbOne;
-    } else {
-        // Idle lanes: code stays 0, so they always decode symbol 0, whose
-        // frequency 65535 never forces a renormalisation.
-        tab[lane] = 0xFFFFu << 16;
-        for (int s = 1; s < A; ++s) tab[s * 64 + lane] = (uint32_t)s | (1u << 16);
+        tab[s * 64 + lane] = entry;
     }
-    if (lane < 8) stage[S * kStageTile + lane] = 0;  // the byte read past every stream
-    if (FUSED) {
+    uint32_t sc_v[S][4];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const uint16_t *sp = a.scale + (int64_t)slab * a.T + t0[s];
-            for (int t = lane; t < n[s]; t += 64) sc[s * kChunk + t] = sp[t];
+    for (int s = 0; s < S; ++s) {
+        const uint16_t *sp = a.scale + (int64_t)slab * a.T + t0[s];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = 64 * k + lane;
+            sc_v[s][k] = FUSED && t < n[s] ? (uint32_t)sp[t] : 0u;
         }
+    }
+    if (FUSED && wv == 0) {
         dq[lane] = __fdiv_rn((float)(lane - M), (float)M);
         dq[lane + 64] = __fdiv_rn((float)(lane + 64 - M), (float)M);
     }
@@ -349,33 +413,35 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     for (int s = 0; s < S; ++s) rowoff[s] = (uint32_t)t0[s] * (uint32_t)a.C * esz;
 
     uint64_t bad_mask = 0;
-    decode_loop<S, FUSED, LOGA, CLAMP>(a, st, n, staged, rowoff, tab, dq, sc, stage, out_rsrc, out_voff,
-                                       lane, bad_mask);
+    if (staged)
+        decode_loop<S, FUSED, LOGA, CLAMP, true>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc, out_voff,
+                                                 lane, bad_mask);
+    else
+        decode_loop<S, FUSED, LOGA, CLAMP, false>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc, out_voff,
+                                                  lane, bad_mask);
     if ((__ballot(active && (corrupt || bad_table)) | (bad_mask & __ballot(active))) && lane == 0)
         atomicOr(a.status, kStCorrupt);
 }
 
-template <int S, bool FUSED, int LOGA>
+template <int S, bool FUSED, int LOGA, int NW>
 static hipError_t launch_decode_s(const Dims &d, const DecArgs &a, hipStream_t s) {
-    static_assert(kStageTile % 4 == 0, "stage holds whole words");
-    const size_t lds = 0;  // all LDS is static
-    const int ngroups = (d.NC + S - 1) / S;
+    const int ngroups = (d.NC + S * NW - 1) / (S * NW);
     const dim3 grid((unsigned)((int64_t)ngroups * 2 * d.L * d.CB));
     if (d.A == (1 << LOGA))
-        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, false>), grid, dim3(64), lds, s, a);
+        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, false, NW>), grid, dim3(64 * NW), 0, s, a);
     else
-        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, true>), grid, dim3(64), lds, s, a);
+        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, true, NW>), grid, dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
-template <int S, bool FUSED>
+template <int S, bool FUSED, int NW>
 static hipError_t launch_decode_f(const Dims &d, const DecArgs &a, hipStream_t s) {
-    if (d.A <= 4) return launch_decode_s<S, FUSED, 2>(d, a, s);
-    if (d.A <= 8) return launch_decode_s<S, FUSED, 3>(d, a, s);
-    if (d.A <= 16) return launch_decode_s<S, FUSED, 4>(d, a, s);
-    if (d.A <= 32) return launch_decode_s<S, FUSED, 5>(d, a, s);
-    if (d.A <= 64) return launch_decode_s<S, FUSED, 6>(d, a, s);
-    return launch_decode_s<S, FUSED, 7>(d, a, s);
+    if (d.A <= 4) return launch_decode_s<S, FUSED, 2, NW>(d, a, s);
+    if (d.A <= 8) return launch_decode_s<S, FUSED, 3, NW>(d, a, s);
+    if (d.A <= 16) return launch_decode_s<S, FUSED, 4, NW>(d, a, s);
+    if (d.A <= 32) return launch_decode_s<S, FUSED, 5, NW>(d, a, s);
+    if (d.A <= 64) return launch_decode_s<S, FUSED, 6, NW>(d, a, s);
+    return launch_decode_s<S, FUSED, 7, NW>(d, a, s);
 }
 
 hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, const DecodeOut &out,
@@ -402,9 +468,12 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     a.A = d.A;
     a.NC = d.NC;
     a.CB = d.CB;
+    // Two streams per lane and four waves per block when there are enough
+    // chunks; otherwise one stream per lane and as few waves as chunks.
     const bool fused = out.kv != nullptr;
-    if (d.NC >= 2) return fused ? launch_decode_f<2, true>(d, a, s) : launch_decode_f<2, false>(d, a, s);
-    return fused ? launch_decode_f<1, true>(d, a, s) : launch_decode_f<1, false>(d, a, s);
+    if (d.NC >= 8) return fused ? launch_decode_f<2, true, 4>(d, a, s) : launch_decode_f<2, false, 4>(d, a, s);
+    if (d.NC >= 2) return fused ? launch_decode_f<1, true, 2>(d, a, s) : launch_decode_f<1, false, 2>(d, a, s);
+    return fused ? launch_decode_f<1, true, 1>(d, a, s) : launch_decode_f<1, false, 1>(d, a, s);
 }
 
 }  // namespace cg

@@ -136,77 +136,97 @@ __device__ __forceinline__ int64_t tile_index(int j, int slab, int cb, int L, in
     return ((int64_t)j * 2 * L + slab) * CB + cb;
 }
 
-// Range coder that writes finished bytes straight to the tile's staging
-// slot ([byte][lane], 64-byte rows). The last byte and the run of 0xFF bytes
-// after it are held back in registers until no carry can reach them, so no
-// byte is ever rewritten. pos starts at -1: the first byte released is the
-// placeholder in front of the stream and is dropped.
+// Range coder. Every byte is written as soon as it is shifted out, except the
+// last one, `pend`, which still takes the carry of the next step. A carry
+// that lifts pend past 0xFF is added to the bytes already written, walking
+// back through the run of 0xFF bytes (rare: the written prefix must end in
+// 0xFF). Bytes go to an LDS stage of R + 1 rows ([row][lane], row 0 holds the
+// placeholder in front of the stream, which no carry ever reaches); bytes
+// past row R go straight to the tile's staging slot in global memory, row
+// pos - 1, through a buffer whose range is the slot (bytes past the slot are
+// dropped; such a stream is re-coded by k_fixup).
+template <int R>
 struct Coder {
-    uint32_t low, range, carry, cache, nff;
-    int pos;
-    __device__ __forceinline__ void init() {
+    uint32_t low, range, pend;
+    int pos;          // row of the next byte (the placeholder is row 0)
+    uint32_t lrow0;   // LDS byte address of this lane's row 0
+    __device__ __forceinline__ void init(uint32_t lds_row0) {
         low = 0;
         range = 0xFFFFFFFFu;
-        carry = 0;
-        cache = 0;
-        nff = 0;
-        pos = -1;
+        pend = 0;
+        pos = 0;
+        lrow0 = lds_row0;
     }
-    __device__ __forceinline__ void put(uint8_t *slot, int lane, uint32_t b) {
-        if ((uint32_t)pos < (uint32_t)kStageBytes) slot[pos * 64 + lane] = (uint8_t)b;
+    __device__ __forceinline__ void put(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane, uint32_t b) {
+        if (pos <= R) lds[lrow0 + pos * 64] = (uint8_t)b;
+        else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, slot, (pos - 1) * 64 + lane, 0, 0);
         ++pos;
     }
-    __device__ __forceinline__ void shift(uint8_t *slot, int lane) {
-        const uint32_t top = low >> 24;
-        if (top != 0xFFu || carry) {
-            put(slot, lane, cache + carry);
-            if (nff) {
-                const uint32_t ff = (0xFFu + carry) & 0xFFu;
-                for (; nff; --nff) put(slot, lane, ff);
+    __device__ __forceinline__ void carry_back(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
+        uint32_t c = pend >> 8;
+        for (int k = min(pos, kStageBytes + 1) - 1; k >= 1 && c; --k) {
+            uint32_t v;
+            if (k <= R) {
+                v = lds[lrow0 + k * 64] + c;
+                lds[lrow0 + k * 64] = (uint8_t)v;
+            } else {
+                v = __builtin_amdgcn_raw_buffer_load_b8(slot, (k - 1) * 64 + lane, 0, 0) + c;
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, slot, (k - 1) * 64 + lane, 0, 0);
             }
-            cache = top;
-            carry = 0;
-        } else {
-            ++nff;
+            c = v >> 8;
         }
+    }
+    __device__ __forceinline__ void shift(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
+        if (pend > 0xFFu) carry_back(lds, slot, lane);
+        put(lds, slot, lane, pend);
+        pend = low >> 24;
         low <<= 8;
     }
-    __device__ __forceinline__ void step(uint32_t e, uint8_t *slot, int lane) {
+    __device__ __forceinline__ void step(uint32_t e, uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
         const uint32_t r = range >> 16;
-        const uint32_t nl = low + __umul24(r, e & 0xFFFFu);
-        carry += (uint32_t)(nl < low);  // at most one wrap between two shifts
+        uint32_t nl;
+        const bool c = __builtin_add_overflow(low, (uint32_t)__umul24(r, e & 0xFFFFu), &nl);
         low = nl;
+        pend += (uint32_t)c;  // at most one wrap between two shifts
         range = __umul24(r, e >> 16);
         // range >= 2^8 here (r >= 2^8, freq >= 1), so two shifts restore it.
         if (range < kTop) {
-            shift(slot, lane);
+            shift(lds, slot, lane);
             range <<= 8;
             if (range < kTop) {
-                shift(slot, lane);
+                shift(lds, slot, lane);
                 range <<= 8;
             }
         }
     }
     // Final value: the smallest multiple of 2^24 >= low; returns the length.
-    __device__ __forceinline__ uint32_t flush(uint8_t *slot, int lane) {
+    __device__ __forceinline__ uint32_t flush(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
         uint32_t b = (low >> 24) + ((low & 0xFFFFFFu) != 0);  // 0..256
-        uint32_t cc = carry;
         if (b == 256u) {
-            cc += 1;
+            pend += 1;
             b = 0;
         }
-        put(slot, lane, (cache + cc) & 0xFFu);
-        const uint32_t ff = (0xFFu + cc) & 0xFFu;
-        for (; nff; --nff) put(slot, lane, ff);
-        if (b) put(slot, lane, b);
-        return (uint32_t)pos;
+        if (pend > 0xFFu) carry_back(lds, slot, lane);
+        put(lds, slot, lane, pend);
+        if (b) put(lds, slot, lane, b);
+        return (uint32_t)(pos - 1);
     }
 };
 
-template <int S, int LOGA>
-__global__ __launch_bounds__(64) void k_encode(EncArgs a) {
-    __shared__ uint32_t tab[(1 << LOGA) * 64];  // [symbol][lane]; the kernel's only LDS
-    const int lane = threadIdx.x;
+constexpr int kLdsRows = 44;  // LDS stage rows per stream (most streams fit)
+
+// Block of NW waves for one (K|V, layer, 64-channel block); wave w codes the
+// S chunks (group * NW + w) * S + s, lane = channel, with the table the
+// waves share.
+template <int S, int LOGA, int NW>
+__global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
+    constexpr int R = kLdsRows;
+    __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
+    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * S * (R + 1) * 64];  // [wave][stream][row][lane]
+    const int lane = threadIdx.x & 63;
+    // Wave index, uniform across the wave (readfirstlane keeps what derives
+    // from it in scalar registers).
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int A = a.A;
 
     // Block -> (chunk group g, slab, cb); all wave-uniform.
@@ -221,15 +241,16 @@ __global__ __launch_bounds__(64) void k_encode(EncArgs a) {
     // Row r of stream s is at rowbase[s] + r * C (uniform), plus lane_off.
     int n[S];
     const uint8_t *rowbase[S];
-    uint8_t *slot[S];
+    __amdgpu_buffer_rsrc_t slot[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const int j = g * S + s;
+        const int j = (g * NW + wv) * S + s;
         n[s] = j < a.NC ? min(kChunk, a.T - j * kChunk) : 0;
         rowbase[s] = a.sym + ((int64_t)slab * a.T + (int64_t)min(j, a.NC - 1) * kChunk) * a.C + cb * 64;
-        slot[s] = a.staging + tile_index(min(j, a.NC - 1), slab, cb, a.L, a.CB) * (kStageBytes * 64);
+        slot[s] = make_rsrc(a.staging + tile_index(min(j, a.NC - 1), slab, cb, a.L, a.CB) * (kStageBytes * 64),
+                            kStageBytes * 64);
     }
-    const int nmax = n[0];  // the first chunk of a group is never the short one
+    const int nmax = n[0];  // the first chunk of a wave is never the short one
 
     // Prefetch ring: symbol of token t of stream s sits in ring[s][t % kRing]
     // from kRing tokens before it is coded. Loads are unconditional (rows are
@@ -245,33 +266,32 @@ __global__ __launch_bounds__(64) void k_encode(EncArgs a) {
         }
     }
 
-    // Tables: one per lane, packed, [symbol][lane].
+    // Tables, built by the block's waves together: one per lane, packed
+    // start | freq << 16, [symbol][lane].
     bool bad = false;
-    if (active) {
-        const int32_t *src = a.cdf + ((int64_t)slab * a.C + c) * (A + 1);
-        uint32_t prev = (uint32_t)src[0];
-        bad = prev != 0 || (uint32_t)src[A] != kProbOne;
-        for (int s = 0; s < A; ++s) {
-            const uint32_t nxt = (uint32_t)src[s + 1];
-            uint32_t f = nxt - prev;
-            if (nxt <= prev || nxt > kProbOne) {
+    for (int s = wv; s < A; s += NW) {
+        uint32_t entry;
+        if (active) {
+            const int32_t *src = a.cdf + ((int64_t)slab * a.C + c) * (A + 1);
+            const uint32_t lo = (uint32_t)src[s], hi = (uint32_t)src[s + 1];
+            uint32_t f = hi - lo;
+            if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == A - 1 && hi != kProbOne)) {
                 bad = true;
                 f = 1;
             }
-            tab[s * 64 + lane] = (prev & 0xFFFFu) | (f << 16);
-            prev = nxt;
+            entry = (lo & 0xFFFFu) | (f << 16);
+        } else {
+            // Idle lanes code with frequency 65535 whatever their symbol: they
+            // never shift a byte out.
+            entry = 0xFFFFu << 16;
         }
-    } else {
-        // Idle lanes code with frequency 65535 whatever their symbol: they
-        // never shift a byte out, so they do not force the wave through the
-        // slow path.
-        for (int s = 0; s < A; ++s) tab[s * 64 + lane] = 0xFFFFu << 16;
+        tab[s * 64 + lane] = entry;
     }
     __syncthreads();
 
-    Coder cd[S];
+    Coder<R> cd[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) cd[s].init();
+    for (int s = 0; s < S; ++s) cd[s].init((uint32_t)((wv * S + s) * (R + 1) * 64 + lane));
     const uint32_t amax = (uint32_t)A - 1;
     uint32_t qmax = 0;
     // Table entry of the next token of every stream, read one step ahead.
@@ -300,16 +320,22 @@ __global__ __launch_bounds__(64) void k_encode(EncArgs a) {
             }
 #pragma unroll
             for (int s = 0; s < S; ++s)
-                if (t < n[s]) cd[s].step(e[s], slot[s], lane);
+                if (t < n[s]) cd[s].step(e[s], stage, slot[s], lane);
         }
     }
 
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         if (n[s] == 0) continue;
-        const uint32_t len0 = cd[s].flush(slot[s], lane);
+        const uint32_t len0 = cd[s].flush(stage, slot[s], lane);
         const uint32_t len = active ? len0 : 0u;
-        const int j = g * S + s;
+        // Copy the used LDS rows 1.. to the slot's rows 0.. (64 lanes write
+        // 256 contiguous bytes per store).
+        const uint32_t rows = min(wave_max_u32(len0), (uint32_t)R);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(stage + (wv * S + s) * (R + 1) * 64 + 64);
+        for (uint32_t w = lane; w < rows * 16; w += 64)
+            __builtin_amdgcn_raw_buffer_store_b32(src[w], slot[s], (int)(w * 4), 0, 0);
+        const int j = (g * NW + wv) * S + s;
         if (active) a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] = (uint16_t)len;
         uint32_t sum = len;
 #pragma unroll
@@ -511,19 +537,26 @@ hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, 
     a.A = d.A;
     a.NC = d.NC;
     a.CB = d.CB;
-    const int ngroups = (d.NC + S - 1) / S;
+    // Four waves per block share a table when there are enough chunks.
+    const int NW = d.NC >= 8 ? 4 : 1;
+    const int ngroups = (d.NC + S * NW - 1) / (S * NW);
     const unsigned blocks = (unsigned)((int64_t)ngroups * 2 * d.L * d.CB);
-    const dim3 grid(blocks), block(64);
-    if (S == 2) {
-        if (d.A <= 16) hipLaunchKernelGGL((k_encode<2, 4>), grid, block, 0, s, a);
-        else if (d.A <= 32) hipLaunchKernelGGL((k_encode<2, 5>), grid, block, 0, s, a);
-        else if (d.A <= 64) hipLaunchKernelGGL((k_encode<2, 6>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_encode<2, 7>), grid, block, 0, s, a);
+    const dim3 grid(blocks), block(64 * NW);
+    if (NW == 4) {
+        if (d.A <= 16) hipLaunchKernelGGL((k_encode<2, 4, 4>), grid, block, 0, s, a);
+        else if (d.A <= 32) hipLaunchKernelGGL((k_encode<2, 5, 4>), grid, block, 0, s, a);
+        else if (d.A <= 64) hipLaunchKernelGGL((k_encode<2, 6, 4>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_encode<2, 7, 4>), grid, block, 0, s, a);
+    } else if (S == 2) {
+        if (d.A <= 16) hipLaunchKernelGGL((k_encode<2, 4, 1>), grid, block, 0, s, a);
+        else if (d.A <= 32) hipLaunchKernelGGL((k_encode<2, 5, 1>), grid, block, 0, s, a);
+        else if (d.A <= 64) hipLaunchKernelGGL((k_encode<2, 6, 1>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_encode<2, 7, 1>), grid, block, 0, s, a);
     } else {
-        if (d.A <= 16) hipLaunchKernelGGL((k_encode<1, 4>), grid, block, 0, s, a);
-        else if (d.A <= 32) hipLaunchKernelGGL((k_encode<1, 5>), grid, block, 0, s, a);
-        else if (d.A <= 64) hipLaunchKernelGGL((k_encode<1, 6>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_encode<1, 7>), grid, block, 0, s, a);
+        if (d.A <= 16) hipLaunchKernelGGL((k_encode<1, 4, 1>), grid, block, 0, s, a);
+        else if (d.A <= 32) hipLaunchKernelGGL((k_encode<1, 5, 1>), grid, block, 0, s, a);
+        else if (d.A <= 64) hipLaunchKernelGGL((k_encode<1, 6, 1>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_encode<1, 7, 1>), grid, block, 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -57,11 +57,99 @@ __global__ __launch_bounds__(256) void k_histogram(const uint8_t *__restrict__ s
     }
 }
 
+// Histogram for C % 4 == 0: one wave owns 256 channels (4 per lane, read as
+// one 32-bit word per token row) of one (K|V, layer) over a tile of at most
+// 65535 tokens, so two 16-bit counts fit one 32-bit word. Counters are
+// lane-private in LDS as uint32 [symbol][pair][lane] (pair 0 holds channels
+// 4*lane and 4*lane+1 in its low and high halves, pair 1 the next two), which
+// keeps every ds_add of a wave on distinct banks; 32 rows are in flight per
+// lane. The table covers 2^LOGA symbols; symbols are read as LOGA-bit fields
+// (so the LDS index stays in range) and the OR of all words flags symbols
+// >= 2^LOGA; a count for a symbol in [A, 2^LOGA) flags the rest.
+template <int LOGA>
+__global__ __launch_bounds__(64) void k_histogram4(const uint8_t *__restrict__ sym,
+                                                   uint32_t *__restrict__ counts,
+                                                   uint32_t *__restrict__ status, int T, int C, int A,
+                                                   int TT) {
+    constexpr int NS = 1 << LOGA;
+    constexpr int U = 32;
+    __shared__ __attribute__((aligned(16))) uint32_t hist[NS * 2 * 64];
+    const int lane = threadIdx.x;
+    const int slab = blockIdx.z;
+    const int c0 = blockIdx.y * 256 + lane * 4;
+    const int t0 = blockIdx.x * TT;
+    const int t1 = min(T, t0 + TT);
+    uint4 *h4 = reinterpret_cast<uint4 *>(hist);
+#pragma unroll
+    for (int i = 0; i < NS * 2 * 64 / 4 / 64; ++i) h4[i * 64 + lane] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+    if (c0 >= C) return;
+    const uint8_t *p = sym + ((int64_t)slab * T + t0) * C + c0;
+    const uint32_t lane4 = (uint32_t)lane * 4;
+    uint8_t *hb = reinterpret_cast<uint8_t *>(hist);
+    uint32_t acc = 0;
+    auto bump = [&](uint32_t w) {
+        acc |= w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t q = __builtin_amdgcn_ubfe(w, 8 * e, LOGA);
+            uint32_t *cnt = reinterpret_cast<uint32_t *>(hb + (q << 9) + lane4 + (e >> 1) * 256);
+            __hip_atomic_fetch_add(cnt, (e & 1) ? 0x10000u : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+        }
+    };
+    int t = t0;
+    for (; t + U <= t1; t += U) {
+        uint32_t w[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) w[i] = *reinterpret_cast<const uint32_t *>(p + (int64_t)i * C);
+        p += (int64_t)U * C;
+#pragma unroll
+        for (int i = 0; i < U; ++i) bump(w[i]);
+    }
+    for (; t < t1; ++t, p += C) bump(*reinterpret_cast<const uint32_t *>(p));
+    bool bad = (acc & ~(0x01010101u * (uint32_t)(NS - 1))) != 0;
+    __builtin_amdgcn_wave_barrier();
+    uint32_t *dst = counts + ((int64_t)slab * C + c0) * A;
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const uint32_t v = hist[(s * 2 + pr) * 64 + lane];
+            if (!v) continue;
+            if (s >= A) {
+                bad = true;
+                continue;
+            }
+            const uint32_t lo = v & 0xFFFFu, hi = v >> 16;
+            if (lo) atomicAdd(dst + (2 * pr) * A + s, lo);
+            if (hi) atomicAdd(dst + (2 * pr + 1) * A + s, hi);
+        }
+    }
+    if (bad) atomicOr(status, kStCorrupt);
+}
+
 hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts,
                             uint32_t *status, hipStream_t s) {
-    // Token tiles: enough blocks to fill the chip.
-    const int cgroups = (d.C + 255) / 256;
     const int64_t slabs = 2LL * d.L;
+    if (d.C % 4 == 0 && (uintptr_t)sym % 4 == 0) {
+        // Token tiles of at most 65535 (16-bit counts) and enough waves to fill the chip.
+        const int cgroups = (d.C + 255) / 256;
+        int TT = min(d.T, 32768);
+        while (slabs * cgroups * ((d.T + TT - 1) / TT) < 8192 && TT > 256) TT = (TT + 1) / 2;
+        const dim3 grid((unsigned)((d.T + TT - 1) / TT), (unsigned)cgroups, (unsigned)slabs);
+        int loga = 2;
+        while ((1 << loga) < d.A) ++loga;
+        switch (loga) {
+        case 2: hipLaunchKernelGGL(k_histogram4<2>, grid, dim3(64), 0, s, sym, counts, status, d.T, d.C, d.A, TT); break;
+        case 3: hipLaunchKernelGGL(k_histogram4<3>, grid, dim3(64), 0, s, sym, counts, status, d.T, d.C, d.A, TT); break;
+        case 4: hipLaunchKernelGGL(k_histogram4<4>, grid, dim3(64), 0, s, sym, counts, status, d.T, d.C, d.A, TT); break;
+        case 5: hipLaunchKernelGGL(k_histogram4<5>, grid, dim3(64), 0, s, sym, counts, status, d.T, d.C, d.A, TT); break;
+        case 6: hipLaunchKernelGGL(k_histogram4<6>, grid, dim3(64), 0, s, sym, counts, status, d.T, d.C, d.A, TT); break;
+        default: hipLaunchKernelGGL(k_histogram4<7>, grid, dim3(64), 0, s, sym, counts, status, d.T, d.C, d.A, TT); break;
+        }
+        return hipGetLastError();
+    }
+    // Any C: one byte per thread and channel.
+    const int cgroups = (d.C + 255) / 256;
     int TT = d.T;
     while (slabs * cgroups * ((d.T + TT - 1) / TT) < 2048 && TT > 512) TT = (TT + 1) / 2;
     const dim3 grid((unsigned)((d.T + TT - 1) / TT), (unsigned)cgroups, (unsigned)slabs);

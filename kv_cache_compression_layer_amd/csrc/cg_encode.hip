@@ -140,11 +140,15 @@ __device__ __forceinline__ int64_t tile_index(int j, int slab, int cb, int L, in
 // last one, `pend`, which still takes the carry of the next step. A carry
 // that lifts pend past 0xFF is added to the bytes already written, walking
 // back through the run of 0xFF bytes (rare: the written prefix must end in
-// 0xFF). Bytes go to an LDS stage of R + 1 rows ([row][lane], row 0 holds the
+// 0xFF). Bytes go to an LDS stage of R + 1 rows ([row][lane], rows kRowPitch
+// bytes apart; a wider pitch that spreads a column over the banks costs a
+// block of residency per CU, which is worth more; row 0 holds the
 // placeholder in front of the stream, which no carry ever reaches); bytes
 // past row R go straight to the tile's staging slot in global memory, row
 // pos - 1, through a buffer whose range is the slot (bytes past the slot are
 // dropped; such a stream is re-coded by k_fixup).
+constexpr int kRowPitch = 64;  // LDS stage row pitch in bytes
+
 template <int R>
 struct Coder {
     uint32_t low, range, pend;
@@ -158,7 +162,7 @@ struct Coder {
         lrow0 = lds_row0;
     }
     __device__ __forceinline__ void put(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane, uint32_t b) {
-        if (pos <= R) lds[lrow0 + pos * 64] = (uint8_t)b;
+        if (pos <= R) lds[lrow0 + pos * kRowPitch] = (uint8_t)b;
         else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, slot, (pos - 1) * 64 + lane, 0, 0);
         ++pos;
     }
@@ -167,8 +171,8 @@ struct Coder {
         for (int k = min(pos, kStageBytes + 1) - 1; k >= 1 && c; --k) {
             uint32_t v;
             if (k <= R) {
-                v = lds[lrow0 + k * 64] + c;
-                lds[lrow0 + k * 64] = (uint8_t)v;
+                v = lds[lrow0 + k * kRowPitch] + c;
+                lds[lrow0 + k * kRowPitch] = (uint8_t)v;
             } else {
                 v = __builtin_amdgcn_raw_buffer_load_b8(slot, (k - 1) * 64 + lane, 0, 0) + c;
                 __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, slot, (k - 1) * 64 + lane, 0, 0);
@@ -222,7 +226,7 @@ template <int S, int LOGA, int NW>
 __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     constexpr int R = kLdsRows;
     __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
-    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * S * (R + 1) * 64];  // [wave][stream][row][lane]
+    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * S * (R + 1) * kRowPitch];  // [wave][stream][row][lane]
     const int lane = threadIdx.x & 63;
     // Wave index, uniform across the wave (readfirstlane keeps what derives
     // from it in scalar registers).
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
 
     Coder<R> cd[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) cd[s].init((uint32_t)((wv * S + s) * (R + 1) * 64 + lane));
+    for (int s = 0; s < S; ++s) cd[s].init((uint32_t)((wv * S + s) * (R + 1) * kRowPitch + lane));
     const uint32_t amax = (uint32_t)A - 1;
     uint32_t qmax = 0;
     // Table entry of the next token of every stream, read one step ahead.
@@ -329,19 +333,52 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
         if (n[s] == 0) continue;
         const uint32_t len0 = cd[s].flush(stage, slot[s], lane);
         const uint32_t len = active ? len0 : 0u;
-        // Copy the used LDS rows 1.. to the slot's rows 0.. (64 lanes write
-        // 256 contiguous bytes per store).
-        const uint32_t rows = min(wave_max_u32(len0), (uint32_t)R);
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(stage + (wv * S + s) * (R + 1) * 64 + 64);
-        for (uint32_t w = lane; w < rows * 16; w += 64)
-            __builtin_amdgcn_raw_buffer_store_b32(src[w], slot[s], (int)(w * 4), 0, 0);
+        const uint32_t incl = wave_incl_scan_u32(len, lane);
+        const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+        const uint32_t excl = incl - len;
+        const uint8_t *lst = stage + (wv * S + s) * (R + 1) * kRowPitch;
+        if (total <= (uint32_t)(R * 64) && !__ballot(len > (uint32_t)kStageBytes)) {
+            // Compact tile: gather the streams' bytes in stream order into
+            // slot bytes [0, total) (64 consecutive bytes per store). Output
+            // byte p belongs to the last stream k with excl_k <= p, found by a
+            // binary search over the lanes' offsets; the spilled rows (>= R)
+            // it may read lie beyond total. The fence orders the spill stores
+            // of other lanes before these loads.
+            // The loop is wave-uniform: the search reads other lanes' offsets.
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+            for (uint32_t p0 = 0; p0 < total; p0 += 64) {
+                const uint32_t p = p0 + (uint32_t)lane;
+                int k = 0;
+                uint32_t sk = 0;
+#pragma unroll
+                for (int step = 32; step > 0; step >>= 1) {
+                    const uint32_t sc = (uint32_t)__shfl((int)excl, k + step, 64);
+                    if (sc <= p) {
+                        k += step;
+                        sk = sc;
+                    }
+                }
+                if (p < total) {
+                    const uint32_t i = p - sk;
+                    uint32_t b;
+                    if (i < (uint32_t)R) b = lst[(i + 1) * kRowPitch + k];
+                    else b = __builtin_amdgcn_raw_buffer_load_b8(slot[s], (int)(i * 64 + k), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, slot[s], (int)p, 0, 0);
+                }
+            }
+        } else {
+            // Copy the used LDS rows 1.. to the slot's rows 0.. (64 lanes write
+            // 256 contiguous bytes per store); k_compact gathers this tile.
+            const uint32_t rows = min(wave_max_u32(len0), (uint32_t)R);
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(lst);
+            for (uint32_t w = lane; w < rows * 16; w += 64)
+                __builtin_amdgcn_raw_buffer_store_b32(src[((w >> 4) + 1) * (kRowPitch / 4) + (w & 15)], slot[s],
+                                                      (int)(w * 4), 0, 0);
+        }
         const int j = (g * NW + wv) * S + s;
         if (active) a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] = (uint16_t)len;
-        uint32_t sum = len;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) sum += (uint32_t)__shfl_xor((int)sum, o, 64);
         const int64_t tile = tile_index(j, slab, cb, a.L, a.CB);
-        if (lane == 0) a.tile_sum[tile] = sum;
+        if (lane == 0) a.tile_sum[tile] = total;
         if (__ballot(len > (uint32_t)kStageBytes) && lane == 0)
             a.overflow_list[atomicAdd(&a.hdr->overflow_count, 1u)] = (uint32_t)tile;
     }
@@ -441,7 +478,6 @@ struct CompactArgs {
 };
 
 __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
-    __shared__ uint32_t start[65];
     const int lane = threadIdx.x;
     const int64_t tile = blockIdx.x;
     const int cb = (int)(tile % a.CB);
@@ -450,22 +486,42 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
     const uint32_t len = c < a.C ? a.lengths[js * a.C + c] : 0u;
     if (__ballot(len > (uint32_t)kStageBytes)) return;  // k_fixup writes this tile
     const uint32_t incl = wave_incl_scan_u32(len, lane);
-    start[lane + 1] = incl;
-    if (lane == 0) start[0] = 0;
-    __syncthreads();
-    const uint32_t total = start[64];
+    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+    const uint32_t excl = incl - len;
     const uint64_t base = a.chunk_off[tile / a.tiles_per_chunk] + a.tile_off[tile];
     const uint8_t *src = a.staging + tile * (kStageBytes * 64);
-    bool over = false;
-    for (uint32_t p = lane; p < total; p += 64) {
-        // Stream k with start[k] <= p < start[k+1].
-        uint32_t k = 0;
+    bool over = base + total > a.cap;
+    if (total <= (uint32_t)(kLdsRows * 64)) {
+        // The encoder left the tile's bytes contiguous: copy them.
+        uint32_t p = lane;
+        for (; p + 192 < total; p += 256) {
+            uint32_t b[4];
 #pragma unroll
-        for (int step = 32; step > 0; step >>= 1)
-            if (start[k + step] <= p) k += step;
-        const uint8_t b = src[(p - start[k]) * 64 + k];
-        if (base + p < a.cap) a.payload[base + p] = b;
-        else over = true;
+            for (int u = 0; u < 4; ++u) b[u] = src[p + 64 * u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (base + p + 64 * u < a.cap) a.payload[base + p + 64 * u] = (uint8_t)b[u];
+        }
+        for (; p < total; p += 64)
+            if (base + p < a.cap) a.payload[base + p] = src[p];
+    } else {
+        // [byte][lane] rows: output byte p belongs to the last stream k with
+        // excl_k <= p (binary search over the lanes' offsets; the loop is
+        // wave-uniform because the search reads other lanes).
+        for (uint32_t p0 = 0; p0 < total; p0 += 64) {
+            const uint32_t p = p0 + (uint32_t)lane;
+            int k = 0;
+            uint32_t sk = 0;
+#pragma unroll
+            for (int step = 32; step > 0; step >>= 1) {
+                const uint32_t sc = (uint32_t)__shfl((int)excl, k + step, 64);
+                if (sc <= p) {
+                    k += step;
+                    sk = sc;
+                }
+            }
+            if (p < total && base + p < a.cap) a.payload[base + p] = src[(p - sk) * 64 + k];
+        }
     }
     if (__ballot(over) && lane == 0) atomicOr(a.status, kStCapacity);
 }

@@ -11,34 +11,32 @@
 //   finish with the smallest multiple of 2^24 that is >= low (one byte, or
 //   none if that byte is zero or the value carries into the bytes before).
 //
-// Three kernels:
+// Kernels:
 //
-// k_encode: one wave per tile = 64 consecutive channels (lane = channel) of
-// one (K|V, layer) and S consecutive 256-token chunks; each lane codes the S
-// streams of its channel interleaved (independent dependency chains), with
-// one table per lane staged in LDS as start | freq << 16 laid out
-// [symbol][lane] (no bank conflicts whatever the symbols); the table is the
-// only LDS the kernel uses, which keeps many waves resident. Symbols come
+// k_encode: a block of four waves owns 64 consecutive channels (lane =
+// channel) of one (K|V, layer) and eight 256-token chunks; each wave codes
+// two chunks per lane interleaved (independent dependency chains). The
+// waves share one table per lane in LDS, start | freq << 16 laid out
+// [symbol][lane] (no bank conflicts whatever the symbols). Symbols come
 // straight from global memory (64 lanes read one 64-byte row per load) into
-// a 16-deep register ring, so the loop never waits on them. Finished bytes
-// go straight to the tile's staging slot in global memory as [byte][lane]
-// rows; the last byte and the run of 0xFF bytes after it are held back in
-// registers until no carry can reach them (the classic "cache + pending"
-// form of the byte range coder), so nothing is ever rewritten. The kernel
-// writes the stream lengths and the tile's byte total. Streams longer than
-// the slot (kStageBytes) mark the tile for k_fixup.
+// a 16-deep register ring, so the loop never waits on them. Bytes are
+// written as soon as they are shifted out into an LDS stage per stream
+// ([row][lane]); rows past the stage spill to the tile's 16 KiB staging slot
+// in global memory. At the end the wave gathers the tile's streams in
+// stream order into the slot, contiguously, and writes the stream lengths
+// and the tile's byte total. A stream longer than the slot (256 bytes)
+// marks the tile for k_fixup.
 //
 // k_tile_scan + k_chunk_scan: exclusive scan of the tile totals in stream
 // order (per chunk, then over the chunk totals) -> tile offsets, chunk
 // offsets and the payload size.
 //
-// k_compact: one wave per tile copies its streams from the staging slot to
-// their final offsets; each lane writes consecutive payload bytes (64 bytes
-// per store instruction), finding its source stream by a search over the
-// scanned lengths.
+// k_compact: one wave per tile copies the gathered tile to its offset (a
+// tile too large for the LDS gather is gathered here from the slot's rows).
 //
 // k_fixup: re-encodes every stream of a marked tile straight to its final
-// offset with the same held-back-byte coder.
+// offset with a byte-at-a-time coder that holds back the last byte and the
+// run of 0xFF after it until no carry can reach them.
 #include "cg_internal.hpp"
 
 namespace cg {

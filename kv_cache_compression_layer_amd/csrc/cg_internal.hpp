@@ -40,7 +40,7 @@ struct Dims {
 // Header of every workspace (first 256 bytes).
 struct WsHeader {
     uint32_t status;
-    uint32_t tile_counter;     // dynamic tile ids for the in-order look-back
+    uint32_t reserved0;
     uint32_t overflow_count;   // tiles whose streams did not fit in LDS
     uint32_t pad0;
     uint64_t payload_total;    // sum of all stream lengths (encode)

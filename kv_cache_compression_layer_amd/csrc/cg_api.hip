@@ -395,10 +395,16 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
     uint8_t *sym = at<uint8_t>(ws, w.sym);
     if ((rc = clear_ws(ws, w, s))) return rc;
     if ((rc = hip_rc(launch_blob_header(blob, hb, b, d, s)))) return rc;
-    if ((rc = hip_rc(launch_quantize(d, mt, reinterpret_cast<const uint16_t *>(kv), sym,
-                                     at<uint16_t>(blob, b.off_scales), status, s))))
-        return rc;
-    if ((rc = hip_rc(launch_histogram(d, sym, counts, status, s)))) return rc;
+    if (quantize_hist_fits(d, kv, sym)) {
+        if ((rc = hip_rc(launch_quantize_hist(d, mt, reinterpret_cast<const uint16_t *>(kv), sym,
+                                              at<uint16_t>(blob, b.off_scales), counts, status, s))))
+            return rc;
+    } else {
+        if ((rc = hip_rc(launch_quantize(d, mt, reinterpret_cast<const uint16_t *>(kv), sym,
+                                         at<uint16_t>(blob, b.off_scales), status, s))))
+            return rc;
+        if ((rc = hip_rc(launch_histogram(d, sym, counts, status, s)))) return rc;
+    }
     if ((rc = hip_rc(launch_cdf(d, counts, cdf, at<uint16_t>(blob, b.off_cdf), status, s)))) return rc;
     EncodeOut o{blob + b.off_payload,
                 (uint64_t)cap - b.off_payload,

@@ -170,6 +170,11 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
         }
     };
 
+    auto store_all = [&](int t) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) store(s, t);
+    };
+
     for (int t = 0; t < nmax; ++t) {
         if (FUSED && t > 0 && (t & 63) == 0) {
 #pragma unroll
@@ -200,10 +205,7 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
             }
         }
         // The previous token's output, now that its LDS reads have landed.
-        if (p_t >= 0) {
-#pragma unroll
-            for (int s = 0; s < S; ++s) store(s, p_t);
-        }
+        if (p_t >= 0) store_all(p_t);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             // Every stream steps every token (a finished stream keeps decoding
@@ -243,10 +245,7 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
         }
         p_t = t;
     }
-    if (p_t >= 0) {
-#pragma unroll
-        for (int s = 0; s < S; ++s) store(s, p_t);
-    }
+    if (p_t >= 0) store_all(p_t);
 }
 
 // Reads the aligned 32-bit word at payload offset g (g % 4 == 0), with the

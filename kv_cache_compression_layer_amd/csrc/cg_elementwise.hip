@@ -62,6 +62,21 @@ __device__ __forceinline__ uint32_t quant1(uint32_t bits16, float f, float Mf) {
 
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 
+// Maximum over the wave, returned in a scalar register: DPP shifts within
+// each row of 16 lanes (max is idempotent, so overlapping windows are fine),
+// then the four row maxima by readlane.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    return max(max(r0, r1), max(r2, r3));
+}
+
 // Per-half max of |bf16| bit patterns (sign cleared) with packed 16-bit max.
 __device__ __forceinline__ uint32_t absmax2(uint32_t acc, uint32_t w) {
     ushort2_t a = __builtin_bit_cast(ushort2_t, acc);
@@ -69,17 +84,20 @@ __device__ __forceinline__ uint32_t absmax2(uint32_t acc, uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
 }
 
-// NV 16-byte vectors per lane hold the row (C <= NV * 512, C % 8 == 0).
-template <int NV>
+// NV 16-byte vectors per lane hold the row (C <= NV * 512, C % 8 == 0;
+// FULL: C == NV * 512, so no lane is idle).
+template <int NV, bool FULL>
 __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict__ kv,
                                                       uint8_t *__restrict__ sym,
                                                       uint16_t *__restrict__ scale,
                                                       uint32_t *__restrict__ status, int L, int T,
                                                       int C, MaxTable mt) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // The row is uniform across the wave; readfirstlane lets the compiler
+    // keep the row arithmetic in scalar registers.
+    const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     if (t >= T) return;
-    const int slab = blockIdx.y, k = slab / L, l = slab - k * L;  // grid: (tokens/4, 2L)
+    const int slab = blockIdx.y, k = slab >= L ? 1 : 0, l = slab - k * L;  // grid: (tokens/4, 2L)
     const int64_t row = (int64_t)slab * T + t;
     const uint16_t *src = kv + (((int64_t)l * 2 + k) * T + t) * C;
     uint8_t *dst = sym + row * C;
@@ -89,7 +107,7 @@ __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int c0 = (i * 64 + lane) * 8;
-        if (c0 < C) {
+        if (FULL || c0 < C) {
             v[i] = *reinterpret_cast<const uint4 *>(src + c0);
         } else {
             v[i] = make_uint4(0, 0, 0, 0);
@@ -97,7 +115,7 @@ __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict
         am2 = absmax2(absmax2(absmax2(absmax2(am2, v[i].x), v[i].y), v[i].z), v[i].w);
     }
     uint32_t am = max(am2 & 0xFFFFu, am2 >> 16);
-    am = wave_max_u32(am);
+    am = wave_max_dpp(am);
     if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
     const int M = mt.m[k][l];
     const float Mf = (float)M;
@@ -106,7 +124,7 @@ __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int c0 = (i * 64 + lane) * 8;
-        if (c0 < C) {
+        if (FULL || c0 < C) {
             const uint32_t lo = quant4(v[i].x, v[i].y, f, Mf);
             const uint32_t hi = quant4(v[i].z, v[i].w, f, Mf);
             *reinterpret_cast<uint2 *>(dst + c0) = make_uint2(lo, hi);
@@ -124,7 +142,7 @@ __global__ __launch_bounds__(256) void k_quantize_any(const uint16_t *__restrict
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const int slab = blockIdx.y, k = slab / L, l = slab - k * L;  // grid: (tokens/4, 2L)
+    const int slab = blockIdx.y, k = slab >= L ? 1 : 0, l = slab - k * L;  // grid: (tokens/4, 2L)
     const int64_t row = (int64_t)slab * T + t;
     const uint16_t *src = kv + (((int64_t)l * 2 + k) * T + t) * C;
     uint8_t *dst = sym + row * C;
@@ -145,15 +163,162 @@ hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv
     const bool aligned = ((uintptr_t)kv % 16 == 0) && ((uintptr_t)sym % 8 == 0);
     if (aligned && d.C % 8 == 0 && d.C <= 2048) {
         const int nv = (d.C + 511) / 512;
+        const bool full = d.C == nv * 512;
+#define CG_QV(N)                                                                                      \
+    if (full) hipLaunchKernelGGL((k_quantize_vec<N, true>), grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt); \
+    else hipLaunchKernelGGL((k_quantize_vec<N, false>), grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt);
         switch (nv) {
-        case 1: hipLaunchKernelGGL(k_quantize_vec<1>, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt); break;
-        case 2: hipLaunchKernelGGL(k_quantize_vec<2>, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt); break;
-        case 3: hipLaunchKernelGGL(k_quantize_vec<3>, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt); break;
-        default: hipLaunchKernelGGL(k_quantize_vec<4>, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt); break;
+        case 1: CG_QV(1) break;
+        case 2: CG_QV(2) break;
+        case 3: CG_QV(3) break;
+        default: CG_QV(4) break;
         }
+#undef CG_QV
     } else {
         hipLaunchKernelGGL(k_quantize_any, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt);
     }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------- quantise + histogram
+
+// The to_bytes path quantises and counts in one pass, so the symbols are
+// not read back for the histogram. A block of 8 waves owns a tile of TT
+// rows (tokens) of one (K|V, layer); each wave quantises two rows at a time
+// exactly as k_quantize_vec does. Lane l always holds the same 8*NV channels
+// ((i*64 + l)*8 + e), so the block keeps lane-column counters in LDS,
+// uint32 [symbol][pair][lane] with the counts of channels e and e+1 of a
+// pair in the low and high halves (TT <= 65535 keeps them in 16 bits); all
+// lanes of an instruction hit distinct banks. Counts are added to the global
+// uint32 [2,L,C,A] table at the end (non-zero entries only). Symbols are
+// below A by construction.
+template <int NV, int LOGA>
+__global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restrict__ kv,
+                                                       uint8_t *__restrict__ sym,
+                                                       uint16_t *__restrict__ scale,
+                                                       uint32_t *__restrict__ counts,
+                                                       uint32_t *__restrict__ status, int L, int T,
+                                                       int C, int A, int TT, MaxTable mt) {
+    constexpr int NS = 1 << LOGA;
+    constexpr int NP = NV * 4;  // channel pairs per lane
+    __shared__ __attribute__((aligned(16))) uint32_t hist[NS * NP * 64];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int slab = blockIdx.y, k = slab >= L ? 1 : 0, l = slab - k * L;
+    const int t0 = blockIdx.x * TT, t1 = min(T, t0 + TT);
+    uint4 *h4 = reinterpret_cast<uint4 *>(hist);
+    for (int i = threadIdx.x; i < NS * NP * 64 / 4; i += 512) h4[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    const int M = mt.m[k][l];
+    const float Mf = (float)M;
+    uint8_t *hb = reinterpret_cast<uint8_t *>(hist);
+    const uint32_t lane4 = (uint32_t)lane * 4;
+    const uint16_t *kv_slab = kv + ((int64_t)l * 2 + k) * T * (int64_t)C;
+    uint8_t *sym_slab = sym + (int64_t)slab * T * (int64_t)C;
+
+    auto count = [&](uint32_t bits, int pair, bool odd) {
+        const uint32_t q = __builtin_amdgcn_ubfe(bits, 0, LOGA);
+        uint32_t *cnt = reinterpret_cast<uint32_t *>(hb + q * (NP * 256) + lane4 + pair * 256);
+        __hip_atomic_fetch_add(cnt, odd ? 0x10000u : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto load_row = [&](int t, uint4 (&v)[NV]) {
+        const uint16_t *src = kv_slab + (int64_t)t * C;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = *reinterpret_cast<const uint4 *>(src + (i * 64 + lane) * 8);
+    };
+    auto do_row = [&](int t, const uint4 (&v)[NV]) {
+        uint32_t am2 = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            am2 = absmax2(absmax2(absmax2(absmax2(am2, v[i].x), v[i].y), v[i].z), v[i].w);
+        const uint32_t am = wave_max_dpp(max(am2 & 0xFFFFu, am2 >> 16));
+        if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
+        const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
+        uint8_t *dst = sym_slab + (int64_t)t * C;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            uint32_t qb[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                qb[2 * j] = quant_bits(__uint_as_float(w[j] << 16), f, Mf);
+                qb[2 * j + 1] = quant_bits(__uint_as_float(w[j] & 0xFFFF0000u), f, Mf);
+            }
+            const uint32_t lo = __builtin_amdgcn_perm(qb[1], qb[0], 0x0c0c0400u) |
+                                __builtin_amdgcn_perm(qb[3], qb[2], 0x04000c0cu);
+            const uint32_t hi = __builtin_amdgcn_perm(qb[5], qb[4], 0x0c0c0400u) |
+                                __builtin_amdgcn_perm(qb[7], qb[6], 0x04000c0cu);
+            *reinterpret_cast<uint2 *>(dst + (i * 64 + lane) * 8) = make_uint2(lo, hi);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) count(qb[e], i * 4 + e / 2, (e & 1) != 0);
+        }
+        if (lane == 0) scale[(int64_t)slab * T + t] = (uint16_t)am;
+    };
+
+    int t = t0 + wv;
+    for (; t + 8 < t1; t += 16) {
+        uint4 va[NV], vb[NV];
+        load_row(t, va);
+        load_row(t + 8, vb);
+        do_row(t, va);
+        do_row(t + 8, vb);
+    }
+    if (t < t1) {
+        uint4 va[NV];
+        load_row(t, va);
+        do_row(t, va);
+    }
+    __syncthreads();
+
+    // Flush: word (s, pair, lane) holds channels c and c + 1 of symbol s.
+    for (int wi = threadIdx.x; wi < NS * NP * 64; wi += 512) {
+        const uint32_t v = hist[wi];
+        if (!v) continue;
+        const int s = wi / (NP * 64), pr = (wi / 64) % NP, ln = wi % 64;
+        const int c = ((pr / 4) * 64 + ln) * 8 + (pr % 4) * 2;
+        if (s >= A) {
+            atomicOr(status, kStCorrupt);
+            continue;
+        }
+        uint32_t *dst = counts + ((int64_t)slab * C + c) * A + s;
+        if (v & 0xFFFFu) atomicAdd(dst, v & 0xFFFFu);
+        if (v >> 16) atomicAdd(dst + A, v >> 16);
+    }
+}
+
+bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym) {
+    return (d.C == 512 || d.C == 1024) && d.A <= 32 && (uintptr_t)kv % 16 == 0 && (uintptr_t)sym % 8 == 0;
+}
+
+hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
+                                uint16_t *scale, uint32_t *counts, uint32_t *status, hipStream_t s) {
+    // Tiles of rows: about 1024 blocks over the call, at most 65535 rows (16-bit counts).
+    int64_t TT = ((int64_t)d.T * 2 * d.L + 1023) / 1024;
+    TT = ((TT + 15) / 16) * 16;
+    if (TT < 256) TT = 256;
+    if (TT > 32768) TT = 32768;
+    const dim3 grid((unsigned)((d.T + TT - 1) / TT), (unsigned)(2 * d.L)), block(512);
+    int loga = 2;
+    while ((1 << loga) < d.A) ++loga;
+    const int tt = (int)TT;
+#define CG_QH(NV, LG) hipLaunchKernelGGL((k_quantize_hist<NV, LG>), grid, block, 0, s, kv, sym, scale, counts, status, d.L, d.T, d.C, d.A, tt, mt)
+    if (d.C == 512) {
+        switch (loga) {
+        case 2: CG_QH(1, 2); break;
+        case 3: CG_QH(1, 3); break;
+        case 4: CG_QH(1, 4); break;
+        default: CG_QH(1, 5); break;
+        }
+    } else {
+        switch (loga) {
+        case 2: CG_QH(2, 2); break;
+        case 3: CG_QH(2, 3); break;
+        case 4: CG_QH(2, 4); break;
+        default: CG_QH(2, 5); break;
+        }
+    }
+#undef CG_QH
     return hipGetLastError();
 }
 
@@ -171,10 +336,10 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
                                                     uint16_t *__restrict__ out, int L, int T, int C,
                                                     MaxTable mt, int vec8) {
     __shared__ float dq_all[4][128];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int t = blockIdx.x * 4 + wv;
     if (t >= T) return;
-    const int slab = blockIdx.y, k = slab / L, l = slab - k * L;  // grid: (tokens/4, 2L)
+    const int slab = blockIdx.y, k = slab >= L ? 1 : 0, l = slab - k * L;  // grid: (tokens/4, 2L)
     const int64_t row = (int64_t)slab * T + t;
     float *dq = dq_all[wv];
     build_dq(dq, mt.m[k][l], lane);

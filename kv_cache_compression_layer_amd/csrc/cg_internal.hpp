@@ -64,6 +64,12 @@ hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv
 hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts, uint32_t *status,
                             hipStream_t s);
 
+// Quantise and histogram in one pass (counts must be zero on entry); only
+// for the shapes quantize_hist_fits() accepts.
+bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym);
+hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
+                                uint16_t *scale, uint32_t *counts, uint32_t *status, hipStream_t s);
+
 // counts -> cdf int32 [2,L,C,A+1]; optionally the u16 wire form [2,L,C,A].
 hipError_t launch_cdf(const Dims &d, const uint32_t *counts, int32_t *cdf, uint16_t *cdf_wire,
                       uint32_t *status, hipStream_t s);

@@ -175,15 +175,13 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
         for (int s = 0; s < S; ++s) store(s, t);
     };
 
-    for (int t = 0; t < nmax; ++t) {
-        if (FUSED && t > 0 && (t & 63) == 0) {
+    // Tokens in blocks of 64: the scale register of a block is loop-invariant.
+    for (int tb = 0; tb < nmax; tb += 64) {
+    uint32_t cur_sc[S];
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
-                sc_v[s][0] = sc_v[s][1];
-                sc_v[s][1] = sc_v[s][2];
-                sc_v[s][2] = sc_v[s][3];
-            }
-        }
+    for (int s = 0; s < S; ++s) cur_sc[s] = sc_v[s][0];
+    const int tend = min(nmax, tb + 64);
+    for (int t = tb; t < tend; ++t) {
         uint32_t r[S], ad[S];
         // Levels 1 and 2 from registers.
 #pragma unroll
@@ -216,20 +214,22 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
             d.code -= __umul24(r[s], e & 0xFFFFu);
             d.range = __umul24(r[s], e >> 16);
             if (d.range < kTop) {
+                // A second shift (range < 2^16) needs a rare symbol (freq <
+                // 2^16 / r); the wave-uniform test keeps its code out of the
+                // common path.
+                const bool two = d.range < (1u << 16);
                 d.code = (d.code << 8) | nx0[s];
-                d.range <<= 8;
-                uint32_t adv = 1;
-                if (d.range < kTop) {
-                    d.code = (d.code << 8) | nx1[s];
-                    d.range <<= 8;
-                    adv = 2;
+                d.range <<= two ? 16 : 8;
+                if (STAGED) d.ptr += 1u + (uint32_t)two;
+                else d.pos += 1u + (uint32_t)two;
+                if (__builtin_amdgcn_ballot_w64(two)) {
+                    __asm__ volatile("" ::: "memory");  // a real branch, not selects
+                    if (two) d.code = (d.code << 8) | nx1[s];
                 }
                 if (STAGED) {
-                    d.ptr += adv;
                     nx0[s] = pool[d.ptr];
                     nx1[s] = pool[d.ptr + 1];
                 } else {
-                    d.pos += adv;
                     nx0[s] = d.pos < d.len ? (uint32_t)d.gsrc[d.pos] : 0u;
                     nx1[s] = d.pos + 1 < d.len ? (uint32_t)d.gsrc[d.pos + 1] : 0u;
                 }
@@ -238,12 +238,19 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
             if (FUSED) {
                 p_dq[s] = *reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(dq) +
                                                            ((ad[s] >> 6) & ~3u));
-                p_sc[s] = (uint32_t)__builtin_amdgcn_readlane((int)sc_v[s][0], t & 63);
+                p_sc[s] = (uint32_t)__builtin_amdgcn_readlane((int)cur_sc[s], t & 63);
             } else {
                 p_sy[s] = ad[s] >> 8;
             }
         }
         p_t = t;
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        sc_v[s][0] = sc_v[s][1];
+        sc_v[s][1] = sc_v[s][2];
+        sc_v[s][2] = sc_v[s][3];
+    }
     }
     if (p_t >= 0) store_all(p_t);
 }

@@ -138,13 +138,14 @@ __device__ __forceinline__ int64_t tile_index(int j, int slab, int cb, int L, in
 // last one, `pend`, which still takes the carry of the next step. A carry
 // that lifts pend past 0xFF is added to the bytes already written, walking
 // back through the run of 0xFF bytes (rare: the written prefix must end in
-// 0xFF). Bytes go to an LDS stage of R + 1 rows ([row][lane], rows kRowPitch
+// 0xFF). Bytes go to an LDS stage of R + 2 rows ([row][lane], rows kRowPitch
 // bytes apart; a wider pitch that spreads a column over the banks costs a
 // block of residency per CU, which is worth more; row 0 holds the
-// placeholder in front of the stream, which no carry ever reaches); bytes
-// past row R go straight to the tile's staging slot in global memory, row
-// pos - 1, through a buffer whose range is the slot (bytes past the slot are
-// dropped; such a stream is re-coded by k_fixup).
+// placeholder in front of the stream, which no carry ever reaches; row R + 1
+// is a spare that takes the LDS writes of rows past R); bytes past row R also
+// go to the tile's staging slot in global memory, row pos - 1, through a
+// buffer whose range is the slot (bytes past the slot are dropped; such a
+// stream is re-coded by k_fixup).
 constexpr int kRowPitch = 64;  // LDS stage row pitch in bytes
 
 template <int R>
@@ -159,9 +160,19 @@ struct Coder {
         pos = 0;
         lrow0 = lds_row0;
     }
+    // Writes byte b at row p: the LDS stage (rows past R land in the spare
+    // row R + 1), and the global slot for rows past the stage, behind a
+    // wave-uniform test since few lanes get there.
+    __device__ __forceinline__ void put_at(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane, int p,
+                                           uint32_t b) {
+        lds[lrow0 + min(p, R + 1) * kRowPitch] = (uint8_t)b;
+        if (__builtin_amdgcn_ballot_w64(p > R)) {
+            __asm__ volatile("" ::: "memory");
+            if (p > R) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, slot, (p - 1) * 64 + lane, 0, 0);
+        }
+    }
     __device__ __forceinline__ void put(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane, uint32_t b) {
-        if (pos <= R) lds[lrow0 + pos * kRowPitch] = (uint8_t)b;
-        else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, slot, (pos - 1) * 64 + lane, 0, 0);
+        put_at(lds, slot, lane, pos, b);
         ++pos;
     }
     __device__ __forceinline__ void carry_back(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
@@ -178,11 +189,13 @@ struct Coder {
             c = v >> 8;
         }
     }
-    __device__ __forceinline__ void shift(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
-        if (pend > 0xFFu) carry_back(lds, slot, lane);
-        put(lds, slot, lane, pend);
-        pend = low >> 24;
-        low <<= 8;
+    // pend past 0xFF: add its carry to the bytes already written. Rare, so it
+    // sits behind a wave-uniform test (and a real branch).
+    __device__ __forceinline__ void settle(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
+        if (__builtin_amdgcn_ballot_w64(pend > 0xFFu)) {
+            __asm__ volatile("" ::: "memory");
+            if (pend > 0xFFu) carry_back(lds, slot, lane);
+        }
     }
     __device__ __forceinline__ void step(uint32_t e, uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
         const uint32_t r = range >> 16;
@@ -191,14 +204,23 @@ struct Coder {
         low = nl;
         pend += (uint32_t)c;  // at most one wrap between two shifts
         range = __umul24(r, e >> 16);
-        // range >= 2^8 here (r >= 2^8, freq >= 1), so two shifts restore it.
+        // range >= 2^8 here (r >= 2^8, freq >= 1): one shift, or two when
+        // range < 2^16 (a rare symbol). Both are done at once: pend goes out,
+        // the top byte of low goes out too on a double shift (uniform branch),
+        // and the next byte of low becomes pend.
         if (range < kTop) {
-            shift(lds, slot, lane);
-            range <<= 8;
-            if (range < kTop) {
-                shift(lds, slot, lane);
-                range <<= 8;
+            const bool two = range < (1u << 16);
+            settle(lds, slot, lane);
+            put_at(lds, slot, lane, pos, pend);
+            if (__builtin_amdgcn_ballot_w64(two)) {
+                __asm__ volatile("" ::: "memory");
+                if (two) put_at(lds, slot, lane, pos + 1, low >> 24);
             }
+            const uint32_t sh = two ? 16u : 8u;
+            pend = __builtin_amdgcn_ubfe(low, 32 - sh, 8);
+            low <<= sh;
+            range <<= sh;
+            pos += two ? 2 : 1;
         }
     }
     // Final value: the smallest multiple of 2^24 >= low; returns the length.
@@ -224,7 +246,7 @@ template <int S, int LOGA, int NW>
 __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     constexpr int R = kLdsRows;
     __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
-    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * S * (R + 1) * kRowPitch];  // [wave][stream][row][lane]
+    __shared__ __attribute__((aligned(16))) uint8_t stage[NW * S * (R + 2) * kRowPitch];  // [wave][stream][row][lane]
     const int lane = threadIdx.x & 63;
     // Wave index, uniform across the wave (readfirstlane keeps what derives
     // from it in scalar registers).
@@ -293,7 +315,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
 
     Coder<R> cd[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) cd[s].init((uint32_t)((wv * S + s) * (R + 1) * kRowPitch + lane));
+    for (int s = 0; s < S; ++s) cd[s].init((uint32_t)((wv * S + s) * (R + 2) * kRowPitch + lane));
     const uint32_t amax = (uint32_t)A - 1;
     uint32_t qmax = 0;
     // Table entry of the next token of every stream, read one step ahead.
@@ -334,7 +356,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
         const uint32_t incl = wave_incl_scan_u32(len, lane);
         const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
         const uint32_t excl = incl - len;
-        const uint8_t *lst = stage + (wv * S + s) * (R + 1) * kRowPitch;
+        const uint8_t *lst = stage + (wv * S + s) * (R + 2) * kRowPitch;
         if (total <= (uint32_t)(R * 64) && !__ballot(len > (uint32_t)kStageBytes)) {
             // Compact tile: gather the streams' bytes in stream order into
             // slot bytes [0, total) (64 consecutive bytes per store). Output

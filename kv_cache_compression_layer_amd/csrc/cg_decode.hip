@@ -94,7 +94,9 @@ struct DecArgs {
 // bytes past its first byte (two renormalisations per symbol at most, two
 // bytes of look-ahead), so reads of a malformed stream stay inside the
 // block's LDS.
-constexpr uint32_t kPoolPerWave = 5760;
+// The block's LDS stays near 30 KiB: at 32 KiB only four blocks fit a CU
+// instead of five, which costs more than the few tiles that do not fit.
+constexpr uint32_t kPoolPerWave = 5376;
 constexpr uint32_t kPoolSlack = 528;
 
 // One stream's decoder state. Staged streams read pool bytes at `ptr` (each
@@ -119,7 +121,7 @@ struct DecStream {
 // dequantisation and store run one token later, so their LDS reads overlap
 // the next search. The per-token scale is wave-uniform: lane i of sc_v[s][k]
 // holds the scale of token 64k + i of stream s, read out with readlane.
-template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED>
+template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED, bool HALF>
 __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S], const int (&n)[S],
                                             const uint32_t (&rowoff)[S], const uint32_t *tab,
                                             const float *dq, uint32_t (&sc_v)[S][4], const uint8_t *pool,
@@ -146,7 +148,13 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
     const uint8_t *tabb = reinterpret_cast<const uint8_t *>(tab);
     const uint32_t lane4 = (uint32_t)lane * 4;
     const uint32_t amax4 = ((uint32_t)a.A - 1) * 256 + lane4;
-    constexpr uint32_t H1 = 1u << (LOGA - 1), H2 = 1u << (LOGA - 2);
+    // Search depth: the whole table, or (HALF) its lower half when the layer's
+    // symbols all lie below the half's top entry; landing on that top entry
+    // then means a symbol at or above it (only in corrupt streams), and a
+    // rare wave-uniform path continues the search upwards.
+    constexpr int SD = HALF ? LOGA - 1 : LOGA;
+    constexpr uint32_t H1 = 1u << (SD - 1), H2 = 1u << (SD - 2);
+    const uint32_t top4 = ((1u << SD) - 1) * 256 + lane4;
     const uint32_t cdf_a = tab[H1 * 64 + lane] & 0xFFFFu;
     const uint32_t cdf_b = tab[H2 * 64 + lane] & 0xFFFFu;
     const uint32_t cdf_c = tab[(H1 + H2) * 64 + lane] & 0xFFFFu;
@@ -194,7 +202,7 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
         }
         // Remaining levels: interleaved branch-free binary searches over LDS.
 #pragma unroll
-        for (int i = LOGA - 3; i >= 0; --i) {
+        for (int i = SD - 3; i >= 0; --i) {
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const uint32_t cand = ad[s] | (256u << i);
@@ -209,6 +217,16 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
             // Every stream steps every token (a finished stream keeps decoding
             // zeros); only its output and its checks are guarded.
             DecStream &d = st[s];
+            if (HALF && __builtin_amdgcn_ballot_w64(ad[s] == top4)) {
+                __asm__ volatile("" ::: "memory");
+                if (ad[s] == top4) {
+                    for (uint32_t cand = top4 + 256; cand < (1u << LOGA) * 256; cand += 256) {
+                        const uint32_t ec = *reinterpret_cast<const uint32_t *>(tabb + cand);
+                        if (__umul24(r[s], ec & 0xFFFFu) > st[s].code) break;
+                        ad[s] = cand;
+                    }
+                }
+            }
             if (CLAMP) ad[s] = min(ad[s], amax4);
             const uint32_t e = *reinterpret_cast<const uint32_t *>(tabb + ad[s]);
             d.code -= __umul24(r[s], e & 0xFFFFu);
@@ -419,12 +437,24 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     for (int s = 0; s < S; ++s) rowoff[s] = (uint32_t)t0[s] * (uint32_t)a.C * esz;
 
     uint64_t bad_mask = 0;
-    if (staged)
-        decode_loop<S, FUSED, LOGA, CLAMP, true>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc, out_voff,
-                                                 lane, bad_mask);
-    else
-        decode_loop<S, FUSED, LOGA, CLAMP, false>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc, out_voff,
-                                                  lane, bad_mask);
+    // The lower half of the table suffices when every symbol of the layer,
+    // 0..2M, lies below its top entry 2^(LOGA-1) - 1.
+    const bool half = LOGA >= 3 && M + 1 <= (1 << (LOGA - 2));
+    if (half) {
+        if (staged)
+            decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc,
+                                                               out_voff, lane, bad_mask);
+        else
+            decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc,
+                                                                out_voff, lane, bad_mask);
+    } else {
+        if (staged)
+            decode_loop<S, FUSED, LOGA, CLAMP, true, false>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc,
+                                                            out_voff, lane, bad_mask);
+        else
+            decode_loop<S, FUSED, LOGA, CLAMP, false, false>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc,
+                                                             out_voff, lane, bad_mask);
+    }
     if ((__ballot(active && (corrupt || bad_table)) | (bad_mask & __ballot(active))) && lane == 0)
         atomicOr(a.status, kStCorrupt);
 }

@@ -94,9 +94,10 @@ struct DecArgs {
 // bytes past its first byte (two renormalisations per symbol at most, two
 // bytes of look-ahead), so reads of a malformed stream stay inside the
 // block's LDS.
-// The block's LDS stays near 30 KiB: at 32 KiB only four blocks fit a CU
-// instead of five, which costs more than the few tiles that do not fit.
-constexpr uint32_t kPoolPerWave = 5376;
+// Residency beats pool size: with eight waves per block and 3840 bytes per
+// wave (~39 KiB per block) four blocks, 32 waves, fit a CU; the few tiles
+// that do not fit read global memory.
+constexpr uint32_t kPoolPerWave = 3840;
 constexpr uint32_t kPoolSlack = 528;
 
 // One stream's decoder state. Staged streams read pool bytes at `ptr` (each
@@ -504,9 +505,10 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     a.A = d.A;
     a.NC = d.NC;
     a.CB = d.CB;
-    // Two streams per lane and four waves per block when there are enough
-    // chunks; otherwise one stream per lane and as few waves as chunks.
+    // Two streams per lane and eight (or four) waves per block when there are
+    // enough chunks; otherwise one stream per lane and as few waves as chunks.
     const bool fused = out.kv != nullptr;
+    if (d.NC >= 16) return fused ? launch_decode_f<2, true, 8>(d, a, s) : launch_decode_f<2, false, 8>(d, a, s);
     if (d.NC >= 8) return fused ? launch_decode_f<2, true, 4>(d, a, s) : launch_decode_f<2, false, 4>(d, a, s);
     if (d.NC >= 2) return fused ? launch_decode_f<1, true, 2>(d, a, s) : launch_decode_f<1, false, 2>(d, a, s);
     return fused ? launch_decode_f<1, true, 1>(d, a, s) : launch_decode_f<1, false, 1>(d, a, s);

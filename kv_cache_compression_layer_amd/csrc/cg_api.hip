@@ -322,7 +322,7 @@ int cg_encode(const cg_desc *desc, const uint8_t *sym, const int32_t *cdf, uint8
     EncodeOut o{payload, (uint64_t)cap, lengths, chunk_off, nullptr, nullptr, 0};
     EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
                 at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging)};
-    return hip_rc(launch_encode(d, sym, cdf, o, ew, s));
+    return hip_rc(launch_encode(d, sym, cdf, o, ew, false, s));
 }
 
 int cg_decode(const cg_desc *desc, const uint8_t *payload, size_t payload_bytes,
@@ -415,7 +415,7 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
                 b.off_payload};
     EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
                 at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging)};
-    return hip_rc(launch_encode(d, sym, cdf, o, ew, s));
+    return hip_rc(launch_encode(d, sym, cdf, o, ew, true, s));
 }
 
 int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,

@@ -242,7 +242,10 @@ constexpr int kLdsRows = 44;  // LDS stage rows per stream (most streams fit)
 // Block of NW waves for one (K|V, layer, 64-channel block); wave w codes the
 // S chunks (group * NW + w) * S + s, lane = channel, with the table the
 // waves share.
-template <int S, int LOGA, int NW>
+// TRUSTED: the symbols come from this library's quantiser, so every symbol
+// is below A and neither the clamp of the table index nor the range check
+// is needed.
+template <int S, int LOGA, int NW, bool TRUSTED>
 __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     constexpr int R = kLdsRows;
     __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
@@ -262,15 +265,17 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     const bool active = c < a.C;
     const int lane_off = active ? lane : (a.C - 1 - cb * 64);  // in-bounds column for idle lanes
 
-    // Row r of stream s is at rowbase[s] + r * C (uniform), plus lane_off.
-    int n[S];
-    const uint8_t *rowbase[S];
+    // Symbols are read through a buffer over this (K|V, layer) slab: the row
+    // offset is wave-uniform (scalar), the column the lane's constant offset.
+    const __amdgpu_buffer_rsrc_t srsrc = make_rsrc(a.sym + (int64_t)slab * a.T * a.C, (uint32_t)((int64_t)a.T * a.C));
+    const int col = cb * 64 + lane_off;
+    int n[S], row0[S];
     __amdgpu_buffer_rsrc_t slot[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int j = (g * NW + wv) * S + s;
         n[s] = j < a.NC ? min(kChunk, a.T - j * kChunk) : 0;
-        rowbase[s] = a.sym + ((int64_t)slab * a.T + (int64_t)min(j, a.NC - 1) * kChunk) * a.C + cb * 64;
+        row0[s] = min(j, a.NC - 1) * kChunk;
         slot[s] = make_rsrc(a.staging + tile_index(min(j, a.NC - 1), slab, cb, a.L, a.CB) * (kStageBytes * 64),
                             kStageBytes * 64);
     }
@@ -285,8 +290,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
         const int last = max(n[s] - 1, 0);
 #pragma unroll
         for (int k = 0; k < kRing; ++k) {
-            const uint8_t *rowp = rowbase[s] + (int64_t)min(k, last) * a.C;
-            ring[s][k] = rowp[lane_off];
+            ring[s][k] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, col, (row0[s] + min(k, last)) * a.C, 0);
         }
     }
 
@@ -320,10 +324,19 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     uint32_t qmax = 0;
     // Table entry of the next token of every stream, read one step ahead.
     uint32_t e_next[S];
+    // Byte address of (symbol q, this lane) in tab, q * 256 + lane * 4: a
+    // trusted symbol is byte 0 of its load, and one byte permute places it
+    // next to lane * 4 (which is below 256).
+    const uint32_t lane4 = (uint32_t)lane * 4;
+    const uint8_t *tabb = reinterpret_cast<const uint8_t *>(tab);
+    auto entry = [&](uint32_t q) -> uint32_t {
+        if (TRUSTED) return *reinterpret_cast<const uint32_t *>(tabb + __builtin_amdgcn_perm(q, lane4, 0x0c0c0400u));
+        return tab[min(q, amax) * 64 + lane];
+    };
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        qmax = max(qmax, ring[s][0]);
-        e_next[s] = tab[min(ring[s][0], amax) * 64 + lane];
+        if (!TRUSTED) qmax = max(qmax, ring[s][0]);
+        e_next[s] = entry(ring[s][0]);
     }
     for (int t0 = 0; t0 < nmax; t0 += kRing) {
 #pragma unroll
@@ -335,12 +348,11 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
                 e[s] = e_next[s];
                 // Refill the slot just consumed with token t + kRing.
                 const int last = max(n[s] - 1, 0);
-                const uint8_t *rowp = rowbase[s] + (int64_t)min(t + kRing, last) * a.C;
-                ring[s][k] = rowp[lane_off];
+                ring[s][k] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, col, (row0[s] + min(t + kRing, last)) * a.C, 0);
                 // Entry of token t + 1 (its symbol has been in the ring for a while).
                 const uint32_t q = ring[s][(k + 1) % kRing];
-                qmax = max(qmax, q);
-                e_next[s] = tab[min(q, amax) * 64 + lane];
+                if (!TRUSTED) qmax = max(qmax, q);
+                e_next[s] = entry(q);
             }
 #pragma unroll
             for (int s = 0; s < S; ++s)
@@ -597,7 +609,7 @@ __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
 size_t encode_staging_bytes(const Dims &d) { return (size_t)d.tiles * kStageBytes * 64; }
 
 hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, const EncodeOut &o,
-                         const EncodeWs &w, hipStream_t s) {
+                         const EncodeWs &w, bool trusted, hipStream_t s) {
     const int S = d.NC >= 2 ? 2 : 1;
     EncArgs a;
     a.sym = sym;
@@ -618,22 +630,23 @@ hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, 
     const int ngroups = (d.NC + S * NW - 1) / (S * NW);
     const unsigned blocks = (unsigned)((int64_t)ngroups * 2 * d.L * d.CB);
     const dim3 grid(blocks), block(64 * NW);
-    if (NW == 4) {
-        if (d.A <= 16) hipLaunchKernelGGL((k_encode<2, 4, 4>), grid, block, 0, s, a);
-        else if (d.A <= 32) hipLaunchKernelGGL((k_encode<2, 5, 4>), grid, block, 0, s, a);
-        else if (d.A <= 64) hipLaunchKernelGGL((k_encode<2, 6, 4>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_encode<2, 7, 4>), grid, block, 0, s, a);
-    } else if (S == 2) {
-        if (d.A <= 16) hipLaunchKernelGGL((k_encode<2, 4, 1>), grid, block, 0, s, a);
-        else if (d.A <= 32) hipLaunchKernelGGL((k_encode<2, 5, 1>), grid, block, 0, s, a);
-        else if (d.A <= 64) hipLaunchKernelGGL((k_encode<2, 6, 1>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_encode<2, 7, 1>), grid, block, 0, s, a);
-    } else {
-        if (d.A <= 16) hipLaunchKernelGGL((k_encode<1, 4, 1>), grid, block, 0, s, a);
-        else if (d.A <= 32) hipLaunchKernelGGL((k_encode<1, 5, 1>), grid, block, 0, s, a);
-        else if (d.A <= 64) hipLaunchKernelGGL((k_encode<1, 6, 1>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_encode<1, 7, 1>), grid, block, 0, s, a);
-    }
+#define CG_ENC(SS, LG, W)                                                                           \
+    do {                                                                                            \
+        if (trusted) hipLaunchKernelGGL((k_encode<SS, LG, W, true>), grid, block, 0, s, a);         \
+        else hipLaunchKernelGGL((k_encode<SS, LG, W, false>), grid, block, 0, s, a);                \
+    } while (0)
+#define CG_ENC_A(SS, W)                           \
+    do {                                          \
+        if (d.A <= 16) CG_ENC(SS, 4, W);          \
+        else if (d.A <= 32) CG_ENC(SS, 5, W);     \
+        else if (d.A <= 64) CG_ENC(SS, 6, W);     \
+        else CG_ENC(SS, 7, W);                    \
+    } while (0)
+    if (NW == 4) CG_ENC_A(2, 4);
+    else if (S == 2) CG_ENC_A(2, 1);
+    else CG_ENC_A(1, 1);
+#undef CG_ENC_A
+#undef CG_ENC
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 

@@ -96,8 +96,10 @@ struct EncodeWs {
 // Bytes of the staging area k_encode needs (one slot per tile).
 size_t encode_staging_bytes(const Dims &d);
 
+// trusted: the symbols come from this library's quantiser (all below A), so
+// the encoder skips its range check.
 hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, const EncodeOut &o,
-                         const EncodeWs &w, hipStream_t s);
+                         const EncodeWs &w, bool trusted, hipStream_t s);
 
 // Decoder table source: int32 [2,L,C,A+1] or the u16 wire form [2,L,C,A].
 struct DecodeIn {

@@ -202,6 +202,27 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
 int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,
                   void *ws, size_t ws_bytes, void *stream);
 
+/* from_bytes into a paged KV cache (the layout a serving engine keeps: fixed
+ * blocks of block_size tokens, located through a block table), as the decode
+ * step of a remote read that feeds such an engine. Same decode and
+ * dequantisation as cg_from_bytes ([P2 s5]); only the destination of each
+ * token row differs: element (l, kv, t, h, d) of the [L,2,T,H,D] result goes
+ * to the bf16 element
+ *   kv_cache[l*layer_stride + kv*kv_stride
+ *            + (block_table[t / block_size] * block_size + t % block_size) * C
+ *            + h*D + d]
+ * (strides in elements). kv_cache: device bf16, caller-owned, large enough
+ * for every address above; block_table: device int32 [ceil(T/block_size)],
+ * each entry in [0, num_blocks); block_size: a power of two >= 4; one
+ * (layer, K|V) region of num_blocks+1 blocks must span < 4 GiB (CG_E_SHAPE
+ * otherwise). Rows of blocks that are not in the table are left untouched.
+ * A table entry outside [0, num_blocks) records CG_E_CORRUPT and the rows of
+ * that block are not written. Workspace: cg_workspace_bytes(CG_OP_FROM_BYTES). */
+int cg_from_bytes_paged(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_cache,
+                        int64_t layer_stride, int64_t kv_stride, int32_t block_size,
+                        const int32_t *block_table, int32_t num_blocks, void *ws, size_t ws_bytes,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -105,6 +105,8 @@ _SIGNATURES = {
     "cg_dequantize": (ctypes.c_int, [_P, _P, _P, _P, _P, _SZ, _P]),
     "cg_to_bytes": (ctypes.c_int, [_P, _P, _P, _SZ, _P, _P, _SZ, _P]),
     "cg_from_bytes": (ctypes.c_int, [_P, _P, _SZ, _P, _P, _SZ, _P]),
+    "cg_from_bytes_paged": (ctypes.c_int, [_P, _P, _SZ, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                           _P, ctypes.c_int32, _P, _SZ, _P]),
 }
 
 
@@ -369,6 +371,28 @@ def cg_from_bytes(desc, blob, blob_size, kv_out, ws, stream=None):
     _check(lib().cg_from_bytes(desc.ptr, _dev(blob, "blob", torch.uint8), blob_size,
                                _dev(kv_out, "kv_out", (torch.bfloat16, torch.uint16, torch.int16), 2 * L * T * C),
                                p, n, _stream_handle(stream)), "cg_from_bytes")
+
+
+def cg_from_bytes_paged(desc, blob, blob_size, kv_cache, layer_stride, kv_stride, block_size, block_table,
+                        num_blocks, ws, stream=None):
+    """from_bytes into a paged cache: token t of (layer l, K|V kv) goes to row
+    block_table[t // block_size] * block_size + t % block_size of the (l, kv)
+    region kv_cache[l*layer_stride + kv*kv_stride:] (strides in elements)."""
+    torch = _torch()
+    T = desc.ntokens
+    if blob_size > blob.numel():
+        raise ValueError("blob_size exceeds the blob tensor")
+    if block_size < 4 or block_size & (block_size - 1):
+        raise CacheGenValueError(CG_E_INVAL, "block_size must be a power of two >= 4")
+    nblk = (T + block_size - 1) // block_size
+    C = desc.nchannels
+    need = (desc.nlayers - 1) * layer_stride + kv_stride + num_blocks * block_size * C
+    p, n = _ws(ws, desc, CG_OP_FROM_BYTES)
+    _check(lib().cg_from_bytes_paged(desc.ptr, _dev(blob, "blob", torch.uint8), blob_size,
+                                     _dev(kv_cache, "kv_cache", (torch.bfloat16, torch.uint16, torch.int16), need),
+                                     layer_stride, kv_stride, block_size,
+                                     _dev(block_table, "block_table", torch.int32, nblk), num_blocks,
+                                     p, n, _stream_handle(stream)), "cg_from_bytes_paged")
 
 
 # ------------------------------------------------------- conveniences

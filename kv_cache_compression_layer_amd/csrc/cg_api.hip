@@ -443,4 +443,39 @@ int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, vo
     return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint32_t>(ws, 0), s));
 }
 
+int cg_from_bytes_paged(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_cache,
+                        int64_t layer_stride, int64_t kv_stride, int32_t block_size,
+                        const int32_t *block_table, int32_t num_blocks, void *ws, size_t ws_bytes,
+                        void *stream) {
+    Dims d;
+    WsLayout w;
+    int rc = prologue(desc, CG_OP_FROM_BYTES, ws, ws_bytes, d, w);
+    if (rc) return rc;
+    if (!blob || !kv_cache || !block_table) return CG_E_INVAL;
+    if ((uintptr_t)blob % 8 || (uintptr_t)kv_cache % 2) return CG_E_INVAL;
+    if (block_size < 4 || (block_size & (block_size - 1)) || num_blocks < 1) return CG_E_INVAL;
+    if (layer_stride < 0 || kv_stride < 0) return CG_E_INVAL;
+    // One (layer, K|V) region, plus a block of slack for dropped rows, is
+    // addressed with 32-bit byte offsets.
+    if (((uint64_t)num_blocks + 1) * (uint64_t)block_size * (uint64_t)d.C * 2 >= (1ull << 32)) return CG_E_SHAPE;
+    const BlobLayout b = blob_layout(d);
+    if ((uint64_t)blob_size < b.off_payload) return CG_E_CORRUPT;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    MaxTable mt;
+    make_max_table(desc, mt);
+    if ((rc = clear_ws(ws, w, s))) return rc;
+    DecodeIn in{blob + b.off_payload,
+                (uint64_t)blob_size - b.off_payload,
+                reinterpret_cast<const uint16_t *>(blob + b.off_lengths),
+                reinterpret_cast<const uint64_t *>(blob + b.off_chunk_off),
+                nullptr,
+                reinterpret_cast<const uint16_t *>(blob + b.off_cdf)};
+    int log2_bs = 0;
+    while ((1 << log2_bs) < block_size) ++log2_bs;
+    DecodeOut out{nullptr, nullptr, reinterpret_cast<const uint16_t *>(blob + b.off_scales),
+                  PagedOut{reinterpret_cast<uint16_t *>(kv_cache), layer_stride, kv_stride, log2_bs,
+                           block_table, num_blocks}};
+    return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint32_t>(ws, 0), s));
+}
+
 }  // extern "C"

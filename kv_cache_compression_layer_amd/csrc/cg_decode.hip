@@ -85,6 +85,7 @@ struct DecArgs {
     uint16_t *kv;
     const uint16_t *scale;
     uint32_t *status;
+    PagedOut paged;
     MaxTable mt;
     int L, T, C, A, NC, CB;
 };
@@ -122,9 +123,18 @@ struct DecStream {
 // dequantisation and store run one token later, so their LDS reads overlap
 // the next search. The per-token scale is wave-uniform: lane i of sc_v[s][k]
 // holds the scale of token 64k + i of stream s, read out with readlane.
-template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED, bool HALF>
+// Row offsets through the block table (PAGED): lane i of pv[s] holds the
+// physical block of logical block b0[s] + i, for the blocks stream s spans.
+template <int S>
+struct PagedRows {
+    uint32_t pv[S];
+    int t0[S], b0[S];
+};
+
+template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED, bool HALF, bool PAGED>
 __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S], const int (&n)[S],
-                                            const uint32_t (&rowoff)[S], const uint32_t *tab,
+                                            const uint32_t (&rowoff)[S], const PagedRows<S> &pg,
+                                            const uint32_t *tab,
                                             const float *dq, uint32_t (&sc_v)[S][4], const uint8_t *pool,
                                             __amdgpu_buffer_rsrc_t out_rsrc, uint32_t out_voff,
                                             int lane, uint64_t &bad_mask) {
@@ -165,9 +175,20 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
     uint32_t p_sy[S], p_sc[S];
     float p_dq[S];
     int p_t = -1;
+    auto row_off = [&](int s, int t) -> uint32_t {
+        if constexpr (PAGED) {
+            const int tt = pg.t0[s] + t;
+            const uint32_t blk =
+                (uint32_t)__builtin_amdgcn_readlane((int)pg.pv[s], (tt >> a.paged.log2_bs) - pg.b0[s]);
+            const uint32_t row = (blk << a.paged.log2_bs) | (uint32_t)(tt & ((1 << a.paged.log2_bs) - 1));
+            return row * (uint32_t)a.C * 2u;
+        } else {
+            return rowoff[s] + (uint32_t)t * (uint32_t)a.C * (FUSED ? 2u : 1u);
+        }
+    };
     auto store = [&](int s, int t) {
         if (t < n[s]) {
-            const uint32_t off = rowoff[s] + (uint32_t)t * (uint32_t)a.C * (FUSED ? 2u : 1u);
+            const uint32_t off = row_off(s, t);
             if (FUSED) {
                 const float x = __fmul_rn(p_dq[s], __uint_as_float(p_sc[s] << 16));
                 const __hip_bfloat16 h = __float2bfloat16(x);
@@ -287,7 +308,7 @@ __device__ __forceinline__ uint32_t load_word(const uint8_t *payload, uint64_t p
 // Block of NW waves for one (K|V, layer, 64-channel block): wave w decodes
 // the S chunks (group * NW + w) * S + s, lane = channel. The waves share the
 // channel tables, the dequantisation table and an LDS pool for the payload.
-template <int S, bool FUSED, int LOGA, bool CLAMP, int NW>
+template <int S, bool FUSED, int LOGA, bool CLAMP, int NW, bool PAGED>
 __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // Static LDS sized by the template, so every address folds to an immediate.
     __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
@@ -431,7 +452,37 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     const uint64_t slab_elems = (uint64_t)a.T * a.C;
     const void *obase = FUSED ? (const void *)(a.kv + ((int64_t)l * 2 + kv) * (int64_t)slab_elems)
                               : (const void *)(a.sym + (int64_t)slab * (int64_t)slab_elems);
-    const __amdgpu_buffer_rsrc_t out_rsrc = make_rsrc(obase, (uint32_t)(slab_elems * esz));
+    __amdgpu_buffer_rsrc_t out_rsrc = make_rsrc(obase, (uint32_t)(slab_elems * esz));
+    PagedRows<S> pg;
+    if constexpr (PAGED) {
+        // The (l, kv) region of the cache; block table entries outside
+        // [0, num_blocks) become num_blocks, whose rows lie past the buffer,
+        // so their stores are dropped (and the call reports corruption).
+        const uint32_t bs_log = (uint32_t)a.paged.log2_bs;
+        const uint32_t region = ((uint32_t)a.paged.num_blocks << bs_log) * (uint32_t)a.C * 2u;
+        out_rsrc = make_rsrc(a.paged.cache + (int64_t)l * a.paged.layer_stride + (int64_t)kv * a.paged.kv_stride,
+                             region);
+        const int nblk_total = (a.T + (1 << bs_log) - 1) >> bs_log;
+        bool bad_block = false;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            pg.t0[s] = t0[s];
+            pg.b0[s] = t0[s] >> bs_log;
+            const int bi = pg.b0[s] + lane;
+            uint32_t v = 0;
+            if (n[s] && bi < nblk_total && bi <= ((t0[s] + n[s] - 1) >> bs_log)) {
+                const int32_t e = a.paged.table[bi];
+                if (e < 0 || e >= a.paged.num_blocks) {
+                    bad_block = true;
+                    v = (uint32_t)a.paged.num_blocks;
+                } else {
+                    v = (uint32_t)e;
+                }
+            }
+            pg.pv[s] = v;
+        }
+        if (__ballot(bad_block) && lane == 0) atomicOr(a.status, kStCorrupt);
+    }
     const uint32_t out_voff = active ? (uint32_t)(cb * 64 + lane) * esz : 0x7FFFFFF0u;
     uint32_t rowoff[S];
 #pragma unroll
@@ -443,42 +494,42 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     const bool half = LOGA >= 3 && M + 1 <= (1 << (LOGA - 2));
     if (half) {
         if (staged)
-            decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                                out_voff, lane, bad_mask);
         else
-            decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                                 out_voff, lane, bad_mask);
     } else {
         if (staged)
-            decode_loop<S, FUSED, LOGA, CLAMP, true, false>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, true, false, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                             out_voff, lane, bad_mask);
         else
-            decode_loop<S, FUSED, LOGA, CLAMP, false, false>(a, st, n, rowoff, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, false, false, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                              out_voff, lane, bad_mask);
     }
     if ((__ballot(active && (corrupt || bad_table)) | (bad_mask & __ballot(active))) && lane == 0)
         atomicOr(a.status, kStCorrupt);
 }
 
-template <int S, bool FUSED, int LOGA, int NW>
+template <int S, bool FUSED, int LOGA, int NW, bool PAGED>
 static hipError_t launch_decode_s(const Dims &d, const DecArgs &a, hipStream_t s) {
     const int ngroups = (d.NC + S * NW - 1) / (S * NW);
     const dim3 grid((unsigned)((int64_t)ngroups * 2 * d.L * d.CB));
     if (d.A == (1 << LOGA))
-        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, false, NW>), grid, dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, false, NW, PAGED>), grid, dim3(64 * NW), 0, s, a);
     else
-        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, true, NW>), grid, dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, true, NW, PAGED>), grid, dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
-template <int S, bool FUSED, int NW>
+template <int S, bool FUSED, int NW, bool PAGED = false>
 static hipError_t launch_decode_f(const Dims &d, const DecArgs &a, hipStream_t s) {
-    if (d.A <= 4) return launch_decode_s<S, FUSED, 2, NW>(d, a, s);
-    if (d.A <= 8) return launch_decode_s<S, FUSED, 3, NW>(d, a, s);
-    if (d.A <= 16) return launch_decode_s<S, FUSED, 4, NW>(d, a, s);
-    if (d.A <= 32) return launch_decode_s<S, FUSED, 5, NW>(d, a, s);
-    if (d.A <= 64) return launch_decode_s<S, FUSED, 6, NW>(d, a, s);
-    return launch_decode_s<S, FUSED, 7, NW>(d, a, s);
+    if (d.A <= 4) return launch_decode_s<S, FUSED, 2, NW, PAGED>(d, a, s);
+    if (d.A <= 8) return launch_decode_s<S, FUSED, 3, NW, PAGED>(d, a, s);
+    if (d.A <= 16) return launch_decode_s<S, FUSED, 4, NW, PAGED>(d, a, s);
+    if (d.A <= 32) return launch_decode_s<S, FUSED, 5, NW, PAGED>(d, a, s);
+    if (d.A <= 64) return launch_decode_s<S, FUSED, 6, NW, PAGED>(d, a, s);
+    return launch_decode_s<S, FUSED, 7, NW, PAGED>(d, a, s);
 }
 
 hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, const DecodeOut &out,
@@ -498,6 +549,7 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     a.kv = out.kv;
     a.scale = out.scale;
     a.status = status;
+    a.paged = out.paged;
     a.mt = mt;
     a.L = d.L;
     a.T = d.T;
@@ -507,6 +559,12 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     a.CB = d.CB;
     // Two streams per lane and eight (or four) waves per block when there are
     // enough chunks; otherwise one stream per lane and as few waves as chunks.
+    if (out.paged.cache) {
+        if (d.NC >= 16) return launch_decode_f<2, true, 8, true>(d, a, s);
+        if (d.NC >= 8) return launch_decode_f<2, true, 4, true>(d, a, s);
+        if (d.NC >= 2) return launch_decode_f<1, true, 2, true>(d, a, s);
+        return launch_decode_f<1, true, 1, true>(d, a, s);
+    }
     const bool fused = out.kv != nullptr;
     if (d.NC >= 16) return fused ? launch_decode_f<2, true, 8>(d, a, s) : launch_decode_f<2, false, 8>(d, a, s);
     if (d.NC >= 8) return fused ? launch_decode_f<2, true, 4>(d, a, s) : launch_decode_f<2, false, 4>(d, a, s);

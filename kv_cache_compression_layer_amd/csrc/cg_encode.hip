@@ -256,8 +256,10 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int A = a.A;
 
-    // Block -> (chunk group g, slab, cb); all wave-uniform.
-    const int bid = blockIdx.x;
+    // Block -> (chunk group g, slab, cb); all wave-uniform. Neighbouring
+    // channel blocks read the two halves of the same 128-byte symbol lines,
+    // so they are kept on one XCD.
+    const int bid = xcd_work_index(blockIdx.x, gridDim.x);
     const int cb = bid % a.CB;
     const int slab = (bid / a.CB) % (2 * a.L);
     const int g = bid / (a.CB * 2 * a.L);

@@ -111,10 +111,22 @@ struct DecodeIn {
     const uint16_t *cdf16;
 };
 
+// Paged output of the fused decoder: element (l, kv, t, c) goes to
+// cache[l*layer_stride + kv*kv_stride + (table[t >> log2_bs] << log2_bs |
+// (t & (bs-1))) * C + c] (bf16 elements).
+struct PagedOut {
+    uint16_t *cache;           // null: contiguous output
+    int64_t layer_stride, kv_stride;
+    int log2_bs;
+    const int32_t *table;      // [ceil(T / bs)] physical block of each logical block
+    int32_t num_blocks;
+};
+
 struct DecodeOut {
     uint8_t *sym;              // stage output, or
     uint16_t *kv;              // fused dequantised bf16 output [L,2,T,C]
     const uint16_t *scale;     // bf16 [2,L,T] (fused only)
+    PagedOut paged;            // fused output through a block table (cache != null)
 };
 
 hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, const DecodeOut &out,
@@ -140,6 +152,17 @@ hipError_t launch_blob_header(uint8_t *blob, const HeaderBytes &h, const BlobLay
 // beyond `bytes` is dropped (stores) or reads 0 (loads).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2): block b runs on XCD b % 8. This maps block b to a work index such that
+// consecutive work indices run on the same XCD, so neighbouring tiles that
+// share cache lines share an L2. A bijection on [0, n).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_work_index(int b, int n) {
+    const int per = n / kXcds;
+    if (b >= per * kXcds) return b;
+    return (b % kXcds) * per + b / kXcds;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

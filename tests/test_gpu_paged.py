@@ -1,0 +1,112 @@
+"""Decode into a paged KV cache (cg_from_bytes_paged) on the GPU.
+
+The paged call runs the same decode and dequantisation as cg_from_bytes and
+only moves each token row to block_table[t // bs] * bs + t % bs of its
+(layer, K|V) region, so it must equal the contiguous result gathered through
+the block table, bit for bit, and leave every other row untouched. The
+contiguous result itself is checked against the oracle here as well.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import bf16_ulp_distance, to_dev, to_np
+from kv_cache_compression_layer_amd import cachegen as cgb
+from kv_cache_compression_layer_amd.synth import generate_kv
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7F7F  # a bf16 bit pattern no decode produces (a large finite value)
+
+
+def _paged_case(kv, bs, extra_blocks, seed, corrupt_block=None):
+    import torch
+
+    L, _, T, H, D = kv.shape
+    C = H * D
+    bk, bv = oracle.default_bins(L)
+    kv_d = to_dev(kv).view(torch.bfloat16)
+    blob = cgb.to_bytes(kv_d, bk, bv)
+    info, _, _ = cgb.peek(blob)
+    desc = cgb.Desc(L, T, H, D, bk, bv)
+    ref = to_np(cgb.from_bytes(blob).view(torch.int16), np.uint16).reshape(L, 2, T, C)
+
+    nblk = (T + bs - 1) // bs
+    num_blocks = nblk + extra_blocks
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(num_blocks)[:nblk].astype(np.int32)
+    if corrupt_block is not None:
+        table[corrupt_block] = num_blocks  # outside [0, num_blocks)
+    cache = torch.full((L, 2, num_blocks, bs, C), SENTINEL, dtype=torch.int16, device="cuda:0")
+    ws = cgb.alloc_workspace(desc, cgb.CG_OP_FROM_BYTES)
+    cgb.cg_from_bytes_paged(desc, blob, int(info["blob_size"]), cache, 2 * num_blocks * bs * C,
+                            num_blocks * bs * C, bs, to_dev(table), num_blocks, ws)
+    status = cgb.cg_read_status(ws)
+    return ref, to_np(cache, np.uint16), table, status, (L, T, C, bs, num_blocks)
+
+
+def _check_gather(ref, cache, table, dims, skip_block=None):
+    L, T, C, bs, num_blocks = dims
+    written = np.zeros((num_blocks, bs), bool)
+    for b, phys in enumerate(table):
+        if b == skip_block:
+            continue
+        t0, t1 = b * bs, min(T, (b + 1) * bs)
+        got = cache[:, :, phys, : t1 - t0, :]
+        np.testing.assert_array_equal(got, ref[:, :, t0:t1, :])
+        written[phys, : t1 - t0] = True
+    # Every row not in the table (and the tail of the last block) is untouched.
+    assert np.all(cache[:, :, ~written, :] == SENTINEL)
+
+
+@pytest.mark.parametrize(
+    "shape,bs,extra",
+    [
+        ((2, 700, 1, 96), 16, 5),    # ragged T, three chunks, C not a multiple of 64
+        ((3, 768, 2, 64), 64, 0),    # exact blocks
+        ((2, 300, 1, 64), 512, 2),   # block larger than a chunk
+        ((1, 64, 1, 40), 4, 3),      # smallest block size, one chunk
+    ],
+)
+def test_paged_equals_contiguous_gather(shape, bs, extra):
+    L, T, H, D = shape
+    kv = generate_kv(L, T, H, D, outlier_frac=0.05, outlier_scale=10.0, seed=700 + bs)
+    ref, cache, table, status, dims = _paged_case(kv, bs, extra, seed=bs)
+    assert status == cgb.CG_OK
+    _check_gather(ref, cache, table, dims)
+
+
+def test_paged_matches_oracle():
+    kv = generate_kv(2, 520, 1, 64, seed=77)
+    ref, cache, table, status, dims = _paged_case(kv, 32, 4, seed=5)
+    assert status == cgb.CG_OK
+    want = oracle.from_bytes(oracle.to_bytes(kv, *oracle.default_bins(2))).reshape(2, 2, 520, 64)
+    L, T, C, bs, _ = dims
+    got = np.concatenate([cache[:, :, table[b], : min(bs, T - b * bs), :] for b in range(len(table))], axis=2)
+    assert bf16_ulp_distance(got, want).max() <= 1
+
+
+def test_paged_bad_block_is_reported_and_not_written():
+    kv = generate_kv(2, 600, 1, 64, seed=91)
+    ref, cache, table, status, dims = _paged_case(kv, 16, 3, seed=9, corrupt_block=7)
+    assert status == cgb.CG_E_CORRUPT
+    _check_gather(ref, cache, table, dims, skip_block=7)
+
+
+def test_paged_rejects_bad_arguments():
+    import torch
+
+    kv = generate_kv(1, 64, 1, 64, seed=1)
+    bk, bv = oracle.default_bins(1)
+    blob = cgb.to_bytes(to_dev(kv).view(torch.bfloat16), bk, bv)
+    desc = cgb.Desc(1, 64, 1, 64, bk, bv)
+    cache = torch.zeros(2 * 8 * 16 * 64, dtype=torch.int16, device="cuda:0")
+    table = torch.zeros(8, dtype=torch.int32, device="cuda:0")
+    ws = cgb.alloc_workspace(desc, cgb.CG_OP_FROM_BYTES)
+    for bs in (3, 12, 0):  # not a power of two >= 4
+        with pytest.raises(ValueError):
+            cgb.cg_from_bytes_paged(desc, blob, blob.numel(), cache, 2 * 8 * bs * 64 if bs else 0, 8 * 16 * 64,
+                                    bs, table, 8, ws)

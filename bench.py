@@ -67,6 +67,30 @@ def time_events(fn, reps, torch):
     return s.elapsed_time(e) / reps
 
 
+def recorded_traffic(workload):
+    """HBM bytes per launch of the fused decoder, from the calibrated rocprofv3
+    counters committed under profiles/, if they were taken on this workload
+    and on the decoder sources as they are now; otherwise None."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in ("kv_cache_compression_layer_amd/csrc/cg_decode.hip",
+                "kv_cache_compression_layer_amd/csrc/cg_internal.hpp"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("traffic k_decode_fused "):
+                    continue
+                kv = dict(item.split("=", 1) for item in line.split()[2:])
+                if kv.get("workload") == workload and kv.get("source_sha256") == sha:
+                    return int(kv["bytes_per_launch"]), os.path.relpath(path, ROOT)
+    return None
+
+
 def cpu_baseline(w, layers):
     """The oracle (scalar C, one thread) on layers [0, layers) of the workload."""
     import oracle
@@ -199,7 +223,96 @@ def main():
     for ws in (ws_q, ws_c, ws_e, ws_d):
         cgb.check_status(ws, what="stage calls")
     stages_ms["from_bytes"] = dec_ms
+    stages_ms["to_bytes"] = enc_ms
+
+    # Decode into a paged cache (16-token blocks, a shuffled block table with
+    # 1% spare blocks), the layout a serving engine keeps.
+    bs = 16
+    nblk = (T + bs - 1) // bs
+    num_blocks = nblk + nblk // 100 + 1
+    gen = torch.Generator(device="cpu").manual_seed(1234)
+    table = torch.randperm(num_blocks, generator=gen)[:nblk].to(torch.int32).to(dev)
+    cache = torch.empty(L * 2 * num_blocks * bs * C, dtype=torch.int16, device=dev)
+    ws_p = cgb.alloc_workspace(desc, cgb.CG_OP_FROM_BYTES, dev)
+
+    def paged():
+        cgb.cg_from_bytes_paged(desc, blob, blob_size, cache, 2 * num_blocks * bs * C, num_blocks * bs * C,
+                                bs, table, num_blocks, ws_p)
+
+    paged()
+    cgb.check_status(ws_p, what="cg_from_bytes_paged")
+    stages_ms["from_bytes_paged"] = time_events(paged, args.stage_reps, torch)
+    del cache
     log(f"stages (ms): {json.dumps({k: round(v, 4) for k, v in stages_ms.items()})}")
+
+    # The same KV as LMCache stores it: one to_bytes call per 256-token chunk,
+    # each with its own tables. All chunks as one batch call, against the
+    # same calls made one by one on the same stream.
+    ct = 256
+    nb = T // ct
+    batch = None
+    if nb >= 2:
+        desc1 = cgb.Desc(L, ct, H, D, desc.bins_k, desc.bins_v)
+        chunks = kv.view(L, 2, nb, ct, C).permute(2, 0, 1, 3, 4).contiguous()
+        stride = (cgb.cg_blob_bound(desc1) + 7) // 8 * 8
+        blobs = torch.empty(nb * stride, dtype=torch.uint8, device=dev)
+        sizes = torch.zeros(nb, dtype=torch.int64, device=dev)
+        ws_be = cgb.alloc_workspace_batch(desc1, nb, stride, cgb.CG_OP_TO_BYTES, dev)
+        ws_bd = cgb.alloc_workspace_batch(desc1, nb, stride, cgb.CG_OP_FROM_BYTES, dev)
+        chunks_out = torch.empty_like(chunks)
+
+        def b_enc():
+            cgb.cg_to_bytes_batch(desc1, nb, chunks, blobs, stride, sizes, ws_be)
+
+        def b_dec():
+            cgb.cg_from_bytes_batch(desc1, nb, blobs, stride, sizes, chunks_out, ws_bd)
+
+        b_enc()
+        cgb.check_status(ws_be, what="cg_to_bytes_batch")
+        b_dec()
+        cgb.check_status(ws_bd, what="cg_from_bytes_batch")
+        b_enc_ms = time_events(b_enc, args.stage_reps, torch)
+        b_dec_ms = time_events(b_dec, args.stage_reps, torch)
+        sizes_h = [int(x) for x in sizes.cpu()]
+        # One call per chunk (views prepared outside the timed region).
+        ws1e = cgb.alloc_workspace(desc1, cgb.CG_OP_TO_BYTES, dev)
+        ws1d = cgb.alloc_workspace(desc1, cgb.CG_OP_FROM_BYTES, dev)
+        blobs2 = torch.empty_like(blobs)
+        sizes2 = torch.zeros(nb, dtype=torch.int64, device=dev)
+        views = [(chunks[b], blobs2[b * stride:(b + 1) * stride], sizes2[b:b + 1], chunks_out[b])
+                 for b in range(nb)]
+
+        def l_enc():
+            for c_in, bl, sz, _ in views:
+                cgb.cg_to_bytes(desc1, c_in, bl, sz, ws1e)
+
+        def l_dec():
+            for (_, bl, _, c_out), n in zip(views, sizes_h):
+                cgb.cg_from_bytes(desc1, bl, n, c_out, ws1d)
+
+        l_enc()
+        cgb.check_status(ws1e, what="cg_to_bytes")
+        assert torch.equal(sizes2, sizes), "batch and per-call blob sizes differ"
+        l_dec()
+        cgb.check_status(ws1d, what="cg_from_bytes")
+        l_enc_ms = time_events(l_enc, 2, torch)
+        l_dec_ms = time_events(l_dec, 2, torch)
+        craw = chunks.numel() * 2
+        batch = {
+            "calls": nb,
+            "tokens_per_call": ct,
+            "to_bytes_ms": b_enc_ms,
+            "from_bytes_ms": b_dec_ms,
+            "to_bytes_GBps": craw / (b_enc_ms * 1e-3) / 1e9,
+            "from_bytes_GBps": craw / (b_dec_ms * 1e-3) / 1e9,
+            "per_call_to_bytes_ms": l_enc_ms,
+            "per_call_from_bytes_ms": l_dec_ms,
+            "per_call_to_bytes_GBps": craw / (l_enc_ms * 1e-3) / 1e9,
+            "per_call_from_bytes_GBps": craw / (l_dec_ms * 1e-3) / 1e9,
+            "compression_ratio": craw / sum(sizes_h),
+        }
+        log(f"batch of {nb} x {ct} tokens: {json.dumps({k: round(v, 4) for k, v in batch.items()})}")
+        del chunks, chunks_out, blobs, blobs2, ws_be, ws_bd, ws1e, ws1d, views
 
     # Achievable copy bandwidth: a device-to-device copy of the raw KV
     # (read + write of 4 GiB), the practical ceiling beside the 8 TB/s spec.
@@ -245,6 +358,10 @@ def main():
         "avg_ms": stages_ms[dom],
         "frac_of_copy": achieved / copy_GBps,
     }
+    rec = recorded_traffic(w.name) if dom == "from_bytes" else None
+    if rec is not None:
+        roofline["traffic"] = rec[0]
+        roofline["traffic_source"] = rec[1]
 
     enc_GBps = raw / (enc_ms * 1e-3) / 1e9
     dec_GBps = raw / (dec_ms * 1e-3) / 1e9
@@ -279,6 +396,7 @@ def main():
         "decode_ms_median": float(np.median(dec_steps)),
         "decode_ms_min": min(dec_steps),
         "copy_GBps": copy_GBps,
+        "paged_decode_GBps": raw / (stages_ms["from_bytes_paged"] * 1e-3) / 1e9,
         "compression_ratio": raw / blob_size,
         "payload_ratio": raw / payload_bytes,
         "blob_bytes": blob_size,
@@ -287,6 +405,7 @@ def main():
         "encode_copy_frac": (raw + blob_size) / (enc_ms * 1e-3) / 1e9 / copy_GBps,
         "decode_copy_frac": (raw + blob_size) / (dec_ms * 1e-3) / 1e9 / copy_GBps,
         "stages_ms": stages_ms,
+        "chunked_batch": batch,
         "roofline": roofline,
         "cpu_baseline": None,
     }

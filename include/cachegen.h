@@ -202,6 +202,30 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
 int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,
                   void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------- batches
+ * Many small calls of one shape, as LMCache makes them (one to_bytes per KV
+ * chunk of 64..768 tokens, each with its own tables, [P2 benchmark]), in one
+ * launch sequence. Call b's KV is kv + b * (its element count), i.e. kv is
+ * [batch, L, 2, T, H, D]; call b's blob is written at blobs + b * blob_stride
+ * and is byte for byte the blob cg_to_bytes writes for that call alone; its
+ * size goes to blob_sizes_dev[b] (device uint64) and into its header.
+ * blob_stride: a multiple of 8, >= the header and sections (cg_blob_layout's
+ * off_payload); >= cg_blob_bound() can never overflow. With a smaller
+ * stride a call that does not fit records CG_E_CAPACITY: blob_sizes_dev then
+ * holds the size every call needs, and the blobs are not usable. The
+ * workspace depends on the stride: cg_workspace_bytes_batch(desc, batch,
+ * blob_stride, CG_OP_TO_BYTES / CG_OP_FROM_BYTES). batch * nlayers <= 32767.
+ *
+ * cg_from_bytes_batch decodes such a batch of blobs (all with this desc) to
+ * kv_out [batch, L, 2, T, H, D]; blob_sizes_dev holds each blob's size. A
+ * blob whose header, size or chunk offsets disagree with desc or with its
+ * lengths records CG_E_CORRUPT (its tokens are decoded from nothing). */
+int64_t cg_workspace_bytes_batch(const cg_desc *desc, int32_t batch, size_t blob_stride, int op);
+int cg_to_bytes_batch(const cg_desc *desc, int32_t batch, const void *kv, uint8_t *blobs, size_t blob_stride,
+                      uint64_t *blob_sizes_dev, void *ws, size_t ws_bytes, void *stream);
+int cg_from_bytes_batch(const cg_desc *desc, int32_t batch, const uint8_t *blobs, size_t blob_stride,
+                        const uint64_t *blob_sizes_dev, void *kv_out, void *ws, size_t ws_bytes, void *stream);
+
 /* from_bytes into a paged KV cache (the layout a serving engine keeps: fixed
  * blocks of block_size tokens, located through a block table), as the decode
  * step of a remote read that feeds such an engine. Same decode and

@@ -107,6 +107,9 @@ _SIGNATURES = {
     "cg_from_bytes": (ctypes.c_int, [_P, _P, _SZ, _P, _P, _SZ, _P]),
     "cg_from_bytes_paged": (ctypes.c_int, [_P, _P, _SZ, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                            _P, ctypes.c_int32, _P, _SZ, _P]),
+    "cg_workspace_bytes_batch": (_I64, [_P, _I32, _SZ, ctypes.c_int]),
+    "cg_to_bytes_batch": (ctypes.c_int, [_P, _I32, _P, _P, _SZ, _P, _P, _SZ, _P]),
+    "cg_from_bytes_batch": (ctypes.c_int, [_P, _I32, _P, _SZ, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -393,6 +396,56 @@ def cg_from_bytes_paged(desc, blob, blob_size, kv_cache, layer_stride, kv_stride
                                      layer_stride, kv_stride, block_size,
                                      _dev(block_table, "block_table", torch.int32, nblk), num_blocks,
                                      p, n, _stream_handle(stream)), "cg_from_bytes_paged")
+
+
+def cg_workspace_bytes_batch(desc: Desc, batch: int, blob_stride: int, op: int) -> int:
+    return _check(lib().cg_workspace_bytes_batch(desc.ptr, batch, blob_stride, op), "cg_workspace_bytes_batch")
+
+
+def alloc_workspace_batch(desc: Desc, batch: int, blob_stride: int, op: int, device="cuda"):
+    """A uint8 device tensor of cg_workspace_bytes_batch(...), 256-byte aligned."""
+    torch = _torch()
+    need = cg_workspace_bytes_batch(desc, batch, blob_stride, op)
+    raw = torch.empty(need + WS_ALIGN, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % WS_ALIGN
+    return raw[off : off + need]
+
+
+def _ws_batch(ws, desc, batch, blob_stride, op):
+    need = cg_workspace_bytes_batch(desc, batch, blob_stride, op)
+    if ws is None:
+        raise ValueError("workspace required")
+    p = _dev(ws, "ws")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {need}")
+    return p, ws.numel() * ws.element_size()
+
+
+def cg_to_bytes_batch(desc, batch, kv, blobs, blob_stride, blob_sizes_dev, ws, stream=None):
+    """`batch` calls of one shape: kv [batch, L, 2, T, H, D] -> blob b at
+    blobs[b * blob_stride:], its size in blob_sizes_dev[b]."""
+    torch = _torch()
+    L, T, C = desc.nlayers, desc.ntokens, desc.nchannels
+    p, n = _ws_batch(ws, desc, batch, blob_stride, CG_OP_TO_BYTES)
+    _check(lib().cg_to_bytes_batch(desc.ptr, batch,
+                                   _dev(kv, "kv", (torch.bfloat16, torch.uint16, torch.int16), batch * 2 * L * T * C),
+                                   _dev(blobs, "blobs", torch.uint8, batch * blob_stride), blob_stride,
+                                   _dev(blob_sizes_dev, "blob_sizes_dev", (torch.int64, torch.uint64), batch),
+                                   p, n, _stream_handle(stream)), "cg_to_bytes_batch")
+
+
+def cg_from_bytes_batch(desc, batch, blobs, blob_stride, blob_sizes_dev, kv_out, ws, stream=None):
+    """Decode `batch` blobs of one shape (blob b at blobs[b * blob_stride:],
+    size blob_sizes_dev[b]) -> kv_out [batch, L, 2, T, H, D]."""
+    torch = _torch()
+    L, T, C = desc.nlayers, desc.ntokens, desc.nchannels
+    p, n = _ws_batch(ws, desc, batch, blob_stride, CG_OP_FROM_BYTES)
+    _check(lib().cg_from_bytes_batch(desc.ptr, batch, _dev(blobs, "blobs", torch.uint8, batch * blob_stride),
+                                     blob_stride,
+                                     _dev(blob_sizes_dev, "blob_sizes_dev", (torch.int64, torch.uint64), batch),
+                                     _dev(kv_out, "kv_out", (torch.bfloat16, torch.uint16, torch.int16),
+                                          batch * 2 * L * T * C),
+                                     p, n, _stream_handle(stream)), "cg_from_bytes_batch")
 
 
 # ------------------------------------------------------- conveniences

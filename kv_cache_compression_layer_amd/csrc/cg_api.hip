@@ -59,6 +59,38 @@ void make_max_table(const cg_desc *desc, MaxTable &mt) {
     }
 }
 
+// The table of a batch of `batch` calls run as one call of batch * L layers:
+// the constants repeat with period L (written out when they fit the table).
+void make_max_table_batch(const cg_desc *desc, int batch, MaxTable &mt) {
+    make_max_table(desc, mt);
+    const int L = desc->nlayers;
+    if ((int64_t)batch * L <= CG_MAX_LAYERS) {
+        for (int l = L; l < batch * L; ++l) {
+            mt.m[0][l] = mt.m[0][l % L];
+            mt.m[1][l] = mt.m[1][l % L];
+        }
+    } else {
+        mt.lper = (uint32_t)L;
+        mt.lmagic = (uint32_t)(((1ull << 32) + L - 1) / L);
+    }
+}
+
+// Sizes of a batch: one call (d) and the virtual call of batch * L layers (vd).
+constexpr int kMaxBatchLayers = 32767;  // grid y-dimension of the per-slab kernels is 2 * layers
+
+int make_dims_batch(const cg_desc *desc, int batch, Dims &d, Dims &vd) {
+    int rc = make_dims(desc, d);
+    if (rc) return rc;
+    if (batch < 1 || (int64_t)batch * d.L > kMaxBatchLayers) return CG_E_SHAPE;
+    vd = d;
+    vd.L = batch * d.L;
+    vd.N = 2LL * vd.L * vd.T * vd.C;
+    vd.NS = (int64_t)vd.NC * 2 * vd.L * vd.C;
+    vd.tiles = (int64_t)vd.NC * 2 * vd.L * vd.CB;
+    if (vd.N >= (1LL << 40) || vd.tiles >= (1LL << 31)) return CG_E_SHAPE;
+    return CG_OK;
+}
+
 BlobLayout blob_layout(const Dims &d) {
     BlobLayout b;
     b.header_bytes = align_up(kHdrFixed + 2ull * d.L, kAlign);
@@ -72,8 +104,8 @@ BlobLayout blob_layout(const Dims &d) {
 
 // Workspace regions (byte offsets; 0 = unused). Region 0 is the WsHeader.
 struct WsLayout {
-    uint64_t counts = 0, tile_sum = 0, tile_off = 0, chunk_total = 0, overflow = 0, staging = 0, cdf = 0,
-             sym = 0;
+    uint64_t counts = 0, tile_sum = 0, tile_off = 0, chunk_total = 0, overflow = 0, staging = 0, sym = 0,
+             scan = 0;
     uint64_t clear_end = kWsAlign;  // bytes from 0 that must start zeroed
     uint64_t total = kWsAlign;
 };
@@ -97,10 +129,12 @@ WsLayout ws_layout(const Dims &d, int op) {
         w.chunk_total = take(8ull * d.NC);
         w.overflow = take(4ull * d.tiles);
         w.staging = take(encode_staging_bytes(d));
+        w.scan = take(tile_scan_tmp_bytes(d));
         break;
     case CG_OP_DECODE:
     case CG_OP_FROM_BYTES:
         w.tile_off = take(8ull * d.tiles);
+        w.scan = take(tile_scan_tmp_bytes(d));
         break;
     case CG_OP_TO_BYTES:
         w.counts = take(4ull * 2 * d.L * d.C * d.A);
@@ -110,8 +144,8 @@ WsLayout ws_layout(const Dims &d, int op) {
         w.chunk_total = take(8ull * d.NC);
         w.overflow = take(4ull * d.tiles);
         w.staging = take(encode_staging_bytes(d));
-        w.cdf = take(4ull * 2 * d.L * d.C * (d.A + 1));
         w.sym = take((uint64_t)d.N);
+        w.scan = take(tile_scan_tmp_bytes(d));
         break;
     default:
         break;
@@ -152,6 +186,25 @@ uint64_t get_le(const uint8_t *p, int n) {
     return v;
 }
 
+// Header bytes of a blob (the size field, bytes 40..47, is written by the
+// encoder once the payload size is known).
+void make_header(const cg_desc *desc, const Dims &d, const BlobLayout &b, HeaderBytes &hb) {
+    memset(&hb, 0, sizeof hb);
+    hb.n = (uint32_t)b.header_bytes;
+    memcpy(hb.b, "CGMX", 4);
+    put_le(hb.b + 4, 1, 2);
+    put_le(hb.b + 6, 1, 2);
+    put_le(hb.b + 8, (uint64_t)d.L, 4);
+    put_le(hb.b + 12, (uint64_t)d.T, 4);
+    put_le(hb.b + 16, (uint64_t)d.H, 4);
+    put_le(hb.b + 20, (uint64_t)d.D, 4);
+    put_le(hb.b + 24, (uint64_t)kChunk, 4);
+    put_le(hb.b + 28, (uint64_t)d.NC, 4);
+    put_le(hb.b + 32, (uint64_t)d.A, 4);
+    memcpy(hb.b + kHdrFixed, desc->bins_k, (size_t)d.L);
+    memcpy(hb.b + kHdrFixed + d.L, desc->bins_v, (size_t)d.L);
+}
+
 void fill_info(const Dims &d, const BlobLayout &b, cg_blob_info *out) {
     out->nlayers = d.L;
     out->ntokens = d.T;
@@ -168,6 +221,74 @@ void fill_info(const Dims &d, const BlobLayout &b, cg_blob_info *out) {
     out->off_chunk_off = b.off_chunk_off;
     out->off_lengths = b.off_lengths;
     out->off_payload = b.off_payload;
+}
+
+// Quantise, tables and range coding of one call (or of the virtual call of
+// a batch) into the blob sections `scales`, `wire` and `o`; the workspace is
+// ws_layout(d, CG_OP_TO_BYTES). When one quantiser block covers a whole
+// (K|V, layer) slab it builds the tables itself (no counts to clear, no
+// k_cdf); the encoder reads the u16 tables from the blob.
+int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *scales, uint16_t *wire,
+                const EncodeOut &o, void *ws, const WsLayout &w, hipStream_t s) {
+    uint32_t *status = at<uint32_t>(ws, 0);
+    uint32_t *counts = at<uint32_t>(ws, w.counts);
+    uint8_t *sym = at<uint8_t>(ws, w.sym);
+    const uint16_t *kv16 = reinterpret_cast<const uint16_t *>(kv);
+    const bool qh = quantize_hist_fits(d, kv, sym);
+    const bool fused = qh && quantize_hist_fuses_cdf(d, wire);
+    int rc = hip_rc(launch_fill_u32(status, 0u, (int64_t)((fused ? kWsAlign : w.clear_end) / 4), s));
+    if (rc) return rc;
+    if (qh) {
+        rc = hip_rc(launch_quantize_hist(d, mt, kv16, sym, scales, counts, fused ? wire : nullptr, status, s));
+        if (rc) return rc;
+    } else {
+        if ((rc = hip_rc(launch_quantize(d, mt, kv16, sym, scales, status, s)))) return rc;
+        if ((rc = hip_rc(launch_histogram(d, sym, counts, status, s)))) return rc;
+    }
+    if (!fused && (rc = hip_rc(launch_cdf(d, counts, nullptr, wire, status, s)))) return rc;
+    EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
+                at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging),
+                at<uint64_t>(ws, w.scan)};
+    return hip_rc(launch_encode(d, sym, nullptr, wire, o, ew, true, s));
+}
+
+// Workspace of a batch: the virtual call's workspace, then the virtual blob
+// (payload capacity: the batch's blobs' payload capacity), the pieces and
+// the per-(call, chunk, K|V) payload sizes.
+struct BatchWs {
+    WsLayout w;
+    uint64_t vblob = 0, vcap = 0, pieces = 0, piece_len = 0, vsize = 0, total = 0;
+};
+
+BatchWs batch_ws(const Dims &d, const Dims &vd, int B, uint64_t stride, int op) {
+    BatchWs bw;
+    bw.w = ws_layout(vd, op);
+    uint64_t off = bw.w.total;
+    auto take = [&](uint64_t bytes) {
+        const uint64_t o = off;
+        off += align_up(bytes, kWsAlign);
+        return o;
+    };
+    const BlobLayout lay = blob_layout(d), vlay = blob_layout(vd);
+    bw.vcap = (uint64_t)B * (stride > lay.off_payload ? stride - lay.off_payload : 0);
+    bw.vblob = take(vlay.off_payload + bw.vcap);
+    bw.pieces = take((uint64_t)B * (4 + 4ull * d.NC) * sizeof(Piece));
+    bw.piece_len = take(16ull * B * d.NC);
+    bw.vsize = take(8);
+    bw.total = off;
+    return bw;
+}
+
+BatchGeom batch_geom(const Dims &d, const Dims &vd, int B, uint64_t stride) {
+    BatchGeom g;
+    g.d = d;
+    g.vd = vd;
+    g.lay = blob_layout(d);
+    g.vlay = blob_layout(vd);
+    g.B = B;
+    g.stride = stride;
+    g.npieces = 4 + 4 * d.NC;
+    return g;
 }
 
 }  // namespace
@@ -321,8 +442,9 @@ int cg_encode(const cg_desc *desc, const uint8_t *sym, const int32_t *cdf, uint8
     if ((rc = clear_ws(ws, w, s))) return rc;
     EncodeOut o{payload, (uint64_t)cap, lengths, chunk_off, nullptr, nullptr, 0};
     EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
-                at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging)};
-    return hip_rc(launch_encode(d, sym, cdf, o, ew, false, s));
+                at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging),
+                at<uint64_t>(ws, w.scan)};
+    return hip_rc(launch_encode(d, sym, cdf, nullptr, o, ew, false, s));
 }
 
 int cg_decode(const cg_desc *desc, const uint8_t *payload, size_t payload_bytes,
@@ -339,7 +461,8 @@ int cg_decode(const cg_desc *desc, const uint8_t *payload, size_t payload_bytes,
     if ((rc = clear_ws(ws, w, s))) return rc;
     DecodeIn in{payload, (uint64_t)payload_bytes, lengths, chunk_off, cdf, nullptr};
     DecodeOut out{sym, nullptr, nullptr};
-    return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint32_t>(ws, 0), s));
+    return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
+                                at<uint32_t>(ws, 0), s));
 }
 
 int cg_dequantize(const cg_desc *desc, const uint8_t *sym, const uint16_t *scale, void *kv_out,
@@ -374,38 +497,9 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
     make_max_table(desc, mt);
 
     HeaderBytes hb;
-    memset(&hb, 0, sizeof hb);
-    hb.n = (uint32_t)b.header_bytes;
-    memcpy(hb.b, "CGMX", 4);
-    put_le(hb.b + 4, 1, 2);
-    put_le(hb.b + 6, 1, 2);
-    put_le(hb.b + 8, (uint64_t)d.L, 4);
-    put_le(hb.b + 12, (uint64_t)d.T, 4);
-    put_le(hb.b + 16, (uint64_t)d.H, 4);
-    put_le(hb.b + 20, (uint64_t)d.D, 4);
-    put_le(hb.b + 24, (uint64_t)kChunk, 4);
-    put_le(hb.b + 28, (uint64_t)d.NC, 4);
-    put_le(hb.b + 32, (uint64_t)d.A, 4);
-    memcpy(hb.b + kHdrFixed, desc->bins_k, (size_t)d.L);
-    memcpy(hb.b + kHdrFixed + d.L, desc->bins_v, (size_t)d.L);
+    make_header(desc, d, b, hb);
 
-    uint32_t *status = at<uint32_t>(ws, 0);
-    uint32_t *counts = at<uint32_t>(ws, w.counts);
-    int32_t *cdf = at<int32_t>(ws, w.cdf);
-    uint8_t *sym = at<uint8_t>(ws, w.sym);
-    if ((rc = clear_ws(ws, w, s))) return rc;
     if ((rc = hip_rc(launch_blob_header(blob, hb, b, d, s)))) return rc;
-    if (quantize_hist_fits(d, kv, sym)) {
-        if ((rc = hip_rc(launch_quantize_hist(d, mt, reinterpret_cast<const uint16_t *>(kv), sym,
-                                              at<uint16_t>(blob, b.off_scales), counts, status, s))))
-            return rc;
-    } else {
-        if ((rc = hip_rc(launch_quantize(d, mt, reinterpret_cast<const uint16_t *>(kv), sym,
-                                         at<uint16_t>(blob, b.off_scales), status, s))))
-            return rc;
-        if ((rc = hip_rc(launch_histogram(d, sym, counts, status, s)))) return rc;
-    }
-    if ((rc = hip_rc(launch_cdf(d, counts, cdf, at<uint16_t>(blob, b.off_cdf), status, s)))) return rc;
     EncodeOut o{blob + b.off_payload,
                 (uint64_t)cap - b.off_payload,
                 at<uint16_t>(blob, b.off_lengths),
@@ -413,9 +507,7 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
                 blob_size_dev,
                 blob + 40,
                 b.off_payload};
-    EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
-                at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging)};
-    return hip_rc(launch_encode(d, sym, cdf, o, ew, true, s));
+    return encode_call(d, mt, kv, at<uint16_t>(blob, b.off_scales), at<uint16_t>(blob, b.off_cdf), o, ws, w, s);
 }
 
 int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,
@@ -440,7 +532,93 @@ int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, vo
                 reinterpret_cast<const uint16_t *>(blob + b.off_cdf)};
     DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
                   reinterpret_cast<const uint16_t *>(blob + b.off_scales)};
-    return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint32_t>(ws, 0), s));
+    return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
+                                at<uint32_t>(ws, 0), s));
+}
+
+int64_t cg_workspace_bytes_batch(const cg_desc *desc, int32_t batch, size_t blob_stride, int op) {
+    Dims d, vd;
+    const int rc = make_dims_batch(desc, batch, d, vd);
+    if (rc) return rc;
+    if (op != CG_OP_TO_BYTES && op != CG_OP_FROM_BYTES) return CG_E_INVAL;
+    return (int64_t)batch_ws(d, vd, batch, (uint64_t)blob_stride, op).total;
+}
+
+int cg_to_bytes_batch(const cg_desc *desc, int32_t batch, const void *kv, uint8_t *blobs, size_t blob_stride,
+                      uint64_t *blob_sizes_dev, void *ws, size_t ws_bytes, void *stream) {
+    Dims d, vd;
+    int rc = make_dims_batch(desc, batch, d, vd);
+    if (rc) return rc;
+    if (!kv || !blobs || !blob_sizes_dev || !ws) return CG_E_INVAL;
+    if ((uintptr_t)blobs % 8 || blob_stride % 8 || (uintptr_t)ws % kWsAlign) return CG_E_INVAL;
+    const BlobLayout lay = blob_layout(d), vlay = blob_layout(vd);
+    if ((uint64_t)blob_stride < lay.off_payload) return CG_E_CAPACITY;
+    const BatchWs bw = batch_ws(d, vd, batch, blob_stride, CG_OP_TO_BYTES);
+    if ((uint64_t)ws_bytes < bw.total) return CG_E_WORKSPACE;
+    const WsLayout &w = bw.w;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    MaxTable mt;
+    make_max_table_batch(desc, batch, mt);
+    HeaderBytes hb;
+    make_header(desc, d, lay, hb);
+
+    uint32_t *status = at<uint32_t>(ws, 0);
+    uint8_t *vblob = at<uint8_t>(ws, bw.vblob);
+    if ((rc = hip_rc(launch_blob_header(blobs, hb, lay, d, s, batch, blob_stride)))) return rc;
+    EncodeOut o{vblob + vlay.off_payload,
+                bw.vcap,
+                at<uint16_t>(vblob, vlay.off_lengths),
+                at<uint64_t>(vblob, vlay.off_chunk_off),
+                at<uint64_t>(ws, bw.vsize),
+                nullptr,
+                vlay.off_payload};
+    if ((rc = encode_call(vd, mt, kv, at<uint16_t>(vblob, vlay.off_scales), at<uint16_t>(vblob, vlay.off_cdf), o,
+                          ws, w, s)))
+        return rc;
+    const BatchGeom g = batch_geom(d, vd, batch, blob_stride);
+    Piece *pieces = at<Piece>(ws, bw.pieces);
+    if ((rc = hip_rc(launch_split_plan(g, vblob, at<uint64_t>(ws, w.tile_off), blobs, blob_sizes_dev, pieces, status,
+                                       s))))
+        return rc;
+    return hip_rc(launch_copy_pieces(g, pieces, vblob, 0, blobs, blob_stride, s));
+}
+
+int cg_from_bytes_batch(const cg_desc *desc, int32_t batch, const uint8_t *blobs, size_t blob_stride,
+                        const uint64_t *blob_sizes_dev, void *kv_out, void *ws, size_t ws_bytes, void *stream) {
+    Dims d, vd;
+    int rc = make_dims_batch(desc, batch, d, vd);
+    if (rc) return rc;
+    if (!blobs || !blob_sizes_dev || !kv_out || !ws) return CG_E_INVAL;
+    if ((uintptr_t)blobs % 8 || blob_stride % 8 || (uintptr_t)ws % kWsAlign) return CG_E_INVAL;
+    const BlobLayout lay = blob_layout(d), vlay = blob_layout(vd);
+    if ((uint64_t)blob_stride < lay.off_payload) return CG_E_INVAL;
+    const BatchWs bw = batch_ws(d, vd, batch, blob_stride, CG_OP_FROM_BYTES);
+    if ((uint64_t)ws_bytes < bw.total) return CG_E_WORKSPACE;
+    const WsLayout &w = bw.w;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    MaxTable mt;
+    make_max_table_batch(desc, batch, mt);
+    HeaderBytes hb;
+    make_header(desc, d, lay, hb);
+    uint32_t *status = at<uint32_t>(ws, 0);
+    uint8_t *vblob = at<uint8_t>(ws, bw.vblob);
+    if ((rc = clear_ws(ws, w, s))) return rc;
+    const BatchGeom g = batch_geom(d, vd, batch, blob_stride);
+    Piece *pieces = at<Piece>(ws, bw.pieces);
+    if ((rc = hip_rc(launch_merge_plan(g, blobs, blob_sizes_dev, hb, vblob, at<uint64_t>(ws, bw.piece_len), pieces,
+                                       status, s))))
+        return rc;
+    if ((rc = hip_rc(launch_copy_pieces(g, pieces, blobs, blob_stride, vblob, 0, s)))) return rc;
+    DecodeIn in{vblob + vlay.off_payload,
+                bw.vcap,
+                reinterpret_cast<const uint16_t *>(vblob + vlay.off_lengths),
+                reinterpret_cast<const uint64_t *>(vblob + vlay.off_chunk_off),
+                nullptr,
+                reinterpret_cast<const uint16_t *>(vblob + vlay.off_cdf)};
+    DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
+                  reinterpret_cast<const uint16_t *>(vblob + vlay.off_scales)};
+    return hip_rc(
+        launch_decode(vd, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan), status, s));
 }
 
 int cg_from_bytes_paged(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_cache,
@@ -475,7 +653,8 @@ int cg_from_bytes_paged(const cg_desc *desc, const uint8_t *blob, size_t blob_si
     DecodeOut out{nullptr, nullptr, reinterpret_cast<const uint16_t *>(blob + b.off_scales),
                   PagedOut{reinterpret_cast<uint16_t *>(kv_cache), layer_stride, kv_stride, log2_bs,
                            block_table, num_blocks}};
-    return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint32_t>(ws, 0), s));
+    return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
+                                at<uint32_t>(ws, 0), s));
 }
 
 }  // extern "C"

@@ -159,47 +159,59 @@ hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts,
     return hipGetLastError();
 }
 
-// round_half_even(num / T) for num < 2^48: a double-precision quotient is
-// within one of the true quotient; the integer remainder fixes it exactly.
-__device__ __forceinline__ uint64_t div_rne(uint64_t num, uint32_t T, double invT) {
-    int64_t q = (int64_t)((double)num * invT);
-    int64_t r = (int64_t)num - q * (int64_t)T;
-    while (r < 0) { --q; r += T; }
-    while (r >= (int64_t)T) { ++q; r -= T; }
-    if (2 * r > (int64_t)T || (2 * r == (int64_t)T && (q & 1))) ++q;
-    return (uint64_t)q;
-}
-
-// One thread per table: cdf[k] = round_half_even(cum[k] * (2^16 - A) / T) + k.
+// cdf[k] = round_half_even(cum[k] * (2^16 - A) / T) + k, cum[k] the count of
+// symbols below k. G lanes per table (G = the power of two >= A, at most 64;
+// 64 / G tables per wave): lane k reads count k (coalesced), the segmented
+// scan of G lanes gives cum, and lane k writes entry k of the table (the
+// last lane of a table also writes entry A). An alphabet above 64 takes two
+// rounds of 64, the second starting from the first one's total.
+template <int G>
 __global__ __launch_bounds__(256) void k_cdf(const uint32_t *__restrict__ counts,
                                              int32_t *__restrict__ cdf,
                                              uint16_t *__restrict__ wire,
                                              uint32_t *__restrict__ status, int64_t ntab, int A,
                                              int T) {
-    const int64_t tab = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (tab >= ntab) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t tab = wave * (64 / G) + lane / G;
+    const int k0 = lane & (G - 1);
+    const bool live = tab < ntab;
     const uint64_t S = kProbOne - (uint32_t)A;
     const double invT = 1.0 / (double)T;
-    const uint32_t *h = counts + tab * A;
-    int32_t *out = cdf + tab * (A + 1);
-    uint16_t *w = wire ? wire + tab * A : nullptr;
-    uint64_t cum = 0;
-    for (int k = 0; k <= A; ++k) {
-        const uint32_t v = (uint32_t)(div_rne(cum * S, (uint32_t)T, invT) + (uint64_t)k);
-        out[k] = (int32_t)v;
-        if (k < A) {
-            if (w) w[k] = (uint16_t)v;
-            cum += h[k];
+    uint64_t base = 0;
+    for (int kb = 0; kb < A; kb += G) {
+        const int k = kb + k0;
+        const uint32_t h = live && k < A ? counts[tab * A + k] : 0u;
+        uint32_t incl = h;
+#pragma unroll
+        for (int o = 1; o < G; o <<= 1) {
+            const uint32_t t = (uint32_t)__shfl_up((int)incl, o, G);
+            if (k0 >= o) incl += t;
         }
+        if (live && k < A) {
+            const uint32_t v = (uint32_t)(div_rne((base + incl - h) * S, (uint32_t)T, invT) + (uint64_t)k);
+            if (cdf) cdf[tab * (A + 1) + k] = (int32_t)v;
+            if (wire) wire[tab * A + k] = (uint16_t)v;
+        }
+        base += (uint32_t)__shfl((int)incl, G - 1, G);
     }
-    if (cum != (uint64_t)T) atomicOr(status, kStCorrupt);
+    if (live && k0 == 0) {
+        if (cdf) cdf[tab * (A + 1) + A] = (int32_t)(div_rne(base * S, (uint32_t)T, invT) + (uint64_t)A);
+        if (base != (uint64_t)T) atomicOr(status, kStCorrupt);
+    }
 }
 
 hipError_t launch_cdf(const Dims &d, const uint32_t *counts, int32_t *cdf, uint16_t *cdf_wire,
                       uint32_t *status, hipStream_t s) {
     const int64_t ntab = 2LL * d.L * d.C;
-    hipLaunchKernelGGL(k_cdf, dim3((unsigned)((ntab + 255) / 256)), dim3(256), 0, s, counts, cdf,
-                       cdf_wire, status, ntab, d.A, d.T);
+#define CG_CDF(GG)                                                                                      \
+    hipLaunchKernelGGL(k_cdf<GG>, dim3((unsigned)((ntab + 4 * (64 / GG) - 1) / (4 * (64 / GG)))), dim3(256), \
+                       0, s, counts, cdf, cdf_wire, status, ntab, d.A, d.T)
+    if (d.A <= 8) CG_CDF(8);
+    else if (d.A <= 16) CG_CDF(16);
+    else if (d.A <= 32) CG_CDF(32);
+    else CG_CDF(64);
+#undef CG_CDF
     return hipGetLastError();
 }
 

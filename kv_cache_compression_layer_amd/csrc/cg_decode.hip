@@ -6,10 +6,10 @@
 // as t = (t - M) / M * scale before being stacked back to [L, 2, T, H, D] in
 // the input dtype.
 //
-// Pass 1 (k_lenscan, one block per 256-token chunk) turns the uint16 lengths
-// into the byte offset of every 64-stream tile: the chunk offset plus the
-// prefix sum of the lengths before it, and checks that the chunk's lengths
-// add up to the next chunk offset.
+// Pass 1 (launch_tile_scan) turns the uint16 lengths into the byte offset of
+// every 64-stream tile: the chunk offset plus the prefix sum of the lengths
+// before it, and checks that the chunk's lengths add up to the next chunk
+// offset.
 //
 // Pass 2 (k_decode): a block of NW waves owns 64 channels of one (K|V,
 // layer) (lane = channel) and NW * S chunks; each wave decodes S streams per
@@ -29,50 +29,6 @@
 #include "cg_internal.hpp"
 
 namespace cg {
-
-// Block-wide exclusive scan of one uint32 per thread (256 threads).
-__device__ __forceinline__ uint32_t block_excl_scan_256(uint32_t v, uint32_t *tmp,
-                                                        uint32_t &total) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const uint32_t incl = wave_incl_scan_u32(v, lane);
-    if (lane == 63) tmp[wv] = incl;
-    __syncthreads();
-    uint32_t before = 0;
-    for (int i = 0; i < wv; ++i) before += tmp[i];
-    total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
-    __syncthreads();
-    return before + incl - v;
-}
-
-__global__ __launch_bounds__(256) void k_lenscan(const uint16_t *__restrict__ lengths,
-                                                 const uint64_t *__restrict__ chunk_off,
-                                                 uint64_t *__restrict__ tile_off,
-                                                 uint32_t *__restrict__ status, int L, int C,
-                                                 int CB, int NC, uint64_t payload_bytes) {
-    __shared__ uint32_t tmp[4];
-    const int j = blockIdx.x;
-    const int ntc = 2 * L * CB;
-    uint64_t base = chunk_off[j];
-    for (int seg = 0; seg < ntc; seg += 256) {
-        const int tl = seg + threadIdx.x;
-        uint32_t sum = 0;
-        if (tl < ntc) {
-            const int slab = tl / CB, cb = tl - slab * CB;
-            const uint16_t *p = lengths + ((int64_t)j * 2 * L + slab) * C + cb * 64;
-            const int nch = min(64, C - cb * 64);
-            for (int i = 0; i < nch; ++i) sum += p[i];
-        }
-        uint32_t total;
-        const uint32_t excl = block_excl_scan_256(sum, tmp, total);
-        if (tl < ntc) tile_off[(int64_t)j * ntc + tl] = base + excl;
-        base += total;
-    }
-    if (threadIdx.x == 0) {
-        const bool bad = (j == 0 && chunk_off[0] != 0) || base != chunk_off[j + 1] ||
-                         chunk_off[j + 1] > payload_bytes;
-        if (bad) atomicOr(status, kStCorrupt);
-    }
-}
 
 struct DecArgs {
     const uint8_t *payload;
@@ -328,7 +284,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     const int kv = slab / a.L, l = slab - kv * a.L;
     const int c = cb * 64 + lane;
     const bool active = c < a.C;
-    const int M = a.mt.m[kv][l];
+    const int M = a.mt.m[kv][local_layer(a.mt, l)];
 
     // This wave's streams: lengths, offsets and the pool bytes they need
     // (alignment head + bytes + four zero bytes after each of the 64 streams).
@@ -533,10 +489,10 @@ static hipError_t launch_decode_f(const Dims &d, const DecArgs &a, hipStream_t s
 }
 
 hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, const DecodeOut &out,
-                         uint64_t *tile_off, uint32_t *status, hipStream_t s) {
-    hipLaunchKernelGGL(k_lenscan, dim3((unsigned)d.NC), dim3(256), 0, s, in.lengths, in.chunk_off,
-                       tile_off, status, d.L, d.C, d.CB, d.NC, in.payload_bytes);
-    hipError_t e = hipGetLastError();
+                         uint64_t *tile_off, uint64_t *scan_tmp, uint32_t *status, hipStream_t s) {
+    TileScan ts{nullptr, in.lengths, tile_off, scan_tmp, nullptr, in.chunk_off, in.payload_bytes, status,
+                d.L, d.C, d.CB, d.NC};
+    hipError_t e = launch_tile_scan(ts, s);
     if (e != hipSuccess) return e;
     DecArgs a;
     a.payload = in.payload;

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict
     uint32_t am = max(am2 & 0xFFFFu, am2 >> 16);
     am = wave_max_dpp(am);
     if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
-    const int M = mt.m[k][l];
+    const int M = mt.m[k][local_layer(mt, l)];
     const float Mf = (float)M;
     // m == 0 gives f == 0, so every symbol is exactly M.
     const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void k_quantize_any(const uint16_t *__restrict
     for (int c = lane; c < C; c += 64) am = max(am, (uint32_t)src[c] & 0x7FFFu);
     am = wave_max_u32(am);
     if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
-    const int M = mt.m[k][l];
+    const int M = mt.m[k][local_layer(mt, l)];
     const float Mf = (float)M;
     const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
     for (int c = lane; c < C; c += 64) dst[c] = (uint8_t)quant1(src[c], f, Mf);
@@ -197,6 +197,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
                                                        uint8_t *__restrict__ sym,
                                                        uint16_t *__restrict__ scale,
                                                        uint32_t *__restrict__ counts,
+                                                       uint16_t *__restrict__ wire,
                                                        uint32_t *__restrict__ status, int L, int T,
                                                        int C, int A, int TT, MaxTable mt) {
     constexpr int NS = 1 << LOGA;
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
     for (int i = threadIdx.x; i < NS * NP * 64 / 4; i += 512) h4[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
-    const int M = mt.m[k][l];
+    const int M = mt.m[k][local_layer(mt, l)];
     const float Mf = (float)M;
     uint8_t *hb = reinterpret_cast<uint8_t *>(hist);
     const uint32_t lane4 = (uint32_t)lane * 4;
@@ -271,6 +272,57 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
     }
     __syncthreads();
 
+    if (wire) {
+        // The block saw every token of the slab: build its CDF tables here.
+        // Thread col < NP * 64 owns the counter column (pair, lane), i.e.
+        // channels c and c + 1; it scans its A counts of each channel into
+        // the tables, then writes them back over the counters as u16 [c][s]
+        // (C * A * 2 bytes, which fit there since A <= NS) for a coalesced
+        // copy to the slab's wire tables.
+        constexpr int NCOL = NP * 64;
+        const int col = threadIdx.x;
+        uint32_t tabv[NS];
+        bool bad = false;
+        if (col < NCOL) {
+            const uint64_t S = kProbOne - (uint32_t)A;
+            const double invT = 1.0 / (double)T;
+            uint32_t cum_lo = 0, cum_hi = 0;
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                const uint32_t v = hist[q * NCOL + col];
+                if (q < A) {
+                    const uint32_t a0 = (uint32_t)(div_rne((uint64_t)cum_lo * S, (uint32_t)T, invT) + q);
+                    const uint32_t a1 = (uint32_t)(div_rne((uint64_t)cum_hi * S, (uint32_t)T, invT) + q);
+                    tabv[q] = (a0 & 0xFFFFu) | (a1 << 16);
+                    cum_lo += v & 0xFFFFu;
+                    cum_hi += v >> 16;
+                } else {
+                    tabv[q] = 0;
+                    bad |= v != 0;
+                }
+            }
+        }
+        __syncthreads();
+        uint16_t *wl = reinterpret_cast<uint16_t *>(hist);
+        if (col < NCOL) {
+            const int pr = col / 64, ln = col % 64;
+            const int c = ((pr / 4) * 64 + ln) * 8 + (pr % 4) * 2;
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                if (q < A) {
+                    wl[c * A + q] = (uint16_t)tabv[q];
+                    wl[(c + 1) * A + q] = (uint16_t)(tabv[q] >> 16);
+                }
+            }
+        }
+        if (__ballot(bad) && lane == 0) atomicOr(status, kStCorrupt);
+        __syncthreads();
+        const uint4 *src4 = reinterpret_cast<const uint4 *>(hist);
+        uint4 *dst4 = reinterpret_cast<uint4 *>(wire + (int64_t)slab * C * A);
+        for (int i = threadIdx.x; i < C * A / 8; i += 512) dst4[i] = src4[i];
+        return;
+    }
+
     // Flush: word (s, pair, lane) holds channels c and c + 1 of symbol s.
     for (int wi = threadIdx.x; wi < NS * NP * 64; wi += 512) {
         const uint32_t v = hist[wi];
@@ -291,18 +343,32 @@ bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym) {
     return (d.C == 512 || d.C == 1024) && d.A <= 32 && (uintptr_t)kv % 16 == 0 && (uintptr_t)sym % 8 == 0;
 }
 
-hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
-                                uint16_t *scale, uint32_t *counts, uint32_t *status, hipStream_t s) {
-    // Tiles of rows: about 1024 blocks over the call, at most 65535 rows (16-bit counts).
+// Tokens per block: about 1024 blocks over the call, at most 32768 rows
+// (16-bit counters).
+static int64_t quantize_hist_rows(const Dims &d) {
     int64_t TT = ((int64_t)d.T * 2 * d.L + 1023) / 1024;
     TT = ((TT + 15) / 16) * 16;
     if (TT < 256) TT = 256;
     if (TT > 32768) TT = 32768;
+    return TT;
+}
+
+bool quantize_hist_fuses_cdf(const Dims &d, const void *wire) {
+    return quantize_hist_rows(d) >= d.T && (uintptr_t)wire % 16 == 0;
+}
+
+hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
+                                uint16_t *scale, uint32_t *counts, uint16_t *wire, uint32_t *status,
+                                hipStream_t s) {
+    const int64_t TT = quantize_hist_rows(d);
+    if (wire && !quantize_hist_fuses_cdf(d, wire)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((d.T + TT - 1) / TT), (unsigned)(2 * d.L)), block(512);
     int loga = 2;
     while ((1 << loga) < d.A) ++loga;
     const int tt = (int)TT;
-#define CG_QH(NV, LG) hipLaunchKernelGGL((k_quantize_hist<NV, LG>), grid, block, 0, s, kv, sym, scale, counts, status, d.L, d.T, d.C, d.A, tt, mt)
+#define CG_QH(NV, LG)                                                                                     \
+    hipLaunchKernelGGL((k_quantize_hist<NV, LG>), grid, block, 0, s, kv, sym, scale, counts, wire, status, d.L, \
+                       d.T, d.C, d.A, tt, mt)
     if (d.C == 512) {
         switch (loga) {
         case 2: CG_QH(1, 2); break;
@@ -342,7 +408,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
     const int slab = blockIdx.y, k = slab >= L ? 1 : 0, l = slab - k * L;  // grid: (tokens/4, 2L)
     const int64_t row = (int64_t)slab * T + t;
     float *dq = dq_all[wv];
-    build_dq(dq, mt.m[k][l], lane);
+    build_dq(dq, mt.m[k][local_layer(mt, l)], lane);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     const float m = bf16_to_f32(scale[row]);
@@ -378,10 +444,12 @@ hipError_t launch_dequantize(const Dims &d, const MaxTable &mt, const uint8_t *s
 
 // ------------------------------------------------------------ blob header
 
-__global__ __launch_bounds__(256) void k_blob_header(uint8_t *__restrict__ blob, HeaderBytes h,
+// One block per blob (blob b at blob + b * stride).
+__global__ __launch_bounds__(256) void k_blob_header(uint8_t *__restrict__ blob, uint64_t stride, HeaderBytes h,
                                                      BlobLayout lay, uint64_t end_scales,
                                                      uint64_t end_cdf, uint64_t end_off,
                                                      uint64_t end_len) {
+    blob += (uint64_t)blockIdx.x * stride;
     for (uint32_t i = threadIdx.x; i < h.n; i += blockDim.x) blob[i] = h.b[i];
     // Zero the gaps between the end of each section and the next one.
     const uint64_t from[4] = {end_scales, end_cdf, end_off, end_len};
@@ -391,13 +459,13 @@ __global__ __launch_bounds__(256) void k_blob_header(uint8_t *__restrict__ blob,
 }
 
 hipError_t launch_blob_header(uint8_t *blob, const HeaderBytes &h, const BlobLayout &lay,
-                              const Dims &d, hipStream_t s) {
+                              const Dims &d, hipStream_t s, int nblobs, uint64_t stride) {
     const uint64_t end_scales = lay.off_scales + 4ull * d.L * d.T;
     const uint64_t end_cdf = lay.off_cdf + 4ull * d.L * d.C * d.A;
     const uint64_t end_off = lay.off_chunk_off + 8ull * (d.NC + 1);
     const uint64_t end_len = lay.off_lengths + 4ull * d.NC * d.L * d.C;
-    hipLaunchKernelGGL(k_blob_header, dim3(1), dim3(256), 0, s, blob, h, lay, end_scales, end_cdf,
-                       end_off, end_len);
+    hipLaunchKernelGGL(k_blob_header, dim3((unsigned)nblobs), dim3(256), 0, s, blob, stride, h, lay, end_scales,
+                       end_cdf, end_off, end_len);
     return hipGetLastError();
 }
 

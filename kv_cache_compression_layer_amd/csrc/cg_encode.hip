@@ -27,8 +27,8 @@
 // and the tile's byte total. A stream longer than the slot (256 bytes)
 // marks the tile for k_fixup.
 //
-// k_tile_scan + k_chunk_scan: exclusive scan of the tile totals in stream
-// order (per chunk, then over the chunk totals) -> tile offsets, chunk
+// launch_tile_scan + k_chunk_scan: exclusive scan of the tile totals in
+// stream order (per chunk, then over the chunk totals) -> tile offsets, chunk
 // offsets and the payload size.
 //
 // k_compact: one wave per tile copies the gathered tile to its offset (a
@@ -119,7 +119,8 @@ struct GlobalSink {
 
 struct EncArgs {
     const uint8_t *sym;
-    const int32_t *cdf;
+    const int32_t *cdf;        // int32 tables, or
+    const uint16_t *cdf16;     // u16 wire tables
     uint8_t *staging;          // [tiles][kStageBytes][64] bytes
     uint32_t *tile_sum;        // [tiles]
     uint16_t *lengths;         // [NC, 2L, C]
@@ -302,8 +303,8 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     for (int s = wv; s < A; s += NW) {
         uint32_t entry;
         if (active) {
-            const int32_t *src = a.cdf + ((int64_t)slab * a.C + c) * (A + 1);
-            const uint32_t lo = (uint32_t)src[s], hi = (uint32_t)src[s + 1];
+            uint32_t lo, hi;
+            cdf_bounds(a.cdf, a.cdf16, (int64_t)slab * a.C + c, A, s, lo, hi);
             uint32_t f = hi - lo;
             if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == A - 1 && hi != kProbOne)) {
                 bad = true;
@@ -419,33 +420,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     if (__ballot((active && (qmax > amax || bad))) && lane == 0) atomicOr(&a.hdr->status, kStCorrupt);
 }
 
-// ------------------------------------------------------------ tile scan
-
-// Pass 1: one block per chunk scans the totals of the chunk's tiles (stream
-// order) into offsets relative to the chunk and writes the chunk's total.
-__global__ __launch_bounds__(256) void k_tile_scan(const uint32_t *__restrict__ tile_sum,
-                                                   uint64_t *__restrict__ tile_off,
-                                                   uint64_t *__restrict__ chunk_total,
-                                                   int64_t tiles_per_chunk) {
-    __shared__ uint32_t wsum[4];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int64_t base = (int64_t)blockIdx.x * tiles_per_chunk;
-    uint64_t run = 0;
-    for (int64_t seg = 0; seg < tiles_per_chunk; seg += 256) {
-        const int64_t i = seg + tid;
-        const uint32_t v = i < tiles_per_chunk ? tile_sum[base + i] : 0u;
-        const uint32_t incl = wave_incl_scan_u32(v, lane);
-        if (lane == 63) wsum[wv] = incl;
-        __syncthreads();
-        uint32_t before = 0;
-        for (int k = 0; k < wv; ++k) before += wsum[k];
-        const uint32_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-        if (i < tiles_per_chunk) tile_off[base + i] = run + before + incl - v;
-        run += total;
-        __syncthreads();
-    }
-    if (tid == 0) chunk_total[blockIdx.x] = run;
-}
+// ------------------------------------------------------------ chunk scan
 
 struct ChunkScanArgs {
     const uint64_t *chunk_total;
@@ -565,6 +540,7 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
 struct FixupArgs {
     const uint8_t *sym;
     const int32_t *cdf;
+    const uint16_t *cdf16;
     const uint16_t *lengths;
     const uint64_t *tile_off;   // relative to the chunk
     const uint64_t *chunk_off;
@@ -590,14 +566,15 @@ __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
         const uint32_t len = active ? a.lengths[js * a.C + c] : 0u;
         const uint32_t incl = wave_incl_scan_u32(len, lane);
         if (!active) continue;
-        const int32_t *tab = a.cdf + ((int64_t)slab * a.C + c) * (a.A + 1);
+        const int64_t tab = (int64_t)slab * a.C + c;
         const uint8_t *sp = a.sym + ((int64_t)slab * a.T + (int64_t)j * kChunk) * a.C + c;
         RcEncHold enc;
         enc.init();
         GlobalSink sink{a.payload, a.chunk_off[j] + a.tile_off[tile] + incl - len, a.cap, 0u, false};
         for (int t = 0; t < n; ++t) {
             const uint32_t s = min((uint32_t)sp[(int64_t)t * a.C], (uint32_t)a.A - 1);
-            const uint32_t lo = (uint32_t)tab[s], hi = (uint32_t)tab[s + 1];
+            uint32_t lo, hi;
+            cdf_bounds(a.cdf, a.cdf16, tab, a.A, (int)s, lo, hi);
             const uint32_t f = hi > lo ? hi - lo : 1u;
             enc.encode(lo & 0xFFFFu, f, sink);
         }
@@ -610,12 +587,13 @@ __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
 
 size_t encode_staging_bytes(const Dims &d) { return (size_t)d.tiles * kStageBytes * 64; }
 
-hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, const EncodeOut &o,
-                         const EncodeWs &w, bool trusted, hipStream_t s) {
+hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, const uint16_t *cdf16,
+                         const EncodeOut &o, const EncodeWs &w, bool trusted, hipStream_t s) {
     const int S = d.NC >= 2 ? 2 : 1;
     EncArgs a;
     a.sym = sym;
     a.cdf = cdf;
+    a.cdf16 = cdf16;
     a.staging = w.staging;
     a.tile_sum = w.tile_sum;
     a.lengths = o.lengths;
@@ -653,9 +631,9 @@ hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, 
     if (e != hipSuccess) return e;
 
     const int64_t tpc = 2LL * d.L * d.CB;
-    hipLaunchKernelGGL(k_tile_scan, dim3((unsigned)d.NC), dim3(256), 0, s, w.tile_sum, w.tile_off,
-                       w.chunk_total, tpc);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    TileScan ts{w.tile_sum, nullptr, w.tile_off, w.scan_tmp, w.chunk_total, nullptr, 0, &w.hdr->status,
+                d.L, d.C, d.CB, d.NC};
+    if ((e = launch_tile_scan(ts, s)) != hipSuccess) return e;
     ChunkScanArgs sa;
     sa.chunk_total = w.chunk_total;
     sa.chunk_off = o.chunk_off;
@@ -688,6 +666,7 @@ hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, 
     FixupArgs fa;
     fa.sym = sym;
     fa.cdf = cdf;
+    fa.cdf16 = cdf16;
     fa.lengths = o.lengths;
     fa.tile_off = w.tile_off;
     fa.chunk_off = o.chunk_off;

@@ -26,7 +26,18 @@ constexpr uint32_t kStCapacity = 4u;
 // every kernel that needs it (2 KiB of kernel arguments).
 struct MaxTable {
     uint8_t m[2][CG_MAX_LAYERS];
+    // Batched calls run as one call of batch * L layers: layer l then takes
+    // the constant of layer l mod lper (lper = 0: no period). lmagic =
+    // ceil(2^32 / lper) turns the modulo into a multiply-high, exact for
+    // l < 2^16 and lper <= 1024.
+    uint32_t lper, lmagic;
 };
+
+__device__ __forceinline__ int local_layer(const MaxTable &mt, int l) {
+    if (mt.lper == 0) return l;
+    if (mt.lper == 1) return 0;
+    return l - (int)mt.lper * (int)__umulhi((uint32_t)l, mt.lmagic);
+}
 
 // Derived sizes of one call.
 struct Dims {
@@ -65,14 +76,37 @@ hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts,
                             hipStream_t s);
 
 // Quantise and histogram in one pass (counts must be zero on entry); only
-// for the shapes quantize_hist_fits() accepts.
+// for the shapes quantize_hist_fits() accepts. When one block covers a whole
+// (K|V, layer) slab (quantize_hist_fuses_cdf), the block builds the slab's
+// u16 CDF tables itself: pass `wire` and no counts are written (nor read).
 bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym);
+bool quantize_hist_fuses_cdf(const Dims &d, const void *wire);
 hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
-                                uint16_t *scale, uint32_t *counts, uint32_t *status, hipStream_t s);
+                                uint16_t *scale, uint32_t *counts, uint16_t *wire, uint32_t *status,
+                                hipStream_t s);
 
-// counts -> cdf int32 [2,L,C,A+1]; optionally the u16 wire form [2,L,C,A].
+// counts -> cdf int32 [2,L,C,A+1] and / or the u16 wire form [2,L,C,A]
+// (either may be null).
 hipError_t launch_cdf(const Dims &d, const uint32_t *counts, int32_t *cdf, uint16_t *cdf_wire,
                       uint32_t *status, hipStream_t s);
+
+// Tile offsets in stream order (three passes over blocks of 256 tiles). The
+// byte count of each tile is tile_sum[t], or, with tile_sum null, the sum of
+// its 64 lengths. Offsets are relative to the chunk, or, with chunk_off set,
+// absolute, each chunk then checked against chunk_off (kStCorrupt).
+struct TileScan {
+    const uint32_t *tile_sum;    // [tiles] or null
+    const uint16_t *lengths;     // [NC,2,L,C] when tile_sum is null
+    uint64_t *tile_off;          // out [tiles]
+    uint64_t *tmp;               // tile_scan_tmp_bytes(d)
+    uint64_t *chunk_total;       // out [NC], or null
+    const uint64_t *chunk_off;   // [NC+1] or null
+    uint64_t payload_bytes;      // bound of chunk_off (with chunk_off)
+    uint32_t *status;
+    int L, C, CB, NC;
+};
+size_t tile_scan_tmp_bytes(const Dims &d);
+hipError_t launch_tile_scan(const TileScan &a, hipStream_t s);
 
 struct EncodeOut {
     uint8_t *payload;
@@ -91,15 +125,18 @@ struct EncodeWs {
     uint64_t *chunk_total;    // [NC] bytes of each chunk
     uint32_t *overflow_list;  // [tiles] tiles with a stream beyond the LDS stage
     uint8_t *staging;         // encode_staging_bytes(d)
+    uint64_t *scan_tmp;       // tile_scan_tmp_bytes(d)
 };
 
 // Bytes of the staging area k_encode needs (one slot per tile).
 size_t encode_staging_bytes(const Dims &d);
 
-// trusted: the symbols come from this library's quantiser (all below A), so
-// the encoder skips its range check.
-hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, const EncodeOut &o,
-                         const EncodeWs &w, bool trusted, hipStream_t s);
+// Tables: int32 [2,L,C,A+1] (cdf32) or the u16 wire form [2,L,C,A] (cdf16,
+// entry A taken as 2^16); exactly one is set. trusted: the symbols come from
+// this library's quantiser (all below A), so the encoder skips its range
+// check.
+hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf32, const uint16_t *cdf16,
+                         const EncodeOut &o, const EncodeWs &w, bool trusted, hipStream_t s);
 
 // Decoder table source: int32 [2,L,C,A+1] or the u16 wire form [2,L,C,A].
 struct DecodeIn {
@@ -130,7 +167,7 @@ struct DecodeOut {
 };
 
 hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, const DecodeOut &out,
-                         uint64_t *tile_off, uint32_t *status, hipStream_t s);
+                         uint64_t *tile_off, uint64_t *scan_tmp, uint32_t *status, hipStream_t s);
 
 hipError_t launch_dequantize(const Dims &d, const MaxTable &mt, const uint8_t *sym,
                              const uint16_t *scale, uint16_t *kv_out, hipStream_t s);
@@ -141,7 +178,38 @@ struct HeaderBytes {
     uint32_t n;
 };
 hipError_t launch_blob_header(uint8_t *blob, const HeaderBytes &h, const BlobLayout &lay,
-                              const Dims &d, hipStream_t s);
+                              const Dims &d, hipStream_t s, int nblobs = 1, uint64_t stride = 0);
+
+// ---------------------------------------------------------------- batches
+// A batch of B calls of the same shape runs as one virtual call of B * L
+// layers (Dims vd); these kernels move the virtual blob's sections to and
+// from the B per-call blobs (Dims d, blob b at blobs + b * stride).
+struct Piece {
+    uint64_t src, dst, len;  // byte offsets from the source / destination base
+};
+
+struct BatchGeom {
+    Dims d, vd;                 // one call / the virtual call
+    BlobLayout lay, vlay;       // their blob layouts
+    int B;
+    uint64_t stride;            // bytes between per-call blobs
+    int npieces;                // pieces per call: 2 scales + 2 cdf + 2*NC lengths + 2*NC payload
+};
+
+// Split (to_bytes): plan the pieces of every call from the virtual blob's
+// chunk offsets and tile offsets, write each call's chunk offsets and size.
+hipError_t launch_split_plan(const BatchGeom &g, const uint8_t *vblob, const uint64_t *vtile_off,
+                             uint8_t *blobs, uint64_t *sizes_dev, Piece *pieces, uint32_t *status,
+                             hipStream_t s);
+// Merge (from_bytes): check each call's header against hdr, plan the pieces
+// into the virtual blob from the calls' lengths and chunk offsets, write the
+// virtual chunk offsets.
+hipError_t launch_merge_plan(const BatchGeom &g, const uint8_t *blobs, const uint64_t *sizes_dev,
+                             const HeaderBytes &hdr, uint8_t *vblob, uint64_t *piece_len, Piece *pieces,
+                             uint32_t *status, hipStream_t s);
+// Copies every piece: src_base + b * src_stride + src -> dst_base + b * dst_stride + dst.
+hipError_t launch_copy_pieces(const BatchGeom &g, const Piece *pieces, const uint8_t *src_base,
+                              uint64_t src_stride, uint8_t *dst_base, uint64_t dst_stride, hipStream_t s);
 
 // ----------------------------------------------------------- device helpers
 
@@ -163,6 +231,32 @@ __device__ __forceinline__ int xcd_work_index(int b, int n) {
     const int per = n / kXcds;
     if (b >= per * kXcds) return b;
     return (b % kXcds) * per + b / kXcds;
+}
+
+// round_half_even(num / T) for num < 2^48: a double-precision quotient is
+// within one of the true quotient; the integer remainder fixes it exactly.
+__device__ __forceinline__ uint64_t div_rne(uint64_t num, uint32_t T, double invT) {
+    int64_t q = (int64_t)((double)num * invT);
+    int64_t r = (int64_t)num - q * (int64_t)T;
+    while (r < 0) { --q; r += T; }
+    while (r >= (int64_t)T) { ++q; r -= T; }
+    if (2 * r > (int64_t)T || (2 * r == (int64_t)T && (q & 1))) ++q;
+    return (uint64_t)q;
+}
+
+// Start and end of symbol s in table `tab` of an int32 [.., A+1] or u16 wire
+// [.., A] table set (exactly one pointer set).
+__device__ __forceinline__ void cdf_bounds(const int32_t *c32, const uint16_t *c16, int64_t tab, int A, int s,
+                                           uint32_t &lo, uint32_t &hi) {
+    if (c16) {
+        const uint16_t *w = c16 + tab * A;
+        lo = w[s];
+        hi = s + 1 < A ? (uint32_t)w[s + 1] : kProbOne;
+    } else {
+        const int32_t *p = c32 + tab * (A + 1);
+        lo = (uint32_t)p[s];
+        hi = (uint32_t)p[s + 1];
+    }
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

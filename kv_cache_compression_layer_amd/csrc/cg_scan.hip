@@ -1,0 +1,127 @@
+// Byte offset of every 64-stream coder tile within the payload, on gfx950.
+//
+// LMCache CacheGen page (0539edu.com/news/4720135), sections 4 and 5: the
+// streams of a chunk are concatenated in (K|V, layer, channel) order, and a
+// stream is found again from the prefix sum of the uint16 lengths before it.
+// A tile's offset is the exclusive prefix sum of the tile byte counts of its
+// chunk. There are 2 * L * ceil(C / 64) tiles per chunk: few for one long
+// call, very many for a batch of short calls run as one call, so the scan is
+// spread over blocks of 256 tiles in three passes:
+//
+//   1. k_scan_local (block per 256 tiles of a chunk): each tile's byte count
+//      (given, or summed from its 64 lengths), the exclusive scan within the
+//      block, and the block's total;
+//   2. k_scan_blocks (block per chunk): the exclusive scan of the block
+//      totals of the chunk, the chunk total, and, for the decoder, the check
+//      of the chunk against the stored chunk offsets;
+//   3. k_scan_add (as pass 1): adds the block's offset (and, for the
+//      decoder, the chunk offset) to every tile of the block.
+#include "cg_internal.hpp"
+
+namespace cg {
+
+namespace {
+
+constexpr int kScanBlock = 256;
+
+int64_t tiles_per_chunk(const TileScan &a) { return 2LL * a.L * a.CB; }
+int64_t blocks_per_chunk(const TileScan &a) { return (tiles_per_chunk(a) + kScanBlock - 1) / kScanBlock; }
+
+}  // namespace
+
+size_t tile_scan_tmp_bytes(const Dims &d) {
+    const int64_t tpc = 2LL * d.L * d.CB;
+    return (size_t)(8 * d.NC * ((tpc + kScanBlock - 1) / kScanBlock));
+}
+
+__global__ __launch_bounds__(kScanBlock) void k_scan_local(TileScan a, int64_t tpc, int64_t nbpc) {
+    __shared__ uint32_t wsum[kScanBlock / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t bid = blockIdx.x;
+    const int64_t j = bid / nbpc, seg = bid - j * nbpc;
+    const int64_t tl = seg * kScanBlock + tid;
+    uint32_t v = 0;
+    if (tl < tpc) {
+        if (a.tile_sum) {
+            v = a.tile_sum[j * tpc + tl];
+        } else {
+            const int64_t slab = tl / a.CB;
+            const int cb = (int)(tl - slab * a.CB);
+            const uint16_t *p = a.lengths + (j * 2 * a.L + slab) * a.C + cb * 64;
+            const int nch = min(64, a.C - cb * 64);
+            for (int i = 0; i < nch; ++i) v += p[i];
+        }
+    }
+    const uint32_t incl = wave_incl_scan_u32(v, lane);
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < kScanBlock / 64; ++k) {
+        if (k < wv) before += wsum[k];
+        total += wsum[k];
+    }
+    if (tl < tpc) a.tile_off[j * tpc + tl] = before + incl - v;
+    if (tid == 0) a.tmp[bid] = total;
+}
+
+__global__ __launch_bounds__(kScanBlock) void k_scan_blocks(TileScan a, int64_t nbpc) {
+    __shared__ uint64_t wsum[kScanBlock / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t j = blockIdx.x;
+    uint64_t *t = a.tmp + j * nbpc;
+    uint64_t run = 0;
+    for (int64_t seg = 0; seg < nbpc; seg += kScanBlock) {
+        const int64_t i = seg + tid;
+        const uint64_t v = i < nbpc ? t[i] : 0ull;
+        uint64_t incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)incl, o, 64);
+            const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(incl >> 32), o, 64);
+            if (lane >= o) incl += ((uint64_t)hi << 32) | lo;
+        }
+        if (lane == 63) wsum[wv] = incl;
+        __syncthreads();
+        uint64_t before = 0, total = 0;
+#pragma unroll
+        for (int k = 0; k < kScanBlock / 64; ++k) {
+            if (k < wv) before += wsum[k];
+            total += wsum[k];
+        }
+        if (i < nbpc) t[i] = run + before + incl - v;
+        run += total;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        if (a.chunk_total) a.chunk_total[j] = run;
+        if (a.chunk_off) {
+            const uint64_t c0 = a.chunk_off[j], c1 = a.chunk_off[j + 1];
+            const bool bad = (j == 0 && c0 != 0) || c1 < c0 || c1 - c0 != run || c1 > a.payload_bytes;
+            if (bad) atomicOr(a.status, kStCorrupt);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kScanBlock) void k_scan_add(TileScan a, int64_t tpc, int64_t nbpc) {
+    const int64_t bid = blockIdx.x;
+    const int64_t j = bid / nbpc, seg = bid - j * nbpc;
+    const int64_t tl = seg * kScanBlock + threadIdx.x;
+    if (tl >= tpc) return;
+    const uint64_t add = a.tmp[bid] + (a.chunk_off ? a.chunk_off[j] : 0ull);
+    a.tile_off[j * tpc + tl] += add;
+}
+
+hipError_t launch_tile_scan(const TileScan &a, hipStream_t s) {
+    const int64_t tpc = tiles_per_chunk(a), nbpc = blocks_per_chunk(a);
+    const unsigned nblk = (unsigned)(a.NC * nbpc);
+    hipLaunchKernelGGL(k_scan_local, dim3(nblk), dim3(kScanBlock), 0, s, a, tpc, nbpc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_scan_blocks, dim3((unsigned)a.NC), dim3(kScanBlock), 0, s, a, nbpc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_scan_add, dim3(nblk), dim3(kScanBlock), 0, s, a, tpc, nbpc);
+    return hipGetLastError();
+}
+
+}  // namespace cg

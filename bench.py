@@ -45,6 +45,8 @@ def parse_args():
     ap.add_argument("--workload", default="llama31_8b_t32k")
     ap.add_argument("--stage-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chunked-batch", action="store_true",
+                    help="skip the 256-token-chunk batch measurement (e.g. under a profiler)")
     ap.add_argument("--cpu-sample-layers", type=int, default=4)
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
@@ -251,7 +253,7 @@ def main():
     ct = 256
     nb = T // ct
     batch = None
-    if nb >= 2:
+    if nb >= 2 and not args.no_chunked_batch:
         desc1 = cgb.Desc(L, ct, H, D, desc.bins_k, desc.bins_v)
         chunks = kv.view(L, 2, nb, ct, C).permute(2, 0, 1, 3, 4).contiguous()
         stride = (cgb.cg_blob_bound(desc1) + 7) // 8 * 8

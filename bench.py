@@ -47,6 +47,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunked-batch", action="store_true",
                     help="skip the 256-token-chunk batch measurement (e.g. under a profiler)")
+    ap.add_argument("--no-streaming", action="store_true",
+                    help="skip the pipelined host-to-device load measurement")
     ap.add_argument("--cpu-sample-layers", type=int, default=4)
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
@@ -247,6 +249,72 @@ def main():
     del cache
     log(f"stages (ms): {json.dumps({k: round(v, 4) for k, v in stages_ms.items()})}")
 
+    # Loading the blob from host memory while it arrives: the host-to-device
+    # copy of the payload piece by piece on one stream, the decode of each
+    # piece's chunks on another as soon as it is there; against copying the
+    # whole blob first. The link-time model prices 100/500/1000 Mbps links
+    # with the measured decode times.
+    streaming = None
+    if not args.no_streaming:
+        from kv_cache_compression_layer_amd import streaming as stm
+
+        host_blob = torch.empty(blob_size, dtype=torch.uint8, pin_memory=True)
+        host_blob.copy_(blob[:blob_size].cpu())
+        dev_blob = torch.empty(blob_size, dtype=torch.uint8, device=dev)
+        kv_s = torch.empty_like(kv)
+        ws_s = cgb.alloc_workspace(desc, cgb.CG_OP_FROM_BYTES, dev)
+        off_c = info["off_chunk_off"]
+        chunk_off_h = blob[off_c:off_c + 8 * (desc.nchunks + 1)].cpu().numpy().view(np.uint64)
+        cpp = max(1, desc.nchunks // 8)
+        pieces = stm.plan_pieces(info["off_payload"], chunk_off_h, cpp)
+        copy_s, dec_s = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+
+        def wall_ms(fn, reps):
+            best = []
+            for _ in range(reps):
+                torch.cuda.synchronize()
+                t = time.perf_counter()
+                fn()
+                torch.cuda.synchronize()
+                best.append(1e3 * (time.perf_counter() - t))
+            return float(np.median(best))
+
+        def serial():
+            with torch.cuda.stream(copy_s):
+                dev_blob.copy_(host_blob, non_blocking=True)
+            cgb.cg_from_bytes(desc, dev_blob, blob_size, kv_s, ws_s, copy_s)
+
+        def pipelined():
+            stm.enqueue_pipelined_load(desc, host_blob, dev_blob, kv_s, ws_s, pieces, copy_s, dec_s)
+
+        def copy_only():
+            with torch.cuda.stream(copy_s):
+                dev_blob.copy_(host_blob, non_blocking=True)
+
+        pipelined()
+        torch.cuda.synchronize()
+        cgb.check_status(ws_s, what="pipelined cg_from_bytes_chunks")
+        assert torch.equal(kv_s, kv_out), "pipelined load differs from the whole decode"
+        copy_ms = wall_ms(copy_only, 5)
+        serial_ms = wall_ms(serial, 5)
+        pipe_ms = wall_ms(pipelined, 5)
+        last = pieces[-1]
+        last_ms = time_events(lambda: cgb.cg_from_bytes_chunks(desc, blob, blob_size, last.chunk_begin,
+                                                               last.chunk_end, kv_s, ws_s), args.stage_reps, torch)
+        streaming = {
+            "pieces": len(pieces),
+            "chunks_per_piece": cpp,
+            "h2d_copy_ms": copy_ms,
+            "h2d_GBps": blob_size / (copy_ms * 1e-3) / 1e9,
+            "serial_copy_then_decode_ms": serial_ms,
+            "pipelined_ms": pipe_ms,
+            "last_piece_decode_ms": last_ms,
+            "link_model": stm.link_model(raw, blob_size, dec_ms, last_ms),
+        }
+        log(f"streaming: copy {copy_ms:.3f} ms, serial {serial_ms:.3f} ms, pipelined {pipe_ms:.3f} ms, "
+            f"last piece {last_ms:.3f} ms")
+        del host_blob, dev_blob, kv_s
+
     # The same KV as LMCache stores it: one to_bytes call per 256-token chunk,
     # each with its own tables. All chunks as one batch call, against the
     # same calls made one by one on the same stream.
@@ -408,6 +476,7 @@ def main():
         "decode_copy_frac": (raw + blob_size) / (dec_ms * 1e-3) / 1e9 / copy_GBps,
         "stages_ms": stages_ms,
         "chunked_batch": batch,
+        "streaming": streaming,
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -202,6 +202,24 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
 int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,
                   void *ws, size_t ws_bytes, void *stream);
 
+/* from_bytes of a range of chunks: decodes chunks [chunk_begin, chunk_end)
+ * (tokens [256*chunk_begin, min(256*chunk_end, T))) of a blob whose bytes
+ * have arrived only up to blob_size: the header and sections before the
+ * payload, and the payload up to the end of chunk chunk_end - 1
+ * (off_payload + chunk_off[chunk_end] bytes). Those tokens of kv_out
+ * [L,2,T,H,D] are written as cg_from_bytes writes them; the other tokens are
+ * left untouched. With this a receiver decodes chunk j while chunk j + 1 is
+ * still in transfer: the stream decomposition of [P2 s4] makes every chunk
+ * decodable on its own once its lengths and tables are known ([P2 s5]).
+ * 0 <= chunk_begin < chunk_end <= nchunks, else CG_E_INVAL. A chunk of the
+ * range whose chunk offsets disagree with its lengths or reach beyond
+ * blob_size records CG_E_CORRUPT. Bytes of the blob beyond blob_size are
+ * never read, so they may be in transfer meanwhile.
+ * Workspace: cg_workspace_bytes(CG_OP_FROM_BYTES); calls that overlap in time
+ * need workspaces of their own. */
+int cg_from_bytes_chunks(const cg_desc *desc, const uint8_t *blob, size_t blob_size, int32_t chunk_begin,
+                         int32_t chunk_end, void *kv_out, void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------- batches
  * Many small calls of one shape, as LMCache makes them (one to_bytes per KV
  * chunk of 64..768 tokens, each with its own tables, [P2 benchmark]), in one

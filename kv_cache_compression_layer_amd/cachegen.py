@@ -107,6 +107,7 @@ _SIGNATURES = {
     "cg_from_bytes": (ctypes.c_int, [_P, _P, _SZ, _P, _P, _SZ, _P]),
     "cg_from_bytes_paged": (ctypes.c_int, [_P, _P, _SZ, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                            _P, ctypes.c_int32, _P, _SZ, _P]),
+    "cg_from_bytes_chunks": (ctypes.c_int, [_P, _P, _SZ, _I32, _I32, _P, _P, _SZ, _P]),
     "cg_workspace_bytes_batch": (_I64, [_P, _I32, _SZ, ctypes.c_int]),
     "cg_to_bytes_batch": (ctypes.c_int, [_P, _I32, _P, _P, _SZ, _P, _P, _SZ, _P]),
     "cg_from_bytes_batch": (ctypes.c_int, [_P, _I32, _P, _SZ, _P, _P, _P, _SZ, _P]),
@@ -374,6 +375,20 @@ def cg_from_bytes(desc, blob, blob_size, kv_out, ws, stream=None):
     _check(lib().cg_from_bytes(desc.ptr, _dev(blob, "blob", torch.uint8), blob_size,
                                _dev(kv_out, "kv_out", (torch.bfloat16, torch.uint16, torch.int16), 2 * L * T * C),
                                p, n, _stream_handle(stream)), "cg_from_bytes")
+
+
+def cg_from_bytes_chunks(desc, blob, blob_size, chunk_begin, chunk_end, kv_out, ws, stream=None):
+    """Decode chunks [chunk_begin, chunk_end) of a blob whose first blob_size
+    bytes have arrived; writes those tokens of kv_out [L,2,T,H,D]."""
+    torch = _torch()
+    L, T, C = desc.nlayers, desc.ntokens, desc.nchannels
+    if blob_size > blob.numel():
+        raise ValueError("blob_size exceeds the blob tensor")
+    p, n = _ws(ws, desc, CG_OP_FROM_BYTES)
+    _check(lib().cg_from_bytes_chunks(desc.ptr, _dev(blob, "blob", torch.uint8), blob_size, chunk_begin, chunk_end,
+                                      _dev(kv_out, "kv_out", (torch.bfloat16, torch.uint16, torch.int16),
+                                           2 * L * T * C),
+                                      p, n, _stream_handle(stream)), "cg_from_bytes_chunks")
 
 
 def cg_from_bytes_paged(desc, blob, blob_size, kv_cache, layer_stride, kv_stride, block_size, block_table,

@@ -536,6 +536,35 @@ int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, vo
                                 at<uint32_t>(ws, 0), s));
 }
 
+int cg_from_bytes_chunks(const cg_desc *desc, const uint8_t *blob, size_t blob_size, int32_t chunk_begin,
+                         int32_t chunk_end, void *kv_out, void *ws, size_t ws_bytes, void *stream) {
+    Dims d;
+    WsLayout w;
+    int rc = prologue(desc, CG_OP_FROM_BYTES, ws, ws_bytes, d, w);
+    if (rc) return rc;
+    if (!blob || !kv_out) return CG_E_INVAL;
+    if ((uintptr_t)blob % 8) return CG_E_INVAL;
+    if (chunk_begin < 0 || chunk_end > d.NC || chunk_begin >= chunk_end) return CG_E_INVAL;
+    const BlobLayout b = blob_layout(d);
+    if ((uint64_t)blob_size < b.off_payload) return CG_E_CORRUPT;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    MaxTable mt;
+    make_max_table(desc, mt);
+    if ((rc = clear_ws(ws, w, s))) return rc;
+    DecodeIn in{blob + b.off_payload,
+                (uint64_t)blob_size - b.off_payload,
+                reinterpret_cast<const uint16_t *>(blob + b.off_lengths),
+                reinterpret_cast<const uint64_t *>(blob + b.off_chunk_off),
+                nullptr,
+                reinterpret_cast<const uint16_t *>(blob + b.off_cdf),
+                chunk_begin,
+                chunk_end};
+    DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
+                  reinterpret_cast<const uint16_t *>(blob + b.off_scales)};
+    return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
+                                at<uint32_t>(ws, 0), s));
+}
+
 int64_t cg_workspace_bytes_batch(const cg_desc *desc, int32_t batch, size_t blob_stride, int op) {
     Dims d, vd;
     const int rc = make_dims_batch(desc, batch, d, vd);

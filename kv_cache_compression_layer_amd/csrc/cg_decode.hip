@@ -44,6 +44,7 @@ struct DecArgs {
     PagedOut paged;
     MaxTable mt;
     int L, T, C, A, NC, CB;
+    int j0, NCr;   // the chunks decoded: [j0, j0 + NCr)
 };
 
 // Bytes of the LDS pool a block of NW waves shares for its tiles' payload,
@@ -295,9 +296,9 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     uint32_t need_total = 0;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const int j = (g * NW + wv) * S + s;
-        n[s] = j < a.NC ? min(kChunk, a.T - j * kChunk) : 0;
-        t0[s] = min(j, a.NC - 1) * kChunk;
+        const int jr = (g * NW + wv) * S + s, j = a.j0 + jr;
+        n[s] = jr < a.NCr ? min(kChunk, a.T - j * kChunk) : 0;
+        t0[s] = (a.j0 + min(jr, a.NCr - 1)) * kChunk;
         uint32_t total = 0;
         len[s] = excl[s] = 0;
         base[s] = 0;
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
 
 template <int S, bool FUSED, int LOGA, int NW, bool PAGED>
 static hipError_t launch_decode_s(const Dims &d, const DecArgs &a, hipStream_t s) {
-    const int ngroups = (d.NC + S * NW - 1) / (S * NW);
+    const int ngroups = (a.NCr + S * NW - 1) / (S * NW);
     const dim3 grid((unsigned)((int64_t)ngroups * 2 * d.L * d.CB));
     if (d.A == (1 << LOGA))
         hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, false, NW, PAGED>), grid, dim3(64 * NW), 0, s, a);
@@ -490,8 +491,9 @@ static hipError_t launch_decode_f(const Dims &d, const DecArgs &a, hipStream_t s
 
 hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, const DecodeOut &out,
                          uint64_t *tile_off, uint64_t *scan_tmp, uint32_t *status, hipStream_t s) {
+    const int j0 = in.j0, j1 = in.j1 < 0 ? d.NC : in.j1;
     TileScan ts{nullptr, in.lengths, tile_off, scan_tmp, nullptr, in.chunk_off, in.payload_bytes, status,
-                d.L, d.C, d.CB, d.NC};
+                d.L, d.C, d.CB, d.NC, j0, j1 - j0};
     hipError_t e = launch_tile_scan(ts, s);
     if (e != hipSuccess) return e;
     DecArgs a;
@@ -512,19 +514,22 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     a.C = d.C;
     a.A = d.A;
     a.NC = d.NC;
+    a.j0 = j0;
+    a.NCr = j1 - j0;
+    const int ncr = a.NCr;
     a.CB = d.CB;
     // Two streams per lane and eight (or four) waves per block when there are
     // enough chunks; otherwise one stream per lane and as few waves as chunks.
     if (out.paged.cache) {
-        if (d.NC >= 16) return launch_decode_f<2, true, 8, true>(d, a, s);
-        if (d.NC >= 8) return launch_decode_f<2, true, 4, true>(d, a, s);
-        if (d.NC >= 2) return launch_decode_f<1, true, 2, true>(d, a, s);
+        if (ncr >= 16) return launch_decode_f<2, true, 8, true>(d, a, s);
+        if (ncr >= 8) return launch_decode_f<2, true, 4, true>(d, a, s);
+        if (ncr >= 2) return launch_decode_f<1, true, 2, true>(d, a, s);
         return launch_decode_f<1, true, 1, true>(d, a, s);
     }
     const bool fused = out.kv != nullptr;
-    if (d.NC >= 16) return fused ? launch_decode_f<2, true, 8>(d, a, s) : launch_decode_f<2, false, 8>(d, a, s);
-    if (d.NC >= 8) return fused ? launch_decode_f<2, true, 4>(d, a, s) : launch_decode_f<2, false, 4>(d, a, s);
-    if (d.NC >= 2) return fused ? launch_decode_f<1, true, 2>(d, a, s) : launch_decode_f<1, false, 2>(d, a, s);
+    if (ncr >= 16) return fused ? launch_decode_f<2, true, 8>(d, a, s) : launch_decode_f<2, false, 8>(d, a, s);
+    if (ncr >= 8) return fused ? launch_decode_f<2, true, 4>(d, a, s) : launch_decode_f<2, false, 4>(d, a, s);
+    if (ncr >= 2) return fused ? launch_decode_f<1, true, 2>(d, a, s) : launch_decode_f<1, false, 2>(d, a, s);
     return fused ? launch_decode_f<1, true, 1>(d, a, s) : launch_decode_f<1, false, 1>(d, a, s);
 }
 

@@ -104,6 +104,7 @@ struct TileScan {
     uint64_t payload_bytes;      // bound of chunk_off (with chunk_off)
     uint32_t *status;
     int L, C, CB, NC;
+    int j0 = 0, NCr = -1;        // chunks [j0, j0 + NCr) only (NCr < 0: all NC)
 };
 size_t tile_scan_tmp_bytes(const Dims &d);
 hipError_t launch_tile_scan(const TileScan &a, hipStream_t s);
@@ -146,6 +147,7 @@ struct DecodeIn {
     const uint64_t *chunk_off;
     const int32_t *cdf32;      // one of cdf32 / cdf16 is set
     const uint16_t *cdf16;
+    int j0 = 0, j1 = -1;       // decode chunks [j0, j1) only (j1 < 0: all); their tokens are written
 };
 
 // Paged output of the fused decoder: element (l, kv, t, c) goes to

@@ -16,6 +16,10 @@
 //      of the chunk against the stored chunk offsets;
 //   3. k_scan_add (as pass 1): adds the block's offset (and, for the
 //      decoder, the chunk offset) to every tile of the block.
+//
+// A range of chunks [j0, j0 + NCr) can be scanned alone (the decoder of a
+// blob whose payload has arrived up to some chunk): only those chunks' tiles
+// are written and only those chunks are checked.
 #include "cg_internal.hpp"
 
 namespace cg {
@@ -26,6 +30,7 @@ constexpr int kScanBlock = 256;
 
 int64_t tiles_per_chunk(const TileScan &a) { return 2LL * a.L * a.CB; }
 int64_t blocks_per_chunk(const TileScan &a) { return (tiles_per_chunk(a) + kScanBlock - 1) / kScanBlock; }
+int chunks_in_range(const TileScan &a) { return a.NCr < 0 ? a.NC : a.NCr; }
 
 }  // namespace
 
@@ -38,7 +43,7 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_local(TileScan a, int64_t t
     __shared__ uint32_t wsum[kScanBlock / 64];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t bid = blockIdx.x;
-    const int64_t j = bid / nbpc, seg = bid - j * nbpc;
+    const int64_t jr = bid / nbpc, seg = bid - jr * nbpc, j = a.j0 + jr;
     const int64_t tl = seg * kScanBlock + tid;
     uint32_t v = 0;
     if (tl < tpc) {
@@ -68,8 +73,8 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_local(TileScan a, int64_t t
 __global__ __launch_bounds__(kScanBlock) void k_scan_blocks(TileScan a, int64_t nbpc) {
     __shared__ uint64_t wsum[kScanBlock / 64];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int64_t j = blockIdx.x;
-    uint64_t *t = a.tmp + j * nbpc;
+    const int64_t j = a.j0 + (int64_t)blockIdx.x;
+    uint64_t *t = a.tmp + (int64_t)blockIdx.x * nbpc;
     uint64_t run = 0;
     for (int64_t seg = 0; seg < nbpc; seg += kScanBlock) {
         const int64_t i = seg + tid;
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_blocks(TileScan a, int64_t 
 
 __global__ __launch_bounds__(kScanBlock) void k_scan_add(TileScan a, int64_t tpc, int64_t nbpc) {
     const int64_t bid = blockIdx.x;
-    const int64_t j = bid / nbpc, seg = bid - j * nbpc;
+    const int64_t jr = bid / nbpc, seg = bid - jr * nbpc, j = a.j0 + jr;
     const int64_t tl = seg * kScanBlock + threadIdx.x;
     if (tl >= tpc) return;
     const uint64_t add = a.tmp[bid] + (a.chunk_off ? a.chunk_off[j] : 0ull);
@@ -114,11 +119,12 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_add(TileScan a, int64_t tpc
 
 hipError_t launch_tile_scan(const TileScan &a, hipStream_t s) {
     const int64_t tpc = tiles_per_chunk(a), nbpc = blocks_per_chunk(a);
-    const unsigned nblk = (unsigned)(a.NC * nbpc);
+    const int ncr = chunks_in_range(a);
+    const unsigned nblk = (unsigned)(ncr * nbpc);
     hipLaunchKernelGGL(k_scan_local, dim3(nblk), dim3(kScanBlock), 0, s, a, tpc, nbpc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_scan_blocks, dim3((unsigned)a.NC), dim3(kScanBlock), 0, s, a, nbpc);
+    hipLaunchKernelGGL(k_scan_blocks, dim3((unsigned)ncr), dim3(kScanBlock), 0, s, a, nbpc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_scan_add, dim3(nblk), dim3(kScanBlock), 0, s, a, tpc, nbpc);
     return hipGetLastError();

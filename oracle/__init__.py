@@ -56,6 +56,10 @@ def lib():
             "ocg_quantize": (i32, [i32, i32, i32, p, p, p, p, p]),
             "ocg_histogram": (i32, [i32, i32, i32, i32, p, p]),
             "ocg_cdf": (i32, [i32, i32, i32, i32, p, p]),
+            "ocg_cdf_w": (i32, [i32, i32, i32, i32, p, p, p]),
+            "ocg_encode_w": (i64, [i32, i32, i32, i32, p, p, p, p, i64, p, p]),
+            "ocg_decode_w": (i32, [i32, i32, i32, i32, p, p, i64, p, p, p, p]),
+            "ocg_to_bytes_fmt": (i64, [i32, i32, i32, i32, p, p, i32, p, p, i64]),
             "ocg_encode_stream": (i64, [p, i32, p, i32, p, i64]),
             "ocg_decode_stream": (i32, [p, i64, i32, p, i32, p]),
             "ocg_encode": (i64, [i32, i32, i32, i32, p, p, p, i64, p, p]),
@@ -121,16 +125,34 @@ def histogram(sym: np.ndarray, A: int):
     return cnt
 
 
-def cdf_from_counts(cnt: np.ndarray, T: int):
+def table_widths(bins_k, bins_v, table_format: int = 0):
+    """Width of the tables of each (kv, layer) -> uint8 [2, L]: the call's
+    alphabet for format 0, the layer's bins for format 1."""
+    bk, bv = _u8(bins_k), _u8(bins_v)
+    if table_format == 0:
+        A = alphabet(bk, bv)
+        return np.full((2, len(bk)), A, np.uint8)
+    if table_format == 1:
+        return np.ascontiguousarray(np.stack([bk, bv]))
+    raise ValueError("table_format must be 0 or 1")
+
+
+def cdf_from_counts(cnt: np.ndarray, T: int, widths=None):
+    """-> int32 [2,L,C,A+1]; widths (uint8 [2,L]) gives each table its own
+    alphabet (entries past a table's end hold 2^16)."""
     _, L, C, A = cnt.shape
     cnt = np.ascontiguousarray(cnt, dtype=np.uint32)
     cdf = np.empty((2, L, C, A + 1), np.int32)
-    _check(lib().ocg_cdf(L, T, C, A, _p(cnt), _p(cdf)), "cdf")
+    if widths is None:
+        _check(lib().ocg_cdf(L, T, C, A, _p(cnt), _p(cdf)), "cdf")
+    else:
+        w = _u8(widths).reshape(2 * L)
+        _check(lib().ocg_cdf_w(L, T, C, A, _p(w), _p(cnt), _p(cdf)), "cdf_w")
     return cdf
 
 
-def build_cdf(sym: np.ndarray, A: int):
-    return cdf_from_counts(histogram(sym, A), sym.shape[2])
+def build_cdf(sym: np.ndarray, A: int, widths=None):
+    return cdf_from_counts(histogram(sym, A), sym.shape[2], widths)
 
 
 def encode_stream(symbols, cdf_row) -> bytes:
@@ -155,7 +177,7 @@ def nchunks(T: int) -> int:
     return (T + CHUNK_TOKENS - 1) // CHUNK_TOKENS
 
 
-def encode(sym: np.ndarray, cdf: np.ndarray):
+def encode(sym: np.ndarray, cdf: np.ndarray, widths=None):
     """-> (payload bytes as uint8 array, lengths uint16 [NC,2L,C], chunk_off uint64 [NC+1])."""
     _, L, T, C = sym.shape
     A = cdf.shape[-1] - 1
@@ -166,12 +188,18 @@ def encode(sym: np.ndarray, cdf: np.ndarray):
     payload = np.empty(max(cap, 1), np.uint8)
     lengths = np.empty((NC, 2 * L, C), np.uint16)
     chunk_off = np.empty(NC + 1, np.uint64)
-    n = _check(lib().ocg_encode(L, T, C, A, _p(sym), _p(cdf), _p(payload), cap, _p(lengths), _p(chunk_off)),
-               "encode")
+    if widths is None:
+        n = _check(lib().ocg_encode(L, T, C, A, _p(sym), _p(cdf), _p(payload), cap, _p(lengths), _p(chunk_off)),
+                   "encode")
+    else:
+        w = _u8(widths).reshape(2 * L)
+        n = _check(lib().ocg_encode_w(L, T, C, A, _p(w), _p(sym), _p(cdf), _p(payload), cap, _p(lengths),
+                                      _p(chunk_off)), "encode_w")
     return payload[:n].copy(), lengths, chunk_off
 
 
-def decode(payload: np.ndarray, lengths: np.ndarray, chunk_off: np.ndarray, cdf: np.ndarray, T: int):
+def decode(payload: np.ndarray, lengths: np.ndarray, chunk_off: np.ndarray, cdf: np.ndarray, T: int,
+           widths=None):
     NC, twoL, C = lengths.shape
     L = twoL // 2
     A = cdf.shape[-1] - 1
@@ -180,8 +208,13 @@ def decode(payload: np.ndarray, lengths: np.ndarray, chunk_off: np.ndarray, cdf:
     chunk_off = np.ascontiguousarray(chunk_off, dtype=np.uint64)
     cdf = np.ascontiguousarray(cdf, dtype=np.int32)
     sym = np.empty((2, L, T, C), np.uint8)
-    _check(lib().ocg_decode(L, T, C, A, _p(pay), len(payload), _p(lengths), _p(chunk_off), _p(cdf), _p(sym)),
-           "decode")
+    if widths is None:
+        _check(lib().ocg_decode(L, T, C, A, _p(pay), len(payload), _p(lengths), _p(chunk_off), _p(cdf), _p(sym)),
+               "decode")
+    else:
+        w = _u8(widths).reshape(2 * L)
+        _check(lib().ocg_decode_w(L, T, C, A, _p(w), _p(pay), len(payload), _p(lengths), _p(chunk_off), _p(cdf),
+                                  _p(sym)), "decode_w")
     return sym
 
 
@@ -196,24 +229,25 @@ def dequantize(sym: np.ndarray, scale: np.ndarray, bins_k, bins_v):
     return out
 
 
-def to_bytes(kv: np.ndarray, bins_k, bins_v) -> bytes:
+def to_bytes(kv: np.ndarray, bins_k, bins_v, table_format: int = 0) -> bytes:
     L, two, T, H, D = kv.shape
     kv = np.ascontiguousarray(kv, dtype=np.uint16)
     bk, bv = _u8(bins_k), _u8(bins_v)
     cap = _check(lib().ocg_blob_bound(L, T, H, D, _p(bk), _p(bv)), "blob_bound")
     blob = np.empty(cap, np.uint8)
-    n = _check(lib().ocg_to_bytes(L, T, H, D, _p(bk), _p(bv), _p(kv), _p(blob), cap), "to_bytes")
+    n = _check(lib().ocg_to_bytes_fmt(L, T, H, D, _p(bk), _p(bv), int(table_format), _p(kv), _p(blob), cap),
+               "to_bytes")
     return blob[:n].tobytes()
 
 
 def blob_header(blob: bytes):
     """-> (dims dict, bins_k, bins_v)."""
     buf = np.frombuffer(blob, np.uint8).copy()
-    dims = np.zeros(7, np.int32)
+    dims = np.zeros(8, np.int32)
     bk = np.zeros(1024, np.uint8)
     bv = np.zeros(1024, np.uint8)
     _check(lib().ocg_blob_header(_p(buf), len(blob), _p(dims), _p(bk), _p(bv), 1024), "blob_header")
-    names = ["nlayers", "ntokens", "nheads", "head_size", "chunk_tokens", "nchunks", "alphabet"]
+    names = ["nlayers", "ntokens", "nheads", "head_size", "chunk_tokens", "nchunks", "alphabet", "table_format"]
     d = dict(zip(names, map(int, dims)))
     return d, bk[: d["nlayers"]].copy(), bv[: d["nlayers"]].copy()
 

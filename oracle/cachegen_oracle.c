@@ -190,29 +190,59 @@ int ocg_histogram(int L, int T, int C, int A, const uint8_t *sym, uint32_t *cnt)
 }
 
 /* The cumulative distribution of a (kv, layer, channel) table is cum[k]/T
- * with cum[k] = sum_{s<k} cnt[s], k = 0..A (A+1 = Lp entries). It is scaled to
- * 16-bit precision by multiplying with 2^16 - (Lp - 1) = 2^16 - A and adding
- * the ramp k, so that every symbol keeps a frequency of at least 1 and the
- * table is strictly increasing, from 0 to 2^16. The scaled value cum*S/T is
- * rounded half-to-even from the exact rational. */
-int ocg_cdf(int L, int T, int C, int A, const uint32_t *cnt, int32_t *cdf)
+ * with cum[k] = sum_{s<k} cnt[s], k = 0..W (Lp = W + 1 entries, W the table's
+ * alphabet). It is scaled to 16-bit precision by multiplying with
+ * 2^16 - (Lp - 1) = 2^16 - W and adding the ramp k, so that every symbol
+ * keeps a frequency of at least 1 and the table is strictly increasing, from
+ * 0 to 2^16. The scaled value cum*S/T is rounded half-to-even from the exact
+ * rational.
+ *
+ * The page normalises with one Lp but leaves open what it is. Two readings
+ * are built: every table of the call has the call's alphabet, W = A = the
+ * largest bins of any layer (widths == NULL, the default), or every table of
+ * (kv, layer) has its layer's own alphabet, W = bins of that layer (widths =
+ * [2, L] table widths). Tables are stored [2, L, C, A + 1] either way; the
+ * entries of a narrower table past its end W hold 2^16 (they belong to no
+ * symbol). A count at or past W is an error. */
+static int cdf_tables(int L, int T, int C, int A, const uint8_t *widths, const uint32_t *cnt,
+                      int32_t *cdf)
 {
     if (L < 1 || T < 1 || C < 1 || A < 2 || A > 255 || !cnt || !cdf)
         return OCG_ERR_ARG;
-    const uint64_t S = PROB_ONE - (uint64_t)A;
     for (size_t tab = 0; tab < 2 * (size_t)L * C; ++tab) {
+        const int W = widths ? widths[tab / (size_t)C] : A;
+        if (W < 2 || W > A)
+            return OCG_ERR_ARG;
+        const uint64_t S = PROB_ONE - (uint64_t)W;
         const uint32_t *h = cnt + tab * A;
         int32_t *out = cdf + tab * (A + 1);
         uint64_t cum = 0;
-        for (int k = 0; k <= A; ++k) {
+        for (int k = 0; k <= W; ++k) {
             out[k] = (int32_t)(div_round_half_even(cum * S, (uint64_t)T) + (uint64_t)k);
-            if (k < A)
+            if (k < W)
                 cum += h[k];
         }
+        for (int k = W + 1; k <= A; ++k)
+            out[k] = (int32_t)PROB_ONE;
+        for (int k = W; k < A; ++k)
+            if (h[k])
+                return OCG_ERR_ARG;
         if (cum != (uint64_t)T)
             return OCG_ERR_ARG;
     }
     return 0;
+}
+
+int ocg_cdf(int L, int T, int C, int A, const uint32_t *cnt, int32_t *cdf)
+{
+    return cdf_tables(L, T, C, A, NULL, cnt, cdf);
+}
+
+int ocg_cdf_w(int L, int T, int C, int A, const uint8_t *widths, const uint32_t *cnt, int32_t *cdf)
+{
+    if (!widths)
+        return OCG_ERR_ARG;
+    return cdf_tables(L, T, C, A, widths, cnt, cdf);
 }
 
 /* ------------------------------------------------- [P2 s4] range coder */
@@ -321,8 +351,10 @@ int ocg_decode_stream(const uint8_t *in, int64_t len, int n, const int32_t *cdf,
 
 static int nchunks_of(int T) { return (T + CHUNK_TOKENS - 1) / CHUNK_TOKENS; }
 
-int64_t ocg_encode(int L, int T, int C, int A, const uint8_t *sym, const int32_t *cdf,
-                   uint8_t *payload, int64_t cap, uint16_t *lengths, uint64_t *chunk_off)
+/* Tables of width W (widths[kv*L + l], or A for all) stored with stride A + 1. */
+static int64_t encode_all(int L, int T, int C, int A, const uint8_t *widths, const uint8_t *sym,
+                          const int32_t *cdf, uint8_t *payload, int64_t cap, uint16_t *lengths,
+                          uint64_t *chunk_off)
 {
     if (L < 1 || T < 1 || C < 1 || A < 2 || !sym || !cdf || !lengths || !chunk_off)
         return OCG_ERR_ARG;
@@ -340,7 +372,8 @@ int64_t ocg_encode(int L, int T, int C, int A, const uint8_t *sym, const int32_t
                     for (int i = 0; i < n; ++i)
                         stream[i] = sym[(((size_t)k * L + l) * T + t0 + i) * C + c];
                     const int32_t *tab = cdf + (((size_t)k * L + l) * C + c) * (A + 1);
-                    int64_t len = ocg_encode_stream(stream, n, tab, A, tmp, sizeof tmp);
+                    const int W = widths ? widths[k * L + l] : A;
+                    int64_t len = ocg_encode_stream(stream, n, tab, W, tmp, sizeof tmp);
                     if (len < 0)
                         return len;
                     if (len > 0xFFFF)
@@ -357,9 +390,24 @@ int64_t ocg_encode(int L, int T, int C, int A, const uint8_t *sym, const int32_t
     return off;
 }
 
-int ocg_decode(int L, int T, int C, int A, const uint8_t *payload, int64_t payload_bytes,
-               const uint16_t *lengths, const uint64_t *chunk_off, const int32_t *cdf,
-               uint8_t *sym)
+int64_t ocg_encode(int L, int T, int C, int A, const uint8_t *sym, const int32_t *cdf,
+                   uint8_t *payload, int64_t cap, uint16_t *lengths, uint64_t *chunk_off)
+{
+    return encode_all(L, T, C, A, NULL, sym, cdf, payload, cap, lengths, chunk_off);
+}
+
+int64_t ocg_encode_w(int L, int T, int C, int A, const uint8_t *widths, const uint8_t *sym,
+                     const int32_t *cdf, uint8_t *payload, int64_t cap, uint16_t *lengths,
+                     uint64_t *chunk_off)
+{
+    if (!widths)
+        return OCG_ERR_ARG;
+    return encode_all(L, T, C, A, widths, sym, cdf, payload, cap, lengths, chunk_off);
+}
+
+static int decode_all(int L, int T, int C, int A, const uint8_t *widths, const uint8_t *payload,
+                      int64_t payload_bytes, const uint16_t *lengths, const uint64_t *chunk_off,
+                      const int32_t *cdf, uint8_t *sym)
 {
     if (L < 1 || T < 1 || C < 1 || A < 2 || !lengths || !chunk_off || !cdf || !sym)
         return OCG_ERR_ARG;
@@ -378,7 +426,8 @@ int ocg_decode(int L, int T, int C, int A, const uint8_t *payload, int64_t paylo
                     if (off + len > (uint64_t)payload_bytes)
                         return OCG_ERR_CORRUPT;
                     const int32_t *tab = cdf + (((size_t)k * L + l) * C + c) * (A + 1);
-                    int rc = ocg_decode_stream(payload + off, len, n, tab, A, stream);
+                    const int W = widths ? widths[k * L + l] : A;
+                    int rc = ocg_decode_stream(payload + off, len, n, tab, W, stream);
                     if (rc)
                         return rc;
                     for (int i = 0; i < n; ++i)
@@ -389,6 +438,22 @@ int ocg_decode(int L, int T, int C, int A, const uint8_t *payload, int64_t paylo
             return OCG_ERR_CORRUPT;
     }
     return 0;
+}
+
+int ocg_decode(int L, int T, int C, int A, const uint8_t *payload, int64_t payload_bytes,
+               const uint16_t *lengths, const uint64_t *chunk_off, const int32_t *cdf,
+               uint8_t *sym)
+{
+    return decode_all(L, T, C, A, NULL, payload, payload_bytes, lengths, chunk_off, cdf, sym);
+}
+
+int ocg_decode_w(int L, int T, int C, int A, const uint8_t *widths, const uint8_t *payload,
+                 int64_t payload_bytes, const uint16_t *lengths, const uint64_t *chunk_off,
+                 const int32_t *cdf, uint8_t *sym)
+{
+    if (!widths)
+        return OCG_ERR_ARG;
+    return decode_all(L, T, C, A, widths, payload, payload_bytes, lengths, chunk_off, cdf, sym);
 }
 
 /* ------------------------------------------------------ [P2 s5] dequantise */
@@ -435,14 +500,27 @@ struct layout {
     int64_t header, scales, cdf, offsets, lengths, payload;
 };
 
-static struct layout layout_of(int L, int T, int C, int A)
+/* Table widths of the blob format: fmt 0 gives every table the call's
+ * alphabet A, fmt 1 gives the tables of (kv, l) the bins of that layer. */
+static void table_widths(int L, const uint8_t *bk, const uint8_t *bv, int fmt, uint8_t *w)
+{
+    const int A = max_bins(L, bk, bv);
+    for (int l = 0; l < L; ++l) {
+        w[l] = (uint8_t)(fmt ? bk[l] : A);
+        w[L + l] = (uint8_t)(fmt ? bv[l] : A);
+    }
+}
+
+/* entries = the sum of the table widths over the 2L (kv, layer) slabs; the
+ * u16 table section holds C tables of each slab, slab after slab. */
+static struct layout layout_of(int L, int T, int C, int64_t entries)
 {
     struct layout s;
     int64_t NC = nchunks_of(T);
     s.header = 0;
     s.scales = align_up(HDR_FIXED + 2 * (int64_t)L);
     s.cdf = s.scales + align_up(2 * 2 * (int64_t)L * T);
-    s.offsets = s.cdf + align_up(2 * 2 * (int64_t)L * C * A);
+    s.offsets = s.cdf + align_up(2 * (int64_t)C * entries);
     s.lengths = s.offsets + align_up(8 * (NC + 1));
     s.payload = s.lengths + align_up(2 * NC * 2 * (int64_t)L * C);
     return s;
@@ -460,18 +538,24 @@ int64_t ocg_blob_bound(int L, int T, int H, int D, const uint8_t *bins_k, const 
     if (L < 1 || T < 1 || H < 1 || D < 1 || !bins_ok(L, bins_k, bins_v))
         return OCG_ERR_ARG;
     int C = H * D;
-    struct layout s = layout_of(L, T, C, max_bins(L, bins_k, bins_v));
+    struct layout s = layout_of(L, T, C, 2 * (int64_t)L * max_bins(L, bins_k, bins_v));
     int64_t NS = (int64_t)nchunks_of(T) * 2 * L * C;
     return s.payload + NS * (4 * CHUNK_TOKENS);
 }
 
-int64_t ocg_to_bytes(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v,
-                     const uint16_t *kv, uint8_t *blob, int64_t cap)
+int64_t ocg_to_bytes_fmt(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v,
+                         int fmt, const uint16_t *kv, uint8_t *blob, int64_t cap)
 {
-    if (L < 1 || T < 1 || H < 1 || D < 1 || !kv || !blob || !bins_ok(L, bins_k, bins_v))
+    if (L < 1 || L > 1024 || T < 1 || H < 1 || D < 1 || !kv || !blob || !bins_ok(L, bins_k, bins_v) ||
+        (fmt != 0 && fmt != 1))
         return OCG_ERR_ARG;
     int C = H * D, A = max_bins(L, bins_k, bins_v), NC = nchunks_of(T);
-    struct layout s = layout_of(L, T, C, A);
+    uint8_t W[2048];
+    table_widths(L, bins_k, bins_v, fmt, W);
+    int64_t entries = 0;
+    for (int i = 0; i < 2 * L; ++i)
+        entries += W[i];
+    struct layout s = layout_of(L, T, C, entries);
     if (cap < s.payload)
         return OCG_ERR_CAPACITY;
     size_t n = 2 * (size_t)L * T * C;
@@ -488,10 +572,10 @@ int64_t ocg_to_bytes(int L, int T, int H, int D, const uint8_t *bins_k, const ui
         goto done;
     if ((rc = ocg_histogram(L, T, C, A, sym, cnt)))
         goto done;
-    if ((rc = ocg_cdf(L, T, C, A, cnt, cdf)))
+    if ((rc = cdf_tables(L, T, C, A, W, cnt, cdf)))
         goto done;
     memset(blob, 0, (size_t)s.payload);
-    int64_t pay = ocg_encode(L, T, C, A, sym, cdf, blob + s.payload, cap - s.payload, lengths, chunk_off);
+    int64_t pay = encode_all(L, T, C, A, W, sym, cdf, blob + s.payload, cap - s.payload, lengths, chunk_off);
     if (pay < 0) {
         rc = pay;
         goto done;
@@ -507,15 +591,21 @@ int64_t ocg_to_bytes(int L, int T, int H, int D, const uint8_t *bins_k, const ui
     put32(blob + 24, CHUNK_TOKENS);
     put32(blob + 28, (uint32_t)NC);
     put32(blob + 32, (uint32_t)A);
-    put32(blob + 36, 0);
+    put32(blob + 36, (uint32_t)fmt);
     put64(blob + 40, (uint64_t)(s.payload + pay));
     memcpy(blob + HDR_FIXED, bins_k, (size_t)L);
     memcpy(blob + HDR_FIXED + L, bins_v, (size_t)L);
     for (size_t i = 0; i < 2 * (size_t)L * T; ++i)
         put16(blob + s.scales + 2 * i, scale[i]);
-    for (size_t tab = 0; tab < 2 * (size_t)L * C; ++tab)
-        for (int k = 0; k < A; ++k)
-            put16(blob + s.cdf + 2 * (tab * A + k), (uint16_t)cdf[tab * (A + 1) + k]);
+    {
+        /* Entries 0..W-1 of every table, slab after slab (entry W is 2^16). */
+        int64_t e = 0;
+        for (size_t tab = 0; tab < 2 * (size_t)L * C; ++tab) {
+            const int w = W[tab / (size_t)C];
+            for (int k = 0; k < w; ++k)
+                put16(blob + s.cdf + 2 * (e++), (uint16_t)cdf[tab * (A + 1) + k]);
+        }
+    }
     for (int j = 0; j <= NC; ++j)
         put64(blob + s.offsets + 8 * j, chunk_off[j]);
     for (size_t i = 0; i < (size_t)NC * 2 * L * C; ++i)
@@ -531,14 +621,24 @@ done:
     return rc;
 }
 
-int ocg_blob_header(const uint8_t *blob, int64_t size, int32_t dims[7], uint8_t *bins_k,
+int64_t ocg_to_bytes(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v,
+                     const uint16_t *kv, uint8_t *blob, int64_t cap)
+{
+    return ocg_to_bytes_fmt(L, T, H, D, bins_k, bins_v, 0, kv, blob, cap);
+}
+
+/* dims: nlayers, ntokens, nheads, head_size, chunk_tokens, nchunks, alphabet,
+ * table format. */
+int ocg_blob_header(const uint8_t *blob, int64_t size, int32_t dims[8], uint8_t *bins_k,
                     uint8_t *bins_v, int max_layers)
 {
     if (!blob || size < HDR_FIXED || memcmp(blob, "CGMX", 4) || get16(blob + 4) != 1 ||
         get16(blob + 6) != 1)
         return OCG_ERR_CORRUPT;
-    for (int i = 0; i < 7; ++i)
+    for (int i = 0; i < 8; ++i)
         dims[i] = (int32_t)get32(blob + 8 + 4 * i);
+    if (dims[7] != 0 && dims[7] != 1)
+        return OCG_ERR_CORRUPT;
     int L = dims[0];
     if (L < 1 || L > max_layers || size < HDR_FIXED + 2 * (int64_t)L)
         return OCG_ERR_CORRUPT;
@@ -553,13 +653,18 @@ int ocg_blob_header(const uint8_t *blob, int64_t size, int32_t dims[7], uint8_t 
 
 int ocg_from_bytes(const uint8_t *blob, int64_t size, uint16_t *kv_out)
 {
-    int32_t dims[7];
+    int32_t dims[8];
     uint8_t bk[1024], bv[1024];
     int rc = ocg_blob_header(blob, size, dims, bk, bv, 1024);
     if (rc)
         return rc;
     int L = dims[0], T = dims[1], C = dims[2] * dims[3], NC = dims[5], A = dims[6];
-    struct layout s = layout_of(L, T, C, A);
+    uint8_t W[2048];
+    table_widths(L, bk, bv, dims[7], W);
+    int64_t entries = 0;
+    for (int i = 0; i < 2 * L; ++i)
+        entries += W[i];
+    struct layout s = layout_of(L, T, C, entries);
     if (size < s.payload)
         return OCG_ERR_CORRUPT;
     uint16_t *scale = malloc(sizeof(uint16_t) * 2 * (size_t)L * T);
@@ -573,15 +678,21 @@ int ocg_from_bytes(const uint8_t *blob, int64_t size, uint16_t *kv_out)
     for (size_t i = 0; i < 2 * (size_t)L * T; ++i)
         scale[i] = get16(blob + s.scales + 2 * i);
     rc = OCG_ERR_CORRUPT;
-    for (size_t tab = 0; tab < 2 * (size_t)L * C; ++tab) {
-        for (int k = 0; k < A; ++k)
-            cdf[tab * (A + 1) + k] = get16(blob + s.cdf + 2 * (tab * A + k));
-        cdf[tab * (A + 1) + A] = PROB_ONE;
-        if (cdf[tab * (A + 1)] != 0)
-            goto done;
-        for (int k = 0; k < A; ++k)
-            if (cdf[tab * (A + 1) + k + 1] <= cdf[tab * (A + 1) + k])
+    {
+        int64_t e = 0;
+        for (size_t tab = 0; tab < 2 * (size_t)L * C; ++tab) {
+            const int w = W[tab / (size_t)C];
+            int32_t *t = cdf + tab * (A + 1);
+            for (int k = 0; k < w; ++k)
+                t[k] = get16(blob + s.cdf + 2 * (e++));
+            for (int k = w; k <= A; ++k)
+                t[k] = PROB_ONE;
+            if (t[0] != 0)
                 goto done;
+            for (int k = 0; k < w; ++k)
+                if (t[k + 1] <= t[k])
+                    goto done;
+        }
     }
     for (int j = 0; j <= NC; ++j)
         chunk_off[j] = get64(blob + s.offsets + 8 * j);
@@ -589,7 +700,7 @@ int ocg_from_bytes(const uint8_t *blob, int64_t size, uint16_t *kv_out)
         lengths[i] = get16(blob + s.lengths + 2 * i);
     if ((int64_t)chunk_off[NC] != size - s.payload)
         goto done;
-    if ((rc = ocg_decode(L, T, C, A, blob + s.payload, size - s.payload, lengths, chunk_off, cdf, sym)))
+    if ((rc = decode_all(L, T, C, A, W, blob + s.payload, size - s.payload, lengths, chunk_off, cdf, sym)))
         goto done;
     rc = ocg_dequantize(L, T, C, bk, bv, sym, scale, kv_out);
 done:

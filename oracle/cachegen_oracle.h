@@ -47,6 +47,11 @@ int ocg_histogram(int L, int T, int C, int A, const uint8_t *sym, uint32_t *cnt)
  * cdf[k] = round_half_even(cum[k] * (2^16 - A) / T) + k. */
 int ocg_cdf(int L, int T, int C, int A, const uint32_t *cnt, int32_t *cdf);
 
+/* The same with a width per (kv, layer) table (widths [2, L], each in
+ * [2, A]): table (kv, l, c) has widths[kv*L + l] symbols and is normalised
+ * with 2^16 - that width; entries past its end hold 2^16. */
+int ocg_cdf_w(int L, int T, int C, int A, const uint8_t *widths, const uint32_t *cnt, int32_t *cdf);
+
 /* Range-code one stream of n symbols with the table cdf[0..A]. Returns the
  * number of bytes written to out, or a negative code. */
 int64_t ocg_encode_stream(const uint8_t *sym, int n, const int32_t *cdf, int A,
@@ -63,12 +68,18 @@ int ocg_decode_stream(const uint8_t *in, int64_t len, int n, const int32_t *cdf,
  * Returns the payload size or a negative code. */
 int64_t ocg_encode(int L, int T, int C, int A, const uint8_t *sym, const int32_t *cdf,
                    uint8_t *payload, int64_t cap, uint16_t *lengths, uint64_t *chunk_off);
+int64_t ocg_encode_w(int L, int T, int C, int A, const uint8_t *widths, const uint8_t *sym,
+                     const int32_t *cdf, uint8_t *payload, int64_t cap, uint16_t *lengths,
+                     uint64_t *chunk_off);
 
 /* Inverse of ocg_encode ([P2] section 5): offsets of each stream are the
  * chunk offset plus the prefix sum of the lengths. */
 int ocg_decode(int L, int T, int C, int A, const uint8_t *payload, int64_t payload_bytes,
                const uint16_t *lengths, const uint64_t *chunk_off, const int32_t *cdf,
                uint8_t *sym);
+int ocg_decode_w(int L, int T, int C, int A, const uint8_t *widths, const uint8_t *payload,
+                 int64_t payload_bytes, const uint16_t *lengths, const uint64_t *chunk_off,
+                 const int32_t *cdf, uint8_t *sym);
 
 /* Dequantise ([P2] section 5): x = (q - M) / M * scale with M = bins//2 - 1
  * of the element's layer, evaluated in double precision and rounded once to
@@ -90,8 +101,14 @@ int ocg_dequantize(int L, int T, int C, const uint8_t *bins_k, const uint8_t *bi
 int64_t ocg_blob_bound(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v);
 int64_t ocg_to_bytes(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v,
                      const uint16_t *kv, uint8_t *blob, int64_t cap);
+/* The same for table format fmt: 0 = one alphabet A for every table, 1 = the
+ * tables of (kv, layer) have the bins of that layer; the u16 table section is
+ * then ragged (C tables of width W per slab, slab after slab) and header
+ * bytes 36..39 hold fmt. */
+int64_t ocg_to_bytes_fmt(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v,
+                         int fmt, const uint16_t *kv, uint8_t *blob, int64_t cap);
 /* Parses the header; dims = {L, T, H, D, chunk, NC, A}. */
-int ocg_blob_header(const uint8_t *blob, int64_t size, int32_t dims[7], uint8_t *bins_k,
+int ocg_blob_header(const uint8_t *blob, int64_t size, int32_t dims[8], uint8_t *bins_k,
                     uint8_t *bins_v, int max_layers);
 int ocg_from_bytes(const uint8_t *blob, int64_t size, uint16_t *kv_out);
 

@@ -381,8 +381,34 @@ def main():
             "per_call_from_bytes_GBps": craw / (l_dec_ms * 1e-3) / 1e9,
             "compression_ratio": craw / sum(sizes_h),
         }
-        log(f"batch of {nb} x {ct} tokens: {json.dumps({k: round(v, 4) for k, v in batch.items()})}")
-        del chunks, chunks_out, blobs, blobs2, ws_be, ws_bd, ws1e, ws1d, views
+        del blobs2, ws1e, ws1d, views
+        # The same batch with per-layer tables (every (K|V, layer) table has
+        # its layer's bins): the tables are most of a 256-token blob.
+        desc1p = cgb.Desc(L, ct, H, D, desc.bins_k, desc.bins_v, cgb.CG_TABLES_PER_LAYER)
+        stride_p = (cgb.cg_blob_bound(desc1p) + 7) // 8 * 8
+        ws_pe = cgb.alloc_workspace_batch(desc1p, nb, stride_p, cgb.CG_OP_TO_BYTES, dev)
+        ws_pd = cgb.alloc_workspace_batch(desc1p, nb, stride_p, cgb.CG_OP_FROM_BYTES, dev)
+        sizes_p = torch.zeros(nb, dtype=torch.int64, device=dev)
+        out_p = torch.empty_like(chunks)
+
+        def p_enc():
+            cgb.cg_to_bytes_batch(desc1p, nb, chunks, blobs, stride_p, sizes_p, ws_pe)
+
+        def p_dec():
+            cgb.cg_from_bytes_batch(desc1p, nb, blobs, stride_p, sizes_p, out_p, ws_pd)
+
+        p_enc()
+        cgb.check_status(ws_pe, what="cg_to_bytes_batch (per-layer tables)")
+        p_dec()
+        cgb.check_status(ws_pd, what="cg_from_bytes_batch (per-layer tables)")
+        assert torch.equal(out_p, chunks_out), "per-layer tables decode differently"
+        batch["per_layer_tables"] = {
+            "to_bytes_ms": time_events(p_enc, args.stage_reps, torch),
+            "from_bytes_ms": time_events(p_dec, args.stage_reps, torch),
+            "compression_ratio": craw / int(sizes_p.sum().item()),
+        }
+        log(f"batch of {nb} x {ct} tokens: {json.dumps(batch)}")
+        del chunks, chunks_out, out_p, blobs, ws_be, ws_bd, ws_pe, ws_pd
 
     # Achievable copy bandwidth: a device-to-device copy of the raw KV
     # (read + write of 4 GiB), the practical ceiling beside the 8 TB/s spec.

@@ -60,11 +60,24 @@ extern "C" {
 #define CG_MAX_BINS         128
 #define CG_MAX_STREAM_BYTES 513  /* worst-case coded size of a 256-symbol stream */
 
+/* Table formats ([P2 s3] normalises each table with 2^16 - (Lp - 1) and
+ * the ramp arange(Lp) but leaves Lp open).
+ * CG_TABLES_SHARED: every table has the call's alphabet A = the largest bins
+ *   of any K or V layer (Lp = A + 1); the u16 table section is [2,L,C,A].
+ * CG_TABLES_PER_LAYER: the tables of (K|V, layer) have that layer's own
+ *   alphabet W = its bins (Lp = W + 1, S = 2^16 - W); the u16 table section
+ *   holds, for each (K|V, layer) in turn, C tables of W entries. Same
+ *   symbols, coder and output; fewer table bytes when the bins differ, which
+ *   matters for short calls (at 256 tokens the tables are most of a blob). */
+#define CG_TABLES_SHARED    0
+#define CG_TABLES_PER_LAYER 1
+
 /* Problem descriptor. bins_k / bins_v are HOST arrays of length nlayers
  * holding the number of quantisation bins of each layer ([P2 s1]); each must
  * be in [4, 128]. Valid shapes: 1 <= nlayers <= 1024, ntokens >= 1,
  * nheads >= 1, head_size >= 1, 2*nlayers*ntokens*nheads*head_size < 2^40 and
- * ntokens*nheads*head_size < 2^31 (one (K|V, layer) slab). */
+ * ntokens*nheads*head_size < 2^31 (one (K|V, layer) slab). table_format:
+ * CG_TABLES_SHARED or CG_TABLES_PER_LAYER (else CG_E_INVAL); reserved: 0. */
 typedef struct cg_desc {
     int32_t nlayers;
     int32_t ntokens;
@@ -72,19 +85,23 @@ typedef struct cg_desc {
     int32_t head_size;
     const uint8_t *bins_k;
     const uint8_t *bins_v;
+    int32_t table_format;
+    int32_t reserved;
 } cg_desc;
 
 /* Blob layout, as written by cg_to_bytes and read by cg_blob_peek. Offsets
  * are byte offsets from the start of the blob; every section is 64-byte
  * aligned and the gaps are zero. Header (little-endian): "CGMX", u16
  * version 1, u16 dtype 1 (bf16), u32 nlayers, ntokens, nheads, head_size,
- * chunk_tokens (256), nchunks, alphabet, reserved (0), u64 blob_size, then
+ * chunk_tokens (256), nchunks, alphabet, table_format, u64 blob_size, then
  * u8 bins_k[nlayers], u8 bins_v[nlayers]. Sections: scales bf16 [2,L,T];
- * cdf u16 [2,L,C,A] (entries 0..A-1 of each table, entry A is 2^16);
- * chunk_off u64 [NC+1]; lengths u16 [NC,2L,C]; payload. */
+ * cdf u16: entries 0..W-1 of each table (entry W is 2^16), [2,L,C,A] for
+ * CG_TABLES_SHARED, per (K|V, layer) C tables of its bins entries for
+ * CG_TABLES_PER_LAYER; chunk_off u64 [NC+1]; lengths u16 [NC,2L,C];
+ * payload. */
 typedef struct cg_blob_info {
     int32_t nlayers, ntokens, nheads, head_size;
-    int32_t chunk_tokens, nchunks, alphabet, reserved;
+    int32_t chunk_tokens, nchunks, alphabet, table_format;
     uint64_t blob_size;      /* 0 when unknown (cg_blob_layout)           */
     uint64_t header_bytes;
     uint64_t off_scales, off_cdf, off_chunk_off, off_lengths, off_payload;
@@ -106,7 +123,7 @@ enum cg_op {
 /* Message for a status code (static storage). */
 const char *cg_strerror(int code);
 
-/* Library ABI version (1). */
+/* Library ABI version (2: cg_desc carries the table format). */
 int cg_version(void);
 
 /* Default bins ([P2 s1]): with fewer than 10 layers every K and V layer gets
@@ -155,10 +172,11 @@ int cg_quantize(const cg_desc *desc, const void *kv, uint8_t *sym, uint16_t *sca
                 size_t ws_bytes, void *stream);
 
 /* [P2 s3] Histogram of each (kv, layer, channel) over all ntokens tokens and
- * its integer CDF: cdf[k] = round_half_even(cum[k] * (2^16 - A) / T) + k for
- * k = 0..A, so cdf[0] = 0, cdf[A] = 2^16 and every symbol keeps frequency
- * >= 1. sym: device uint8 [2,L,T,C] (every symbol < A); cdf: device int32
- * [2,L,C,A+1]. */
+ * its integer CDF: cdf[k] = round_half_even(cum[k] * (2^16 - W) / T) + k for
+ * k = 0..W, so cdf[0] = 0, cdf[W] = 2^16 and every symbol keeps frequency
+ * >= 1, with W the table's width (A, or the layer's bins for
+ * CG_TABLES_PER_LAYER; entries W+1..A then hold 2^16). sym: device uint8
+ * [2,L,T,C] (every symbol < W); cdf: device int32 [2,L,C,A+1]. */
 int cg_build_cdf(const cg_desc *desc, const uint8_t *sym, int32_t *cdf, void *ws,
                  size_t ws_bytes, void *stream);
 
@@ -167,7 +185,9 @@ int cg_build_cdf(const cg_desc *desc, const uint8_t *sym, int32_t *cdf, void *ws
  * `cap` bytes (cap >= cg_encode_bound() can never overflow; a smaller cap
  * records CG_E_CAPACITY if exceeded); lengths: device uint16 [NC,2L,C]
  * bytes per stream; chunk_off: device uint64 [NC+1], chunk_off[NC] is the
- * payload size. */
+ * payload size. cdf: int32 [2,L,C,A+1] tables of the desc's format (as
+ * cg_build_cdf writes them); a symbol at or past its table's width records
+ * CG_E_CORRUPT. */
 int cg_encode(const cg_desc *desc, const uint8_t *sym, const int32_t *cdf, uint8_t *payload,
               size_t cap, uint16_t *lengths, uint64_t *chunk_off, void *ws, size_t ws_bytes,
               void *stream);

@@ -36,6 +36,9 @@ CG_OP_DEQUANTIZE = 4
 CG_OP_TO_BYTES = 5
 CG_OP_FROM_BYTES = 6
 
+CG_TABLES_SHARED = 0
+CG_TABLES_PER_LAYER = 1
+
 CHUNK_TOKENS = 256
 MAX_LAYERS = 1024
 MAX_STREAM_BYTES = 513
@@ -50,6 +53,8 @@ class CgDescC(ctypes.Structure):
         ("head_size", ctypes.c_int32),
         ("bins_k", ctypes.c_void_p),
         ("bins_v", ctypes.c_void_p),
+        ("table_format", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -62,7 +67,7 @@ class CgBlobInfoC(ctypes.Structure):
         ("chunk_tokens", ctypes.c_int32),
         ("nchunks", ctypes.c_int32),
         ("alphabet", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("table_format", ctypes.c_int32),
         ("blob_size", ctypes.c_uint64),
         ("header_bytes", ctypes.c_uint64),
         ("off_scales", ctypes.c_uint64),
@@ -149,7 +154,8 @@ def _check(rc: int, what: str) -> int:
 class Desc:
     """A cg_desc plus the host bins arrays it points to."""
 
-    def __init__(self, nlayers, ntokens, nheads, head_size, bins_k=None, bins_v=None):
+    def __init__(self, nlayers, ntokens, nheads, head_size, bins_k=None, bins_v=None,
+                 table_format=CG_TABLES_SHARED):
         if bins_k is None or bins_v is None:
             dk, dv = cg_default_bins(nlayers)
             bins_k = dk if bins_k is None else bins_k
@@ -159,15 +165,19 @@ class Desc:
         if self.bins_k.shape != (nlayers,) or self.bins_v.shape != (nlayers,):
             raise ValueError("bins_k and bins_v need one entry per layer")
         self.c = CgDescC(nlayers, ntokens, nheads, head_size,
-                         self.bins_k.ctypes.data, self.bins_v.ctypes.data)
+                         self.bins_k.ctypes.data, self.bins_v.ctypes.data, int(table_format), 0)
         _check(lib().cg_desc_check(self.ptr), "cg_desc_check")
 
     @classmethod
-    def for_kv(cls, shape, bins_k=None, bins_v=None):
+    def for_kv(cls, shape, bins_k=None, bins_v=None, table_format=CG_TABLES_SHARED):
         L, two, T, H, D = shape
         if two != 2:
             raise ValueError("KV must be [nlayers, 2, ntokens, nheads, head_size]")
-        return cls(L, T, H, D, bins_k, bins_v)
+        return cls(L, T, H, D, bins_k, bins_v, table_format)
+
+    @property
+    def table_format(self):
+        return self.c.table_format
 
     @property
     def ptr(self):
@@ -470,10 +480,10 @@ def check_status(ws, stream=None, what="device status"):
     _check(cg_read_status(ws, stream), what)
 
 
-def to_bytes(kv, bins_k=None, bins_v=None, stream=None):
+def to_bytes(kv, bins_k=None, bins_v=None, stream=None, table_format=CG_TABLES_SHARED):
     """Encode bf16 KV [L,2,T,H,D] on the device -> uint8 device tensor (the blob)."""
     torch = _torch()
-    desc = Desc.for_kv(tuple(kv.shape), bins_k, bins_v)
+    desc = Desc.for_kv(tuple(kv.shape), bins_k, bins_v, table_format)
     blob = torch.empty(cg_blob_bound(desc), dtype=torch.uint8, device=kv.device)
     size = torch.zeros(1, dtype=torch.int64, device=kv.device)
     ws = alloc_workspace(desc, CG_OP_TO_BYTES, kv.device)
@@ -498,7 +508,7 @@ def from_bytes(blob, stream=None, out=None):
     info, bk, bv = peek(blob)
     if info["blob_size"] != blob.numel():
         raise CacheGenValueError(CG_E_CORRUPT, "blob size disagrees with its header")
-    desc = Desc(info["nlayers"], info["ntokens"], info["nheads"], info["head_size"], bk, bv)
+    desc = Desc(info["nlayers"], info["ntokens"], info["nheads"], info["head_size"], bk, bv, info["table_format"])
     if out is None:
         out = torch.empty(desc.kv_shape, dtype=torch.bfloat16, device=blob.device)
     ws = alloc_workspace(desc, CG_OP_FROM_BYTES, blob.device)

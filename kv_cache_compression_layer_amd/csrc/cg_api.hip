@@ -3,6 +3,8 @@
 // for the contract of every call.
 #include <string.h>
 
+#include <algorithm>
+
 #include "cg_internal.hpp"
 
 using namespace cg;
@@ -40,6 +42,14 @@ int make_dims(const cg_desc *desc, Dims &d) {
     for (int l = 0; l < d.L; ++l) A = A > desc->bins_k[l] ? A : desc->bins_k[l];
     for (int l = 0; l < d.L; ++l) A = A > desc->bins_v[l] ? A : desc->bins_v[l];
     d.A = A;
+    if (desc->table_format != CG_TABLES_SHARED && desc->table_format != CG_TABLES_PER_LAYER) return CG_E_INVAL;
+    d.fmt = desc->table_format;
+    d.tab_entries = 0;
+    d.wmin = A;
+    for (int l = 0; l < d.L; ++l) {
+        d.tab_entries += d.fmt ? (int64_t)desc->bins_k[l] + desc->bins_v[l] : 2LL * A;
+        if (d.fmt) d.wmin = std::min<int>(d.wmin, std::min(desc->bins_k[l], desc->bins_v[l]));
+    }
     d.NC = (d.T + kChunk - 1) / kChunk;
     d.CB = (d.C + 63) / 64;
     d.N = 2LL * d.L * d.T * d.C;
@@ -51,23 +61,25 @@ int make_dims(const cg_desc *desc, Dims &d) {
     return CG_OK;
 }
 
-void make_max_table(const cg_desc *desc, MaxTable &mt) {
+void make_max_table(const cg_desc *desc, const Dims &d, MaxTable &mt) {
     memset(&mt, 0, sizeof mt);
     for (int l = 0; l < desc->nlayers; ++l) {
-        mt.m[0][l] = (uint8_t)(desc->bins_k[l] / 2 - 1);
-        mt.m[1][l] = (uint8_t)(desc->bins_v[l] / 2 - 1);
+        mt.bins[0][l] = desc->bins_k[l];
+        mt.bins[1][l] = desc->bins_v[l];
     }
+    mt.per_layer = d.fmt == CG_TABLES_PER_LAYER;
+    mt.A = d.A;
 }
 
 // The table of a batch of `batch` calls run as one call of batch * L layers:
 // the constants repeat with period L (written out when they fit the table).
-void make_max_table_batch(const cg_desc *desc, int batch, MaxTable &mt) {
-    make_max_table(desc, mt);
+void make_max_table_batch(const cg_desc *desc, const Dims &d, int batch, MaxTable &mt) {
+    make_max_table(desc, d, mt);
     const int L = desc->nlayers;
     if ((int64_t)batch * L <= CG_MAX_LAYERS) {
         for (int l = L; l < batch * L; ++l) {
-            mt.m[0][l] = mt.m[0][l % L];
-            mt.m[1][l] = mt.m[1][l % L];
+            mt.bins[0][l] = mt.bins[0][l % L];
+            mt.bins[1][l] = mt.bins[1][l % L];
         }
     } else {
         mt.lper = (uint32_t)L;
@@ -84,6 +96,7 @@ int make_dims_batch(const cg_desc *desc, int batch, Dims &d, Dims &vd) {
     if (batch < 1 || (int64_t)batch * d.L > kMaxBatchLayers) return CG_E_SHAPE;
     vd = d;
     vd.L = batch * d.L;
+    vd.tab_entries = (int64_t)batch * d.tab_entries;
     vd.N = 2LL * vd.L * vd.T * vd.C;
     vd.NS = (int64_t)vd.NC * 2 * vd.L * vd.C;
     vd.tiles = (int64_t)vd.NC * 2 * vd.L * vd.CB;
@@ -96,7 +109,7 @@ BlobLayout blob_layout(const Dims &d) {
     b.header_bytes = align_up(kHdrFixed + 2ull * d.L, kAlign);
     b.off_scales = b.header_bytes;
     b.off_cdf = b.off_scales + align_up(4ull * d.L * d.T, kAlign);
-    b.off_chunk_off = b.off_cdf + align_up(4ull * d.L * d.C * d.A, kAlign);
+    b.off_chunk_off = b.off_cdf + align_up(2ull * d.C * (uint64_t)d.tab_entries, kAlign);
     b.off_lengths = b.off_chunk_off + align_up(8ull * (d.NC + 1), kAlign);
     b.off_payload = b.off_lengths + align_up(4ull * d.NC * d.L * d.C, kAlign);
     return b;
@@ -105,7 +118,7 @@ BlobLayout blob_layout(const Dims &d) {
 // Workspace regions (byte offsets; 0 = unused). Region 0 is the WsHeader.
 struct WsLayout {
     uint64_t counts = 0, tile_sum = 0, tile_off = 0, chunk_total = 0, overflow = 0, staging = 0, sym = 0,
-             scan = 0;
+             scan = 0, wpre = 0;
     uint64_t clear_end = kWsAlign;  // bytes from 0 that must start zeroed
     uint64_t total = kWsAlign;
 };
@@ -132,9 +145,13 @@ WsLayout ws_layout(const Dims &d, int op) {
         w.scan = take(tile_scan_tmp_bytes(d));
         break;
     case CG_OP_DECODE:
+        w.tile_off = take(8ull * d.tiles);
+        w.scan = take(tile_scan_tmp_bytes(d));
+        break;
     case CG_OP_FROM_BYTES:
         w.tile_off = take(8ull * d.tiles);
         w.scan = take(tile_scan_tmp_bytes(d));
+        w.wpre = take(4ull * (2 * d.L + 1));
         break;
     case CG_OP_TO_BYTES:
         w.counts = take(4ull * 2 * d.L * d.C * d.A);
@@ -146,6 +163,7 @@ WsLayout ws_layout(const Dims &d, int op) {
         w.staging = take(encode_staging_bytes(d));
         w.sym = take((uint64_t)d.N);
         w.scan = take(tile_scan_tmp_bytes(d));
+        w.wpre = take(4ull * (2 * d.L + 1));
         break;
     default:
         break;
@@ -201,6 +219,7 @@ void make_header(const cg_desc *desc, const Dims &d, const BlobLayout &b, Header
     put_le(hb.b + 24, (uint64_t)kChunk, 4);
     put_le(hb.b + 28, (uint64_t)d.NC, 4);
     put_le(hb.b + 32, (uint64_t)d.A, 4);
+    put_le(hb.b + 36, (uint64_t)d.fmt, 4);
     memcpy(hb.b + kHdrFixed, desc->bins_k, (size_t)d.L);
     memcpy(hb.b + kHdrFixed + d.L, desc->bins_v, (size_t)d.L);
 }
@@ -213,7 +232,7 @@ void fill_info(const Dims &d, const BlobLayout &b, cg_blob_info *out) {
     out->chunk_tokens = kChunk;
     out->nchunks = d.NC;
     out->alphabet = d.A;
-    out->reserved = 0;
+    out->table_format = d.fmt;
     out->blob_size = 0;
     out->header_bytes = b.header_bytes;
     out->off_scales = b.off_scales;
@@ -232,24 +251,27 @@ int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *sca
                 const EncodeOut &o, void *ws, const WsLayout &w, hipStream_t s) {
     uint32_t *status = at<uint32_t>(ws, 0);
     uint32_t *counts = at<uint32_t>(ws, w.counts);
+    uint32_t *wpre = at<uint32_t>(ws, w.wpre);
     uint8_t *sym = at<uint8_t>(ws, w.sym);
     const uint16_t *kv16 = reinterpret_cast<const uint16_t *>(kv);
     const bool qh = quantize_hist_fits(d, kv, sym);
     const bool fused = qh && quantize_hist_fuses_cdf(d, wire);
     int rc = hip_rc(launch_fill_u32(status, 0u, (int64_t)((fused ? kWsAlign : w.clear_end) / 4), s));
     if (rc) return rc;
+    if ((rc = hip_rc(launch_table_prefix(d, mt, wpre, s)))) return rc;
     if (qh) {
-        rc = hip_rc(launch_quantize_hist(d, mt, kv16, sym, scales, counts, fused ? wire : nullptr, status, s));
+        rc = hip_rc(
+            launch_quantize_hist(d, mt, kv16, sym, scales, counts, fused ? wire : nullptr, wpre, status, s));
         if (rc) return rc;
     } else {
         if ((rc = hip_rc(launch_quantize(d, mt, kv16, sym, scales, status, s)))) return rc;
         if ((rc = hip_rc(launch_histogram(d, sym, counts, status, s)))) return rc;
     }
-    if (!fused && (rc = hip_rc(launch_cdf(d, counts, nullptr, wire, status, s)))) return rc;
+    if (!fused && (rc = hip_rc(launch_cdf(d, mt, counts, nullptr, wire, wpre, status, s)))) return rc;
     EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
                 at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging),
                 at<uint64_t>(ws, w.scan)};
-    return hip_rc(launch_encode(d, sym, nullptr, wire, o, ew, true, s));
+    return hip_rc(launch_encode(d, mt, sym, nullptr, wire, wpre, o, ew, true, s));
 }
 
 // Workspace of a batch: the virtual call's workspace, then the virtual blob
@@ -279,7 +301,7 @@ BatchWs batch_ws(const Dims &d, const Dims &vd, int B, uint64_t stride, int op) 
     return bw;
 }
 
-BatchGeom batch_geom(const Dims &d, const Dims &vd, int B, uint64_t stride) {
+BatchGeom batch_geom(const cg_desc *desc, const Dims &d, const Dims &vd, int B, uint64_t stride) {
     BatchGeom g;
     g.d = d;
     g.vd = vd;
@@ -288,6 +310,11 @@ BatchGeom batch_geom(const Dims &d, const Dims &vd, int B, uint64_t stride) {
     g.B = B;
     g.stride = stride;
     g.npieces = 4 + 4 * d.NC;
+    g.wsum[0] = g.wsum[1] = 0;
+    for (int l = 0; l < d.L; ++l) {
+        g.wsum[0] += d.fmt ? desc->bins_k[l] : (uint64_t)d.A;
+        g.wsum[1] += d.fmt ? desc->bins_v[l] : (uint64_t)d.A;
+    }
     return g;
 }
 
@@ -309,7 +336,7 @@ const char *cg_strerror(int code) {
     }
 }
 
-int cg_version(void) { return 1; }
+int cg_version(void) { return 2; }
 
 int cg_default_bins(int32_t nlayers, uint8_t *bins_k, uint8_t *bins_v) {
     if (!bins_k || !bins_v) return CG_E_INVAL;
@@ -375,7 +402,9 @@ int cg_blob_peek(const void *header, size_t n, cg_blob_info *out, uint8_t *bins_
     const uint64_t T = get_le(h + 12, 4), H = get_le(h + 16, 4), D = get_le(h + 20, 4);
     if (T < 1 || T > 0x7FFFFFFF || H < 1 || H > 0x7FFFFFFF || D < 1 || D > 0x7FFFFFFF)
         return CG_E_CORRUPT;
-    cg_desc desc = {(int32_t)L, (int32_t)T, (int32_t)H, (int32_t)D, bins_k, bins_v};
+    const uint64_t fmt = get_le(h + 36, 4);
+    if (fmt != CG_TABLES_SHARED && fmt != CG_TABLES_PER_LAYER) return CG_E_CORRUPT;
+    cg_desc desc = {(int32_t)L, (int32_t)T, (int32_t)H, (int32_t)D, bins_k, bins_v, (int32_t)fmt, 0};
     Dims d;
     if (make_dims(&desc, d) != CG_OK) return CG_E_CORRUPT;
     if (get_le(h + 24, 4) != (uint64_t)kChunk || get_le(h + 28, 4) != (uint64_t)d.NC ||
@@ -409,7 +438,7 @@ int cg_quantize(const cg_desc *desc, const void *kv, uint8_t *sym, uint16_t *sca
     if (!kv || !sym || !scale) return CG_E_INVAL;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
-    make_max_table(desc, mt);
+    make_max_table(desc, d, mt);
     if ((rc = clear_ws(ws, w, s))) return rc;
     return hip_rc(launch_quantize(d, mt, reinterpret_cast<const uint16_t *>(kv), sym, scale,
                                   at<uint32_t>(ws, 0), s));
@@ -427,7 +456,9 @@ int cg_build_cdf(const cg_desc *desc, const uint8_t *sym, int32_t *cdf, void *ws
     uint32_t *status = at<uint32_t>(ws, 0);
     uint32_t *counts = at<uint32_t>(ws, w.counts);
     if ((rc = hip_rc(launch_histogram(d, sym, counts, status, s)))) return rc;
-    return hip_rc(launch_cdf(d, counts, cdf, nullptr, status, s));
+    MaxTable mt;
+    make_max_table(desc, d, mt);
+    return hip_rc(launch_cdf(d, mt, counts, cdf, nullptr, nullptr, status, s));
 }
 
 int cg_encode(const cg_desc *desc, const uint8_t *sym, const int32_t *cdf, uint8_t *payload,
@@ -444,7 +475,9 @@ int cg_encode(const cg_desc *desc, const uint8_t *sym, const int32_t *cdf, uint8
     EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
                 at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging),
                 at<uint64_t>(ws, w.scan)};
-    return hip_rc(launch_encode(d, sym, cdf, nullptr, o, ew, false, s));
+    MaxTable mt;
+    make_max_table(desc, d, mt);
+    return hip_rc(launch_encode(d, mt, sym, cdf, nullptr, nullptr, o, ew, false, s));
 }
 
 int cg_decode(const cg_desc *desc, const uint8_t *payload, size_t payload_bytes,
@@ -457,9 +490,9 @@ int cg_decode(const cg_desc *desc, const uint8_t *payload, size_t payload_bytes,
     if (!lengths || !chunk_off || !cdf || !sym || (!payload && payload_bytes)) return CG_E_INVAL;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
-    make_max_table(desc, mt);
+    make_max_table(desc, d, mt);
     if ((rc = clear_ws(ws, w, s))) return rc;
-    DecodeIn in{payload, (uint64_t)payload_bytes, lengths, chunk_off, cdf, nullptr};
+    DecodeIn in{payload, (uint64_t)payload_bytes, lengths, chunk_off, cdf, nullptr, nullptr};
     DecodeOut out{sym, nullptr, nullptr};
     return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
                                 at<uint32_t>(ws, 0), s));
@@ -478,7 +511,7 @@ int cg_dequantize(const cg_desc *desc, const uint8_t *sym, const uint16_t *scale
         if ((rc = clear_ws(ws, w, s))) return rc;
     }
     MaxTable mt;
-    make_max_table(desc, mt);
+    make_max_table(desc, d, mt);
     return hip_rc(launch_dequantize(d, mt, sym, scale, reinterpret_cast<uint16_t *>(kv_out), s));
 }
 
@@ -494,7 +527,7 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
     if ((uint64_t)cap < b.off_payload) return CG_E_CAPACITY;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
-    make_max_table(desc, mt);
+    make_max_table(desc, d, mt);
 
     HeaderBytes hb;
     make_header(desc, d, b, hb);
@@ -522,14 +555,15 @@ int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, vo
     if ((uint64_t)blob_size < b.off_payload) return CG_E_CORRUPT;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
-    make_max_table(desc, mt);
+    make_max_table(desc, d, mt);
     if ((rc = clear_ws(ws, w, s))) return rc;
     DecodeIn in{blob + b.off_payload,
                 (uint64_t)blob_size - b.off_payload,
                 reinterpret_cast<const uint16_t *>(blob + b.off_lengths),
                 reinterpret_cast<const uint64_t *>(blob + b.off_chunk_off),
                 nullptr,
-                reinterpret_cast<const uint16_t *>(blob + b.off_cdf)};
+                reinterpret_cast<const uint16_t *>(blob + b.off_cdf),
+                at<uint32_t>(ws, w.wpre)};
     DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
                   reinterpret_cast<const uint16_t *>(blob + b.off_scales)};
     return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
@@ -549,7 +583,7 @@ int cg_from_bytes_chunks(const cg_desc *desc, const uint8_t *blob, size_t blob_s
     if ((uint64_t)blob_size < b.off_payload) return CG_E_CORRUPT;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
-    make_max_table(desc, mt);
+    make_max_table(desc, d, mt);
     if ((rc = clear_ws(ws, w, s))) return rc;
     DecodeIn in{blob + b.off_payload,
                 (uint64_t)blob_size - b.off_payload,
@@ -557,6 +591,7 @@ int cg_from_bytes_chunks(const cg_desc *desc, const uint8_t *blob, size_t blob_s
                 reinterpret_cast<const uint64_t *>(blob + b.off_chunk_off),
                 nullptr,
                 reinterpret_cast<const uint16_t *>(blob + b.off_cdf),
+                at<uint32_t>(ws, w.wpre),
                 chunk_begin,
                 chunk_end};
     DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
@@ -587,7 +622,7 @@ int cg_to_bytes_batch(const cg_desc *desc, int32_t batch, const void *kv, uint8_
     const WsLayout &w = bw.w;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
-    make_max_table_batch(desc, batch, mt);
+    make_max_table_batch(desc, d, batch, mt);
     HeaderBytes hb;
     make_header(desc, d, lay, hb);
 
@@ -604,7 +639,7 @@ int cg_to_bytes_batch(const cg_desc *desc, int32_t batch, const void *kv, uint8_
     if ((rc = encode_call(vd, mt, kv, at<uint16_t>(vblob, vlay.off_scales), at<uint16_t>(vblob, vlay.off_cdf), o,
                           ws, w, s)))
         return rc;
-    const BatchGeom g = batch_geom(d, vd, batch, blob_stride);
+    const BatchGeom g = batch_geom(desc, d, vd, batch, blob_stride);
     Piece *pieces = at<Piece>(ws, bw.pieces);
     if ((rc = hip_rc(launch_split_plan(g, vblob, at<uint64_t>(ws, w.tile_off), blobs, blob_sizes_dev, pieces, status,
                                        s))))
@@ -626,13 +661,13 @@ int cg_from_bytes_batch(const cg_desc *desc, int32_t batch, const uint8_t *blobs
     const WsLayout &w = bw.w;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
-    make_max_table_batch(desc, batch, mt);
+    make_max_table_batch(desc, d, batch, mt);
     HeaderBytes hb;
     make_header(desc, d, lay, hb);
     uint32_t *status = at<uint32_t>(ws, 0);
     uint8_t *vblob = at<uint8_t>(ws, bw.vblob);
     if ((rc = clear_ws(ws, w, s))) return rc;
-    const BatchGeom g = batch_geom(d, vd, batch, blob_stride);
+    const BatchGeom g = batch_geom(desc, d, vd, batch, blob_stride);
     Piece *pieces = at<Piece>(ws, bw.pieces);
     if ((rc = hip_rc(launch_merge_plan(g, blobs, blob_sizes_dev, hb, vblob, at<uint64_t>(ws, bw.piece_len), pieces,
                                        status, s))))
@@ -643,7 +678,8 @@ int cg_from_bytes_batch(const cg_desc *desc, int32_t batch, const uint8_t *blobs
                 reinterpret_cast<const uint16_t *>(vblob + vlay.off_lengths),
                 reinterpret_cast<const uint64_t *>(vblob + vlay.off_chunk_off),
                 nullptr,
-                reinterpret_cast<const uint16_t *>(vblob + vlay.off_cdf)};
+                reinterpret_cast<const uint16_t *>(vblob + vlay.off_cdf),
+                at<uint32_t>(ws, w.wpre)};
     DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
                   reinterpret_cast<const uint16_t *>(vblob + vlay.off_scales)};
     return hip_rc(
@@ -669,14 +705,15 @@ int cg_from_bytes_paged(const cg_desc *desc, const uint8_t *blob, size_t blob_si
     if ((uint64_t)blob_size < b.off_payload) return CG_E_CORRUPT;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
-    make_max_table(desc, mt);
+    make_max_table(desc, d, mt);
     if ((rc = clear_ws(ws, w, s))) return rc;
     DecodeIn in{blob + b.off_payload,
                 (uint64_t)blob_size - b.off_payload,
                 reinterpret_cast<const uint16_t *>(blob + b.off_lengths),
                 reinterpret_cast<const uint64_t *>(blob + b.off_chunk_off),
                 nullptr,
-                reinterpret_cast<const uint16_t *>(blob + b.off_cdf)};
+                reinterpret_cast<const uint16_t *>(blob + b.off_cdf),
+                at<uint32_t>(ws, w.wpre)};
     int log2_bs = 0;
     while ((1 << log2_bs) < block_size) ++log2_bs;
     DecodeOut out{nullptr, nullptr, reinterpret_cast<const uint16_t *>(blob + b.off_scales),

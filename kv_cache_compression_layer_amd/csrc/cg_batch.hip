@@ -10,7 +10,7 @@
 // piece is contiguous in both layouts:
 //
 //   piece 0, 1          scales of K, V          L*T bf16
-//   piece 2, 3          CDF tables of K, V      L*C*A u16
+//   piece 2, 3          CDF tables of K, V      C * (sum of the K (V) table widths) u16
 //   piece 4 + 2j + kv   lengths of (chunk j, K|V)   L*C u16
 //   piece 4+2NC+2j+kv   payload of (chunk j, K|V)   the streams' bytes
 //
@@ -35,10 +35,13 @@ __device__ void fixed_piece(const BatchGeom &g, int b, int p, uint64_t &v, uint6
         c = g.lay.off_scales + (uint64_t)((int64_t)kv * d.L * d.T) * 2;
         len = (uint64_t)d.L * d.T * 2;
     } else if (p < 4) {
+        // The tables of call b's K (V) layers: in the virtual call they
+        // follow the K tables of every call (for V) and those of calls < b.
         const int kv = p - 2;
-        v = g.vlay.off_cdf + (uint64_t)((kv * Lv + (int64_t)b * d.L) * d.C) * d.A * 2;
-        c = g.lay.off_cdf + (uint64_t)((int64_t)kv * d.L * d.C) * d.A * 2;
-        len = (uint64_t)d.L * d.C * d.A * 2;
+        const uint64_t before = (kv ? (uint64_t)g.B * g.wsum[0] : 0) + (uint64_t)b * g.wsum[kv];
+        v = g.vlay.off_cdf + before * d.C * 2;
+        c = g.lay.off_cdf + (kv ? g.wsum[0] : 0) * d.C * 2;
+        len = g.wsum[kv] * d.C * 2;
     } else {
         const int q = p - 4, j = q >> 1, kv = q & 1;
         v = g.vlay.off_lengths + (uint64_t)(((int64_t)j * 2 * Lv + kv * Lv + (int64_t)b * d.L) * d.C) * 2;

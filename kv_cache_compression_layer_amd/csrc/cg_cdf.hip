@@ -159,29 +159,40 @@ hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts,
     return hipGetLastError();
 }
 
-// cdf[k] = round_half_even(cum[k] * (2^16 - A) / T) + k, cum[k] the count of
-// symbols below k. G lanes per table (G = the power of two >= A, at most 64;
-// 64 / G tables per wave): lane k reads count k (coalesced), the segmented
-// scan of G lanes gives cum, and lane k writes entry k of the table (the
-// last lane of a table also writes entry A). An alphabet above 64 takes two
-// rounds of 64, the second starting from the first one's total.
+// cdf[k] = round_half_even(cum[k] * (2^16 - W) / T) + k, cum[k] the count of
+// symbols below k, k = 0..W, W the table's width (the call's alphabet A, or
+// the layer's bins for per-layer tables). G lanes per table (G = the power
+// of two >= A, at most 64; 64 / G tables per wave): lane k reads count k
+// (coalesced), the segmented scan of G lanes gives cum, and lane k writes
+// entry k of the table (the first lane of a table also writes entry W). An
+// alphabet above 64 takes two rounds of 64, the second starting from the
+// first one's total. int32 tables are [2,L,C,A+1] with 2^16 past entry W; u16
+// wire tables hold entries 0..W-1 at wpre[slab] * C + c * W.
 template <int G>
 __global__ __launch_bounds__(256) void k_cdf(const uint32_t *__restrict__ counts,
                                              int32_t *__restrict__ cdf,
                                              uint16_t *__restrict__ wire,
+                                             const uint32_t *__restrict__ wpre,
                                              uint32_t *__restrict__ status, int64_t ntab, int A,
-                                             int T) {
+                                             int T, int L, int C, MaxTable mt) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t tab = wave * (64 / G) + lane / G;
     const int k0 = lane & (G - 1);
     const bool live = tab < ntab;
-    const uint64_t S = kProbOne - (uint32_t)A;
+    const int slab = live ? (int)(tab / C) : 0;
+    const int c = (int)(tab - (int64_t)slab * C);
+    const int kv = slab >= L ? 1 : 0;
+    const int W = layer_w(mt, kv, slab - kv * L);
+    const uint64_t S = kProbOne - (uint32_t)W;
     const double invT = 1.0 / (double)T;
+    uint16_t *wt = wire && live ? wire + (int64_t)wpre[slab] * C + (int64_t)c * W : nullptr;
     uint64_t base = 0;
+    bool bad = false;
     for (int kb = 0; kb < A; kb += G) {
         const int k = kb + k0;
         const uint32_t h = live && k < A ? counts[tab * A + k] : 0u;
+        bad |= k >= W && h != 0;
         uint32_t incl = h;
 #pragma unroll
         for (int o = 1; o < G; o <<= 1) {
@@ -189,29 +200,67 @@ __global__ __launch_bounds__(256) void k_cdf(const uint32_t *__restrict__ counts
             if (k0 >= o) incl += t;
         }
         if (live && k < A) {
-            const uint32_t v = (uint32_t)(div_rne((base + incl - h) * S, (uint32_t)T, invT) + (uint64_t)k);
+            const uint32_t v = k < W ? (uint32_t)(div_rne((base + incl - h) * S, (uint32_t)T, invT) + (uint64_t)k)
+                                     : kProbOne;
             if (cdf) cdf[tab * (A + 1) + k] = (int32_t)v;
-            if (wire) wire[tab * A + k] = (uint16_t)v;
+            if (wt && k < W) wt[k] = (uint16_t)v;
         }
         base += (uint32_t)__shfl((int)incl, G - 1, G);
     }
     if (live && k0 == 0) {
-        if (cdf) cdf[tab * (A + 1) + A] = (int32_t)(div_rne(base * S, (uint32_t)T, invT) + (uint64_t)A);
-        if (base != (uint64_t)T) atomicOr(status, kStCorrupt);
+        // Entry W is 2^16 exactly when the counts add up to T.
+        if (cdf) cdf[tab * (A + 1) + A] = W == A ? (int32_t)(div_rne(base * S, (uint32_t)T, invT) + (uint64_t)A)
+                                                 : (int32_t)kProbOne;
+        bad |= base != (uint64_t)T;
     }
+    if (__ballot(live && bad) && lane == 0) atomicOr(status, kStCorrupt);
 }
 
-hipError_t launch_cdf(const Dims &d, const uint32_t *counts, int32_t *cdf, uint16_t *cdf_wire,
-                      uint32_t *status, hipStream_t s) {
+hipError_t launch_cdf(const Dims &d, const MaxTable &mt, const uint32_t *counts, int32_t *cdf,
+                      uint16_t *cdf_wire, const uint32_t *wpre, uint32_t *status, hipStream_t s) {
     const int64_t ntab = 2LL * d.L * d.C;
 #define CG_CDF(GG)                                                                                      \
     hipLaunchKernelGGL(k_cdf<GG>, dim3((unsigned)((ntab + 4 * (64 / GG) - 1) / (4 * (64 / GG)))), dim3(256), \
-                       0, s, counts, cdf, cdf_wire, status, ntab, d.A, d.T)
+                       0, s, counts, cdf, cdf_wire, wpre, status, ntab, d.A, d.T, d.L, d.C, mt)
     if (d.A <= 8) CG_CDF(8);
     else if (d.A <= 16) CG_CDF(16);
     else if (d.A <= 32) CG_CDF(32);
     else CG_CDF(64);
 #undef CG_CDF
+    return hipGetLastError();
+}
+
+// wpre[s] = the sum of the table widths of the (K|V, layer) slabs before s,
+// s = 0..2L (so wpre[2L] is the whole section's entries per channel).
+__global__ __launch_bounds__(1024) void k_table_prefix(MaxTable mt, int L, uint32_t *__restrict__ wpre) {
+    __shared__ uint32_t wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = 2 * L;
+    uint32_t run = 0;
+    for (int seg = 0; seg < n; seg += 1024) {
+        const int i = seg + tid;
+        uint32_t v = 0;
+        if (i < n) {
+            const int kv = i >= L ? 1 : 0;
+            v = (uint32_t)layer_w(mt, kv, i - kv * L);
+        }
+        const uint32_t incl = wave_incl_scan_u32(v, lane);
+        if (lane == 63) wsum[wv] = incl;
+        __syncthreads();
+        uint32_t before = 0, total = 0;
+        for (int k = 0; k < 16; ++k) {
+            if (k < wv) before += wsum[k];
+            total += wsum[k];
+        }
+        if (i < n) wpre[i] = run + before + incl - v;
+        run += total;
+        __syncthreads();
+    }
+    if (tid == 0) wpre[n] = run;
+}
+
+hipError_t launch_table_prefix(const Dims &d, const MaxTable &mt, uint32_t *wpre, hipStream_t s) {
+    hipLaunchKernelGGL(k_table_prefix, dim3(1), dim3(1024), 0, s, mt, d.L, wpre);
     return hipGetLastError();
 }
 

@@ -37,6 +37,7 @@ struct DecArgs {
     const uint64_t *tile_off;
     const int32_t *cdf32;
     const uint16_t *cdf16;
+    const uint32_t *wpre;
     uint8_t *sym;
     uint16_t *kv;
     const uint16_t *scale;
@@ -70,9 +71,9 @@ struct DecStream {
 
 // The per-token loop of k_decode.
 //
-// The table holds 2^LOGA entries per lane; entries past the alphabet have
-// start 0xFFFF, so the search can only land on them when the symbol is the
-// last one, and one clamp at the end maps them back (CLAMP).
+// The table holds 2^LOGA entries per lane; entries past the table's width W
+// have start 0xFFFF, so the search can only land on them when the symbol is
+// the last one, W - 1, and one clamp at the end maps them back (CLAMP).
 //
 // Latency: the first two levels of the binary search compare against CDF
 // values held in registers (the same candidates every token); the two bytes
@@ -94,7 +95,7 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
                                             const uint32_t *tab,
                                             const float *dq, uint32_t (&sc_v)[S][4], const uint8_t *pool,
                                             __amdgpu_buffer_rsrc_t out_rsrc, uint32_t out_voff,
-                                            int lane, uint64_t &bad_mask) {
+                                            int lane, int W, uint64_t &bad_mask) {
     auto fetch = [&](int s) -> uint32_t {
         DecStream &d = st[s];
         if (STAGED) return pool[d.ptr++];
@@ -115,7 +116,7 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
     // Byte address in tab of (symbol s, this lane) is s * 256 + lane * 4.
     const uint8_t *tabb = reinterpret_cast<const uint8_t *>(tab);
     const uint32_t lane4 = (uint32_t)lane * 4;
-    const uint32_t amax4 = ((uint32_t)a.A - 1) * 256 + lane4;
+    const uint32_t amax4 = ((uint32_t)W - 1) * 256 + lane4;
     // Search depth: the whole table, or (HALF) its lower half when the layer's
     // symbols all lie below the half's top entry; landing on that top entry
     // then means a symbol at or above it (only in corrupt streams), and a
@@ -285,7 +286,8 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     const int kv = slab / a.L, l = slab - kv * a.L;
     const int c = cb * 64 + lane;
     const bool active = c < a.C;
-    const int M = a.mt.m[kv][local_layer(a.mt, l)];
+    const int M = layer_m(a.mt, kv, l);
+    const int W = layer_w(a.mt, kv, l);  // symbols of this slab's tables
 
     // This wave's streams: lengths, offsets and the pool bytes they need
     // (alignment head + bytes + four zero bytes after each of the 64 streams).
@@ -360,27 +362,21 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     }
 
     // Tables, built by the block's waves together: wave w writes symbols w,
-    // w + NW, ...; entries past the alphabet (up to 2^LOGA) have start 0xFFFF.
+    // w + NW, ...; entries past the table's width W (up to 2^LOGA) have start
+    // 0xFFFF.
     bool bad_table = false;
     for (int s = wv; s < (1 << LOGA); s += NW) {
         uint32_t entry = 0xFFFFu;
-        if (s < A && active) {
-            const int64_t row = (int64_t)slab * a.C + c;
+        if (s < W && active) {
             uint32_t lo, hi;
-            if (a.cdf32) {
-                lo = (uint32_t)a.cdf32[row * (A + 1) + s];
-                hi = (uint32_t)a.cdf32[row * (A + 1) + s + 1];
-            } else {
-                lo = (uint32_t)a.cdf16[row * A + s];
-                hi = s + 1 < A ? (uint32_t)a.cdf16[row * A + s + 1] : kProbOne;
-            }
+            cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, c, A, W, s, lo, hi);
             uint32_t f = hi - lo;
-            if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == A - 1 && hi != kProbOne)) {
+            if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)) {
                 bad_table = true;
                 f = 1;
             }
             entry = (lo & 0xFFFFu) | (f << 16);
-        } else if (s < A) {
+        } else if (s < W) {
             // Idle lanes: code stays 0, so they always decode symbol 0, whose
             // frequency 65535 never forces a renormalisation.
             entry = s == 0 ? 0xFFFFu << 16 : (uint32_t)s | (1u << 16);
@@ -452,17 +448,17 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     if (half) {
         if (staged)
             decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                               out_voff, lane, bad_mask);
+                                                               out_voff, lane, W, bad_mask);
         else
             decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                                out_voff, lane, bad_mask);
+                                                                out_voff, lane, W, bad_mask);
     } else {
         if (staged)
             decode_loop<S, FUSED, LOGA, CLAMP, true, false, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                            out_voff, lane, bad_mask);
+                                                            out_voff, lane, W, bad_mask);
         else
             decode_loop<S, FUSED, LOGA, CLAMP, false, false, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                             out_voff, lane, bad_mask);
+                                                             out_voff, lane, W, bad_mask);
     }
     if ((__ballot(active && (corrupt || bad_table)) | (bad_mask & __ballot(active))) && lane == 0)
         atomicOr(a.status, kStCorrupt);
@@ -472,7 +468,7 @@ template <int S, bool FUSED, int LOGA, int NW, bool PAGED>
 static hipError_t launch_decode_s(const Dims &d, const DecArgs &a, hipStream_t s) {
     const int ngroups = (a.NCr + S * NW - 1) / (S * NW);
     const dim3 grid((unsigned)((int64_t)ngroups * 2 * d.L * d.CB));
-    if (d.A == (1 << LOGA))
+    if (d.A == (1 << LOGA) && d.wmin == d.A)  // every table fills the 2^LOGA entries: no clamp
         hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, false, NW, PAGED>), grid, dim3(64 * NW), 0, s, a);
     else
         hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, true, NW, PAGED>), grid, dim3(64 * NW), 0, s, a);
@@ -492,6 +488,10 @@ static hipError_t launch_decode_f(const Dims &d, const DecArgs &a, hipStream_t s
 hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, const DecodeOut &out,
                          uint64_t *tile_off, uint64_t *scan_tmp, uint32_t *status, hipStream_t s) {
     const int j0 = in.j0, j1 = in.j1 < 0 ? d.NC : in.j1;
+    if (in.cdf16) {
+        hipError_t e0 = launch_table_prefix(d, mt, in.wpre, s);
+        if (e0 != hipSuccess) return e0;
+    }
     TileScan ts{nullptr, in.lengths, tile_off, scan_tmp, nullptr, in.chunk_off, in.payload_bytes, status,
                 d.L, d.C, d.CB, d.NC, j0, j1 - j0};
     hipError_t e = launch_tile_scan(ts, s);
@@ -503,6 +503,7 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     a.tile_off = tile_off;
     a.cdf32 = in.cdf32;
     a.cdf16 = in.cdf16;
+    a.wpre = in.wpre;
     a.sym = out.sym;
     a.kv = out.kv;
     a.scale = out.scale;

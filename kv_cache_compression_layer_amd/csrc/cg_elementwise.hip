@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict
     uint32_t am = max(am2 & 0xFFFFu, am2 >> 16);
     am = wave_max_dpp(am);
     if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
-    const int M = mt.m[k][local_layer(mt, l)];
+    const int M = layer_m(mt, k, l);
     const float Mf = (float)M;
     // m == 0 gives f == 0, so every symbol is exactly M.
     const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void k_quantize_any(const uint16_t *__restrict
     for (int c = lane; c < C; c += 64) am = max(am, (uint32_t)src[c] & 0x7FFFu);
     am = wave_max_u32(am);
     if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
-    const int M = mt.m[k][local_layer(mt, l)];
+    const int M = layer_m(mt, k, l);
     const float Mf = (float)M;
     const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
     for (int c = lane; c < C; c += 64) dst[c] = (uint8_t)quant1(src[c], f, Mf);
@@ -198,6 +198,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
                                                        uint16_t *__restrict__ scale,
                                                        uint32_t *__restrict__ counts,
                                                        uint16_t *__restrict__ wire,
+                                                       const uint32_t *__restrict__ wpre,
                                                        uint32_t *__restrict__ status, int L, int T,
                                                        int C, int A, int TT, MaxTable mt) {
     constexpr int NS = 1 << LOGA;
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
     for (int i = threadIdx.x; i < NS * NP * 64 / 4; i += 512) h4[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
-    const int M = mt.m[k][local_layer(mt, l)];
+    const int M = layer_m(mt, k, l);
     const float Mf = (float)M;
     uint8_t *hb = reinterpret_cast<uint8_t *>(hist);
     const uint32_t lane4 = (uint32_t)lane * 4;
@@ -275,22 +276,23 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
     if (wire) {
         // The block saw every token of the slab: build its CDF tables here.
         // Thread col < NP * 64 owns the counter column (pair, lane), i.e.
-        // channels c and c + 1; it scans its A counts of each channel into
-        // the tables, then writes them back over the counters as u16 [c][s]
-        // (C * A * 2 bytes, which fit there since A <= NS) for a coalesced
-        // copy to the slab's wire tables.
+        // channels c and c + 1; it scans the W counts of each channel into
+        // the tables (W = the slab's table width), then writes them back over
+        // the counters as u16 [c][s] (C * W * 2 bytes, which fit there since
+        // W <= NS) for a coalesced copy to the slab's wire tables.
         constexpr int NCOL = NP * 64;
         const int col = threadIdx.x;
+        const int W = layer_w(mt, k, l);
         uint32_t tabv[NS];
         bool bad = false;
         if (col < NCOL) {
-            const uint64_t S = kProbOne - (uint32_t)A;
+            const uint64_t S = kProbOne - (uint32_t)W;
             const double invT = 1.0 / (double)T;
             uint32_t cum_lo = 0, cum_hi = 0;
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
                 const uint32_t v = hist[q * NCOL + col];
-                if (q < A) {
+                if (q < W) {
                     const uint32_t a0 = (uint32_t)(div_rne((uint64_t)cum_lo * S, (uint32_t)T, invT) + q);
                     const uint32_t a1 = (uint32_t)(div_rne((uint64_t)cum_hi * S, (uint32_t)T, invT) + q);
                     tabv[q] = (a0 & 0xFFFFu) | (a1 << 16);
@@ -309,17 +311,19 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
             const int c = ((pr / 4) * 64 + ln) * 8 + (pr % 4) * 2;
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
-                if (q < A) {
-                    wl[c * A + q] = (uint16_t)tabv[q];
-                    wl[(c + 1) * A + q] = (uint16_t)(tabv[q] >> 16);
+                if (q < W) {
+                    wl[c * W + q] = (uint16_t)tabv[q];
+                    wl[(c + 1) * W + q] = (uint16_t)(tabv[q] >> 16);
                 }
             }
         }
         if (__ballot(bad) && lane == 0) atomicOr(status, kStCorrupt);
         __syncthreads();
+        // C is 512 or 1024, so the slab's C * W entries and its offset
+        // wpre[slab] * C are whole 16-byte units.
         const uint4 *src4 = reinterpret_cast<const uint4 *>(hist);
-        uint4 *dst4 = reinterpret_cast<uint4 *>(wire + (int64_t)slab * C * A);
-        for (int i = threadIdx.x; i < C * A / 8; i += 512) dst4[i] = src4[i];
+        uint4 *dst4 = reinterpret_cast<uint4 *>(wire + (int64_t)wpre[slab] * C);
+        for (int i = threadIdx.x; i < C * W / 8; i += 512) dst4[i] = src4[i];
         return;
     }
 
@@ -358,8 +362,8 @@ bool quantize_hist_fuses_cdf(const Dims &d, const void *wire) {
 }
 
 hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
-                                uint16_t *scale, uint32_t *counts, uint16_t *wire, uint32_t *status,
-                                hipStream_t s) {
+                                uint16_t *scale, uint32_t *counts, uint16_t *wire, const uint32_t *wpre,
+                                uint32_t *status, hipStream_t s) {
     const int64_t TT = quantize_hist_rows(d);
     if (wire && !quantize_hist_fuses_cdf(d, wire)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((d.T + TT - 1) / TT), (unsigned)(2 * d.L)), block(512);
@@ -367,8 +371,8 @@ hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_
     while ((1 << loga) < d.A) ++loga;
     const int tt = (int)TT;
 #define CG_QH(NV, LG)                                                                                     \
-    hipLaunchKernelGGL((k_quantize_hist<NV, LG>), grid, block, 0, s, kv, sym, scale, counts, wire, status, d.L, \
-                       d.T, d.C, d.A, tt, mt)
+    hipLaunchKernelGGL((k_quantize_hist<NV, LG>), grid, block, 0, s, kv, sym, scale, counts, wire, wpre, status, \
+                       d.L, d.T, d.C, d.A, tt, mt)
     if (d.C == 512) {
         switch (loga) {
         case 2: CG_QH(1, 2); break;
@@ -408,7 +412,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
     const int slab = blockIdx.y, k = slab >= L ? 1 : 0, l = slab - k * L;  // grid: (tokens/4, 2L)
     const int64_t row = (int64_t)slab * T + t;
     float *dq = dq_all[wv];
-    build_dq(dq, mt.m[k][local_layer(mt, l)], lane);
+    build_dq(dq, layer_m(mt, k, l), lane);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     const float m = bf16_to_f32(scale[row]);

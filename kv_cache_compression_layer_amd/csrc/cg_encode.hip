@@ -120,13 +120,15 @@ struct GlobalSink {
 struct EncArgs {
     const uint8_t *sym;
     const int32_t *cdf;        // int32 tables, or
-    const uint16_t *cdf16;     // u16 wire tables
+    const uint16_t *cdf16;     // u16 wire tables, placed by wpre
+    const uint32_t *wpre;
     uint8_t *staging;          // [tiles][kStageBytes][64] bytes
     uint32_t *tile_sum;        // [tiles]
     uint16_t *lengths;         // [NC, 2L, C]
     WsHeader *hdr;
     uint32_t *overflow_list;   // [tiles]
     int L, T, C, A, NC, CB;
+    MaxTable mt;               // table width of each (K|V, layer)
 };
 
 // Tile = (chunk j, slab = kv*L + l, 64-channel block cb); tile index in
@@ -244,8 +246,8 @@ constexpr int kLdsRows = 44;  // LDS stage rows per stream (most streams fit)
 // S chunks (group * NW + w) * S + s, lane = channel, with the table the
 // waves share.
 // TRUSTED: the symbols come from this library's quantiser, so every symbol
-// is below A and neither the clamp of the table index nor the range check
-// is needed.
+// is at most 2M < bins <= W (the table width) and neither the clamp of the
+// table index nor the range check is needed.
 template <int S, int LOGA, int NW, bool TRUSTED>
 __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     constexpr int R = kLdsRows;
@@ -298,15 +300,16 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     }
 
     // Tables, built by the block's waves together: one per lane, packed
-    // start | freq << 16, [symbol][lane].
+    // start | freq << 16, [symbol][lane]; W symbols (the slab's table width).
+    const int W = layer_w(a.mt, slab >= a.L ? 1 : 0, slab >= a.L ? slab - a.L : slab);
     bool bad = false;
-    for (int s = wv; s < A; s += NW) {
+    for (int s = wv; s < W; s += NW) {
         uint32_t entry;
         if (active) {
             uint32_t lo, hi;
-            cdf_bounds(a.cdf, a.cdf16, (int64_t)slab * a.C + c, A, s, lo, hi);
+            cdf_bounds(a.cdf, a.cdf16, a.wpre, slab, a.C, c, A, W, s, lo, hi);
             uint32_t f = hi - lo;
-            if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == A - 1 && hi != kProbOne)) {
+            if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)) {
                 bad = true;
                 f = 1;
             }
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     Coder<R> cd[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) cd[s].init((uint32_t)((wv * S + s) * (R + 2) * kRowPitch + lane));
-    const uint32_t amax = (uint32_t)A - 1;
+    const uint32_t amax = (uint32_t)W - 1;
     uint32_t qmax = 0;
     // Table entry of the next token of every stream, read one step ahead.
     uint32_t e_next[S];
@@ -541,6 +544,7 @@ struct FixupArgs {
     const uint8_t *sym;
     const int32_t *cdf;
     const uint16_t *cdf16;
+    const uint32_t *wpre;
     const uint16_t *lengths;
     const uint64_t *tile_off;   // relative to the chunk
     const uint64_t *chunk_off;
@@ -549,6 +553,7 @@ struct FixupArgs {
     uint8_t *payload;
     uint64_t cap;
     int L, T, C, A, CB;
+    MaxTable mt;
 };
 
 __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
@@ -566,15 +571,15 @@ __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
         const uint32_t len = active ? a.lengths[js * a.C + c] : 0u;
         const uint32_t incl = wave_incl_scan_u32(len, lane);
         if (!active) continue;
-        const int64_t tab = (int64_t)slab * a.C + c;
+        const int W = layer_w(a.mt, slab >= a.L ? 1 : 0, slab >= a.L ? slab - a.L : slab);
         const uint8_t *sp = a.sym + ((int64_t)slab * a.T + (int64_t)j * kChunk) * a.C + c;
         RcEncHold enc;
         enc.init();
         GlobalSink sink{a.payload, a.chunk_off[j] + a.tile_off[tile] + incl - len, a.cap, 0u, false};
         for (int t = 0; t < n; ++t) {
-            const uint32_t s = min((uint32_t)sp[(int64_t)t * a.C], (uint32_t)a.A - 1);
+            const uint32_t s = min((uint32_t)sp[(int64_t)t * a.C], (uint32_t)W - 1);
             uint32_t lo, hi;
-            cdf_bounds(a.cdf, a.cdf16, tab, a.A, (int)s, lo, hi);
+            cdf_bounds(a.cdf, a.cdf16, a.wpre, slab, a.C, c, a.A, W, (int)s, lo, hi);
             const uint32_t f = hi > lo ? hi - lo : 1u;
             enc.encode(lo & 0xFFFFu, f, sink);
         }
@@ -587,13 +592,16 @@ __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
 
 size_t encode_staging_bytes(const Dims &d) { return (size_t)d.tiles * kStageBytes * 64; }
 
-hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, const uint16_t *cdf16,
-                         const EncodeOut &o, const EncodeWs &w, bool trusted, hipStream_t s) {
+hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, const int32_t *cdf,
+                         const uint16_t *cdf16, const uint32_t *wpre, const EncodeOut &o, const EncodeWs &w,
+                         bool trusted, hipStream_t s) {
     const int S = d.NC >= 2 ? 2 : 1;
     EncArgs a;
     a.sym = sym;
     a.cdf = cdf;
     a.cdf16 = cdf16;
+    a.wpre = wpre;
+    a.mt = mt;
     a.staging = w.staging;
     a.tile_sum = w.tile_sum;
     a.lengths = o.lengths;
@@ -667,6 +675,8 @@ hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf, 
     fa.sym = sym;
     fa.cdf = cdf;
     fa.cdf16 = cdf16;
+    fa.wpre = wpre;
+    fa.mt = mt;
     fa.lengths = o.lengths;
     fa.tile_off = w.tile_off;
     fa.chunk_off = o.chunk_off;

@@ -22,15 +22,19 @@ constexpr uint32_t kStNonfinite = 1u;
 constexpr uint32_t kStCorrupt = 2u;
 constexpr uint32_t kStCapacity = 4u;
 
-// Per-(K|V, layer) quantisation constant M = bins//2 - 1, passed by value to
-// every kernel that needs it (2 KiB of kernel arguments).
+// Per-(K|V, layer) bins, passed by value to every kernel that needs them
+// (2 KiB of kernel arguments): the quantisation constant M = bins//2 - 1 and
+// the table width W (the call's alphabet A, or with per-layer tables the
+// layer's bins) follow from them.
 struct MaxTable {
-    uint8_t m[2][CG_MAX_LAYERS];
+    uint8_t bins[2][CG_MAX_LAYERS];
     // Batched calls run as one call of batch * L layers: layer l then takes
-    // the constant of layer l mod lper (lper = 0: no period). lmagic =
+    // the bins of layer l mod lper (lper = 0: no period). lmagic =
     // ceil(2^32 / lper) turns the modulo into a multiply-high, exact for
     // l < 2^16 and lper <= 1024.
     uint32_t lper, lmagic;
+    int32_t per_layer;  // table format: 0 = width A for all tables, 1 = width = the layer's bins
+    int32_t A;
 };
 
 __device__ __forceinline__ int local_layer(const MaxTable &mt, int l) {
@@ -38,10 +42,20 @@ __device__ __forceinline__ int local_layer(const MaxTable &mt, int l) {
     if (mt.lper == 1) return 0;
     return l - (int)mt.lper * (int)__umulhi((uint32_t)l, mt.lmagic);
 }
+__device__ __forceinline__ int layer_bins(const MaxTable &mt, int kv, int l) {
+    return mt.bins[kv][local_layer(mt, l)];
+}
+__device__ __forceinline__ int layer_m(const MaxTable &mt, int kv, int l) { return (layer_bins(mt, kv, l) >> 1) - 1; }
+__device__ __forceinline__ int layer_w(const MaxTable &mt, int kv, int l) {
+    return mt.per_layer ? layer_bins(mt, kv, l) : mt.A;
+}
 
 // Derived sizes of one call.
 struct Dims {
     int L, T, H, D, C, A, NC;
+    int fmt;         // table format (CG_TABLES_*)
+    int wmin;        // narrowest table width of the call
+    int64_t tab_entries;  // sum of the table widths over the 2L (K|V, layer) slabs
     int CB;          // 64-channel blocks per (kv, layer): ceil(C / 64)
     int64_t N;       // 2*L*T*C symbols
     int64_t NS;      // NC*2*L*C streams
@@ -82,13 +96,19 @@ hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts,
 bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym);
 bool quantize_hist_fuses_cdf(const Dims &d, const void *wire);
 hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
-                                uint16_t *scale, uint32_t *counts, uint16_t *wire, uint32_t *status,
-                                hipStream_t s);
+                                uint16_t *scale, uint32_t *counts, uint16_t *wire, const uint32_t *wpre,
+                                uint32_t *status, hipStream_t s);
 
-// counts -> cdf int32 [2,L,C,A+1] and / or the u16 wire form [2,L,C,A]
-// (either may be null).
-hipError_t launch_cdf(const Dims &d, const uint32_t *counts, int32_t *cdf, uint16_t *cdf_wire,
-                      uint32_t *status, hipStream_t s);
+// Table placement: table (slab, c) of width W = layer_w starts at entry
+// wpre[slab] * C + c * W of the u16 wire section; wpre[2L] = the section's
+// entries / C. The int32 tables are [2,L,C,A+1] whatever W (entries past W
+// hold 2^16).
+hipError_t launch_table_prefix(const Dims &d, const MaxTable &mt, uint32_t *wpre, hipStream_t s);
+
+// counts -> cdf int32 [2,L,C,A+1] and / or the u16 wire form (either may be
+// null; the wire form needs wpre).
+hipError_t launch_cdf(const Dims &d, const MaxTable &mt, const uint32_t *counts, int32_t *cdf,
+                      uint16_t *cdf_wire, const uint32_t *wpre, uint32_t *status, hipStream_t s);
 
 // Tile offsets in stream order (three passes over blocks of 256 tiles). The
 // byte count of each tile is tile_sum[t], or, with tile_sum null, the sum of
@@ -136,8 +156,9 @@ size_t encode_staging_bytes(const Dims &d);
 // entry A taken as 2^16); exactly one is set. trusted: the symbols come from
 // this library's quantiser (all below A), so the encoder skips its range
 // check.
-hipError_t launch_encode(const Dims &d, const uint8_t *sym, const int32_t *cdf32, const uint16_t *cdf16,
-                         const EncodeOut &o, const EncodeWs &w, bool trusted, hipStream_t s);
+hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, const int32_t *cdf32,
+                         const uint16_t *cdf16, const uint32_t *wpre, const EncodeOut &o, const EncodeWs &w,
+                         bool trusted, hipStream_t s);
 
 // Decoder table source: int32 [2,L,C,A+1] or the u16 wire form [2,L,C,A].
 struct DecodeIn {
@@ -147,6 +168,7 @@ struct DecodeIn {
     const uint64_t *chunk_off;
     const int32_t *cdf32;      // one of cdf32 / cdf16 is set
     const uint16_t *cdf16;
+    uint32_t *wpre;            // with cdf16: table offsets, filled by launch_decode
     int j0 = 0, j1 = -1;       // decode chunks [j0, j1) only (j1 < 0: all); their tokens are written
 };
 
@@ -196,6 +218,7 @@ struct BatchGeom {
     int B;
     uint64_t stride;            // bytes between per-call blobs
     int npieces;                // pieces per call: 2 scales + 2 cdf + 2*NC lengths + 2*NC payload
+    uint64_t wsum[2];           // table widths summed over one call's K (V) layers
 };
 
 // Split (to_bytes): plan the pieces of every call from the virtual blob's
@@ -246,16 +269,17 @@ __device__ __forceinline__ uint64_t div_rne(uint64_t num, uint32_t T, double inv
     return (uint64_t)q;
 }
 
-// Start and end of symbol s in table `tab` of an int32 [.., A+1] or u16 wire
-// [.., A] table set (exactly one pointer set).
-__device__ __forceinline__ void cdf_bounds(const int32_t *c32, const uint16_t *c16, int64_t tab, int A, int s,
-                                           uint32_t &lo, uint32_t &hi) {
+// Start and end of symbol s < W of table (slab, c): from the int32 tables
+// [2L, C, A+1], or from the u16 wire tables placed by wpre (exactly one of
+// c32 / c16 set; entry W of a wire table is 2^16).
+__device__ __forceinline__ void cdf_bounds(const int32_t *c32, const uint16_t *c16, const uint32_t *wpre, int slab,
+                                           int C, int c, int A, int W, int s, uint32_t &lo, uint32_t &hi) {
     if (c16) {
-        const uint16_t *w = c16 + tab * A;
+        const uint16_t *w = c16 + (int64_t)wpre[slab] * C + (int64_t)c * W;
         lo = w[s];
-        hi = s + 1 < A ? (uint32_t)w[s + 1] : kProbOne;
+        hi = s + 1 < W ? (uint32_t)w[s + 1] : kProbOne;
     } else {
-        const int32_t *p = c32 + tab * (A + 1);
+        const int32_t *p = c32 + ((int64_t)slab * C + c) * (A + 1);
         lo = (uint32_t)p[s];
         hi = (uint32_t)p[s + 1];
     }

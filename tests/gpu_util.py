@@ -41,10 +41,10 @@ def bf16_ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
     return np.abs(line(a_bits.view(np.uint16)) - line(b_bits.view(np.uint16)))
 
 
-def run_stages(kv_bits: np.ndarray, bins_k, bins_v):
+def run_stages(kv_bits: np.ndarray, bins_k, bins_v, table_format=0):
     """All stage calls on the GPU. kv_bits: uint16 [L,2,T,H,D]."""
     torch = torch_mod()
-    desc = cgb.Desc.for_kv(kv_bits.shape, bins_k, bins_v)
+    desc = cgb.Desc.for_kv(kv_bits.shape, bins_k, bins_v, table_format)
     L, T, C, A = desc.nlayers, desc.ntokens, desc.nchannels, desc.alphabet
     kv = to_dev(kv_bits)
     dev = kv.device

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(cgb._SIGNATURES) == set(names)
-    assert lib.cg_version() == 1
+    assert lib.cg_version() == 2
 
 
 def test_default_bins_matches_oracle():
@@ -119,13 +119,38 @@ def test_peek_rejects_bad_headers():
     blob = bytearray(oracle.to_bytes(kv, bk, bv))
     good = bytes(blob[:52])
     cgb.cg_blob_peek(good)
-    for pos, val in [(0, ord("X")), (4, 2), (6, 7), (8, 0), (24, 128), (28, 9), (32, 31), (48, 3)]:
+    for pos, val in [(0, ord("X")), (4, 2), (6, 7), (8, 0), (24, 128), (28, 9), (32, 31), (36, 2), (48, 3)]:
         bad = bytearray(good)
         bad[pos] = val
         with pytest.raises(ValueError):
             cgb.cg_blob_peek(bytes(bad))
     with pytest.raises(ValueError):
         cgb.cg_blob_peek(good[:50])  # bins cut off
+
+
+def test_per_layer_tables_layout_and_peek():
+    """The per-layer table format: the library's layout and header parse
+    agree with an oracle blob parsed independently."""
+    from blob_format import parse
+
+    L, T, H, D = 12, 300, 2, 16
+    kv = generate_kv(L, T, H, D, seed=8)
+    bk, bv = oracle.default_bins(L)
+    blob = oracle.to_bytes(kv, bk, bv, 1)
+    p = parse(blob)
+    info, pk, pv = cgb.cg_blob_peek(blob[:48 + 2 * L])
+    assert info["table_format"] == 1 and info["blob_size"] == len(blob)
+    d = cgb.Desc(L, T, H, D, bk, bv, cgb.CG_TABLES_PER_LAYER)
+    lay = cgb.cg_blob_layout(d)
+    assert lay["table_format"] == 1
+    for k in ["off_scales", "off_cdf", "off_chunk_off", "off_lengths", "off_payload"]:
+        assert info[k] == lay[k], k
+    assert lay["off_payload"] == len(blob) - len(p["payload"])
+    assert lay["off_chunk_off"] - lay["off_cdf"] == (2 * H * D * int(p["widths"].sum()) + 63) // 64 * 64
+    shared = cgb.cg_blob_layout(cgb.Desc(L, T, H, D, bk, bv))
+    assert shared["table_format"] == 0 and shared["off_payload"] > lay["off_payload"]
+    with pytest.raises(ValueError):
+        cgb.Desc(L, T, H, D, bk, bv, 2)
 
 
 def test_strerror():

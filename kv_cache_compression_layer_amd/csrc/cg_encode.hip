@@ -240,7 +240,7 @@ struct Coder {
     }
 };
 
-constexpr int kLdsRows = 44;  // LDS stage rows per stream (most streams fit)
+constexpr int kLdsRows = 28;  // LDS stage rows per stream (most streams fit)
 
 // Block of NW waves for one (K|V, layer, 64-channel block); wave w codes the
 // S chunks (group * NW + w) * S + s, lane = channel, with the table the

@@ -129,6 +129,9 @@ struct EncArgs {
     uint32_t *overflow_list;   // [tiles]
     int L, T, C, A, NC, CB;
     MaxTable mt;               // table width of each (K|V, layer)
+    // This launch codes only the slabs whose symbol count 2M+1 lies in
+    // [nsym_lo, nsym_hi]; the other blocks return at once.
+    int nsym_lo, nsym_hi;
 };
 
 // Tile = (chunk j, slab = kv*L + l, 64-channel block cb); tile index in
@@ -269,6 +272,9 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     const int c = cb * 64 + lane;
     const bool active = c < a.C;
     const int lane_off = active ? lane : (a.C - 1 - cb * 64);  // in-bounds column for idle lanes
+    const int kvs = slab >= a.L ? 1 : 0, ls = slab - kvs * a.L;
+    const int nsym = 2 * layer_m(a.mt, kvs, ls) + 1;
+    if (nsym < a.nsym_lo || nsym > a.nsym_hi) return;  // block-uniform
 
     // Symbols are read through a buffer over this (K|V, layer) slab: the row
     // offset is wave-uniform (scalar), the column the lane's constant offset.
@@ -301,9 +307,12 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
 
     // Tables, built by the block's waves together: one per lane, packed
     // start | freq << 16, [symbol][lane]; W symbols (the slab's table width).
-    const int W = layer_w(a.mt, slab >= a.L ? 1 : 0, slab >= a.L ? slab - a.L : slab);
+    const int W = layer_w(a.mt, kvs, ls);
     bool bad = false;
-    for (int s = wv; s < W; s += NW) {
+    // A launch for slabs of at most 2^LOGA symbols holds only that many
+    // entries of a wider table: the quantiser's symbols never reach the rest.
+    const int WT = min(W, 1 << LOGA);
+    for (int s = wv; s < WT; s += NW) {
         uint32_t entry;
         if (active) {
             uint32_t lo, hi;
@@ -618,25 +627,51 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     const int ngroups = (d.NC + S * NW - 1) / (S * NW);
     const unsigned blocks = (unsigned)((int64_t)ngroups * 2 * d.L * d.CB);
     const dim3 grid(blocks), block(64 * NW);
+    int loga = 4;
+    while ((1 << loga) < d.A) ++loga;
 #define CG_ENC(SS, LG, W)                                                                           \
     do {                                                                                            \
         if (trusted) hipLaunchKernelGGL((k_encode<SS, LG, W, true>), grid, block, 0, s, a);         \
         else hipLaunchKernelGGL((k_encode<SS, LG, W, false>), grid, block, 0, s, a);                \
     } while (0)
-#define CG_ENC_A(SS, W)                           \
+#define CG_ENC_A(SS, W, LOGA_)                    \
     do {                                          \
-        if (d.A <= 16) CG_ENC(SS, 4, W);          \
-        else if (d.A <= 32) CG_ENC(SS, 5, W);     \
-        else if (d.A <= 64) CG_ENC(SS, 6, W);     \
+        if (LOGA_ <= 4) CG_ENC(SS, 4, W);         \
+        else if (LOGA_ == 5) CG_ENC(SS, 5, W);    \
+        else if (LOGA_ == 6) CG_ENC(SS, 6, W);    \
         else CG_ENC(SS, 7, W);                    \
     } while (0)
-    if (NW == 4) CG_ENC_A(2, 4);
-    else if (S == 2) CG_ENC_A(2, 1);
-    else CG_ENC_A(1, 1);
+    auto launch = [&](int lg) {
+        if (NW == 4) CG_ENC_A(2, 4, lg);
+        else if (S == 2) CG_ENC_A(2, 1, lg);
+        else CG_ENC_A(1, 1, lg);
+        return hipGetLastError();
+    };
+    // The quantiser's symbols of a slab stay below 2M + 1, so with trusted
+    // symbols the slabs of at most 16 symbols (16-bin layers) take a launch
+    // with 16-entry tables, whose blocks need half the LDS and fit the CU
+    // more densely; the other slabs take the full width.
+    bool small = false, large = false;
+    const int nl = mt.lper ? (int)mt.lper : (d.L < CG_MAX_LAYERS ? d.L : CG_MAX_LAYERS);
+    for (int kv = 0; kv < 2; ++kv)
+        for (int l = 0; l < nl; ++l) (2 * (mt.bins[kv][l] / 2 - 1) + 1 <= 16 ? small : large) = true;
+    hipError_t e;
+    if (trusted && loga > 4 && small) {
+        a.nsym_lo = 0;
+        a.nsym_hi = 16;
+        if ((e = launch(4)) != hipSuccess) return e;
+        if (large) {
+            a.nsym_lo = 17;
+            a.nsym_hi = 1 << 30;
+            if ((e = launch(loga)) != hipSuccess) return e;
+        }
+    } else {
+        a.nsym_lo = 0;
+        a.nsym_hi = 1 << 30;
+        if ((e = launch(loga)) != hipSuccess) return e;
+    }
 #undef CG_ENC_A
 #undef CG_ENC
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
 
     const int64_t tpc = 2LL * d.L * d.CB;
     TileScan ts{w.tile_sum, nullptr, w.tile_off, w.scan_tmp, w.chunk_total, nullptr, 0, &w.hdr->status,

@@ -251,14 +251,14 @@ int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *sca
                 const EncodeOut &o, void *ws, const WsLayout &w, hipStream_t s) {
     uint32_t *status = at<uint32_t>(ws, 0);
     uint32_t *counts = at<uint32_t>(ws, w.counts);
-    uint32_t *wpre = at<uint32_t>(ws, w.wpre);
+    uint32_t *wpre = d.fmt == CG_TABLES_PER_LAYER ? at<uint32_t>(ws, w.wpre) : nullptr;
     uint8_t *sym = at<uint8_t>(ws, w.sym);
     const uint16_t *kv16 = reinterpret_cast<const uint16_t *>(kv);
     const bool qh = quantize_hist_fits(d, kv, sym);
     const bool fused = qh && quantize_hist_fuses_cdf(d, wire);
     int rc = hip_rc(launch_fill_u32(status, 0u, (int64_t)((fused ? kWsAlign : w.clear_end) / 4), s));
     if (rc) return rc;
-    if ((rc = hip_rc(launch_table_prefix(d, mt, wpre, s)))) return rc;
+    if (wpre && (rc = hip_rc(launch_table_prefix(d, mt, wpre, s)))) return rc;
     if (qh) {
         rc = hip_rc(
             launch_quantize_hist(d, mt, kv16, sym, scales, counts, fused ? wire : nullptr, wpre, status, s));

@@ -167,7 +167,8 @@ hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts,
 // entry k of the table (the first lane of a table also writes entry W). An
 // alphabet above 64 takes two rounds of 64, the second starting from the
 // first one's total. int32 tables are [2,L,C,A+1] with 2^16 past entry W; u16
-// wire tables hold entries 0..W-1 at wpre[slab] * C + c * W.
+// wire tables hold entries 0..W-1 at wpre[slab] * C + c * W (wpre null: one
+// width A, slab * A).
 template <int G>
 __global__ __launch_bounds__(256) void k_cdf(const uint32_t *__restrict__ counts,
                                              int32_t *__restrict__ cdf,
@@ -186,7 +187,8 @@ __global__ __launch_bounds__(256) void k_cdf(const uint32_t *__restrict__ counts
     const int W = layer_w(mt, kv, slab - kv * L);
     const uint64_t S = kProbOne - (uint32_t)W;
     const double invT = 1.0 / (double)T;
-    uint16_t *wt = wire && live ? wire + (int64_t)wpre[slab] * C + (int64_t)c * W : nullptr;
+    uint16_t *wt = wire && live ? wire + (wpre ? (int64_t)wpre[slab] : (int64_t)slab * A) * C + (int64_t)c * W
+                                : nullptr;
     uint64_t base = 0;
     bool bad = false;
     for (int kb = 0; kb < A; kb += G) {

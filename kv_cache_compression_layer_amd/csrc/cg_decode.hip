@@ -494,8 +494,10 @@ static hipError_t launch_decode_f(const Dims &d, const DecArgs &a, hipStream_t s
 hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, const DecodeOut &out,
                          uint64_t *tile_off, uint64_t *scan_tmp, uint32_t *status, hipStream_t s) {
     const int j0 = in.j0, j1 = in.j1 < 0 ? d.NC : in.j1;
-    if (in.cdf16) {
-        hipError_t e0 = launch_table_prefix(d, mt, in.wpre, s);
+    // Table offsets: only the per-layer format needs them computed.
+    uint32_t *wpre = in.cdf16 && d.fmt == CG_TABLES_PER_LAYER ? in.wpre : nullptr;
+    if (wpre) {
+        hipError_t e0 = launch_table_prefix(d, mt, wpre, s);
         if (e0 != hipSuccess) return e0;
     }
     TileScan ts{nullptr, in.lengths, tile_off, scan_tmp, nullptr, in.chunk_off, in.payload_bytes, status,
@@ -509,7 +511,7 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     a.tile_off = tile_off;
     a.cdf32 = in.cdf32;
     a.cdf16 = in.cdf16;
-    a.wpre = in.wpre;
+    a.wpre = wpre;
     a.sym = out.sym;
     a.kv = out.kv;
     a.scale = out.scale;

@@ -322,7 +322,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
         // C is 512 or 1024, so the slab's C * W entries and its offset
         // wpre[slab] * C are whole 16-byte units.
         const uint4 *src4 = reinterpret_cast<const uint4 *>(hist);
-        uint4 *dst4 = reinterpret_cast<uint4 *>(wire + (int64_t)wpre[slab] * C);
+        uint4 *dst4 = reinterpret_cast<uint4 *>(wire + (wpre ? (int64_t)wpre[slab] : (int64_t)slab * A) * C);
         for (int i = threadIdx.x; i < C * W / 8; i += 512) dst4[i] = src4[i];
         return;
     }

@@ -656,7 +656,8 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     for (int kv = 0; kv < 2; ++kv)
         for (int l = 0; l < nl; ++l) (2 * (mt.bins[kv][l] / 2 - 1) + 1 <= 16 ? small : large) = true;
     hipError_t e;
-    if (trusted && loga > 4 && small) {
+    // Only worth a second launch when the grid is large (big calls, batches).
+    if (trusted && loga > 4 && small && (!large || blocks >= 16384)) {
         a.nsym_lo = 0;
         a.nsym_hi = 16;
         if ((e = launch(4)) != hipSuccess) return e;

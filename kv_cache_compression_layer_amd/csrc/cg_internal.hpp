@@ -101,8 +101,9 @@ hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_
 
 // Table placement: table (slab, c) of width W = layer_w starts at entry
 // wpre[slab] * C + c * W of the u16 wire section; wpre[2L] = the section's
-// entries / C. The int32 tables are [2,L,C,A+1] whatever W (entries past W
-// hold 2^16).
+// entries / C. With one width A for every table wpre is not needed (null:
+// wpre[slab] = slab * A). The int32 tables are [2,L,C,A+1] whatever W
+// (entries past W hold 2^16).
 hipError_t launch_table_prefix(const Dims &d, const MaxTable &mt, uint32_t *wpre, hipStream_t s);
 
 // counts -> cdf int32 [2,L,C,A+1] and / or the u16 wire form (either may be
@@ -270,12 +271,13 @@ __device__ __forceinline__ uint64_t div_rne(uint64_t num, uint32_t T, double inv
 }
 
 // Start and end of symbol s < W of table (slab, c): from the int32 tables
-// [2L, C, A+1], or from the u16 wire tables placed by wpre (exactly one of
-// c32 / c16 set; entry W of a wire table is 2^16).
+// [2L, C, A+1], or from the u16 wire tables placed by wpre (or [2L, C, A]
+// when wpre is null); exactly one of c32 / c16 set; entry W of a wire table
+// is 2^16.
 __device__ __forceinline__ void cdf_bounds(const int32_t *c32, const uint16_t *c16, const uint32_t *wpre, int slab,
                                            int C, int c, int A, int W, int s, uint32_t &lo, uint32_t &hi) {
     if (c16) {
-        const uint16_t *w = c16 + (int64_t)wpre[slab] * C + (int64_t)c * W;
+        const uint16_t *w = c16 + (wpre ? (int64_t)wpre[slab] : (int64_t)slab * A) * C + (int64_t)c * W;
         lo = w[s];
         hi = s + 1 < W ? (uint32_t)w[s + 1] : kProbOne;
     } else {

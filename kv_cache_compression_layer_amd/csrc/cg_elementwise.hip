@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void k_blob_header(uint8_t *__restrict__ blob,
 hipError_t launch_blob_header(uint8_t *blob, const HeaderBytes &h, const BlobLayout &lay,
                               const Dims &d, hipStream_t s, int nblobs, uint64_t stride) {
     const uint64_t end_scales = lay.off_scales + 4ull * d.L * d.T;
-    const uint64_t end_cdf = lay.off_cdf + 4ull * d.L * d.C * d.A;
+    const uint64_t end_cdf = lay.off_cdf + 2ull * d.C * (uint64_t)d.tab_entries;
     const uint64_t end_off = lay.off_chunk_off + 8ull * (d.NC + 1);
     const uint64_t end_len = lay.off_lengths + 4ull * d.NC * d.L * d.C;
     hipLaunchKernelGGL(k_blob_header, dim3((unsigned)nblobs), dim3(256), 0, s, blob, stride, h, lay, end_scales,

@@ -149,3 +149,26 @@ def test_corrupt_table_is_reported():
     ws = cgb.alloc_workspace(desc, cgb.CG_OP_FROM_BYTES)
     cgb.cg_from_bytes(desc, dev, dev.numel(), out, ws)
     assert cgb.cg_read_status(ws) == cgb.CG_E_CORRUPT
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_section_gaps_are_zero_in_a_dirty_buffer(fmt):
+    """The blob is written into a buffer full of 0xAB: every byte the
+    library does not fill with data (header padding, the gaps after each
+    section, including the ragged table section) must still equal the
+    oracle's zero padding."""
+    import torch
+
+    L, T, H, D = 5, 255, 1, 40
+    rng = np.random.default_rng(2)
+    bk = rng.integers(4, 129, L).astype(np.uint8)
+    bv = rng.integers(4, 129, L).astype(np.uint8)
+    kv = generate_kv(L, T, H, D, outlier_frac=0.0, outlier_scale=1.0, seed=13)
+    want = oracle.to_bytes(kv, bk, bv, fmt)
+    desc = cgb.Desc(L, T, H, D, bk, bv, fmt)
+    blob = torch.full((cgb.cg_blob_bound(desc),), 0xAB, dtype=torch.uint8, device="cuda:0")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    ws = cgb.alloc_workspace(desc, cgb.CG_OP_TO_BYTES)
+    cgb.cg_to_bytes(desc, to_dev(kv), blob, size, ws)
+    assert cgb.cg_read_status(ws) == cgb.CG_OK
+    assert to_np(blob[: int(size.item())]).tobytes() == want

@@ -43,11 +43,11 @@ def _stride(desc):
     return (cgb.cg_blob_bound(desc) + 7) // 8 * 8
 
 
-def _to_bytes_batch(kv, bk, bv, stride=None):
+def _to_bytes_batch(kv, bk, bv, stride=None, fmt=0):
     import torch
 
     B, L, _, T, H, D = kv.shape
-    desc = cgb.Desc(L, T, H, D, bk, bv)
+    desc = cgb.Desc(L, T, H, D, bk, bv, fmt)
     stride = _stride(desc) if stride is None else stride
     blobs = torch.zeros(B * stride, dtype=torch.uint8, device="cuda:0")
     sizes = torch.zeros(B, dtype=torch.int64, device="cuda:0")
@@ -111,30 +111,32 @@ def test_batch_blobs_equal_oracle_per_call(B, shape):
 
 
 @pytest.mark.parametrize(
-    "B,L,H,D",
+    "B,L,H,D,fmt",
     [
-        (1100, 1, 1, 64),   # 1100 layers: every virtual layer takes call layer 0
-        (150, 7, 1, 64),    # 1050 layers, period 7
-        (100, 12, 1, 64),   # 1200 layers, bins differ across a call's layers
-        (40, 32, 8, 128),   # 1280 layers of C = 1024 (tables built by the quantiser)
+        (1100, 1, 1, 64, 0),   # 1100 layers: every virtual layer takes call layer 0
+        (150, 7, 1, 64, 0),    # 1050 layers, period 7
+        (100, 12, 1, 64, 0),   # 1200 layers, bins differ across a call's layers
+        (40, 32, 8, 128, 0),   # 1280 layers of C = 1024 (tables built by the quantiser)
+        (100, 12, 1, 64, 1),   # the same with per-layer tables (widths taken modulo L)
+        (40, 32, 8, 128, 1),
     ],
 )
-def test_batch_many_layers(B, L, H, D):
+def test_batch_many_layers(B, L, H, D, fmt):
     import torch
 
     T = 16
     kv = _batch_kv(B, L, T, H, D, seed=1300 + L, specials=False)
     bk, bv = oracle.default_bins(L)
-    desc, stride, blobs, sizes, status = _to_bytes_batch(kv, bk, bv)
+    desc, stride, blobs, sizes, status = _to_bytes_batch(kv, bk, bv, fmt=fmt)
     assert status == cgb.CG_OK
     blobs_np, sizes_np = to_np(blobs), to_np(sizes)
     # Every call equals the plain GPU call; a sample also equals the oracle.
     kv_d = to_dev(kv).view(torch.bfloat16)
     for b in range(B):
-        one = to_np(cgb.to_bytes(kv_d[b], bk, bv)).tobytes()
+        one = to_np(cgb.to_bytes(kv_d[b], bk, bv, table_format=fmt)).tobytes()
         assert _blob(blobs_np, stride, sizes_np, b) == one, f"call {b}"
     for b in (0, 1, B // 2, B - 1):
-        assert _blob(blobs_np, stride, sizes_np, b) == oracle.to_bytes(kv[b], bk, bv), f"call {b}"
+        assert _blob(blobs_np, stride, sizes_np, b) == oracle.to_bytes(kv[b], bk, bv, fmt), f"call {b}"
 
     got, st = _from_bytes_batch(desc, B, blobs, stride, sizes)
     assert st == cgb.CG_OK

@@ -121,3 +121,38 @@ def test_two_streams_at_once():
             assert to_np(blobs[i][:n]).tobytes() == want[i], (rep, i)
             ref = np.asarray(oracle.from_bytes(want[i])).view(np.uint16).reshape(-1)
             assert bf16_ulp_distance(to_np(outs[i], np.uint16), ref).max() <= 1
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize(
+    "L,T,H,D",
+    [
+        (1024, 3, 1, 8),     # the largest layer count: every entry of the per-layer tables in use
+        (1, 40, 64, 128),    # C = 8192: 128 channel blocks per slab, the generic quantiser
+        (2, 300, 3, 1000),   # C = 3000, not a multiple of 64
+    ],
+)
+def test_size_limits(L, T, H, D, fmt):
+    import torch
+
+    rng = np.random.default_rng(L + T + H)
+    bk = rng.integers(4, 129, L).astype(np.uint8)
+    bv = rng.integers(4, 129, L).astype(np.uint8)
+    kv = generate_kv(L, T, H, D, outlier_frac=0.01, outlier_scale=10.0, seed=L * 7 + D)
+    want = oracle.to_bytes(kv, bk, bv, fmt)
+    blob = cgb.to_bytes(to_dev(kv).view(torch.bfloat16), bk, bv, table_format=fmt)
+    assert to_np(blob).tobytes() == want
+    out = to_np(cgb.from_bytes(blob).view(torch.int16), np.uint16).reshape(-1)
+    ref = np.asarray(oracle.from_bytes(want)).view(np.uint16).reshape(-1)
+    assert bf16_ulp_distance(out, ref).max() <= 1
+
+
+def test_shape_limits_are_rejected():
+    bk, bv = oracle.default_bins(2)
+    for shape in [(2, 0, 1, 8), (0, 4, 1, 8), (2, 4, 0, 8), (1025, 4, 1, 8)]:
+        L = shape[0]
+        b = np.full(max(L, 1), 16, np.uint8)
+        with pytest.raises(ValueError):
+            cgb.Desc(*shape, b[:L] if L else b[:0], b[:L] if L else b[:0])
+    with pytest.raises(ValueError):  # one (K|V, layer) slab of 2^31 elements
+        cgb.Desc(2, 1 << 21, 8, 128, bk, bv)

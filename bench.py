@@ -49,7 +49,7 @@ def parse_args():
                     help="skip the 256-token-chunk batch measurement (e.g. under a profiler)")
     ap.add_argument("--no-streaming", action="store_true",
                     help="skip the pipelined host-to-device load measurement")
-    ap.add_argument("--cpu-sample-layers", type=int, default=4)
+    ap.add_argument("--cpu-sample-layers", type=int, default=8)
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 

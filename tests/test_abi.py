@@ -156,3 +156,16 @@ def test_per_layer_tables_layout_and_peek():
 def test_strerror():
     assert "workspace" in cgb.strerror(cgb.CG_E_WORKSPACE)
     assert cgb.strerror(0) == "ok"
+
+
+def test_shape_limits_are_rejected():
+    bk, bv = oracle.default_bins(2)
+    for shape in [(2, 0, 1, 8), (0, 4, 1, 8), (2, 4, 0, 8), (1025, 4, 1, 8)]:
+        L = shape[0]
+        b = np.full(max(L, 1), 16, np.uint8)
+        with pytest.raises(ValueError):
+            cgb.Desc(*shape, b[:L], b[:L])
+    with pytest.raises(ValueError):  # one (K|V, layer) slab of 2^31 elements
+        cgb.Desc(2, 1 << 21, 8, 128, bk, bv)
+    with pytest.raises(ValueError):  # batch beyond 32767 layers
+        cgb.cg_workspace_bytes_batch(cgb.Desc(32, 16, 1, 64), 1024, 1 << 20, cgb.CG_OP_TO_BYTES)

@@ -46,6 +46,7 @@ struct DecArgs {
     MaxTable mt;
     int L, T, C, A, NC, CB;
     int j0, NCr;   // the chunks decoded: [j0, j0 + NCr)
+    int nsym_lo, nsym_hi;
 };
 
 // Bytes of the LDS pool a block of NW waves shares for its tiles' payload,
@@ -89,13 +90,13 @@ struct PagedRows {
     int t0[S], b0[S];
 };
 
-template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED, bool HALF, bool PAGED>
+template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED, bool HALF, bool PAGED, bool TAIL>
 __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S], const int (&n)[S],
                                             const uint32_t (&rowoff)[S], const PagedRows<S> &pg,
                                             const uint32_t *tab,
                                             const float *dq, uint32_t (&sc_v)[S][4], const uint8_t *pool,
                                             __amdgpu_buffer_rsrc_t out_rsrc, uint32_t out_voff,
-                                            int lane, int W, uint64_t &bad_mask) {
+                                            int lane, int W, int slab, int c, uint64_t &bad_mask) {
     auto fetch = [&](int s) -> uint32_t {
         DecStream &d = st[s];
         if (STAGED) return pool[d.ptr++];
@@ -116,7 +117,12 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
     // Byte address in tab of (symbol s, this lane) is s * 256 + lane * 4.
     const uint8_t *tabb = reinterpret_cast<const uint8_t *>(tab);
     const uint32_t lane4 = (uint32_t)lane * 4;
-    const uint32_t amax4 = ((uint32_t)W - 1) * 256 + lane4;
+    // The LDS table holds min(W, 2^LOGA) entries; with TAIL and a wider
+    // table, symbols from 2^LOGA up are found in the table in global memory.
+    const int WL = W < (1 << LOGA) ? W : (1 << LOGA);
+    const uint32_t amax4 = ((uint32_t)WL - 1) * 256 + lane4;
+    const bool tail_on = TAIL && W > (1 << LOGA);
+    const uint32_t ltop4 = ((1u << LOGA) - 1) * 256 + lane4;
     // Search depth: the whole table, or (HALF) its lower half when the layer's
     // symbols all lie below the half's top entry; landing on that top entry
     // then means a symbol at or above it (only in corrupt streams), and a
@@ -208,7 +214,26 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
                 }
             }
             if (CLAMP) ad[s] = min(ad[s], amax4);
-            const uint32_t e = *reinterpret_cast<const uint32_t *>(tabb + ad[s]);
+            uint32_t e = *reinterpret_cast<const uint32_t *>(tabb + ad[s]);
+            if (tail_on && __builtin_amdgcn_ballot_w64(ad[s] == ltop4)) {
+                // The search stopped at the last LDS entry: the symbol may lie
+                // above it (never for the quantiser's symbols, which stay below
+                // 2M + 1 <= 2^LOGA). Continue upwards in global memory.
+                __asm__ volatile("" ::: "memory");
+                if (ad[s] == ltop4) {
+                    bool bad = false;
+                    for (int sy = 1 << LOGA; sy < W; ++sy) {
+                        uint32_t lo, hi;
+                        cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, c, a.A, W, sy, lo, hi);
+                        if (__umul24(r[s], lo & 0xFFFFu) > st[s].code) break;
+                        bad |= hi <= lo || hi > kProbOne;
+                        ad[s] = (uint32_t)sy * 256 + lane4;
+                        e = (lo & 0xFFFFu) | ((hi - lo) << 16);
+                    }
+                    if (bad) e = (e & 0xFFFFu) | (1u << 16);
+                    bad_mask |= __ballot(bad);
+                }
+            }
             d.code -= __umul24(r[s], e & 0xFFFFu);
             d.range = __umul24(r[s], e >> 16);
             if (d.range < kTop) {
@@ -266,7 +291,7 @@ __device__ __forceinline__ uint32_t load_word(const uint8_t *payload, uint64_t p
 // Block of NW waves for one (K|V, layer, 64-channel block): wave w decodes
 // the S chunks (group * NW + w) * S + s, lane = channel. The waves share the
 // channel tables, the dequantisation table and an LDS pool for the payload.
-template <int S, bool FUSED, int LOGA, bool CLAMP, int NW, bool PAGED>
+template <int S, bool FUSED, int LOGA, bool CLAMP, int NW, bool PAGED, bool TAIL>
 __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // Static LDS sized by the template, so every address folds to an immediate.
     __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
@@ -294,6 +319,9 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     const bool active = c < a.C;
     const int M = layer_m(a.mt, kv, l);
     const int W = layer_w(a.mt, kv, l);  // symbols of this slab's tables
+    // This launch decodes only the slabs whose quantiser symbol count 2M+1
+    // lies in [nsym_lo, nsym_hi]; the other blocks return at once.
+    if (2 * M + 1 < a.nsym_lo || 2 * M + 1 > a.nsym_hi) return;  // block-uniform
 
     // This wave's streams: lengths, offsets and the pool bytes they need
     // (alignment head + bytes + four zero bytes after each of the 64 streams).
@@ -453,42 +481,77 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     const bool half = LOGA >= 3 && M + 1 <= (1 << (LOGA - 2));
     if (half) {
         if (staged)
-            decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                               out_voff, lane, W, bad_mask);
+            decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3, PAGED, TAIL>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+                                                               out_voff, lane, W, slab, c, bad_mask);
         else
-            decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                                out_voff, lane, W, bad_mask);
+            decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3, PAGED, TAIL>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+                                                                out_voff, lane, W, slab, c, bad_mask);
     } else {
         if (staged)
-            decode_loop<S, FUSED, LOGA, CLAMP, true, false, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                            out_voff, lane, W, bad_mask);
+            decode_loop<S, FUSED, LOGA, CLAMP, true, false, PAGED, TAIL>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+                                                            out_voff, lane, W, slab, c, bad_mask);
         else
-            decode_loop<S, FUSED, LOGA, CLAMP, false, false, PAGED>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                             out_voff, lane, W, bad_mask);
+            decode_loop<S, FUSED, LOGA, CLAMP, false, false, PAGED, TAIL>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+                                                             out_voff, lane, W, slab, c, bad_mask);
     }
     if ((__ballot(active && (corrupt || bad_table)) | (bad_mask & __ballot(active))) && lane == 0)
         atomicOr(a.status, kStCorrupt);
 }
 
-template <int S, bool FUSED, int LOGA, int NW, bool PAGED>
-static hipError_t launch_decode_s(const Dims &d, const DecArgs &a, hipStream_t s) {
+template <int S, bool FUSED, int LOGA, int NW, bool PAGED, bool TAIL>
+static hipError_t launch_decode_s(const Dims &d, const DecArgs &a, bool clamp, hipStream_t s) {
     const int ngroups = (a.NCr + S * NW - 1) / (S * NW);
     const dim3 grid((unsigned)((int64_t)ngroups * 2 * d.L * d.CB));
-    if (d.A == (1 << LOGA) && d.wmin == d.A)  // every table fills the 2^LOGA entries: no clamp
-        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, false, NW, PAGED>), grid, dim3(64 * NW), 0, s, a);
+    if (!clamp)  // every table fills the 2^LOGA entries: no clamp
+        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, false, NW, PAGED, TAIL>), grid, dim3(64 * NW), 0, s, a);
     else
-        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, true, NW, PAGED>), grid, dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, true, NW, PAGED, TAIL>), grid, dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
 template <int S, bool FUSED, int NW, bool PAGED = false>
-static hipError_t launch_decode_f(const Dims &d, const DecArgs &a, hipStream_t s) {
-    if (d.A <= 4) return launch_decode_s<S, FUSED, 2, NW, PAGED>(d, a, s);
-    if (d.A <= 8) return launch_decode_s<S, FUSED, 3, NW, PAGED>(d, a, s);
-    if (d.A <= 16) return launch_decode_s<S, FUSED, 4, NW, PAGED>(d, a, s);
-    if (d.A <= 32) return launch_decode_s<S, FUSED, 5, NW, PAGED>(d, a, s);
-    if (d.A <= 64) return launch_decode_s<S, FUSED, 6, NW, PAGED>(d, a, s);
-    return launch_decode_s<S, FUSED, 7, NW, PAGED>(d, a, s);
+static hipError_t launch_decode_f(const Dims &d, const MaxTable &mt, DecArgs a, hipStream_t s) {
+    int loga = 2;
+    while ((1 << loga) < d.A) ++loga;
+    a.nsym_lo = 0;
+    a.nsym_hi = 1 << 30;
+    if constexpr (NW <= 2) {
+        // Blocks of one or two waves are held back by their LDS table. The
+        // slabs whose quantiser symbols fit 16 entries (2M + 1 <= 16, the
+        // 16-bin layers) take a launch with 16-entry tables (a rare symbol
+        // above them is looked up in global memory); the others take the
+        // full width in a second launch.
+        if (loga > 4) {
+            bool small = false, large = false, small_narrow = false;
+            const int nl = mt.lper ? (int)mt.lper : (d.L < CG_MAX_LAYERS ? d.L : CG_MAX_LAYERS);
+            for (int kv = 0; kv < 2; ++kv)
+                for (int l = 0; l < nl; ++l) {
+                    const int b = mt.bins[kv][l], w = mt.per_layer ? b : d.A;
+                    if (2 * (b / 2 - 1) + 1 <= 16) {
+                        small = true;
+                        small_narrow |= w < 16;
+                    } else {
+                        large = true;
+                    }
+                }
+            if (small) {
+                a.nsym_hi = 16;
+                hipError_t e = launch_decode_s<S, FUSED, 4, NW, PAGED, true>(d, a, small_narrow, s);
+                if (e != hipSuccess || !large) return e;
+                a.nsym_lo = 17;
+                a.nsym_hi = 1 << 30;
+            }
+        }
+    }
+    const bool clamp = !(d.A == (1 << loga) && d.wmin == d.A);
+    switch (loga) {
+    case 2: return launch_decode_s<S, FUSED, 2, NW, PAGED, false>(d, a, clamp, s);
+    case 3: return launch_decode_s<S, FUSED, 3, NW, PAGED, false>(d, a, clamp, s);
+    case 4: return launch_decode_s<S, FUSED, 4, NW, PAGED, false>(d, a, clamp, s);
+    case 5: return launch_decode_s<S, FUSED, 5, NW, PAGED, false>(d, a, clamp, s);
+    case 6: return launch_decode_s<S, FUSED, 6, NW, PAGED, false>(d, a, clamp, s);
+    default: return launch_decode_s<S, FUSED, 7, NW, PAGED, false>(d, a, clamp, s);
+    }
 }
 
 hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, const DecodeOut &out,
@@ -530,16 +593,19 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     // Two streams per lane and eight (or four) waves per block when there are
     // enough chunks; otherwise one stream per lane and as few waves as chunks.
     if (out.paged.cache) {
-        if (ncr >= 16) return launch_decode_f<2, true, 8, true>(d, a, s);
-        if (ncr >= 8) return launch_decode_f<2, true, 4, true>(d, a, s);
-        if (ncr >= 2) return launch_decode_f<1, true, 2, true>(d, a, s);
-        return launch_decode_f<1, true, 1, true>(d, a, s);
+        if (ncr >= 16) return launch_decode_f<2, true, 8, true>(d, mt, a, s);
+        if (ncr >= 8) return launch_decode_f<2, true, 4, true>(d, mt, a, s);
+        if (ncr >= 2) return launch_decode_f<1, true, 2, true>(d, mt, a, s);
+        return launch_decode_f<1, true, 1, true>(d, mt, a, s);
     }
     const bool fused = out.kv != nullptr;
-    if (ncr >= 16) return fused ? launch_decode_f<2, true, 8>(d, a, s) : launch_decode_f<2, false, 8>(d, a, s);
-    if (ncr >= 8) return fused ? launch_decode_f<2, true, 4>(d, a, s) : launch_decode_f<2, false, 4>(d, a, s);
-    if (ncr >= 2) return fused ? launch_decode_f<1, true, 2>(d, a, s) : launch_decode_f<1, false, 2>(d, a, s);
-    return fused ? launch_decode_f<1, true, 1>(d, a, s) : launch_decode_f<1, false, 1>(d, a, s);
+    if (ncr >= 16)
+        return fused ? launch_decode_f<2, true, 8>(d, mt, a, s) : launch_decode_f<2, false, 8>(d, mt, a, s);
+    if (ncr >= 8)
+        return fused ? launch_decode_f<2, true, 4>(d, mt, a, s) : launch_decode_f<2, false, 4>(d, mt, a, s);
+    if (ncr >= 2)
+        return fused ? launch_decode_f<1, true, 2>(d, mt, a, s) : launch_decode_f<1, false, 2>(d, mt, a, s);
+    return fused ? launch_decode_f<1, true, 1>(d, mt, a, s) : launch_decode_f<1, false, 1>(d, mt, a, s);
 }
 
 }  // namespace cg

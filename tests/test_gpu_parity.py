@@ -208,3 +208,26 @@ def test_coder_on_symbols_beyond_the_layer_range():
     np.testing.assert_array_equal(g["chunk_off"], chunk_off)
     np.testing.assert_array_equal(g["payload"], payload)
     np.testing.assert_array_equal(g["sym_decoded"], sym)
+
+
+@pytest.mark.parametrize("T", [256, 700])
+def test_symbols_above_16_in_16_bin_layers(T):
+    """The stage coder accepts any symbol below the table width. In the
+    16-bin layers of a call whose widest layer has 32 bins, symbols 16..31
+    are valid though the quantiser never makes them; calls of fewer than 8
+    chunks decode those layers with 16-entry tables in LDS and must find the
+    higher symbols in the table in global memory."""
+    L, C = 12, 64
+    rng = np.random.default_rng(T)
+    sym = rng.integers(0, 32, (2, L, T, C)).astype(np.uint8)
+    low = rng.random((2, L, T, C)) < 0.7  # mostly low symbols, some high ones
+    sym[low] = rng.integers(0, 15, int(low.sum())).astype(np.uint8)
+    bk, bv = oracle.default_bins(L)
+    desc = cgb.Desc(L, T, 1, C, bk, bv)
+    cdf = oracle.build_cdf(sym, 32)
+    g = run_coder(sym, cdf, desc)
+    assert g["encode_status"] == cgb.CG_OK and g["decode_status"] == cgb.CG_OK
+    payload, lengths, chunk_off = oracle.encode(sym, cdf)
+    assert g["payload"].tobytes() == payload.tobytes()
+    np.testing.assert_array_equal(g["lengths"], lengths)
+    np.testing.assert_array_equal(g["sym_decoded"], sym)

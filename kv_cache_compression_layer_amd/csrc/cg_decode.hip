@@ -520,7 +520,10 @@ static hipError_t launch_decode_f(const Dims &d, const MaxTable &mt, DecArgs a, 
         // slabs whose quantiser symbols fit 16 entries (2M + 1 <= 16, the
         // 16-bin layers) take a launch with 16-entry tables (a rare symbol
         // above them is looked up in global memory); the others take the
-        // full width in a second launch.
+        // full width in a second launch. A call too small to fill the GPU
+        // (a single short call) runs both kinds in one launch instead: its
+        // time is one stream's latency, which two launches in a row double.
+        const int64_t blocks = (int64_t)((a.NCr + S * NW - 1) / (S * NW)) * 2 * d.L * d.CB;
         if (loga > 4) {
             bool small = false, large = false, small_narrow = false;
             const int nl = mt.lper ? (int)mt.lper : (d.L < CG_MAX_LAYERS ? d.L : CG_MAX_LAYERS);
@@ -534,7 +537,7 @@ static hipError_t launch_decode_f(const Dims &d, const MaxTable &mt, DecArgs a, 
                         large = true;
                     }
                 }
-            if (small) {
+            if (small && (!large || blocks >= 16384)) {
                 a.nsym_hi = 16;
                 hipError_t e = launch_decode_s<S, FUSED, 4, NW, PAGED, true>(d, a, small_narrow, s);
                 if (e != hipSuccess || !large) return e;

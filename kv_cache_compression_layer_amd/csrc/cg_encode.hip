@@ -152,38 +152,44 @@ __device__ __forceinline__ int64_t tile_index(int j, int slab, int cb, int L, in
 // go to the tile's staging slot in global memory, row pos - 1, through a
 // buffer whose range is the slot (bytes past the slot are dropped; such a
 // stream is re-coded by k_fixup).
+// The coder tracks the LDS address of its next row, `la`, rather than the row
+// number (row = (la - lrow0) / kRowPitch), so a byte costs one min (clamp to
+// the spare row) and one compare (spill test) besides the write.
 constexpr int kRowPitch = 64;  // LDS stage row pitch in bytes
 
 template <int R>
 struct Coder {
     uint32_t low, range, pend;
-    int pos;          // row of the next byte (the placeholder is row 0)
+    uint32_t la;      // LDS byte address of the next byte's row for this lane
     uint32_t lrow0;   // LDS byte address of this lane's row 0
-    __device__ __forceinline__ void init(uint32_t lds_row0) {
+    uint32_t llast;   // LDS byte address of row R (the last row of the stage)
+    uint32_t sbase;   // LDS byte address of the stream's stage (lrow0 - lane), wave-uniform
+    __device__ __forceinline__ void init(uint32_t stream_base, int lane) {
         low = 0;
         range = 0xFFFFFFFFu;
         pend = 0;
-        pos = 0;
-        lrow0 = lds_row0;
+        sbase = stream_base;
+        lrow0 = stream_base + (uint32_t)lane;
+        la = lrow0;
+        llast = lrow0 + (uint32_t)R * kRowPitch;
     }
-    // Writes byte b at row p: the LDS stage (rows past R land in the spare
-    // row R + 1), and the global slot for rows past the stage, behind a
-    // wave-uniform test since few lanes get there.
-    __device__ __forceinline__ void put_at(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane, int p,
-                                           uint32_t b) {
-        lds[lrow0 + min(p, R + 1) * kRowPitch] = (uint8_t)b;
-        if (__builtin_amdgcn_ballot_w64(p > R)) {
+    __device__ __forceinline__ int pos() const { return (int)((la - lrow0) / kRowPitch); }
+    // Writes byte b at the next row: the LDS stage (rows past R land in the
+    // spare row R + 1), and the global slot for rows past the stage (row
+    // p goes to slot row p - 1), behind a wave-uniform test since few lanes
+    // get there.
+    __device__ __forceinline__ void put(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, uint32_t b) {
+        lds[min(la, llast + kRowPitch)] = (uint8_t)b;
+        if (__builtin_amdgcn_ballot_w64(la > llast)) {
             __asm__ volatile("" ::: "memory");
-            if (p > R) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, slot, (p - 1) * 64 + lane, 0, 0);
+            if (la > llast)
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, slot, (int)(la - sbase - kRowPitch), 0, 0);
         }
-    }
-    __device__ __forceinline__ void put(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane, uint32_t b) {
-        put_at(lds, slot, lane, pos, b);
-        ++pos;
+        la += kRowPitch;
     }
     __device__ __forceinline__ void carry_back(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
         uint32_t c = pend >> 8;
-        for (int k = min(pos, kStageBytes + 1) - 1; k >= 1 && c; --k) {
+        for (int k = min(pos(), kStageBytes + 1) - 1; k >= 1 && c; --k) {
             uint32_t v;
             if (k <= R) {
                 v = lds[lrow0 + k * kRowPitch] + c;
@@ -203,6 +209,14 @@ struct Coder {
             if (pend > 0xFFu) carry_back(lds, slot, lane);
         }
     }
+    // One byte shift: pend goes out, the top byte of low becomes pend.
+    __device__ __forceinline__ void shift(uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
+        settle(lds, slot, lane);
+        put(lds, slot, pend);
+        pend = low >> 24;
+        low <<= 8;
+        range <<= 8;
+    }
     __device__ __forceinline__ void step(uint32_t e, uint8_t *lds, __amdgpu_buffer_rsrc_t slot, int lane) {
         const uint32_t r = range >> 16;
         uint32_t nl;
@@ -211,22 +225,19 @@ struct Coder {
         pend += (uint32_t)c;  // at most one wrap between two shifts
         range = __umul24(r, e >> 16);
         // range >= 2^8 here (r >= 2^8, freq >= 1): one shift, or two when
-        // range < 2^16 (a rare symbol). Both are done at once: pend goes out,
-        // the top byte of low goes out too on a double shift (uniform branch),
-        // and the next byte of low becomes pend.
+        // range < 2^16 (a rare symbol), the second behind a wave-uniform
+        // branch. pend is at most 0xFF before the second, so it settles
+        // nothing.
         if (range < kTop) {
-            const bool two = range < (1u << 16);
-            settle(lds, slot, lane);
-            put_at(lds, slot, lane, pos, pend);
-            if (__builtin_amdgcn_ballot_w64(two)) {
+            shift(lds, slot, lane);
+            // Keep the shifted state in its registers: otherwise the second
+            // shift is rebuilt from the unshifted values (low << 16 ...) and
+            // the two paths merge through register copies.
+            __asm__ volatile("" : "+v"(low), "+v"(range), "+v"(pend), "+v"(la));
+            if (__builtin_amdgcn_ballot_w64(range < kTop)) {
                 __asm__ volatile("" ::: "memory");
-                if (two) put_at(lds, slot, lane, pos + 1, low >> 24);
+                if (range < kTop) shift(lds, slot, lane);
             }
-            const uint32_t sh = two ? 16u : 8u;
-            pend = __builtin_amdgcn_ubfe(low, 32 - sh, 8);
-            low <<= sh;
-            range <<= sh;
-            pos += two ? 2 : 1;
         }
     }
     // Final value: the smallest multiple of 2^24 >= low; returns the length.
@@ -237,9 +248,9 @@ struct Coder {
             b = 0;
         }
         if (pend > 0xFFu) carry_back(lds, slot, lane);
-        put(lds, slot, lane, pend);
-        if (b) put(lds, slot, lane, b);
-        return (uint32_t)(pos - 1);
+        put(lds, slot, pend);
+        if (b) put(lds, slot, b);
+        return (uint32_t)(pos() - 1);
     }
 };
 
@@ -334,7 +345,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
 
     Coder<R> cd[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) cd[s].init((uint32_t)((wv * S + s) * (R + 2) * kRowPitch + lane));
+    for (int s = 0; s < S; ++s) cd[s].init((uint32_t)((wv * S + s) * (R + 2) * kRowPitch), lane);
     const uint32_t amax = (uint32_t)W - 1;
     uint32_t qmax = 0;
     // Table entry of the next token of every stream, read one step ahead.

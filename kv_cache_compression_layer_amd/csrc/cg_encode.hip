@@ -523,8 +523,31 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
     const uint64_t base = a.chunk_off[tile / a.tiles_per_chunk] + a.tile_off[tile];
     const uint8_t *src = a.staging + tile * (kStageBytes * 64);
     bool over = base + total > a.cap;
-    if (total <= (uint32_t)(kLdsRows * 64)) {
-        // The encoder left the tile's bytes contiguous: copy them.
+    if (total <= (uint32_t)(kLdsRows * 64) && !over && ((uintptr_t)a.payload & 3u) == 0) {
+        // The encoder left the tile's bytes contiguous: copy them, whole
+        // destination dwords by dword stores (each assembled from the two
+        // aligned source dwords it straddles; the slot is 16 KiB aligned and
+        // far longer than the tile, so the second read stays inside it), and
+        // the at most three bytes at either end, which share their dwords
+        // with the neighbouring tiles, by byte stores.
+        const uint64_t end = base + total;
+        const uint64_t wa = (base + 3) & ~3ull, we = end & ~3ull;
+        const uint32_t *s32 = reinterpret_cast<const uint32_t *>(src);
+        if (wa >= we) {
+            if ((uint32_t)lane < total) a.payload[base + lane] = src[lane];
+        } else {
+            const uint32_t nhead = (uint32_t)(wa - base), ntail = (uint32_t)(end - we);
+            if ((uint32_t)lane < nhead) a.payload[base + lane] = src[lane];
+            if ((uint32_t)lane < ntail) a.payload[we + lane] = src[(uint32_t)(we - base) + lane];
+            uint32_t *d32 = reinterpret_cast<uint32_t *>(a.payload + wa);
+            const uint32_t nw = (uint32_t)((we - wa) >> 2);
+            for (uint32_t w = lane; w < nw; w += 64) {
+                const uint32_t so = nhead + 4 * w;  // source byte of the word
+                d32[w] = __builtin_amdgcn_alignbyte(s32[(so >> 2) + 1], s32[so >> 2], so & 3u);
+            }
+        }
+    } else if (total <= (uint32_t)(kLdsRows * 64)) {
+        // The same copy a byte at a time (capacity overflow, unaligned payload).
         uint32_t p = lane;
         for (; p + 192 < total; p += 256) {
             uint32_t b[4];

@@ -256,12 +256,13 @@ int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *sca
     const uint16_t *kv16 = reinterpret_cast<const uint16_t *>(kv);
     const bool qh = quantize_hist_fits(d, kv, sym);
     const bool fused = qh && quantize_hist_fuses_cdf(d, wire);
+    const bool packed = qh && encode_packs(d, mt);
     int rc = hip_rc(launch_fill_u32(status, 0u, (int64_t)((fused ? kWsAlign : w.clear_end) / 4), s));
     if (rc) return rc;
     if (wpre && (rc = hip_rc(launch_table_prefix(d, mt, wpre, s)))) return rc;
     if (qh) {
         rc = hip_rc(
-            launch_quantize_hist(d, mt, kv16, sym, scales, counts, fused ? wire : nullptr, wpre, status, s));
+            launch_quantize_hist(d, mt, kv16, sym, scales, counts, fused ? wire : nullptr, wpre, status, packed, s));
         if (rc) return rc;
     } else {
         if ((rc = hip_rc(launch_quantize(d, mt, kv16, sym, scales, status, s)))) return rc;
@@ -271,7 +272,7 @@ int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *sca
     EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
                 at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging),
                 at<uint64_t>(ws, w.scan)};
-    return hip_rc(launch_encode(d, mt, sym, nullptr, wire, wpre, o, ew, true, s));
+    return hip_rc(launch_encode(d, mt, sym, nullptr, wire, wpre, o, ew, true, packed, s));
 }
 
 // Workspace of a batch: the virtual call's workspace, then the virtual blob
@@ -477,7 +478,7 @@ int cg_encode(const cg_desc *desc, const uint8_t *sym, const int32_t *cdf, uint8
                 at<uint64_t>(ws, w.scan)};
     MaxTable mt;
     make_max_table(desc, d, mt);
-    return hip_rc(launch_encode(d, mt, sym, cdf, nullptr, nullptr, o, ew, false, s));
+    return hip_rc(launch_encode(d, mt, sym, cdf, nullptr, nullptr, o, ew, false, false, s));
 }
 
 int cg_decode(const cg_desc *desc, const uint8_t *payload, size_t payload_bytes,

@@ -192,7 +192,15 @@ hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv
 // lanes of an instruction hit distinct banks. Counts are added to the global
 // uint32 [2,L,C,A] table at the end (non-zero entries only). Symbols are
 // below A by construction.
-template <int NV, int LOGA>
+//
+// PACK: the symbols are written for the encoder in token groups instead of
+// [T][C] rows (T % 8 == 0). A slab whose symbols fit four bits (2M + 1 <= 16)
+// holds one dword per (8-token group g, channel c) at byte (g*C + c)*4, byte
+// j of which carries token 8g + j in its low nibble and token 8g + 4 + j in
+// its high nibble; the other slabs hold one dword per (4-token group, c), byte
+// j = token 4g + j. Each wave then quantises 8 consecutive rows per group and
+// assembles the dwords in registers.
+template <int NV, int LOGA, bool PACK>
 __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restrict__ kv,
                                                        uint8_t *__restrict__ sym,
                                                        uint16_t *__restrict__ scale,
@@ -229,7 +237,12 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
 #pragma unroll
         for (int i = 0; i < NV; ++i) v[i] = *reinterpret_cast<const uint4 *>(src + (i * 64 + lane) * 8);
     };
-    auto do_row = [&](int t, const uint4 (&v)[NV]) {
+    // Packed: pw[h][i*8 + e] collects rows 4h..4h+3 of the current 8-row
+    // group for channel (i*64 + lane)*8 + e, one byte per row.
+    uint32_t pw[2][NV * 8];
+    // gr: the row's place in its 8-row group (packed only; a constant after
+    // unrolling, so the word and byte it fills are fixed at compile time).
+    auto do_row = [&](int t, const uint4 (&v)[NV], int gr) {
         uint32_t am2 = 0;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
@@ -247,29 +260,87 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
                 qb[2 * j] = quant_bits(__uint_as_float(w[j] << 16), f, Mf);
                 qb[2 * j + 1] = quant_bits(__uint_as_float(w[j] & 0xFFFF0000u), f, Mf);
             }
-            const uint32_t lo = __builtin_amdgcn_perm(qb[1], qb[0], 0x0c0c0400u) |
-                                __builtin_amdgcn_perm(qb[3], qb[2], 0x04000c0cu);
-            const uint32_t hi = __builtin_amdgcn_perm(qb[5], qb[4], 0x0c0c0400u) |
-                                __builtin_amdgcn_perm(qb[7], qb[6], 0x04000c0cu);
-            *reinterpret_cast<uint2 *>(dst + (i * 64 + lane) * 8) = make_uint2(lo, hi);
+            if constexpr (PACK) {
+                // Byte t % 4 of the channel's dword takes this row's symbol
+                // (perm: selector 4 = byte 0 of qb, 0..3 = bytes of pw).
+                const int h = gr >> 2, r = gr & 3;
+                const uint32_t sel = (0x03020100u & ~(0xFFu << (8 * r))) | (4u << (8 * r));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pw[h][i * 8 + e] = __builtin_amdgcn_perm(qb[e], pw[h][i * 8 + e], sel);
+                    // Pin the word: otherwise the four permutes of a word are
+                    // recombined after the last row, holding every row's
+                    // symbols in registers until then.
+                    __asm__ volatile("" : "+v"(pw[h][i * 8 + e]));
+                }
+            } else {
+                const uint32_t lo = __builtin_amdgcn_perm(qb[1], qb[0], 0x0c0c0400u) |
+                                    __builtin_amdgcn_perm(qb[3], qb[2], 0x04000c0cu);
+                const uint32_t hi = __builtin_amdgcn_perm(qb[5], qb[4], 0x0c0c0400u) |
+                                    __builtin_amdgcn_perm(qb[7], qb[6], 0x04000c0cu);
+                *reinterpret_cast<uint2 *>(dst + (i * 64 + lane) * 8) = make_uint2(lo, hi);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) count(qb[e], i * 4 + e / 2, (e & 1) != 0);
         }
         if (lane == 0) scale[(int64_t)slab * T + t] = (uint16_t)am;
     };
 
-    int t = t0 + wv;
-    for (; t + 8 < t1; t += 16) {
-        uint4 va[NV], vb[NV];
-        load_row(t, va);
-        load_row(t + 8, vb);
-        do_row(t, va);
-        do_row(t + 8, vb);
-    }
-    if (t < t1) {
-        uint4 va[NV];
-        load_row(t, va);
-        do_row(t, va);
+    if constexpr (PACK) {
+        // Wave wv takes the 8-row groups t0 + 8*(wv + 8k) (t0 and t1 are
+        // multiples of 8).
+        const bool nib = 2 * M + 1 <= 16;
+#pragma unroll
+        for (int e = 0; e < NV * 8; ++e) pw[0][e] = pw[1][e] = 0;  // every byte is overwritten per group
+        for (int g0 = t0 + 8 * wv; g0 < t1; g0 += 64) {
+            // Four rows in flight at a time.
+#pragma unroll
+            for (int r = 0; r < 8; r += 4) {
+                uint4 va[NV], vb[NV], vc[NV], vd[NV];
+                load_row(g0 + r, va);
+                load_row(g0 + r + 1, vb);
+                load_row(g0 + r + 2, vc);
+                load_row(g0 + r + 3, vd);
+                do_row(g0 + r, va, r);
+                do_row(g0 + r + 1, vb, r + 1);
+                do_row(g0 + r + 2, vc, r + 2);
+                do_row(g0 + r + 3, vd, r + 3);
+            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                // Channels (i*64 + lane)*8 .. +8: 32 contiguous bytes per group row.
+                const int64_t col = (int64_t)(i * 64 + lane) * 8;
+                if (nib) {
+                    uint32_t w[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = pw[0][i * 8 + e] | (pw[1][i * 8 + e] << 4);
+                    uint4 *d4 = reinterpret_cast<uint4 *>(sym_slab + ((int64_t)(g0 >> 3) * C + col) * 4);
+                    d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                    d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        uint4 *d4 = reinterpret_cast<uint4 *>(sym_slab + ((int64_t)((g0 >> 2) + h) * C + col) * 4);
+                        d4[0] = make_uint4(pw[h][i * 8 + 0], pw[h][i * 8 + 1], pw[h][i * 8 + 2], pw[h][i * 8 + 3]);
+                        d4[1] = make_uint4(pw[h][i * 8 + 4], pw[h][i * 8 + 5], pw[h][i * 8 + 6], pw[h][i * 8 + 7]);
+                    }
+                }
+            }
+        }
+    } else {
+        int t = t0 + wv;
+        for (; t + 8 < t1; t += 16) {
+            uint4 va[NV], vb[NV];
+            load_row(t, va);
+            load_row(t + 8, vb);
+            do_row(t, va, 0);
+            do_row(t + 8, vb, 0);
+        }
+        if (t < t1) {
+            uint4 va[NV];
+            load_row(t, va);
+            do_row(t, va, 0);
+        }
     }
     __syncthreads();
 
@@ -344,7 +415,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
 }
 
 bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym) {
-    return (d.C == 512 || d.C == 1024) && d.A <= 32 && (uintptr_t)kv % 16 == 0 && (uintptr_t)sym % 8 == 0;
+    return (d.C == 512 || d.C == 1024) && d.A <= 32 && (uintptr_t)kv % 16 == 0 && (uintptr_t)sym % 16 == 0;
 }
 
 // Tokens per block: about 1024 blocks over the call, at most 32768 rows
@@ -363,16 +434,23 @@ bool quantize_hist_fuses_cdf(const Dims &d, const void *wire) {
 
 hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
                                 uint16_t *scale, uint32_t *counts, uint16_t *wire, const uint32_t *wpre,
-                                uint32_t *status, hipStream_t s) {
+                                uint32_t *status, bool packed, hipStream_t s) {
     const int64_t TT = quantize_hist_rows(d);
     if (wire && !quantize_hist_fuses_cdf(d, wire)) return hipErrorInvalidValue;
+    if (packed && d.T % 8 != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((d.T + TT - 1) / TT), (unsigned)(2 * d.L)), block(512);
     int loga = 2;
     while ((1 << loga) < d.A) ++loga;
     const int tt = (int)TT;
-#define CG_QH(NV, LG)                                                                                     \
-    hipLaunchKernelGGL((k_quantize_hist<NV, LG>), grid, block, 0, s, kv, sym, scale, counts, wire, wpre, status, \
-                       d.L, d.T, d.C, d.A, tt, mt)
+#define CG_QH(NV, LG)                                                                                       \
+    do {                                                                                                    \
+        if (packed)                                                                                         \
+            hipLaunchKernelGGL((k_quantize_hist<NV, LG, true>), grid, block, 0, s, kv, sym, scale, counts, wire, \
+                               wpre, status, d.L, d.T, d.C, d.A, tt, mt);                                   \
+        else                                                                                                \
+            hipLaunchKernelGGL((k_quantize_hist<NV, LG, false>), grid, block, 0, s, kv, sym, scale, counts, \
+                               wire, wpre, status, d.L, d.T, d.C, d.A, tt, mt);                             \
+    } while (0)
     if (d.C == 512) {
         switch (loga) {
         case 2: CG_QH(1, 2); break;

@@ -262,8 +262,12 @@ constexpr int kLdsRows = 28;  // LDS stage rows per stream (most streams fit)
 // TRUSTED: the symbols come from this library's quantiser, so every symbol
 // is at most 2M < bins <= W (the table width) and neither the clamp of the
 // table index nor the range check is needed.
-template <int S, int LOGA, int NW, bool TRUSTED>
+// PK: symbol layout. 0 = u8 [T][C] rows; 1 = nibble dwords of 8-token groups
+// and 2 = byte dwords of 4-token groups, as k_quantize_hist writes them for
+// slabs of at most 16 symbols and for the others (trusted symbols only).
+template <int S, int LOGA, int NW, bool TRUSTED, int PK>
 __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
+    static_assert(PK == 0 || TRUSTED, "packed symbols come from the quantiser");
     constexpr int R = kLdsRows;
     __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
     __shared__ __attribute__((aligned(16))) uint8_t stage[NW * S * (R + 2) * kRowPitch];  // [wave][stream][row][lane]
@@ -307,12 +311,30 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     // from kRing tokens before it is coded. Loads are unconditional (rows are
     // clamped into the stream) so their waits are exact.
     uint32_t ring[S][kRing];
+    // Packed symbols: a ring of RD dwords of TPD tokens each (KR tokens),
+    // group gb[s] + m in slot m; the stream's groups are gb[s] .. gb[s] + gl[s].
+    constexpr int TPD = PK == 1 ? 8 : 4;
+    constexpr int KR = PK == 1 ? 32 : 16;
+    constexpr int RD = KR / TPD;
+    uint32_t rd[S][RD];
+    int gb[S], gl[S];
+    if constexpr (PK == 0) {
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int last = max(n[s] - 1, 0);
+        for (int s = 0; s < S; ++s) {
+            const int last = max(n[s] - 1, 0);
 #pragma unroll
-        for (int k = 0; k < kRing; ++k) {
-            ring[s][k] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, col, (row0[s] + min(k, last)) * a.C, 0);
+            for (int k = 0; k < kRing; ++k) {
+                ring[s][k] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, col, (row0[s] + min(k, last)) * a.C, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            gb[s] = row0[s] / TPD;
+            gl[s] = max(n[s] / TPD - 1, 0);
+#pragma unroll
+            for (int m = 0; m < RD; ++m)
+                rd[s][m] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, col * 4, (gb[s] + min(m, gl[s])) * a.C * 4, 0);
         }
     }
 
@@ -359,6 +381,44 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
         if (TRUSTED) return *reinterpret_cast<const uint32_t *>(tabb + __builtin_amdgcn_perm(q, lane4, 0x0c0c0400u));
         return tab[min(q, amax) * 64 + lane];
     };
+    // Packed: table entry of token p of a group dword w. Byte layout: byte p
+    // goes next to lane4 by one permute; nibble layout: token p sits at bit
+    // 8 * (p % 4) + 4 * (p / 4) and is shifted to bits 8..11.
+    auto pentry = [&](uint32_t w, int p) -> uint32_t {
+        uint32_t ad;
+        if constexpr (PK == 2) {
+            ad = __builtin_amdgcn_perm(w, lane4, 0x0c0c0000u | ((4u + (uint32_t)p) << 8));
+        } else {
+            const int b = 8 * (p & 3) + 4 * (p >> 2);
+            ad = ((b >= 8 ? w >> (b - 8) : w << (8 - b)) & 0xF00u) | lane4;
+        }
+        return *reinterpret_cast<const uint32_t *>(tabb + ad);
+    };
+    if constexpr (PK != 0) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) e_next[s] = pentry(rd[s][0], 0);
+        for (int t0 = 0; t0 < nmax; t0 += KR) {
+#pragma unroll
+            for (int k = 0; k < KR; ++k) {
+                const int t = t0 + k;
+                uint32_t e[S];
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    e[s] = e_next[s];
+                    if (k % TPD == TPD - 1) {
+                        // Group k / TPD is used up: its slot takes the group RD ahead.
+                        const int m = k / TPD;
+                        rd[s][m] = __builtin_amdgcn_raw_buffer_load_b32(
+                            srsrc, col * 4, (gb[s] + min(t0 / TPD + m + RD, gl[s])) * a.C * 4, 0);
+                    }
+                    e_next[s] = pentry(rd[s][((k + 1) / TPD) % RD], (k + 1) % TPD);
+                }
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                    if (t < n[s]) cd[s].step(e[s], stage, slot[s], lane);
+            }
+        }
+    } else {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         if (!TRUSTED) qmax = max(qmax, ring[s][0]);
@@ -384,6 +444,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
             for (int s = 0; s < S; ++s)
                 if (t < n[s]) cd[s].step(e[s], stage, slot[s], lane);
         }
+    }
     }
 
 #pragma unroll
@@ -597,6 +658,7 @@ struct FixupArgs {
     uint64_t cap;
     int L, T, C, A, CB;
     MaxTable mt;
+    bool packed;  // symbols in the quantiser's packed layout (PK 1 or 2 by slab)
 };
 
 __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
@@ -614,13 +676,28 @@ __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
         const uint32_t len = active ? a.lengths[js * a.C + c] : 0u;
         const uint32_t incl = wave_incl_scan_u32(len, lane);
         if (!active) continue;
-        const int W = layer_w(a.mt, slab >= a.L ? 1 : 0, slab >= a.L ? slab - a.L : slab);
+        const int kvs = slab >= a.L ? 1 : 0, ls = slab - kvs * a.L;
+        const int W = layer_w(a.mt, kvs, ls);
+        const bool nib = 2 * layer_m(a.mt, kvs, ls) + 1 <= 16;
         const uint8_t *sp = a.sym + ((int64_t)slab * a.T + (int64_t)j * kChunk) * a.C + c;
+        const uint8_t *slab_sym = a.sym + (int64_t)slab * a.T * a.C;
         RcEncHold enc;
         enc.init();
         GlobalSink sink{a.payload, a.chunk_off[j] + a.tile_off[tile] + incl - len, a.cap, 0u, false};
         for (int t = 0; t < n; ++t) {
-            const uint32_t s = min((uint32_t)sp[(int64_t)t * a.C], (uint32_t)W - 1);
+            uint32_t q;
+            if (!a.packed) {
+                q = sp[(int64_t)t * a.C];
+            } else {
+                const int tt = j * kChunk + t;
+                if (nib) {
+                    const uint8_t b = slab_sym[((int64_t)(tt >> 3) * a.C + c) * 4 + (tt & 3)];
+                    q = (tt & 4) ? b >> 4 : b & 0xFu;
+                } else {
+                    q = slab_sym[((int64_t)(tt >> 2) * a.C + c) * 4 + (tt & 3)];
+                }
+            }
+            const uint32_t s = min(q, (uint32_t)W - 1);
             uint32_t lo, hi;
             cdf_bounds(a.cdf, a.cdf16, a.wpre, slab, a.C, c, a.A, W, (int)s, lo, hi);
             const uint32_t f = hi > lo ? hi - lo : 1u;
@@ -635,10 +712,45 @@ __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
 
 size_t encode_staging_bytes(const Dims &d) { return (size_t)d.tiles * kStageBytes * 64; }
 
+// Launch shape of k_encode: S chunks per lane, NW waves per block, and
+// whether the call has slabs of at most 16 symbols (small) and others (large).
+struct EncPlan {
+    int S, NW, loga;
+    unsigned blocks;
+    bool small, large;
+};
+
+static EncPlan enc_plan(const Dims &d, const MaxTable &mt) {
+    EncPlan p;
+    p.S = d.NC >= 2 ? 2 : 1;
+    // Four waves per block share a table when there are enough chunks.
+    p.NW = d.NC >= 8 ? 4 : 1;
+    const int ngroups = (d.NC + p.S * p.NW - 1) / (p.S * p.NW);
+    p.blocks = (unsigned)((int64_t)ngroups * 2 * d.L * d.CB);
+    p.loga = 4;
+    while ((1 << p.loga) < d.A) ++p.loga;
+    p.small = p.large = false;
+    const int nl = mt.lper ? (int)mt.lper : (d.L < CG_MAX_LAYERS ? d.L : CG_MAX_LAYERS);
+    for (int kv = 0; kv < 2; ++kv)
+        for (int l = 0; l < nl; ++l) (2 * (mt.bins[kv][l] / 2 - 1) + 1 <= 16 ? p.small : p.large) = true;
+    return p;
+}
+
+// Slabs of both kinds share a launch only for small grids; otherwise every
+// trusted launch sees one kind, so one packed layout.
+static bool enc_split(const EncPlan &p) { return p.loga > 4 && p.small && (!p.large || p.blocks >= 16384); }
+
+bool encode_packs(const Dims &d, const MaxTable &mt) {
+    const EncPlan p = enc_plan(d, mt);
+    return d.T % 8 == 0 && (!(p.small && p.large) || enc_split(p));
+}
+
 hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, const int32_t *cdf,
                          const uint16_t *cdf16, const uint32_t *wpre, const EncodeOut &o, const EncodeWs &w,
-                         bool trusted, hipStream_t s) {
-    const int S = d.NC >= 2 ? 2 : 1;
+                         bool trusted, bool packed, hipStream_t s) {
+    const EncPlan plan = enc_plan(d, mt);
+    if (packed && (!trusted || !encode_packs(d, mt))) return hipErrorInvalidValue;
+    const int S = plan.S;
     EncArgs a;
     a.sym = sym;
     a.cdf = cdf;
@@ -656,17 +768,17 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     a.A = d.A;
     a.NC = d.NC;
     a.CB = d.CB;
-    // Four waves per block share a table when there are enough chunks.
-    const int NW = d.NC >= 8 ? 4 : 1;
-    const int ngroups = (d.NC + S * NW - 1) / (S * NW);
-    const unsigned blocks = (unsigned)((int64_t)ngroups * 2 * d.L * d.CB);
+    const int NW = plan.NW;
+    const unsigned blocks = plan.blocks;
     const dim3 grid(blocks), block(64 * NW);
-    int loga = 4;
-    while ((1 << loga) < d.A) ++loga;
+    const int loga = plan.loga;
+    // Packed symbols: nibbles in the 16-entry launch (slabs of at most 16
+    // symbols), bytes in the wider one.
 #define CG_ENC(SS, LG, W)                                                                           \
     do {                                                                                            \
-        if (trusted) hipLaunchKernelGGL((k_encode<SS, LG, W, true>), grid, block, 0, s, a);         \
-        else hipLaunchKernelGGL((k_encode<SS, LG, W, false>), grid, block, 0, s, a);                \
+        if (!trusted) hipLaunchKernelGGL((k_encode<SS, LG, W, false, 0>), grid, block, 0, s, a);    \
+        else if (!packed) hipLaunchKernelGGL((k_encode<SS, LG, W, true, 0>), grid, block, 0, s, a); \
+        else hipLaunchKernelGGL((k_encode<SS, LG, W, true, (LG <= 4 ? 1 : 2)>), grid, block, 0, s, a); \
     } while (0)
 #define CG_ENC_A(SS, W, LOGA_)                    \
     do {                                          \
@@ -685,13 +797,10 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     // symbols the slabs of at most 16 symbols (16-bin layers) take a launch
     // with 16-entry tables, whose blocks need half the LDS and fit the CU
     // more densely; the other slabs take the full width.
-    bool small = false, large = false;
-    const int nl = mt.lper ? (int)mt.lper : (d.L < CG_MAX_LAYERS ? d.L : CG_MAX_LAYERS);
-    for (int kv = 0; kv < 2; ++kv)
-        for (int l = 0; l < nl; ++l) (2 * (mt.bins[kv][l] / 2 - 1) + 1 <= 16 ? small : large) = true;
+    const bool large = plan.large;
     hipError_t e;
     // Only worth a second launch when the grid is large (big calls, batches).
-    if (trusted && loga > 4 && small && (!large || blocks >= 16384)) {
+    if (trusted && enc_split(plan)) {
         a.nsym_lo = 0;
         a.nsym_hi = 16;
         if ((e = launch(4)) != hipSuccess) return e;
@@ -759,6 +868,7 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     fa.C = d.C;
     fa.A = d.A;
     fa.CB = d.CB;
+    fa.packed = packed;
     hipLaunchKernelGGL(k_fixup, dim3(256), dim3(64), 0, s, fa);
     return hipGetLastError();
 }

@@ -95,9 +95,11 @@ hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts,
 // u16 CDF tables itself: pass `wire` and no counts are written (nor read).
 bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym);
 bool quantize_hist_fuses_cdf(const Dims &d, const void *wire);
+// packed: write the symbols in the encoder's packed layout (T % 8 == 0; see
+// k_quantize_hist), as encode_packs() decides.
 hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
                                 uint16_t *scale, uint32_t *counts, uint16_t *wire, const uint32_t *wpre,
-                                uint32_t *status, hipStream_t s);
+                                uint32_t *status, bool packed, hipStream_t s);
 
 // Table placement: table (slab, c) of width W = layer_w starts at entry
 // wpre[slab] * C + c * W of the u16 wire section; wpre[2L] = the section's
@@ -157,9 +159,15 @@ size_t encode_staging_bytes(const Dims &d);
 // entry A taken as 2^16); exactly one is set. trusted: the symbols come from
 // this library's quantiser (all below A), so the encoder skips its range
 // check.
+// packed: the symbols are in the quantiser's packed layout (only with
+// trusted symbols, and only where encode_packs() holds).
 hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, const int32_t *cdf32,
                          const uint16_t *cdf16, const uint32_t *wpre, const EncodeOut &o, const EncodeWs &w,
-                         bool trusted, hipStream_t s);
+                         bool trusted, bool packed, hipStream_t s);
+
+// Whether the trusted encoder can read packed symbols for this call: every
+// launch sees slabs of one kind (at most 16 symbols, or more) and T % 8 == 0.
+bool encode_packs(const Dims &d, const MaxTable &mt);
 
 // Decoder table source: int32 [2,L,C,A+1] or the u16 wire form [2,L,C,A].
 struct DecodeIn {

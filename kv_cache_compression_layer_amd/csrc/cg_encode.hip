@@ -254,7 +254,13 @@ struct Coder {
     }
 };
 
-constexpr int kLdsRows = 28;  // LDS stage rows per stream (most streams fit)
+// LDS stage rows per stream: 44 in four-wave blocks with tables wider than
+// 16 entries (longer streams, which would otherwise spill to the slot), 28
+// elsewhere (the 16-bin slabs' short streams, and one-wave blocks of short
+// calls, whose residency the LDS decides).
+constexpr int kLdsRows = 28;
+constexpr int kLdsRowsWide = 44;
+__host__ __device__ constexpr int enc_rows(int loga, int nw) { return loga >= 5 && nw >= 4 ? kLdsRowsWide : kLdsRows; }
 
 // Block of NW waves for one (K|V, layer, 64-channel block); wave w codes the
 // S chunks (group * NW + w) * S + s, lane = channel, with the table the
@@ -268,7 +274,7 @@ constexpr int kLdsRows = 28;  // LDS stage rows per stream (most streams fit)
 template <int S, int LOGA, int NW, bool TRUSTED, int PK>
 __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     static_assert(PK == 0 || TRUSTED, "packed symbols come from the quantiser");
-    constexpr int R = kLdsRows;
+    constexpr int R = enc_rows(LOGA, NW);
     __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
     __shared__ __attribute__((aligned(16))) uint8_t stage[NW * S * (R + 2) * kRowPitch];  // [wave][stream][row][lane]
     const int lane = threadIdx.x & 63;
@@ -568,6 +574,10 @@ struct CompactArgs {
     uint32_t *status;
     int L, C, CB;
     int64_t tiles_per_chunk;
+    // LDS stage rows the encoder used for slabs of at most 16 symbols and for
+    // the others (they decide which tiles it gathered).
+    int rows_small, rows_large;
+    MaxTable mt;
 };
 
 __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
@@ -576,6 +586,8 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
     const int cb = (int)(tile % a.CB);
     const int64_t js = tile / a.CB;  // j * 2L + slab
     const int c = cb * 64 + lane;
+    const int slab = (int)(js % (2 * a.L)), kvs = slab >= a.L ? 1 : 0;
+    const uint32_t rows = 2 * layer_m(a.mt, kvs, slab - kvs * a.L) + 1 <= 16 ? a.rows_small : a.rows_large;
     const uint32_t len = c < a.C ? a.lengths[js * a.C + c] : 0u;
     if (__ballot(len > (uint32_t)kStageBytes)) return;  // k_fixup writes this tile
     const uint32_t incl = wave_incl_scan_u32(len, lane);
@@ -584,7 +596,7 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
     const uint64_t base = a.chunk_off[tile / a.tiles_per_chunk] + a.tile_off[tile];
     const uint8_t *src = a.staging + tile * (kStageBytes * 64);
     bool over = base + total > a.cap;
-    if (total <= (uint32_t)(kLdsRows * 64) && !over && ((uintptr_t)a.payload & 3u) == 0) {
+    if (total <= rows * 64 && !over && ((uintptr_t)a.payload & 3u) == 0) {
         // The encoder left the tile's bytes contiguous: copy them, whole
         // destination dwords by dword stores (each assembled from the two
         // aligned source dwords it straddles; the slot is 16 KiB aligned and
@@ -607,7 +619,7 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
                 d32[w] = __builtin_amdgcn_alignbyte(s32[(so >> 2) + 1], s32[so >> 2], so & 3u);
             }
         }
-    } else if (total <= (uint32_t)(kLdsRows * 64)) {
+    } else if (total <= rows * 64) {
         // The same copy a byte at a time (capacity overflow, unaligned payload).
         uint32_t p = lane;
         for (; p + 192 < total; p += 256) {
@@ -847,6 +859,12 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     ca.C = d.C;
     ca.CB = d.CB;
     ca.tiles_per_chunk = tpc;
+    // The launches of the encoder above: with the split, slabs of at most 16
+    // symbols took 16-entry tables; otherwise every slab took 2^loga.
+    const bool split = trusted && enc_split(plan);
+    ca.rows_small = split ? enc_rows(4, NW) : enc_rows(loga, NW);
+    ca.rows_large = enc_rows(loga, NW);
+    ca.mt = mt;
     hipLaunchKernelGGL(k_compact, dim3((unsigned)d.tiles), dim3(64), 0, s, ca);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 

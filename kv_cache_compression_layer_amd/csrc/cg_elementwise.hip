@@ -261,7 +261,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
                 qb[2 * j + 1] = quant_bits(__uint_as_float(w[j] & 0xFFFF0000u), f, Mf);
             }
             if constexpr (PACK) {
-                // Byte t % 4 of the channel's dword takes this row's symbol
+                // Byte gr % 4 of the channel's dword takes this row's symbol
                 // (perm: selector 4 = byte 0 of qb, 0..3 = bytes of pw).
                 const int h = gr >> 2, r = gr & 3;
                 const uint32_t sel = (0x03020100u & ~(0xFFu << (8 * r))) | (4u << (8 * r));

@@ -18,9 +18,11 @@
 // two chunks per lane interleaved (independent dependency chains). The
 // waves share one table per lane in LDS, start | freq << 16 laid out
 // [symbol][lane] (no bank conflicts whatever the symbols). Symbols come
-// straight from global memory (64 lanes read one 64-byte row per load) into
-// a 16-deep register ring, so the loop never waits on them. Bytes are
-// written as soon as they are shifted out into an LDS stage per stream
+// straight from global memory into a register ring of prefetches, so the
+// loop never waits on them: from [T][C] byte rows (64 lanes read one 64-byte
+// row per load), or, in cg_to_bytes, from the quantiser's packed layout (one
+// dword per lane per 8 tokens as nibbles, or per 4 tokens as bytes). Bytes
+// are written as soon as they are shifted out into an LDS stage per stream
 // ([row][lane]); rows past the stage spill to the tile's 16 KiB staging slot
 // in global memory. At the end the wave gathers the tile's streams in
 // stream order into the slot, contiguously, and writes the stream lengths

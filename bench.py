@@ -49,6 +49,8 @@ def parse_args():
                     help="skip the 256-token-chunk batch measurement (e.g. under a profiler)")
     ap.add_argument("--no-streaming", action="store_true",
                     help="skip the pipelined host-to-device load measurement")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the encode/decode timing of the other model-shaped workloads")
     ap.add_argument("--cpu-sample-layers", type=int, default=8)
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
@@ -93,6 +95,65 @@ def recorded_traffic(workload):
                 if kv.get("workload") == workload and kv.get("source_sha256") == sha:
                     return int(kv["bytes_per_launch"]), os.path.relpath(path, ROOT)
     return None
+
+
+def other_workloads(torch, cgb, dev, skip):
+    """Whole-blob encode and decode times of the other model-shaped workloads
+    (one call each, inputs resident on the device, HIP events on the current
+    stream): OPT-125m at 64 tokens (latency), Mistral-7B at 256 and 768
+    tokens, GLM-4-9B at 16K tokens (its decode from a blob encoded before the
+    timed region). Medians over the repetitions."""
+    from kv_cache_compression_layer_amd.synth import WORKLOADS, generate_workload
+
+    out = {}
+    for name, reps in (("opt125m_t64", 100), ("mistral7b_t256", 100), ("mistral7b_t768", 100),
+                       ("glm4_9b_t16k", 10)):
+        if name == skip:
+            continue
+        w = WORKLOADS[name]
+        kv = torch.from_numpy(generate_workload(w).view(np.int16)).to(dev).view(torch.bfloat16)
+        desc = cgb.Desc.for_kv(tuple(kv.shape))
+        blob = torch.empty(cgb.cg_blob_bound(desc), dtype=torch.uint8, device=dev)
+        size_dev = torch.zeros(1, dtype=torch.int64, device=dev)
+        ws_e = cgb.alloc_workspace(desc, cgb.CG_OP_TO_BYTES, dev)
+        ws_d = cgb.alloc_workspace(desc, cgb.CG_OP_FROM_BYTES, dev)
+        kv_out = torch.empty_like(kv)
+
+        def enc():
+            cgb.cg_to_bytes(desc, kv, blob, size_dev, ws_e)
+
+        enc()
+        cgb.check_status(ws_e, what=f"cg_to_bytes {name}")
+        nbytes = int(size_dev.item())
+
+        def dec():
+            cgb.cg_from_bytes(desc, blob, nbytes, kv_out, ws_d)
+
+        dec()
+        cgb.check_status(ws_d, what=f"cg_from_bytes {name}")
+
+        def med(fn):
+            for _ in range(max(3, reps // 5)):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            torch.cuda.synchronize()
+            ev[0].record()
+            for i in range(reps):
+                fn()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
+        enc_ms, dec_ms = med(enc), med(dec)
+        raw = kv.numel() * 2
+        out[name] = {"shape": list(kv.shape), "raw_bytes": raw, "blob_bytes": nbytes,
+                     "compression_ratio": raw / nbytes, "encode_ms": enc_ms, "decode_ms": dec_ms,
+                     "encode_GBps": raw / (enc_ms * 1e-3) / 1e9, "decode_GBps": raw / (dec_ms * 1e-3) / 1e9,
+                     "reps": reps}
+        log(f"{name}: {json.dumps({k: v for k, v in out[name].items() if k != 'shape'})}")
+        del kv, blob, ws_e, ws_d, kv_out
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, layers):
@@ -508,6 +569,8 @@ def main():
     }
 
     del sym, sym2, kv_out2, payload
+    if not args.no_other_workloads:
+        result["other_workloads"] = other_workloads(torch, cgb, dev, w.name)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample_layers} layers")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_layers)

@@ -185,8 +185,8 @@ hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv
 // The to_bytes path quantises and counts in one pass, so the symbols are
 // not read back for the histogram. A block of 8 waves owns a tile of TT
 // rows (tokens) of one (K|V, layer); each wave quantises two rows at a time
-// exactly as k_quantize_vec does. Lane l always holds the same 8*NV channels
-// ((i*64 + l)*8 + e), so the block keeps lane-column counters in LDS,
+// exactly as k_quantize_vec does. Lane l always holds the same CW*NV channels
+// ((i*64 + l)*CW + e), so the block keeps lane-column counters in LDS,
 // uint32 [symbol][pair][lane] with the counts of channels e and e+1 of a
 // pair in the low and high halves (TT <= 65535 keeps them in 16 bits); all
 // lanes of an instruction hit distinct banks. Counts are added to the global
@@ -200,7 +200,11 @@ hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv
 // its high nibble; the other slabs hold one dword per (4-token group, c), byte
 // j = token 4g + j. Each wave then quantises 8 consecutive rows per group and
 // assembles the dwords in registers.
-template <int NV, int LOGA, bool PACK>
+//
+// CW: channels per lane and load (8: 16-byte loads, C = 512 or 1024; 4:
+// 8-byte loads, C = 256 or 768); a lane holds channels (i*64 + lane)*CW + e,
+// i < NV, e < CW.
+template <int NV, int CW, int LOGA, bool PACK>
 __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restrict__ kv,
                                                        uint8_t *__restrict__ sym,
                                                        uint16_t *__restrict__ scale,
@@ -210,7 +214,8 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
                                                        uint32_t *__restrict__ status, int L, int T,
                                                        int C, int A, int TT, MaxTable mt) {
     constexpr int NS = 1 << LOGA;
-    constexpr int NP = NV * 4;  // channel pairs per lane
+    constexpr int NWD = CW / 2;      // 32-bit words (two bf16) per load
+    constexpr int NP = NV * NWD;     // channel pairs per lane
     __shared__ __attribute__((aligned(16))) uint32_t hist[NS * NP * 64];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -232,33 +237,45 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
         uint32_t *cnt = reinterpret_cast<uint32_t *>(hb + q * (NP * 256) + lane4 + pair * 256);
         __hip_atomic_fetch_add(cnt, odd ? 0x10000u : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
-    auto load_row = [&](int t, uint4 (&v)[NV]) {
+    auto load_row = [&](int t, uint32_t (&v)[NV][NWD]) {
         const uint16_t *src = kv_slab + (int64_t)t * C;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) v[i] = *reinterpret_cast<const uint4 *>(src + (i * 64 + lane) * 8);
+        for (int i = 0; i < NV; ++i) {
+            if constexpr (CW == 8) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(src + (i * 64 + lane) * 8);
+                v[i][0] = x.x;
+                v[i][1] = x.y;
+                v[i][2] = x.z;
+                v[i][3] = x.w;
+            } else {
+                const uint2 x = *reinterpret_cast<const uint2 *>(src + (i * 64 + lane) * 4);
+                v[i][0] = x.x;
+                v[i][1] = x.y;
+            }
+        }
     };
-    // Packed: pw[h][i*8 + e] collects rows 4h..4h+3 of the current 8-row
-    // group for channel (i*64 + lane)*8 + e, one byte per row.
-    uint32_t pw[2][NV * 8];
+    // Packed: pw[h][i*CW + e] collects rows 4h..4h+3 of the current 8-row
+    // group for channel (i*64 + lane)*CW + e, one byte per row.
+    uint32_t pw[2][NV * CW];
     // gr: the row's place in its 8-row group (packed only; a constant after
     // unrolling, so the word and byte it fills are fixed at compile time).
-    auto do_row = [&](int t, const uint4 (&v)[NV], int gr) {
+    auto do_row = [&](int t, const uint32_t (&v)[NV][NWD], int gr) {
         uint32_t am2 = 0;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            am2 = absmax2(absmax2(absmax2(absmax2(am2, v[i].x), v[i].y), v[i].z), v[i].w);
+#pragma unroll
+            for (int j = 0; j < NWD; ++j) am2 = absmax2(am2, v[i][j]);
         const uint32_t am = wave_max_dpp(max(am2 & 0xFFFFu, am2 >> 16));
         if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
         const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
         uint8_t *dst = sym_slab + (int64_t)t * C;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-            uint32_t qb[8];
+            uint32_t qb[CW];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                qb[2 * j] = quant_bits(__uint_as_float(w[j] << 16), f, Mf);
-                qb[2 * j + 1] = quant_bits(__uint_as_float(w[j] & 0xFFFF0000u), f, Mf);
+            for (int j = 0; j < NWD; ++j) {
+                qb[2 * j] = quant_bits(__uint_as_float(v[i][j] << 16), f, Mf);
+                qb[2 * j + 1] = quant_bits(__uint_as_float(v[i][j] & 0xFFFF0000u), f, Mf);
             }
             if constexpr (PACK) {
                 // Byte gr % 4 of the channel's dword takes this row's symbol
@@ -266,22 +283,26 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
                 const int h = gr >> 2, r = gr & 3;
                 const uint32_t sel = (0x03020100u & ~(0xFFu << (8 * r))) | (4u << (8 * r));
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pw[h][i * 8 + e] = __builtin_amdgcn_perm(qb[e], pw[h][i * 8 + e], sel);
+                for (int e = 0; e < CW; ++e) {
+                    pw[h][i * CW + e] = __builtin_amdgcn_perm(qb[e], pw[h][i * CW + e], sel);
                     // Pin the word: otherwise the four permutes of a word are
                     // recombined after the last row, holding every row's
                     // symbols in registers until then.
-                    __asm__ volatile("" : "+v"(pw[h][i * 8 + e]));
+                    __asm__ volatile("" : "+v"(pw[h][i * CW + e]));
                 }
             } else {
                 const uint32_t lo = __builtin_amdgcn_perm(qb[1], qb[0], 0x0c0c0400u) |
                                     __builtin_amdgcn_perm(qb[3], qb[2], 0x04000c0cu);
-                const uint32_t hi = __builtin_amdgcn_perm(qb[5], qb[4], 0x0c0c0400u) |
-                                    __builtin_amdgcn_perm(qb[7], qb[6], 0x04000c0cu);
-                *reinterpret_cast<uint2 *>(dst + (i * 64 + lane) * 8) = make_uint2(lo, hi);
+                if constexpr (CW == 8) {
+                    const uint32_t hi = __builtin_amdgcn_perm(qb[5], qb[4], 0x0c0c0400u) |
+                                        __builtin_amdgcn_perm(qb[7], qb[6], 0x04000c0cu);
+                    *reinterpret_cast<uint2 *>(dst + (i * 64 + lane) * 8) = make_uint2(lo, hi);
+                } else {
+                    *reinterpret_cast<uint32_t *>(dst + (i * 64 + lane) * 4) = lo;
+                }
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) count(qb[e], i * 4 + e / 2, (e & 1) != 0);
+            for (int e = 0; e < CW; ++e) count(qb[e], i * NWD + e / 2, (e & 1) != 0);
         }
         if (lane == 0) scale[(int64_t)slab * T + t] = (uint16_t)am;
     };
@@ -291,12 +312,12 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
         // multiples of 8).
         const bool nib = 2 * M + 1 <= 16;
 #pragma unroll
-        for (int e = 0; e < NV * 8; ++e) pw[0][e] = pw[1][e] = 0;  // every byte is overwritten per group
+        for (int e = 0; e < NV * CW; ++e) pw[0][e] = pw[1][e] = 0;  // every byte is overwritten per group
         for (int g0 = t0 + 8 * wv; g0 < t1; g0 += 64) {
             // Four rows in flight at a time.
 #pragma unroll
             for (int r = 0; r < 8; r += 4) {
-                uint4 va[NV], vb[NV], vc[NV], vd[NV];
+                uint32_t va[NV][NWD], vb[NV][NWD], vc[NV][NWD], vd[NV][NWD];
                 load_row(g0 + r, va);
                 load_row(g0 + r + 1, vb);
                 load_row(g0 + r + 2, vc);
@@ -308,21 +329,23 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
             }
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                // Channels (i*64 + lane)*8 .. +8: 32 contiguous bytes per group row.
-                const int64_t col = (int64_t)(i * 64 + lane) * 8;
+                // Channels (i*64 + lane)*CW .. +CW: 4*CW contiguous bytes per group row.
+                const int64_t col = (int64_t)(i * 64 + lane) * CW;
                 if (nib) {
-                    uint32_t w[8];
+                    uint32_t w[CW];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) w[e] = pw[0][i * 8 + e] | (pw[1][i * 8 + e] << 4);
+                    for (int e = 0; e < CW; ++e) w[e] = pw[0][i * CW + e] | (pw[1][i * CW + e] << 4);
                     uint4 *d4 = reinterpret_cast<uint4 *>(sym_slab + ((int64_t)(g0 >> 3) * C + col) * 4);
-                    d4[0] = make_uint4(w[0], w[1], w[2], w[3]);
-                    d4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+#pragma unroll
+                    for (int u = 0; u < CW / 4; ++u) d4[u] = make_uint4(w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]);
                 } else {
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         uint4 *d4 = reinterpret_cast<uint4 *>(sym_slab + ((int64_t)((g0 >> 2) + h) * C + col) * 4);
-                        d4[0] = make_uint4(pw[h][i * 8 + 0], pw[h][i * 8 + 1], pw[h][i * 8 + 2], pw[h][i * 8 + 3]);
-                        d4[1] = make_uint4(pw[h][i * 8 + 4], pw[h][i * 8 + 5], pw[h][i * 8 + 6], pw[h][i * 8 + 7]);
+#pragma unroll
+                        for (int u = 0; u < CW / 4; ++u)
+                            d4[u] = make_uint4(pw[h][i * CW + 4 * u], pw[h][i * CW + 4 * u + 1],
+                                               pw[h][i * CW + 4 * u + 2], pw[h][i * CW + 4 * u + 3]);
                     }
                 }
             }
@@ -330,14 +353,14 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
     } else {
         int t = t0 + wv;
         for (; t + 8 < t1; t += 16) {
-            uint4 va[NV], vb[NV];
+            uint32_t va[NV][NWD], vb[NV][NWD];
             load_row(t, va);
             load_row(t + 8, vb);
             do_row(t, va, 0);
             do_row(t + 8, vb, 0);
         }
         if (t < t1) {
-            uint4 va[NV];
+            uint32_t va[NV][NWD];
             load_row(t, va);
             do_row(t, va, 0);
         }
@@ -379,7 +402,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
         uint16_t *wl = reinterpret_cast<uint16_t *>(hist);
         if (col < NCOL) {
             const int pr = col / 64, ln = col % 64;
-            const int c = ((pr / 4) * 64 + ln) * 8 + (pr % 4) * 2;
+            const int c = ((pr / NWD) * 64 + ln) * CW + (pr % NWD) * 2;
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
                 if (q < W) {
@@ -390,7 +413,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
         }
         if (__ballot(bad) && lane == 0) atomicOr(status, kStCorrupt);
         __syncthreads();
-        // C is 512 or 1024, so the slab's C * W entries and its offset
+        // C is a multiple of 256, so the slab's C * W entries and its offset
         // wpre[slab] * C are whole 16-byte units.
         const uint4 *src4 = reinterpret_cast<const uint4 *>(hist);
         uint4 *dst4 = reinterpret_cast<uint4 *>(wire + (wpre ? (int64_t)wpre[slab] : (int64_t)slab * A) * C);
@@ -403,7 +426,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
         const uint32_t v = hist[wi];
         if (!v) continue;
         const int s = wi / (NP * 64), pr = (wi / 64) % NP, ln = wi % 64;
-        const int c = ((pr / 4) * 64 + ln) * 8 + (pr % 4) * 2;
+        const int c = ((pr / NWD) * 64 + ln) * CW + (pr % NWD) * 2;
         if (s >= A) {
             atomicOr(status, kStCorrupt);
             continue;
@@ -414,10 +437,6 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
     }
 }
 
-bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym) {
-    return (d.C == 512 || d.C == 1024) && d.A <= 32 && (uintptr_t)kv % 16 == 0 && (uintptr_t)sym % 16 == 0;
-}
-
 // Tokens per block: about 1024 blocks over the call, at most 32768 rows
 // (16-bit counters).
 static int64_t quantize_hist_rows(const Dims &d) {
@@ -426,6 +445,15 @@ static int64_t quantize_hist_rows(const Dims &d) {
     if (TT < 256) TT = 256;
     if (TT > 32768) TT = 32768;
     return TT;
+}
+
+// Calls too small to give the fused kernel 64 blocks (a few layers of a
+// few tokens) run faster as one wave per row in k_quantize_vec plus the
+// separate histogram (OPT-125m at 64 tokens: 73 vs 83 us).
+bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym) {
+    const int64_t TT = quantize_hist_rows(d);
+    return (d.C == 256 || d.C == 512 || d.C == 768 || d.C == 1024) && d.A <= 32 && (uintptr_t)kv % 16 == 0 &&
+           (uintptr_t)sym % 16 == 0 && 2 * (int64_t)d.L * ((d.T + TT - 1) / TT) >= 64;
 }
 
 bool quantize_hist_fuses_cdf(const Dims &d, const void *wire) {
@@ -442,30 +470,31 @@ hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_
     int loga = 2;
     while ((1 << loga) < d.A) ++loga;
     const int tt = (int)TT;
-#define CG_QH(NV, LG)                                                                                       \
+#define CG_QH(NV, CW, LG)                                                                                   \
     do {                                                                                                    \
         if (packed)                                                                                         \
-            hipLaunchKernelGGL((k_quantize_hist<NV, LG, true>), grid, block, 0, s, kv, sym, scale, counts, wire, \
-                               wpre, status, d.L, d.T, d.C, d.A, tt, mt);                                   \
+            hipLaunchKernelGGL((k_quantize_hist<NV, CW, LG, true>), grid, block, 0, s, kv, sym, scale, counts,  \
+                               wire, wpre, status, d.L, d.T, d.C, d.A, tt, mt);                             \
         else                                                                                                \
-            hipLaunchKernelGGL((k_quantize_hist<NV, LG, false>), grid, block, 0, s, kv, sym, scale, counts, \
+            hipLaunchKernelGGL((k_quantize_hist<NV, CW, LG, false>), grid, block, 0, s, kv, sym, scale, counts, \
                                wire, wpre, status, d.L, d.T, d.C, d.A, tt, mt);                             \
     } while (0)
-    if (d.C == 512) {
-        switch (loga) {
-        case 2: CG_QH(1, 2); break;
-        case 3: CG_QH(1, 3); break;
-        case 4: CG_QH(1, 4); break;
-        default: CG_QH(1, 5); break;
-        }
-    } else {
-        switch (loga) {
-        case 2: CG_QH(2, 2); break;
-        case 3: CG_QH(2, 3); break;
-        case 4: CG_QH(2, 4); break;
-        default: CG_QH(2, 5); break;
-        }
+#define CG_QH_A(NV, CW)                         \
+    do {                                        \
+        switch (loga) {                         \
+        case 2: CG_QH(NV, CW, 2); break;        \
+        case 3: CG_QH(NV, CW, 3); break;        \
+        case 4: CG_QH(NV, CW, 4); break;        \
+        default: CG_QH(NV, CW, 5); break;       \
+        }                                       \
+    } while (0)
+    switch (d.C) {
+    case 256: CG_QH_A(1, 4); break;
+    case 512: CG_QH_A(1, 8); break;
+    case 768: CG_QH_A(3, 4); break;
+    default: CG_QH_A(2, 8); break;
     }
+#undef CG_QH_A
 #undef CG_QH
     return hipGetLastError();
 }

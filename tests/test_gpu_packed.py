@@ -1,6 +1,6 @@
 """The packed symbol layout of the whole-blob encoder on the GPU.
 
-For C = 512 or 1024 and a token count that is a multiple of 8, the fused
+For C = 256, 512, 768 or 1024 and a token count that is a multiple of 8, the fused
 quantiser hands the encoder its symbols packed per token group: 8 tokens per
 dword as nibbles for the slabs of at most 16 symbols (16-bin layers), 4 tokens
 per dword as bytes for the others, provided every encoder launch sees slabs of
@@ -40,30 +40,32 @@ def _roundtrip(kv, bk, bv, fmt=0):
 
 
 @pytest.mark.parametrize("T", [8, 264, 512])
-@pytest.mark.parametrize("H,D", [(4, 128), (8, 128)])
+@pytest.mark.parametrize("H,D", [(2, 128), (4, 128), (6, 128), (8, 128)])
 def test_nibble_layout(T, H, D):
-    """Every layer at 16 bins: all slabs in the 16-entry launch, nibbles."""
-    L = 3
+    """Every layer at 16 bins: all slabs in the 16-entry launch, nibbles.
+    (32 layers give the fused quantiser its minimum of 64 blocks.)"""
+    L = 32
     kv = generate_kv(L, T, H, D, outlier_frac=0.01, outlier_scale=20.0, seed=700 + T + H)
     bins = np.full(L, 16, np.uint8)
     _roundtrip(kv, bins, bins)
 
 
 @pytest.mark.parametrize("bins", [18, 25, 32])
-def test_byte_layout(bins):
+@pytest.mark.parametrize("H", [2, 6, 8])
+def test_byte_layout(bins, H):
     """Every layer above 16 bins: one launch of the wider tables, bytes."""
-    L, T, H, D = 2, 520, 8, 128
-    kv = generate_kv(L, T, H, D, outlier_frac=0.02, outlier_scale=8.0, seed=800 + bins)
+    L, T, D = 32, 520, 128
+    kv = generate_kv(L, T, H, D, outlier_frac=0.02, outlier_scale=8.0, seed=800 + bins + H)
     b = np.full(L, bins, np.uint8)
     _roundtrip(kv, b, b)
 
 
 def test_odd_bins_per_layer_format():
-    """Per-layer tables with bins 17 (nibble slabs, M = 7) and 5..16."""
-    L, T, H, D = 4, 256, 4, 128
+    """Per-layer tables with bins 17 (nibble slabs, M = 7) and 4..16."""
+    L, T, H, D = 32, 256, 4, 128
     kv = generate_kv(L, T, H, D, seed=901)
-    bk = np.array([17, 16, 9, 5], np.uint8)
-    bv = np.array([12, 17, 4, 16], np.uint8)
+    bk = np.tile(np.array([17, 16, 9, 5], np.uint8), 8)
+    bv = np.tile(np.array([12, 17, 4, 16], np.uint8), 8)
     _roundtrip(kv, bk, bv, fmt=1)
 
 
@@ -115,3 +117,17 @@ def test_split_launches_in_a_large_batch():
     for b in list(range(0, B, 37)) + [B - 1]:
         want = oracle.to_bytes(kv[b], bk, bv)
         assert bn[b * stride : b * stride + int(sn[b])].tobytes() == want, b
+
+
+@pytest.mark.parametrize("H", [2, 6])
+@pytest.mark.parametrize("T", [64, 257, 1040])
+def test_fused_quantiser_at_256_and_768_channels(H, T):
+    """C = 256 and 768 (4 channels per lane in the fused quantiser) with the
+    default bins: [T][C] symbols (a small grid with both kinds of slab, or
+    T % 8 != 0), tables built in the quantiser (T <= its tile) or from
+    counts (T = 1040 with 40 layers spans several tiles)."""
+    L = 40 if T == 1040 else 32
+    kv = generate_kv(L, T, H, 128, outlier_frac=0.02, outlier_scale=50.0, innovations="laplace", rho=0.8,
+                     seed=950 + H + T)
+    bk, bv = oracle.default_bins(L)
+    _roundtrip(kv, bk, bv)

@@ -277,7 +277,12 @@ template <int S, int LOGA, int NW, bool TRUSTED, int PK>
 __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     static_assert(PK == 0 || TRUSTED, "packed symbols come from the quantiser");
     constexpr int R = enc_rows(LOGA, NW);
-    __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
+    // One-wave blocks (calls of fewer than eight chunks) are as many per CU as
+    // their LDS allows, so they keep 16-bit starts, [symbol][lane], W + 1 of
+    // them (2^16 stored as 0), and take a symbol's frequency as the
+    // difference of two starts; larger blocks keep start | freq << 16.
+    constexpr bool T16 = NW == 1;
+    __shared__ uint32_t tab[T16 ? ((1 << LOGA) + 1) * 32 : (1 << LOGA) * 64];  // [symbol][lane]
     __shared__ __attribute__((aligned(16))) uint8_t stage[NW * S * (R + 2) * kRowPitch];  // [wave][stream][row][lane]
     const int lane = threadIdx.x & 63;
     // Wave index, uniform across the wave (readfirstlane keeps what derives
@@ -353,6 +358,24 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     // A launch for slabs of at most 2^LOGA symbols holds only that many
     // entries of a wider table: the quantiser's symbols never reach the rest.
     const int WT = min(W, 1 << LOGA);
+    if constexpr (T16) {
+        // Starts 0..WT (start WT is 2^16, stored as 0, when WT == W). Idle
+        // lanes write nothing and read the table of an active column.
+        uint16_t *tab16 = reinterpret_cast<uint16_t *>(tab);
+        if (active) {
+            for (int s = 0; s <= WT; ++s) {
+                uint32_t v = 0;
+                if (s < W) {
+                    uint32_t lo, hi;
+                    cdf_bounds(a.cdf, a.cdf16, a.wpre, slab, a.C, c, A, W, s, lo, hi);
+                    v = lo;
+                    if (s < WT)
+                        bad |= hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne);
+                }
+                tab16[s * 64 + lane] = (uint16_t)v;
+            }
+        }
+    } else
     for (int s = wv; s < WT; s += NW) {
         uint32_t entry;
         if (active) {
@@ -385,7 +408,17 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     // next to lane * 4 (which is below 256).
     const uint32_t lane4 = (uint32_t)lane * 4;
     const uint8_t *tabb = reinterpret_cast<const uint8_t *>(tab);
+    // 16-bit starts: byte address q * 128 + column * 2; the entry is rebuilt
+    // as start | (next start - start) << 16 (the difference mod 2^16 is the
+    // frequency, 2^16 - start for the last symbol).
+    const uint32_t tl2 = (uint32_t)lane_off * 2;
+    auto e16 = [&](uint32_t ad) -> uint32_t {
+        const uint32_t lo = *reinterpret_cast<const uint16_t *>(tabb + ad);
+        const uint32_t hi = *reinterpret_cast<const uint16_t *>(tabb + ad + 128);
+        return lo | ((hi - lo) << 16);
+    };
     auto entry = [&](uint32_t q) -> uint32_t {
+        if constexpr (T16) return e16(((TRUSTED ? q : min(q, amax)) << 7) | tl2);
         if (TRUSTED) return *reinterpret_cast<const uint32_t *>(tabb + __builtin_amdgcn_perm(q, lane4, 0x0c0c0400u));
         return tab[min(q, amax) * 64 + lane];
     };
@@ -393,6 +426,10 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     // goes next to lane4 by one permute; nibble layout: token p sits at bit
     // 8 * (p % 4) + 4 * (p / 4) and is shifted to bits 8..11.
     auto pentry = [&](uint32_t w, int p) -> uint32_t {
+        if constexpr (T16) {
+            const int b = PK == 2 ? 8 * p : 8 * (p & 3) + 4 * (p >> 2);
+            return e16((__builtin_amdgcn_ubfe(w, b, PK == 2 ? 8 : 4) << 7) | tl2);
+        }
         uint32_t ad;
         if constexpr (PK == 2) {
             ad = __builtin_amdgcn_perm(w, lane4, 0x0c0c0000u | ((4u + (uint32_t)p) << 8));

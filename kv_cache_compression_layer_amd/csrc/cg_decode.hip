@@ -90,7 +90,12 @@ struct PagedRows {
     int t0[S], b0[S];
 };
 
-template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED, bool HALF, bool PAGED, bool TAIL>
+// T16: the table holds 16-bit starts [symbol][lane] (2^LOGA + 1 of them:
+// 0xFFFF past the width W, or the true start of symbol 2^LOGA when the table
+// is wider than the LDS part), and a symbol's frequency is the difference of
+// two starts, plus one for the last symbol W - 1 (whose upper bound 2^16 is
+// stored as 0xFFFF so that the search never passes it).
+template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED, bool HALF, bool PAGED, bool TAIL, bool T16>
 __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S], const int (&n)[S],
                                             const uint32_t (&rowoff)[S], const PagedRows<S> &pg,
                                             const uint32_t *tab,
@@ -114,25 +119,32 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
         else st[s].pos -= 2;
     }
 
-    // Byte address in tab of (symbol s, this lane) is s * 256 + lane * 4.
+    // Byte address in tab of (symbol s, this lane) is s * RB + lane * EB.
+    constexpr uint32_t EB = T16 ? 2u : 4u, RB = 64u * EB;
     const uint8_t *tabb = reinterpret_cast<const uint8_t *>(tab);
-    const uint32_t lane4 = (uint32_t)lane * 4;
+    const uint32_t lane4 = (uint32_t)lane * EB;
+    auto start_at = [&](uint32_t a) -> uint32_t {
+        if constexpr (T16) return *reinterpret_cast<const uint16_t *>(tabb + a);
+        return *reinterpret_cast<const uint32_t *>(tabb + a) & 0xFFFFu;
+    };
     // The LDS table holds min(W, 2^LOGA) entries; with TAIL and a wider
     // table, symbols from 2^LOGA up are found in the table in global memory.
     const int WL = W < (1 << LOGA) ? W : (1 << LOGA);
-    const uint32_t amax4 = ((uint32_t)WL - 1) * 256 + lane4;
+    const uint32_t amax4 = ((uint32_t)WL - 1) * RB + lane4;
+    // The last symbol's row (T16: its frequency takes the +1), if in LDS.
+    const uint32_t wlast = W <= (1 << LOGA) ? amax4 : 0xFFFFFFFFu;
     const bool tail_on = TAIL && W > (1 << LOGA);
-    const uint32_t ltop4 = ((1u << LOGA) - 1) * 256 + lane4;
+    const uint32_t ltop4 = ((1u << LOGA) - 1) * RB + lane4;
     // Search depth: the whole table, or (HALF) its lower half when the layer's
     // symbols all lie below the half's top entry; landing on that top entry
     // then means a symbol at or above it (only in corrupt streams), and a
     // rare wave-uniform path continues the search upwards.
     constexpr int SD = HALF ? LOGA - 1 : LOGA;
     constexpr uint32_t H1 = 1u << (SD - 1), H2 = 1u << (SD - 2);
-    const uint32_t top4 = ((1u << SD) - 1) * 256 + lane4;
-    const uint32_t cdf_a = tab[H1 * 64 + lane] & 0xFFFFu;
-    const uint32_t cdf_b = tab[H2 * 64 + lane] & 0xFFFFu;
-    const uint32_t cdf_c = tab[(H1 + H2) * 64 + lane] & 0xFFFFu;
+    const uint32_t top4 = ((1u << SD) - 1) * RB + lane4;
+    const uint32_t cdf_a = start_at(H1 * RB + lane4);
+    const uint32_t cdf_b = start_at(H2 * RB + lane4);
+    const uint32_t cdf_c = start_at((H1 + H2) * RB + lane4);
     const int nmax = n[0];
 
     // Output of the previous token, written one step late.
@@ -184,16 +196,15 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
             const bool hi = __umul24(r[s], cdf_a) <= st[s].code;
             const uint32_t c2 = hi ? cdf_c : cdf_b;
             const bool hi2 = __umul24(r[s], c2) <= st[s].code;
-            ad[s] = lane4 | (hi ? H1 * 256 : 0u) | (hi2 ? H2 * 256 : 0u);
+            ad[s] = lane4 | (hi ? H1 * RB : 0u) | (hi2 ? H2 * RB : 0u);
         }
         // Remaining levels: interleaved branch-free binary searches over LDS.
 #pragma unroll
         for (int i = SD - 3; i >= 0; --i) {
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                const uint32_t cand = ad[s] | (256u << i);
-                const uint32_t ec = *reinterpret_cast<const uint32_t *>(tabb + cand);
-                ad[s] = __umul24(r[s], ec & 0xFFFFu) <= st[s].code ? cand : ad[s];
+                const uint32_t cand = ad[s] | (RB << i);
+                ad[s] = __umul24(r[s], start_at(cand)) <= st[s].code ? cand : ad[s];
             }
         }
         // The previous token's output, now that its LDS reads have landed.
@@ -206,15 +217,20 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
             if (HALF && __builtin_amdgcn_ballot_w64(ad[s] == top4)) {
                 __asm__ volatile("" ::: "memory");
                 if (ad[s] == top4) {
-                    for (uint32_t cand = top4 + 256; cand < (1u << LOGA) * 256; cand += 256) {
-                        const uint32_t ec = *reinterpret_cast<const uint32_t *>(tabb + cand);
-                        if (__umul24(r[s], ec & 0xFFFFu) > st[s].code) break;
+                    for (uint32_t cand = top4 + RB; cand < (1u << LOGA) * RB; cand += RB) {
+                        if (__umul24(r[s], start_at(cand)) > st[s].code) break;
                         ad[s] = cand;
                     }
                 }
             }
             if (CLAMP) ad[s] = min(ad[s], amax4);
-            uint32_t e = *reinterpret_cast<const uint32_t *>(tabb + ad[s]);
+            uint32_t e;
+            if constexpr (T16) {
+                const uint32_t lo = start_at(ad[s]), hi = start_at(ad[s] + RB);
+                e = lo | ((hi - lo + (ad[s] == wlast ? 1u : 0u)) << 16);
+            } else {
+                e = *reinterpret_cast<const uint32_t *>(tabb + ad[s]);
+            }
             if (tail_on && __builtin_amdgcn_ballot_w64(ad[s] == ltop4)) {
                 // The search stopped at the last LDS entry: the symbol may lie
                 // above it (never for the quantiser's symbols, which stay below
@@ -227,7 +243,7 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
                         cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, c, a.A, W, sy, lo, hi);
                         if (__umul24(r[s], lo & 0xFFFFu) > st[s].code) break;
                         bad |= hi <= lo || hi > kProbOne;
-                        ad[s] = (uint32_t)sy * 256 + lane4;
+                        ad[s] = (uint32_t)sy * RB + lane4;
                         e = (lo & 0xFFFFu) | ((hi - lo) << 16);
                     }
                     if (bad) e = (e & 0xFFFFu) | (1u << 16);
@@ -260,10 +276,10 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
             if (t < n[s]) bad_mask |= __ballot(d.code >= d.range);
             if (FUSED) {
                 p_dq[s] = *reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(dq) +
-                                                           ((ad[s] >> 6) & ~3u));
+                                                           ((ad[s] >> (T16 ? 5 : 6)) & ~3u));
                 p_sc[s] = (uint32_t)__builtin_amdgcn_readlane((int)cur_sc[s], t & 63);
             } else {
-                p_sy[s] = ad[s] >> 8;
+                p_sy[s] = ad[s] >> (T16 ? 7 : 8);
             }
         }
         p_t = t;
@@ -294,7 +310,10 @@ __device__ __forceinline__ uint32_t load_word(const uint8_t *payload, uint64_t p
 template <int S, bool FUSED, int LOGA, bool CLAMP, int NW, bool PAGED, bool TAIL>
 __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // Static LDS sized by the template, so every address folds to an immediate.
-    __shared__ uint32_t tab[(1 << LOGA) * 64];                                // [symbol][lane]
+    // Blocks of one or two waves (short calls) are as many per CU as their
+    // LDS allows: they keep 16-bit starts (see decode_loop's T16).
+    constexpr bool T16 = NW <= 2;
+    __shared__ uint32_t tab[T16 ? ((1 << LOGA) + 1) * 32 : (1 << LOGA) * 64];  // [symbol][lane]
     __shared__ float dq[128];
     // Blocks of one or two waves (calls of fewer than eight chunks) keep no
     // pool: what limits them is residency, and at a few bits per symbol a
@@ -399,6 +418,26 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // w + NW, ...; entries past the table's width W (up to 2^LOGA) have start
     // 0xFFFF.
     bool bad_table = false;
+    if constexpr (T16) {
+        // Starts 0..2^LOGA: the symbol's lower bound below W, 0xFFFF from W
+        // on; idle lanes: 0 then 0xFFFF (code 0 always decodes symbol 0 with
+        // frequency 0xFFFF, which never forces a renormalisation).
+        uint16_t *tab16 = reinterpret_cast<uint16_t *>(tab);
+        for (int s = wv; s <= (1 << LOGA); s += NW) {
+            uint32_t v = 0xFFFFu;
+            if (s < W && active) {
+                uint32_t lo, hi;
+                cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, c, A, W, s, lo, hi);
+                if (s < (1 << LOGA) &&
+                    (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)))
+                    bad_table = true;
+                v = lo & 0xFFFFu;
+            } else if (s == 0) {
+                v = 0;
+            }
+            tab16[s * 64 + lane] = (uint16_t)v;
+        }
+    } else
     for (int s = wv; s < (1 << LOGA); s += NW) {
         uint32_t entry = 0xFFFFu;
         if (s < W && active) {
@@ -481,17 +520,17 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     const bool half = LOGA >= 3 && M + 1 <= (1 << (LOGA - 2));
     if (half) {
         if (staged)
-            decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3, PAGED, TAIL>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                                out_voff, lane, W, slab, c, bad_mask);
         else
-            decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3, PAGED, TAIL>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                                 out_voff, lane, W, slab, c, bad_mask);
     } else {
         if (staged)
-            decode_loop<S, FUSED, LOGA, CLAMP, true, false, PAGED, TAIL>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, true, false, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                             out_voff, lane, W, slab, c, bad_mask);
         else
-            decode_loop<S, FUSED, LOGA, CLAMP, false, false, PAGED, TAIL>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, false, false, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                              out_voff, lane, W, slab, c, bad_mask);
     }
     if ((__ballot(active && (corrupt || bad_table)) | (bad_mask & __ballot(active))) && lane == 0)

@@ -15,7 +15,9 @@
 // layer) (lane = channel) and NW * S chunks; each wave decodes S streams per
 // lane interleaved (independent dependency chains) with the one table of its
 // channel. The waves share the tables, staged as start | freq << 16
-// [symbol][lane], and an LDS pool for their tiles' payload: every lane copies
+// [symbol][lane] (blocks of one or two waves, which short calls use and
+// whose residency the LDS decides, keep 16-bit starts instead), and an LDS
+// pool for their tiles' payload: every lane copies
 // its own stream there, followed by four zero bytes (the bytes past a
 // stream's end read as zero), so the byte fetch needs no bounds check. A
 // wave whose tiles do not fit the pool reads global memory instead. The

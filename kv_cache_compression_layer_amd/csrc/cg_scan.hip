@@ -54,7 +54,19 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_local(TileScan a, int64_t t
             const int cb = (int)(tl - slab * a.CB);
             const uint16_t *p = a.lengths + (j * 2 * a.L + slab) * a.C + cb * 64;
             const int nch = min(64, a.C - cb * 64);
-            for (int i = 0; i < nch; ++i) v += p[i];
+            if (nch == 64 && a.C % 8 == 0 && ((uintptr_t)a.lengths & 15) == 0) {
+                // A full tile's 64 lengths are 128 aligned bytes: eight
+                // 16-byte loads, each word holding two lengths.
+                const uint4 *p4 = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint4 w = p4[i];
+                    v += (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) + (w.z & 0xFFFFu) +
+                         (w.z >> 16) + (w.w & 0xFFFFu) + (w.w >> 16);
+                }
+            } else {
+                for (int i = 0; i < nch; ++i) v += p[i];
+            }
         }
     }
     const uint32_t incl = wave_incl_scan_u32(v, lane);

@@ -6,7 +6,9 @@ The product library never links, loads or calls it, and this wrapper never
 imports the product package.
 
 The arithmetic lives in ``cachegen_oracle.c`` (plain scalar C, built with
-``gcc -O2 -ffp-contract=off``); this module only builds, loads and marshals.
+``gcc -O2 -ffp-contract=off``); ``cachegen_oracle_mt.c`` only runs its
+one-layer calls on several threads (``threads=`` below) and moves the results
+into place. This module only builds, loads and marshals.
 All arrays are numpy arrays in C order; bf16 tensors are ``uint16`` bit
 patterns.
 """
@@ -21,6 +23,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "cachegen_oracle.c")
+_SRC_MT = os.path.join(_HERE, "cachegen_oracle_mt.c")
 _LIB_PATH = os.path.join(_HERE, "_build", "libcachegen_oracle.so")
 _lib = None
 
@@ -36,8 +39,8 @@ def build(force: bool = True) -> str:
     os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
-               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall", "-pthread",
+               "-fPIC", "-shared", "-o", tmp, _SRC, _SRC_MT, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -69,6 +72,9 @@ def lib():
             "ocg_to_bytes": (i64, [i32, i32, i32, i32, p, p, p, p, i64]),
             "ocg_blob_header": (i32, [p, i64, p, p, p, i32]),
             "ocg_from_bytes": (i32, [p, i64, p]),
+            "ocg_quantize_mt": (i32, [i32, i32, i32, p, p, p, p, p, i32]),
+            "ocg_to_bytes_mt": (i64, [i32, i32, i32, i32, p, p, i32, p, p, i64, i32]),
+            "ocg_from_bytes_mt": (i32, [p, i64, p, i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -104,8 +110,9 @@ def alphabet(bins_k, bins_v) -> int:
     return int(max(np.max(bins_k), np.max(bins_v)))
 
 
-def quantize(kv: np.ndarray, bins_k, bins_v):
-    """kv: uint16 [L,2,T,H,D] or [L,2,T,C] -> (sym uint8 [2,L,T,C], scale uint16 [2,L,T])."""
+def quantize(kv: np.ndarray, bins_k, bins_v, threads: int = 1):
+    """kv: uint16 [L,2,T,H,D] or [L,2,T,C] -> (sym uint8 [2,L,T,C], scale uint16 [2,L,T]).
+    threads > 1: the same result, layers spread over that many threads."""
     L, two, T = kv.shape[:3]
     assert two == 2
     C = int(np.prod(kv.shape[3:]))
@@ -113,7 +120,11 @@ def quantize(kv: np.ndarray, bins_k, bins_v):
     bk, bv = _u8(bins_k), _u8(bins_v)
     sym = np.empty((2, L, T, C), np.uint8)
     scale = np.empty((2, L, T), np.uint16)
-    _check(lib().ocg_quantize(L, T, C, _p(bk), _p(bv), _p(kv), _p(sym), _p(scale)), "quantize")
+    if threads > 1:
+        _check(lib().ocg_quantize_mt(L, T, C, _p(bk), _p(bv), _p(kv), _p(sym), _p(scale), int(threads)),
+               "quantize_mt")
+    else:
+        _check(lib().ocg_quantize(L, T, C, _p(bk), _p(bv), _p(kv), _p(sym), _p(scale)), "quantize")
     return sym, scale
 
 
@@ -229,14 +240,20 @@ def dequantize(sym: np.ndarray, scale: np.ndarray, bins_k, bins_v):
     return out
 
 
-def to_bytes(kv: np.ndarray, bins_k, bins_v, table_format: int = 0) -> bytes:
+def to_bytes(kv: np.ndarray, bins_k, bins_v, table_format: int = 0, threads: int = 1) -> bytes:
+    """The whole encode; threads > 1 spreads the layers over that many threads
+    (the same bytes)."""
     L, two, T, H, D = kv.shape
     kv = np.ascontiguousarray(kv, dtype=np.uint16)
     bk, bv = _u8(bins_k), _u8(bins_v)
     cap = _check(lib().ocg_blob_bound(L, T, H, D, _p(bk), _p(bv)), "blob_bound")
     blob = np.empty(cap, np.uint8)
-    n = _check(lib().ocg_to_bytes_fmt(L, T, H, D, _p(bk), _p(bv), int(table_format), _p(kv), _p(blob), cap),
-               "to_bytes")
+    if threads > 1:
+        n = _check(lib().ocg_to_bytes_mt(L, T, H, D, _p(bk), _p(bv), int(table_format), _p(kv), _p(blob), cap,
+                                         int(threads)), "to_bytes_mt")
+    else:
+        n = _check(lib().ocg_to_bytes_fmt(L, T, H, D, _p(bk), _p(bv), int(table_format), _p(kv), _p(blob), cap),
+                   "to_bytes")
     return blob[:n].tobytes()
 
 
@@ -252,9 +269,15 @@ def blob_header(blob: bytes):
     return d, bk[: d["nlayers"]].copy(), bv[: d["nlayers"]].copy()
 
 
-def from_bytes(blob: bytes) -> np.ndarray:
+def from_bytes(blob, threads: int = 1) -> np.ndarray:
+    """The whole decode -> bf16 bits [L,2,T,H,D]; blob: bytes or a uint8
+    array. threads > 1 spreads the layers over that many threads."""
     d, _, _ = blob_header(blob)
-    buf = np.frombuffer(blob, np.uint8).copy()
+    buf = np.ascontiguousarray(np.frombuffer(blob, np.uint8) if isinstance(blob, (bytes, bytearray)) else blob,
+                               dtype=np.uint8)
     out = np.empty((d["nlayers"], 2, d["ntokens"], d["nheads"], d["head_size"]), np.uint16)
-    _check(lib().ocg_from_bytes(_p(buf), len(blob), _p(out)), "from_bytes")
+    if threads > 1:
+        _check(lib().ocg_from_bytes_mt(_p(buf), buf.size, _p(out), int(threads)), "from_bytes_mt")
+    else:
+        _check(lib().ocg_from_bytes(_p(buf), buf.size, _p(out)), "from_bytes")
     return out

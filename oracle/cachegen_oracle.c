@@ -543,6 +543,72 @@ int64_t ocg_blob_bound(int L, int T, int H, int D, const uint8_t *bins_k, const 
     return s.payload + NS * (4 * CHUNK_TOKENS);
 }
 
+/* Writes everything of the blob but the payload: the zeroed front, the
+ * header and the scale, table, chunk-offset and length sections. The pay
+ * payload bytes must already sit at the payload offset (or be written there
+ * afterwards). Returns the blob size or a negative code. */
+int64_t ocg_blob_write(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v, int fmt,
+                       const uint16_t *scale, const int32_t *cdf, const uint16_t *lengths,
+                       const uint64_t *chunk_off, int64_t pay, uint8_t *blob, int64_t cap)
+{
+    if (L < 1 || L > 1024 || T < 1 || H < 1 || D < 1 || !blob || !scale || !cdf || !lengths || !chunk_off ||
+        pay < 0 || !bins_ok(L, bins_k, bins_v) || (fmt != 0 && fmt != 1))
+        return OCG_ERR_ARG;
+    int C = H * D, A = max_bins(L, bins_k, bins_v), NC = nchunks_of(T);
+    uint8_t W[2048];
+    table_widths(L, bins_k, bins_v, fmt, W);
+    int64_t entries = 0;
+    for (int i = 0; i < 2 * L; ++i)
+        entries += W[i];
+    struct layout s = layout_of(L, T, C, entries);
+    if (cap < s.payload + pay)
+        return OCG_ERR_CAPACITY;
+    memset(blob, 0, (size_t)s.payload);
+    /* header */
+    memcpy(blob, "CGMX", 4);
+    put16(blob + 4, 1);
+    put16(blob + 6, 1);
+    put32(blob + 8, (uint32_t)L);
+    put32(blob + 12, (uint32_t)T);
+    put32(blob + 16, (uint32_t)H);
+    put32(blob + 20, (uint32_t)D);
+    put32(blob + 24, CHUNK_TOKENS);
+    put32(blob + 28, (uint32_t)NC);
+    put32(blob + 32, (uint32_t)A);
+    put32(blob + 36, (uint32_t)fmt);
+    put64(blob + 40, (uint64_t)(s.payload + pay));
+    memcpy(blob + HDR_FIXED, bins_k, (size_t)L);
+    memcpy(blob + HDR_FIXED + L, bins_v, (size_t)L);
+    for (size_t i = 0; i < 2 * (size_t)L * T; ++i)
+        put16(blob + s.scales + 2 * i, scale[i]);
+    {
+        /* Entries 0..W-1 of every table, slab after slab (entry W is 2^16). */
+        int64_t e = 0;
+        for (size_t tab = 0; tab < 2 * (size_t)L * C; ++tab) {
+            const int w = W[tab / (size_t)C];
+            for (int k = 0; k < w; ++k)
+                put16(blob + s.cdf + 2 * (e++), (uint16_t)cdf[tab * (A + 1) + k]);
+        }
+    }
+    for (int j = 0; j <= NC; ++j)
+        put64(blob + s.offsets + 8 * j, chunk_off[j]);
+    for (size_t i = 0; i < (size_t)NC * 2 * L * C; ++i)
+        put16(blob + s.lengths + 2 * i, lengths[i]);
+    return s.payload + pay;
+}
+
+int64_t ocg_blob_payload_offset(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v, int fmt)
+{
+    if (L < 1 || L > 1024 || T < 1 || H < 1 || D < 1 || !bins_ok(L, bins_k, bins_v) || (fmt != 0 && fmt != 1))
+        return OCG_ERR_ARG;
+    uint8_t W[2048];
+    table_widths(L, bins_k, bins_v, fmt, W);
+    int64_t entries = 0;
+    for (int i = 0; i < 2 * L; ++i)
+        entries += W[i];
+    return layout_of(L, T, H * D, entries).payload;
+}
+
 int64_t ocg_to_bytes_fmt(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v,
                          int fmt, const uint16_t *kv, uint8_t *blob, int64_t cap)
 {
@@ -574,42 +640,13 @@ int64_t ocg_to_bytes_fmt(int L, int T, int H, int D, const uint8_t *bins_k, cons
         goto done;
     if ((rc = cdf_tables(L, T, C, A, W, cnt, cdf)))
         goto done;
-    memset(blob, 0, (size_t)s.payload);
     int64_t pay = encode_all(L, T, C, A, W, sym, cdf, blob + s.payload, cap - s.payload, lengths, chunk_off);
     if (pay < 0) {
         rc = pay;
         goto done;
     }
-    /* header */
-    memcpy(blob, "CGMX", 4);
-    put16(blob + 4, 1);
-    put16(blob + 6, 1);
-    put32(blob + 8, (uint32_t)L);
-    put32(blob + 12, (uint32_t)T);
-    put32(blob + 16, (uint32_t)H);
-    put32(blob + 20, (uint32_t)D);
-    put32(blob + 24, CHUNK_TOKENS);
-    put32(blob + 28, (uint32_t)NC);
-    put32(blob + 32, (uint32_t)A);
-    put32(blob + 36, (uint32_t)fmt);
-    put64(blob + 40, (uint64_t)(s.payload + pay));
-    memcpy(blob + HDR_FIXED, bins_k, (size_t)L);
-    memcpy(blob + HDR_FIXED + L, bins_v, (size_t)L);
-    for (size_t i = 0; i < 2 * (size_t)L * T; ++i)
-        put16(blob + s.scales + 2 * i, scale[i]);
-    {
-        /* Entries 0..W-1 of every table, slab after slab (entry W is 2^16). */
-        int64_t e = 0;
-        for (size_t tab = 0; tab < 2 * (size_t)L * C; ++tab) {
-            const int w = W[tab / (size_t)C];
-            for (int k = 0; k < w; ++k)
-                put16(blob + s.cdf + 2 * (e++), (uint16_t)cdf[tab * (A + 1) + k]);
-        }
-    }
-    for (int j = 0; j <= NC; ++j)
-        put64(blob + s.offsets + 8 * j, chunk_off[j]);
-    for (size_t i = 0; i < (size_t)NC * 2 * L * C; ++i)
-        put16(blob + s.lengths + 2 * i, lengths[i]);
+    if ((rc = ocg_blob_write(L, T, H, D, bins_k, bins_v, fmt, scale, cdf, lengths, chunk_off, pay, blob, cap)) < 0)
+        goto done;
     rc = s.payload + pay;
 done:
     free(sym);
@@ -651,13 +688,22 @@ int ocg_blob_header(const uint8_t *blob, int64_t size, int32_t dims[8], uint8_t 
     return 0;
 }
 
-int ocg_from_bytes(const uint8_t *blob, int64_t size, uint16_t *kv_out)
+/* Reads the scale, table, chunk-offset and length sections of a blob whose
+ * header ocg_blob_header accepted, into arrays sized by that header (scale
+ * [2,L,T], cdf int32 [2,L,C,A+1] with 2^16 past each table's width, lengths
+ * [NC,2L,C], chunk_off [NC+1]); *payload_off receives the payload's offset.
+ * Rejects tables that are not strictly increasing from 0 and a last chunk
+ * offset that is not the payload size. */
+int ocg_blob_sections(const uint8_t *blob, int64_t size, uint16_t *scale, int32_t *cdf, uint16_t *lengths,
+                      uint64_t *chunk_off, int64_t *payload_off)
 {
     int32_t dims[8];
     uint8_t bk[1024], bv[1024];
     int rc = ocg_blob_header(blob, size, dims, bk, bv, 1024);
     if (rc)
         return rc;
+    if (!scale || !cdf || !lengths || !chunk_off || !payload_off)
+        return OCG_ERR_ARG;
     int L = dims[0], T = dims[1], C = dims[2] * dims[3], NC = dims[5], A = dims[6];
     uint8_t W[2048];
     table_widths(L, bk, bv, dims[7], W);
@@ -667,17 +713,8 @@ int ocg_from_bytes(const uint8_t *blob, int64_t size, uint16_t *kv_out)
     struct layout s = layout_of(L, T, C, entries);
     if (size < s.payload)
         return OCG_ERR_CORRUPT;
-    uint16_t *scale = malloc(sizeof(uint16_t) * 2 * (size_t)L * T);
-    int32_t *cdf = malloc(sizeof(int32_t) * 2 * (size_t)L * C * (A + 1));
-    uint16_t *lengths = malloc(sizeof(uint16_t) * (size_t)NC * 2 * L * C);
-    uint64_t *chunk_off = malloc(sizeof(uint64_t) * ((size_t)NC + 1));
-    uint8_t *sym = malloc(2 * (size_t)L * T * C);
-    rc = OCG_ERR_ARG;
-    if (!scale || !cdf || !lengths || !chunk_off || !sym)
-        goto done;
     for (size_t i = 0; i < 2 * (size_t)L * T; ++i)
         scale[i] = get16(blob + s.scales + 2 * i);
-    rc = OCG_ERR_CORRUPT;
     {
         int64_t e = 0;
         for (size_t tab = 0; tab < 2 * (size_t)L * C; ++tab) {
@@ -688,10 +725,10 @@ int ocg_from_bytes(const uint8_t *blob, int64_t size, uint16_t *kv_out)
             for (int k = w; k <= A; ++k)
                 t[k] = PROB_ONE;
             if (t[0] != 0)
-                goto done;
+                return OCG_ERR_CORRUPT;
             for (int k = 0; k < w; ++k)
                 if (t[k + 1] <= t[k])
-                    goto done;
+                    return OCG_ERR_CORRUPT;
         }
     }
     for (int j = 0; j <= NC; ++j)
@@ -699,8 +736,33 @@ int ocg_from_bytes(const uint8_t *blob, int64_t size, uint16_t *kv_out)
     for (size_t i = 0; i < (size_t)NC * 2 * L * C; ++i)
         lengths[i] = get16(blob + s.lengths + 2 * i);
     if ((int64_t)chunk_off[NC] != size - s.payload)
+        return OCG_ERR_CORRUPT;
+    *payload_off = s.payload;
+    return 0;
+}
+
+int ocg_from_bytes(const uint8_t *blob, int64_t size, uint16_t *kv_out)
+{
+    int32_t dims[8];
+    uint8_t bk[1024], bv[1024];
+    int rc = ocg_blob_header(blob, size, dims, bk, bv, 1024);
+    if (rc)
+        return rc;
+    int L = dims[0], T = dims[1], C = dims[2] * dims[3], NC = dims[5], A = dims[6];
+    uint8_t W[2048];
+    table_widths(L, bk, bv, dims[7], W);
+    uint16_t *scale = malloc(sizeof(uint16_t) * 2 * (size_t)L * T);
+    int32_t *cdf = malloc(sizeof(int32_t) * 2 * (size_t)L * C * (A + 1));
+    uint16_t *lengths = malloc(sizeof(uint16_t) * (size_t)NC * 2 * L * C);
+    uint64_t *chunk_off = malloc(sizeof(uint64_t) * ((size_t)NC + 1));
+    uint8_t *sym = malloc(2 * (size_t)L * T * C);
+    int64_t pay_off = 0;
+    rc = OCG_ERR_ARG;
+    if (!scale || !cdf || !lengths || !chunk_off || !sym)
         goto done;
-    if ((rc = decode_all(L, T, C, A, W, blob + s.payload, size - s.payload, lengths, chunk_off, cdf, sym)))
+    if ((rc = ocg_blob_sections(blob, size, scale, cdf, lengths, chunk_off, &pay_off)))
+        goto done;
+    if ((rc = decode_all(L, T, C, A, W, blob + pay_off, size - pay_off, lengths, chunk_off, cdf, sym)))
         goto done;
     rc = ocg_dequantize(L, T, C, bk, bv, sym, scale, kv_out);
 done:

@@ -112,6 +112,30 @@ int ocg_blob_header(const uint8_t *blob, int64_t size, int32_t dims[8], uint8_t 
                     uint8_t *bins_v, int max_layers);
 int ocg_from_bytes(const uint8_t *blob, int64_t size, uint16_t *kv_out);
 
+/* The blob's two halves, for drivers that compute the stages themselves.
+ * ocg_blob_write: header and every section but the payload (the pay payload
+ * bytes sit at the offset ocg_blob_payload_offset returns); returns the blob
+ * size. ocg_blob_sections: the sections of a blob whose header is valid, into
+ * arrays sized by that header (cdf int32 [2,L,C,A+1], 2^16 past each table's
+ * width); checks the tables and the last chunk offset. */
+int64_t ocg_blob_write(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v, int fmt,
+                       const uint16_t *scale, const int32_t *cdf, const uint16_t *lengths,
+                       const uint64_t *chunk_off, int64_t pay, uint8_t *blob, int64_t cap);
+int64_t ocg_blob_payload_offset(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v,
+                                int fmt);
+int ocg_blob_sections(const uint8_t *blob, int64_t size, uint16_t *scale, int32_t *cdf, uint16_t *lengths,
+                      uint64_t *chunk_off, int64_t *payload_off);
+
+/* Multi-threaded drivers (cachegen_oracle_mt.c). They run the single-layer
+ * calls above on each layer's K and V slabs on nthreads POSIX threads and
+ * move the results into place; the arithmetic is that of the calls above,
+ * unchanged, so the output is byte for byte that of the one-thread calls. */
+int ocg_quantize_mt(int L, int T, int C, const uint8_t *bins_k, const uint8_t *bins_v,
+                    const uint16_t *kv, uint8_t *sym, uint16_t *scale, int nthreads);
+int64_t ocg_to_bytes_mt(int L, int T, int H, int D, const uint8_t *bins_k, const uint8_t *bins_v,
+                        int fmt, const uint16_t *kv, uint8_t *blob, int64_t cap, int nthreads);
+int ocg_from_bytes_mt(const uint8_t *blob, int64_t size, uint16_t *kv_out, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,7 @@ def pytest_configure(config):
 def _oracle_built():
     import oracle
 
-    if not os.path.exists(oracle._LIB_PATH):
+    srcs = [oracle._SRC, oracle._SRC_MT, os.path.join(os.path.dirname(oracle._SRC), "cachegen_oracle.h")]
+    if not os.path.exists(oracle._LIB_PATH) or max(map(os.path.getmtime, srcs)) > os.path.getmtime(oracle._LIB_PATH):
         oracle.build()
     yield

@@ -458,6 +458,13 @@ int ocg_decode_w(int L, int T, int C, int A, const uint8_t *widths, const uint8_
 
 /* ------------------------------------------------------ [P2 s5] dequantise */
 
+/* x = (q - M) / M * m for each symbol, then cast back to the input dtype.
+ * The page's expression is two tensor operations on the decoded symbols;
+ * read in fp32, the precision the quantiser is read in ([P2 s2]), they are
+ * the separately rounded operations r = fl((q - M) / M) and x = fl(r * m),
+ * followed by one round-to-nearest-even to bf16. (Where the exact quotient
+ * times m is a bf16 midpoint, these roundings decide the tie, so the
+ * result is not always the bf16 nearest to the exact rational.) */
 int ocg_dequantize(int L, int T, int C, const uint8_t *bins_k, const uint8_t *bins_v,
                    const uint8_t *sym, const uint16_t *scale, uint16_t *out)
 {
@@ -466,12 +473,17 @@ int ocg_dequantize(int L, int T, int C, const uint8_t *bins_k, const uint8_t *bi
     for (int k = 0; k < 2; ++k)
         for (int l = 0; l < L; ++l) {
             int M = (k == 0 ? bins_k[l] : bins_v[l]) / 2 - 1;
+            float Mf = (float)M;
             for (int t = 0; t < T; ++t) {
-                double m = (double)bf16_value(scale[((size_t)k * L + l) * T + t]);
+                float m = bf16_value(scale[((size_t)k * L + l) * T + t]);
                 const uint8_t *q = sym + (((size_t)k * L + l) * T + t) * C;
                 uint16_t *o = out + (((size_t)l * 2 + k) * T + t) * C;
-                for (int c = 0; c < C; ++c)
-                    o[c] = bf16_round_double(((double)q[c] - M) / (double)M * m);
+                for (int c = 0; c < C; ++c) {
+                    float r = (float)((int)q[c] - M) / Mf;
+                    float x = r * m;
+                    /* (double)x is exact, so this is the one rounding of x to bf16. */
+                    o[c] = bf16_round_double((double)x);
+                }
             }
         }
     return 0;

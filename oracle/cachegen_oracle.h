@@ -82,8 +82,9 @@ int ocg_decode_w(int L, int T, int C, int A, const uint8_t *widths, const uint8_
                  const int32_t *cdf, uint8_t *sym);
 
 /* Dequantise ([P2] section 5): x = (q - M) / M * scale with M = bins//2 - 1
- * of the element's layer, evaluated in double precision and rounded once to
- * bf16 (nearest, ties to even). out: bf16 [L,2,T,C]. */
+ * of the element's layer, as two separately rounded fp32 operations (the
+ * quotient, then the product), then rounded to bf16 (nearest, ties to even).
+ * out: bf16 [L,2,T,C]. */
 int ocg_dequantize(int L, int T, int C, const uint8_t *bins_k, const uint8_t *bins_v,
                    const uint8_t *sym, const uint16_t *scale, uint16_t *out);
 

@@ -41,6 +41,20 @@ def bf16_ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
     return np.abs(line(a_bits.view(np.uint16)) - line(b_bits.view(np.uint16)))
 
 
+def assert_bf16_equal(got_bits: np.ndarray, want_bits: np.ndarray, what: str = "") -> None:
+    """Bit-for-bit equality of two bf16 arrays (so +0 and -0 differ too); on a
+    mismatch the message gives the count and the largest ulp distance."""
+    g = np.asarray(got_bits).view(np.uint16).reshape(-1)
+    w = np.asarray(want_bits).view(np.uint16).reshape(-1)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    bad = g != w
+    if bad.any():
+        i = int(np.argmax(bad))
+        raise AssertionError(f"{what}: {int(bad.sum())} of {g.size} bf16 values differ, largest "
+                             f"{int(bf16_ulp_distance(g[bad], w[bad]).max())} ulp; first at {i}: "
+                             f"{g[i]:#06x} vs {w[i]:#06x}")
+
+
 def run_stages(kv_bits: np.ndarray, bins_k, bins_v, table_format=0):
     """All stage calls on the GPU. kv_bits: uint16 [L,2,T,H,D]."""
     torch = torch_mod()

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from blob_format import parse, stream_offsets
-from gpu_util import bf16_ulp_distance, to_dev, to_np
+from gpu_util import assert_bf16_equal, to_dev, to_np
 from kv_cache_compression_layer_amd import cachegen as cgb
 from kv_cache_compression_layer_amd.synth import WORKLOADS, generate_workload
 
@@ -67,6 +67,6 @@ def test_full_size_sampled(name):
             assert got == want, (l, j, k, c)
         ref = oracle.dequantize(sym, scale, bk[l : l + 1], bv[l : l + 1])
         got = to_np(out[l].view(torch.int16), np.uint16).reshape(2, T, C)
-        assert bf16_ulp_distance(got, ref[0]).max() <= 1
+        assert_bf16_equal(got, ref[0])
     ratio = kv.nbytes / blob_np.size
     print(f"[{name}] raw {kv.nbytes} B, blob {blob_np.size} B, ratio {ratio:.2f}", flush=True)

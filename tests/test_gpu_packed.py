@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import bf16_ulp_distance, to_dev, to_np
+from gpu_util import assert_bf16_equal, to_dev, to_np
 from kv_cache_compression_layer_amd import cachegen as cgb
 from kv_cache_compression_layer_amd.synth import f32_to_bf16_bits, generate_kv
 
@@ -35,7 +35,7 @@ def _roundtrip(kv, bk, bv, fmt=0):
     assert got == want
     out = to_np(cgb.from_bytes(blob).view(torch.int16), np.uint16)
     ref = oracle.from_bytes(want)
-    assert bf16_ulp_distance(out.reshape(-1), ref.reshape(-1)).max() <= 1
+    assert_bf16_equal(out.reshape(-1), ref.reshape(-1))
     return got
 
 

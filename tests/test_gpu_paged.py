@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import bf16_ulp_distance, to_dev, to_np
+from gpu_util import assert_bf16_equal, to_dev, to_np
 from kv_cache_compression_layer_amd import cachegen as cgb
 from kv_cache_compression_layer_amd.synth import generate_kv
 
@@ -86,7 +86,7 @@ def test_paged_matches_oracle():
     want = oracle.from_bytes(oracle.to_bytes(kv, *oracle.default_bins(2))).reshape(2, 2, 520, 64)
     L, T, C, bs, _ = dims
     got = np.concatenate([cache[:, :, table[b], : min(bs, T - b * bs), :] for b in range(len(table))], axis=2)
-    assert bf16_ulp_distance(got, want).max() <= 1
+    assert_bf16_equal(got, want)
 
 
 def test_paged_bad_block_is_reported_and_not_written():

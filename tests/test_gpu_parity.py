@@ -1,11 +1,11 @@
 """GPU parity: every stage of the HIP library, called through the C ABI,
 against the CPU oracle on the same seeded inputs.
 
-Bar: symbols, scales, CDFs, payload bytes, lengths, chunk offsets, decoded
-symbols and whole blobs are bit-exact; dequantised bf16 is within 1 bf16 ulp
-of the oracle's double-precision dequantisation (the library computes
-(q - M) / M and the product by the scale in fp32, two roundings before the
-bf16 rounding).
+Bar: everything is bit-exact: symbols, scales, CDFs, payload bytes,
+lengths, chunk offsets, decoded symbols, whole blobs and the dequantised
+bf16 (the oracle and the library both evaluate (q - M) / M and the product
+by the scale as separately rounded fp32 operations before the bf16
+rounding).
 
 Cases: the model-shaped workloads that the oracle finishes in seconds, and
 edge shapes (1, 255, 256, 257, 513 tokens; channel counts that are not
@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import bf16_ulp_distance, run_coder, run_stages, to_dev, to_np
+from gpu_util import assert_bf16_equal, run_coder, run_stages, to_dev, to_np
 from kv_cache_compression_layer_amd import cachegen as cgb
 from kv_cache_compression_layer_amd.synth import WORKLOADS, generate_kv, generate_workload
 
@@ -58,8 +58,7 @@ def _check_all(kv, bk, bv):
     np.testing.assert_array_equal(g["payload"], payload)
     np.testing.assert_array_equal(g["sym_decoded"], sym)
     want = oracle.dequantize(sym, scale, bk, bv)
-    ulps = bf16_ulp_distance(g["kv_out"], want)
-    assert ulps.max() <= 1
+    assert_bf16_equal(g["kv_out"], want, "dequantised KV")
     return g, lengths
 
 
@@ -135,7 +134,7 @@ def test_whole_blob_matches_oracle_and_cross_decodes():
         # GPU decode of the oracle's blob and of its own blob.
         ref = oracle.from_bytes(want)
         out = cgb.from_bytes(to_dev(np.frombuffer(want, np.uint8).copy()))
-        assert bf16_ulp_distance(to_np(out.view(torch.int16), np.uint16), ref).max() <= 1
+        assert_bf16_equal(to_np(out.view(torch.int16), np.uint16), ref)
         out2 = cgb.from_bytes(blob)
         np.testing.assert_array_equal(to_np(out2.view(torch.int16)), to_np(out.view(torch.int16)))
         # Deterministic.

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import bf16_ulp_distance, run_stages, to_dev, to_np
+from gpu_util import assert_bf16_equal, run_stages, to_dev, to_np
 from kv_cache_compression_layer_amd import cachegen as cgb
 from kv_cache_compression_layer_amd.synth import generate_kv
 
@@ -55,7 +55,7 @@ def test_blob_equals_oracle(shape, kind):
     assert to_np(blob).tobytes() == want
     out = to_np(cgb.from_bytes(blob).view(torch.int16), np.uint16)
     ref = np.asarray(oracle.from_bytes(want)).view(np.uint16)
-    assert bf16_ulp_distance(out.reshape(-1), ref.reshape(-1)).max() <= 1
+    assert_bf16_equal(out.reshape(-1), ref.reshape(-1))
     # Same symbols as the shared-table blob, so the same decode bit for bit.
     shared = cgb.to_bytes(kv_d, bk, bv)
     np.testing.assert_array_equal(out, to_np(cgb.from_bytes(shared).view(torch.int16), np.uint16))

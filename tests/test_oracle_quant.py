@@ -135,28 +135,105 @@ def _bf16_round_exact(fr: Fraction) -> float:
     return sign * float(n * quantum)
 
 
-def test_dequantize_matches_exact_rational_rounding():
+def _exact_neighbours(fr: Fraction):
+    """(nearest bf16 by exact rounding, whether fr is a bf16 midpoint, the two
+    bf16 values around a midpoint)."""
+    if fr == 0:
+        return 0.0, False, (0.0, 0.0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    quantum = Fraction(2) ** (max(e, -126) - 7)
+    q = a / quantum
+    n = q.numerator // q.denominator
+    tie = q - n == Fraction(1, 2)
+    return _bf16_round_exact(fr), tie, (sign * float(n * quantum), sign * float((n + 1) * quantum))
+
+
+def _dequant_cases(rng, n_scales):
+    """Scales that make exact bf16 ties likely (significands with factors 3, 5,
+    7, 11, 13 against M = 3..63) plus random ones, normal and subnormal."""
+    sig = np.array([0x80 | m for m in range(128) if (0x80 | m) % 3 == 0 or (0x80 | m) % 5 == 0 or
+                    (0x80 | m) % 7 == 0 or (0x80 | m) % 13 == 0], np.uint16)
+    exps = rng.choice([1, 2, 3, 60, 120, 127, 140, 250], n_scales)
+    bits = ((exps.astype(np.uint16) << 7) | (rng.choice(sig, n_scales) & 0x7F)).astype(np.uint16)
+    bits[: n_scales // 8] = rng.integers(1, 0x80, n_scales // 8)  # subnormal scales
+    return bits
+
+
+def test_dequantize_is_the_exact_rounding_except_at_ties():
+    """Against exact rational arithmetic: every output is the bf16 nearest to
+    (q - M) / M * m, except where that value is exactly a bf16 midpoint; there
+    the fp32 roundings decide, and the output is one of the two neighbours."""
     rng = np.random.default_rng(11)
-    L, T, C = 3, 20, 40
-    bk = np.array([32, 16, 128], np.uint8)
-    bv = np.array([8, 32, 6], np.uint8)
+    L, T = 6, 64
+    bk = np.array([26, 32, 128, 14, 100, 4], np.uint8)
+    bv = np.array([8, 16, 6, 58, 90, 122], np.uint8)
+    C = 2 * (128 // 2 - 1) + 1
     sym = np.empty((2, L, T, C), np.uint8)
     for k in range(2):
         for l in range(L):
             M = (bk if k == 0 else bv)[l] // 2 - 1
-            sym[k, l] = rng.integers(0, 2 * M + 1, (T, C))
-    scale = f32_to_bf16_bits(np.abs(rng.standard_normal((2, L, T))).astype(np.float32) * 3)
+            sym[k, l] = np.arange(C) % (2 * M + 1)
+    scale = _dequant_cases(rng, 2 * L * T).reshape(2, L, T)
     scale[0, 0, 0] = 0
     out = bf16_bits_to_f32(oracle.dequantize(sym, scale, bk, bv))
     sc = bf16_bits_to_f32(scale)
+    ties = 0
     for k in range(2):
         for l in range(L):
             M = int((bk if k == 0 else bv)[l] // 2 - 1)
-            for t in range(0, T, 3):
+            for t in range(T):
                 m = Fraction(float(sc[k, l, t]))
-                for c in range(0, C, 7):
-                    want = _bf16_round_exact(Fraction(int(sym[k, l, t, c]) - M, M) * m)
-                    assert out[l, k, t, c] == want, (k, l, t, c)
+                for c in range(2 * M + 1):
+                    exact = Fraction(c - M, M) * m
+                    nearest, tie, around = _exact_neighbours(exact)
+                    got = out[l, k, t, c]
+                    if tie:
+                        ties += 1
+                        assert got in around, (k, l, t, c)
+                    else:
+                        assert got == nearest, (k, l, t, c)
+    assert ties > 100  # the cases above do reach exact midpoints
+
+
+def test_dequantize_worked_tie():
+    """The hand-derived fp32 tie of the worked examples: the fp32 roundings
+    give 0x80E3 where exact half-to-even rounding would give 0x80E4."""
+    g = GOLD["dequantize_tie"]
+    M = g["bins"] // 2 - 1
+    bins = np.array([g["bins"]], np.uint8)
+    sym = np.full((2, 1, 1, 2 * M + 1), M, np.uint8)
+    sym[:, 0, 0, 0] = g["q"]
+    scale = np.full((2, 1, 1), int(g["scale_bits"], 16), np.uint16)
+    out = oracle.dequantize(sym, scale, bins, bins)
+    assert int(out[0, 0, 0, 0]) == int(g["x_bits"], 16)
+    assert int(out[0, 1, 0, 0]) == int(g["x_bits"], 16)
+    exact, tie, _ = _exact_neighbours(Fraction(g["q"] - M, M) * Fraction(float(bf16_bits_to_f32(scale[0, 0, 0]))))
+    assert tie and f32_to_bf16_bits(np.float32(exact)) == int(g["exact_rounding_bits"], 16)
+
+
+def test_dequantize_matches_numpy_fp32_for_all_bins():
+    """An independent numpy float32 evaluation (numpy never fuses a*b) over
+    every bins value 4..128, every symbol, and scales of every significand at
+    low, middle and high exponents and in the subnormal range."""
+    sig = np.arange(128, dtype=np.uint16)
+    bits = np.concatenate([(np.uint16(e) << 7) | sig for e in (0, 1, 2, 3, 64, 127, 180, 254)])
+    bits = bits[bits != 0]
+    m32 = bf16_bits_to_f32(bits)
+    for bins in range(4, 129):
+        M = bins // 2 - 1
+        q = np.arange(2 * M + 1)
+        r = (q - M).astype(np.float32) / np.float32(M)
+        want = f32_to_bf16_bits(r[None, :] * m32[:, None])
+        b = np.array([bins], np.uint8)
+        sym = np.broadcast_to(q.astype(np.uint8), (2, 1, bits.size, q.size)).copy()
+        scale = np.broadcast_to(bits, (2, 1, bits.size)).copy()
+        got = oracle.dequantize(sym, scale, b, b)
+        np.testing.assert_array_equal(got[0, 0], want, err_msg=f"bins {bins}")
+        np.testing.assert_array_equal(got[0, 1], want, err_msg=f"bins {bins}")
 
 
 def test_dequantize_special_values():

@@ -60,6 +60,22 @@ __device__ __forceinline__ uint32_t quant1(uint32_t bits16, float f, float Mf) {
     return quant_bits(bf16_to_f32(bits16 & 0xFFFFu), f, Mf) & 0xFFu;
 }
 
+// Factor M/m of a row whose absmax has bits am (sign cleared), uniform across
+// the wave. 0 for an all-zero row, so every symbol is M. A row whose factor
+// overflows fp32 (an absmax below about M * 2^-128, so below 2^-122 for any
+// bins) has no finite factor; it is quantised as an all-zero row too, and am
+// becomes 0, the scale stored for it. Non-finite input (am >= 0x7F80) gives
+// 0; the caller reports it.
+__device__ __forceinline__ float row_factor(uint32_t &am, float Mf) {
+    if (am == 0 || am >= 0x7F80u) return 0.0f;
+    const float f = __fdiv_rn(Mf, bf16_to_f32(am));
+    if (__float_as_uint(f) == 0x7F800000u) {
+        am = 0;
+        return 0.0f;
+    }
+    return f;
+}
+
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 
 // Maximum over the wave, returned in a scalar register: DPP shifts within
@@ -120,7 +136,7 @@ __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict
     const int M = layer_m(mt, k, l);
     const float Mf = (float)M;
     // m == 0 gives f == 0, so every symbol is exactly M.
-    const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
+    const float f = row_factor(am, Mf);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int c0 = (i * 64 + lane) * 8;
@@ -152,7 +168,7 @@ __global__ __launch_bounds__(256) void k_quantize_any(const uint16_t *__restrict
     if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
     const int M = layer_m(mt, k, l);
     const float Mf = (float)M;
-    const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
+    const float f = row_factor(am, Mf);
     for (int c = lane; c < C; c += 64) dst[c] = (uint8_t)quant1(src[c], f, Mf);
     if (lane == 0) scale[row] = (uint16_t)am;
 }
@@ -265,9 +281,9 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
         for (int i = 0; i < NV; ++i)
 #pragma unroll
             for (int j = 0; j < NWD; ++j) am2 = absmax2(am2, v[i][j]);
-        const uint32_t am = wave_max_dpp(max(am2 & 0xFFFFu, am2 >> 16));
+        uint32_t am = wave_max_dpp(max(am2 & 0xFFFFu, am2 >> 16));
         if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
-        const float f = (am == 0 || am >= 0x7F80u) ? 0.0f : __fdiv_rn(Mf, bf16_to_f32(am));
+        const float f = row_factor(am, Mf);
         uint8_t *dst = sym_slab + (int64_t)t * C;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {

@@ -124,7 +124,11 @@ int ocg_default_bins(int nlayers, uint8_t *bins_k, uint8_t *bins_v)
  * The page's expression is two tensor operations (a product by the factor,
  * then the addition of M); they are evaluated in fp32 as the three separately
  * rounded operations f = M / m, y = x * f, z = y + M. A row with m == 0 has
- * no scale to divide by; every symbol of it is M (so it decodes to zero). */
+ * no scale to divide by; every symbol of it is M (so it decodes to zero).
+ * Nor has a row whose factor M / m overflows fp32 (m below about
+ * M * 2^-128, so below 2^-122 for any bins): the page's expression gives no
+ * finite value there, and such a row is quantised as an all-zero row, with
+ * scale 0. */
 int ocg_quantize(int L, int T, int C, const uint8_t *bins_k, const uint8_t *bins_v,
                  const uint16_t *kv, uint8_t *sym, uint16_t *scale)
 {
@@ -145,13 +149,18 @@ int ocg_quantize(int L, int T, int C, const uint8_t *bins_k, const uint8_t *bins
                     if (a > m)
                         m = a;
                 }
-                scale[((size_t)k * L + l) * T + t] = bf16_exact_bits(m);
-                if (m == 0.0f) {
+                float f = m == 0.0f ? 0.0f : Mf / m;
+                if (m == 0.0f || isinf(f)) {
+                    /* No finite factor: an all-zero row, or an absmax so
+                     * small (below about M * 2^-128) that M / m overflows
+                     * fp32. Either row is quantised as all-zero: every
+                     * symbol M, scale 0 (it decodes to zeros). */
+                    scale[((size_t)k * L + l) * T + t] = 0;
                     for (int c = 0; c < C; ++c)
                         out[c] = (uint8_t)M;
                     continue;
                 }
-                float f = Mf / m;
+                scale[((size_t)k * L + l) * T + t] = bf16_exact_bits(m);
                 for (int c = 0; c < C; ++c) {
                     float y = bf16_value(row[c]) * f;
                     float z = y + Mf;

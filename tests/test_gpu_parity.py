@@ -103,6 +103,34 @@ def test_degenerate_inputs():
     _check_all(zeros, *oracle.default_bins(1))
 
 
+def test_tiny_rows():
+    """Rows in the subnormal range: some keep a finite factor M / m, others
+    overflow it and are quantised as all-zero rows (scale 0). Stage calls,
+    the fused quantiser of cg_to_bytes (C = 512, T % 8 == 0, so packed
+    symbols too) and the decode must all match the oracle bit for bit, which
+    also needs fp32 subnormals kept, not flushed, on the device."""
+    import torch
+
+    from kv_cache_compression_layer_amd.synth import bf16_bits_to_f32, f32_to_bf16_bits
+
+    L, T, H, D = 2, 264, 4, 128
+    kv = generate_kv(L, T, H, D, outlier_frac=0.02, outlier_scale=8.0, seed=31)
+    x = bf16_bits_to_f32(kv).astype(np.float64)
+    sh = np.random.default_rng(31).integers(118, 140, (L, 2, T, 1, 1)).astype(np.float64)
+    sh[:, :, ::3] = 0  # every third row stays normal
+    kv = f32_to_bf16_bits((x * np.exp2(-sh)).astype(np.float32))
+    bk = np.array([4, 32], np.uint8)
+    bv = np.array([32, 4], np.uint8)
+    sym, scale = oracle.quantize(kv, bk, bv)
+    assert (scale == 0).any() and ((scale > 0) & (scale < 0x80)).any()  # both kinds of tiny row occur
+    _check_all(kv, bk, bv)
+    want = oracle.to_bytes(kv, bk, bv)
+    blob = cgb.to_bytes(to_dev(kv).view(torch.bfloat16), bk, bv)
+    assert to_np(blob).tobytes() == want
+    out = to_np(cgb.from_bytes(blob).view(torch.int16), np.uint16)
+    assert_bf16_equal(out, oracle.from_bytes(want), "decoded tiny rows")
+
+
 def test_long_streams_leave_the_stage():
     """White noise at 128 bins: streams of ~200 bytes exceed the 128-byte
     on-chip stage and go through the fix-up kernel."""

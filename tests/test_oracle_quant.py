@@ -59,19 +59,28 @@ def _numpy_quantize(kv_bits, bins_k, bins_v):
             row = x[l, k]
             m = np.max(np.abs(row), axis=-1)
             scale[k, l] = m
-            with np.errstate(divide="ignore"):
+            with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
                 f = (M / m).astype(np.float32)
-            y = (row * f[:, None]).astype(np.float32)
-            z = (y + M).astype(np.float32)
-            q = np.clip(np.rint(z), 0, 2 * M)
-            q[m == 0] = M
+                y = (row * f[:, None]).astype(np.float32)
+                z = (y + M).astype(np.float32)
+                q = np.clip(np.rint(z), 0, 2 * M)
+            flush = (m == 0) | ~np.isfinite(f)
+            q[flush] = M
+            scale[k, l][flush] = 0
             sym[k, l] = q.astype(np.uint8)
     return sym, scale
 
 
-@pytest.mark.parametrize("seed,L,T,H,D", [(1, 3, 37, 2, 24), (2, 12, 64, 12, 64), (3, 2, 300, 1, 33)])
-def test_quantize_matches_independent_numpy(seed, L, T, H, D):
+@pytest.mark.parametrize("seed,L,T,H,D,tiny", [(1, 3, 37, 2, 24, False), (2, 12, 64, 12, 64, False),
+                                                (3, 2, 300, 1, 33, False), (4, 12, 40, 2, 16, True)])
+def test_quantize_matches_independent_numpy(seed, L, T, H, D, tiny):
     kv = generate_kv(L, T, H, D, outlier_frac=0.05, outlier_scale=20.0, seed=seed).reshape(L, 2, T, H * D)
+    if tiny:
+        # Rows scaled into the subnormal range, 2^-121 .. 2^-136: some keep a
+        # finite factor, others overflow it and are flushed.
+        x = bf16_bits_to_f32(kv).astype(np.float64)
+        sh = np.random.default_rng(seed).integers(121, 137, (L, 2, T, 1))
+        kv = f32_to_bf16_bits((x * np.exp2(-sh.astype(np.float64))).astype(np.float32))
     bk, bv = oracle.default_bins(L)
     sym, scale = oracle.quantize(kv, bk, bv)
     ref_sym, ref_scale = _numpy_quantize(kv, bk, bv)
@@ -104,6 +113,30 @@ def test_quantize_invariants():
             assert np.all(s[row == 0] == M)
     assert np.all(sym[0, 1, 3] == (32 // 2 - 1))
     assert scale[0, 1, 3] == 0
+
+
+def test_quantize_tiny_rows():
+    """Rows so small that the factor M / m overflows fp32 (m below about
+    M * 2^-128) are quantised as all-zero rows (every symbol M, scale 0);
+    smaller M keeps a finite factor for the same row. Hand-derived:
+    row [2^-127, -2^-128, 0, 2^-133] (bf16 subnormals 0x0040, 0x8020, 0,
+    0x0001): with bins 4 (M = 1), f = 2^127 is finite, x*f + 1 =
+    [2, 0.5, 1, 1 + 2^-6] -> [2, 0, 1, 1] (0.5 to even 0); with bins 32
+    (M = 15), 15 * 2^127 overflows -> [15] * 4, scale 0. Row [2^-126,
+    -2^-126, 2^-127, 0] (0x0080 normal): bins 4 -> f = 2^126, x*f + 1 =
+    [2, 0, 1.5, 1] -> [2, 0, 2, 1]; bins 32 -> 15 * 2^126 overflows."""
+    rows = np.array([[0x0040, 0x8020, 0x0000, 0x0001], [0x0080, 0x8080, 0x0040, 0x0000]], np.uint16)
+    kv = np.empty((2, 2, 2, 4), np.uint16)
+    kv[:] = rows
+    bk = np.array([4, 32], np.uint8)
+    sym, scale = oracle.quantize(kv, bk, bk)
+    for k in range(2):
+        assert sym[k, 0, 0].tolist() == [2, 0, 1, 1] and scale[k, 0, 0] == 0x0040
+        assert sym[k, 0, 1].tolist() == [2, 0, 2, 1] and scale[k, 0, 1] == 0x0080
+        assert sym[k, 1, 0].tolist() == [15] * 4 and scale[k, 1, 0] == 0
+        assert sym[k, 1, 1].tolist() == [15] * 4 and scale[k, 1, 1] == 0
+    out = oracle.dequantize(sym, scale, bk, bk)
+    assert not out[1].any()  # the flushed rows decode to +0
 
 
 def test_quantize_rejects_nonfinite():

@@ -17,7 +17,9 @@
  * - Pointers marked "device" are HIP device pointers. The caller allocates
  *   and owns every buffer, including the workspace `ws`; the library never
  *   allocates, frees or keeps state between calls, so concurrent calls on
- *   different streams with different workspaces are safe.
+ *   different streams with different workspaces are safe. (The one
+ *   exception is cg_from_bytes_noalloc, whose workspace is a fixed device
+ *   array inside the library; see there.)
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
  *   device work is enqueued asynchronously on it, in order.
  * - Conditions only the device can see (NaN/Inf input, a corrupt stream,
@@ -221,6 +223,22 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
  * in bytes; kv_out: device bf16 [L,2,T,H,D]. */
 int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,
                   void *ws, size_t ws_bytes, void *stream);
+
+/* from_bytes for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same decode and output as cg_from_bytes, with no workspace argument and no
+ * allocation. Its workspace is a fixed 4 MiB device array inside the library,
+ * one per GPU (the current device's), kept until the process ends; calls
+ * whose cg_workspace_bytes(desc, CG_OP_FROM_BYTES) exceeds 4 MiB return
+ * CG_E_WORKSPACE before launching anything (the 32-layer, 1024-channel,
+ * 32768-token call needs about 1.05 MiB). status_dev: caller-owned device
+ * uint32 (4-byte aligned) that the call clears and then sets to the status
+ * bits; cg_read_status(status_dev, stream) turns it into a code. Every call
+ * on a GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (different streams or threads) race and must not be made. The stream's
+ * device must be the current device. */
+int cg_from_bytes_noalloc(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,
+                          uint32_t *status_dev, void *stream);
 
 /* from_bytes of a range of chunks: decodes chunks [chunk_begin, chunk_end)
  * (tokens [256*chunk_begin, min(256*chunk_end, T))) of a blob whose bytes

@@ -110,6 +110,7 @@ _SIGNATURES = {
     "cg_dequantize": (ctypes.c_int, [_P, _P, _P, _P, _P, _SZ, _P]),
     "cg_to_bytes": (ctypes.c_int, [_P, _P, _P, _SZ, _P, _P, _SZ, _P]),
     "cg_from_bytes": (ctypes.c_int, [_P, _P, _SZ, _P, _P, _SZ, _P]),
+    "cg_from_bytes_noalloc": (ctypes.c_int, [_P, _P, _SZ, _P, _P, _P]),
     "cg_from_bytes_paged": (ctypes.c_int, [_P, _P, _SZ, _P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                            _P, ctypes.c_int32, _P, _SZ, _P]),
     "cg_from_bytes_chunks": (ctypes.c_int, [_P, _P, _SZ, _I32, _I32, _P, _P, _SZ, _P]),
@@ -385,6 +386,21 @@ def cg_from_bytes(desc, blob, blob_size, kv_out, ws, stream=None):
     _check(lib().cg_from_bytes(desc.ptr, _dev(blob, "blob", torch.uint8), blob_size,
                                _dev(kv_out, "kv_out", (torch.bfloat16, torch.uint16, torch.int16), 2 * L * T * C),
                                p, n, _stream_handle(stream)), "cg_from_bytes")
+
+
+def cg_from_bytes_noalloc(desc, blob, blob_size, kv_out, status, stream=None):
+    """cg_from_bytes with the library's own fixed workspace (no allocation);
+    status: a device int32/uint32 tensor of at least one element that
+    receives the status word (read it with cg_read_status(status))."""
+    torch = _torch()
+    L, T, C = desc.nlayers, desc.ntokens, desc.nchannels
+    if blob_size > blob.numel():
+        raise ValueError("blob_size exceeds the blob tensor")
+    _check(lib().cg_from_bytes_noalloc(desc.ptr, _dev(blob, "blob", torch.uint8), blob_size,
+                                       _dev(kv_out, "kv_out", (torch.bfloat16, torch.uint16, torch.int16),
+                                            2 * L * T * C),
+                                       _dev(status, "status", (torch.int32, torch.uint32), 1),
+                                       _stream_handle(stream)), "cg_from_bytes_noalloc")
 
 
 def cg_from_bytes_chunks(desc, blob, blob_size, chunk_begin, chunk_end, kv_out, ws, stream=None):

@@ -4,10 +4,19 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "cg_internal.hpp"
 
 using namespace cg;
+
+// Workspace of cg_from_bytes_noalloc: file-scope device memory, one copy per
+// GPU the library runs on, held until the process ends. Host code never
+// passes this name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the device address that hipGetSymbolAddress returns for
+// the current device.
+constexpr size_t kNoAllocScratchBytes = 4u << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -319,6 +328,25 @@ BatchGeom batch_geom(const cg_desc *desc, const Dims &d, const Dims &vd, int B, 
     return g;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CG_E_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CG_E_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -569,6 +597,39 @@ int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, vo
                   reinterpret_cast<const uint16_t *>(blob + b.off_scales)};
     return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
                                 at<uint32_t>(ws, 0), s));
+}
+
+int cg_from_bytes_noalloc(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,
+                          uint32_t *status_dev, void *stream) {
+    Dims d;
+    int rc = make_dims(desc, d);
+    if (rc) return rc;
+    if (!blob || !kv_out || !status_dev) return CG_E_INVAL;
+    if ((uintptr_t)blob % 8 || (uintptr_t)status_dev % 4) return CG_E_INVAL;
+    const WsLayout w = ws_layout(d, CG_OP_FROM_BYTES);
+    if (w.total > kNoAllocScratchBytes) return CG_E_WORKSPACE;
+    const BlobLayout b = blob_layout(d);
+    if ((uint64_t)blob_size < b.off_payload) return CG_E_CORRUPT;
+    void *ws = nullptr;
+    if ((rc = scratch_address(&ws))) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    MaxTable mt;
+    make_max_table(desc, d, mt);
+    // The status word is the caller's; nothing else in the scratch needs to
+    // start at zero (tile offsets and scan partials are written before they
+    // are read).
+    if ((rc = hip_rc(launch_fill_u32(status_dev, 0u, 1, s)))) return rc;
+    DecodeIn in{blob + b.off_payload,
+                (uint64_t)blob_size - b.off_payload,
+                reinterpret_cast<const uint16_t *>(blob + b.off_lengths),
+                reinterpret_cast<const uint64_t *>(blob + b.off_chunk_off),
+                nullptr,
+                reinterpret_cast<const uint16_t *>(blob + b.off_cdf),
+                at<uint32_t>(ws, w.wpre)};
+    DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
+                  reinterpret_cast<const uint16_t *>(blob + b.off_scales)};
+    return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
+                                status_dev, s));
 }
 
 int cg_from_bytes_chunks(const cg_desc *desc, const uint8_t *blob, size_t blob_size, int32_t chunk_begin,

@@ -149,7 +149,10 @@ int64_t cg_blob_bound(const cg_desc *desc);
 /* Section offsets of the blob for `desc` (blob_size set to 0). */
 int cg_blob_layout(const cg_desc *desc, cg_blob_info *out);
 
-/* Parses a blob header held in HOST memory (the first n bytes of a blob; n
+/* [P2 s4, s5] The encoder output carries, beside the streams, what the
+ * decoder needs to restore them (the page pickles it with the bytes and
+ * lengths); this parses the header of the flat blob that replaces the pickle.
+ * Parses a blob header held in HOST memory (the first n bytes of a blob; n
  * must cover the header, i.e. 48 + 2*nlayers bytes). Fills `out` and copies
  * the bins into bins_k / bins_v (host arrays of bins_cap bytes). Returns
  * CG_E_CORRUPT for a bad magic, version, dtype, shape or bins, and
@@ -211,14 +214,18 @@ int cg_dequantize(const cg_desc *desc, const uint8_t *sym, const uint16_t *scale
 
 /* ------------------------------------------------------ whole-blob calls */
 
-/* to_bytes: the whole encode path on [L,2,T,H,D] bf16 KV, writing the blob
+/* [P2 s2-s4] to_bytes (the page's CacheGenSerializer.to_bytes on
+ * [L,2,T,H,D]): split into K and V, quantise, histogram and CDF, range-code
+ * the 256-token streams and serialise. The whole encode path on bf16 KV, writing the blob
  * described at cg_blob_info into `blob` (device, `cap` bytes; cap >=
  * cg_blob_bound() can never overflow). The blob size is written to
  * *blob_size_dev (device uint64) and into the header. */
 int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
                 uint64_t *blob_size_dev, void *ws, size_t ws_bytes, void *stream);
 
-/* from_bytes: the whole decode path. `desc` must be the one cg_blob_peek
+/* [P2 s5] from_bytes (the page's CacheGenDeserializer.from_bytes): stream
+ * offsets from the prefix sums of the lengths, CDF-driven decode, (t - M) / M
+ * * max and the stack back to [L,2,T,H,D] in bf16. The whole decode path. `desc` must be the one cg_blob_peek
  * returned for this blob (bins included); blob: device; blob_size: its size
  * in bytes; kv_out: device bf16 [L,2,T,H,D]. */
 int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,

@@ -11,9 +11,12 @@ per-layer bins, seeded AR(1) generator with 1% outlier channels x20.
 
 Prints ONE JSON line. ``value`` is the round-trip throughput: raw KV bytes /
 (encode time + decode time). Encode and decode GB/s, the compression ratio,
-per-stage times, the roofline of the dominant kernel (timed live with HIP
-events on the stream the library launches on) and the CPU oracle timed on a
-bounded sample are reported beside it.
+per-stage times, the HBM roofline of each direction (whole entry-point calls
+timed live with HIP events on the stream the library launches on; the one
+furthest from its roofline is ``roofline``), and the CPU oracle on the same
+input (all host cores on the whole tensor, one thread on a slab of it) are
+reported beside it; the oracle's blob and decode also check the GPU's
+(``verified``: SHA-256 of the blobs, count of differing decoded values).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -51,7 +54,8 @@ def parse_args():
                     help="skip the pipelined host-to-device load measurement")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the encode/decode timing of the other model-shaped workloads")
-    ap.add_argument("--cpu-sample-layers", type=int, default=8)
+    ap.add_argument("--cpu-slab-layers", type=int, default=4,
+                    help="layers of the benchmark input the one-thread oracle timing takes")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -73,36 +77,45 @@ def time_events(fn, reps, torch):
     return s.elapsed_time(e) / reps
 
 
-def recorded_traffic(workload):
-    """HBM bytes per launch of the fused decoder, from the calibrated rocprofv3
-    counters committed under profiles/, if they were taken on this workload
-    and on the decoder sources as they are now; otherwise None."""
+def source_hash():
+    """SHA-256 over the library's device sources (every kernel)."""
     import glob
     import hashlib
 
     h = hashlib.sha256()
-    for rel in ("kv_cache_compression_layer_amd/csrc/cg_decode.hip",
-                "kv_cache_compression_layer_amd/csrc/cg_internal.hpp"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    sha = h.hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "kv_cache_compression_layer_amd", "csrc", "*"))):
+        if path.endswith((".hip", ".hpp")):
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, entry_point):
+    """HBM bytes per call of an entry point (its kernels' calibrated
+    rocprofv3 FETCH_SIZE + WRITE_SIZE), from the summaries committed under
+    profiles/, if they were taken on this workload and on the device sources
+    as they are now; otherwise None."""
+    import glob
+
+    sha = source_hash()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md"))):
         with open(path) as f:
             for line in f:
-                if not line.startswith("traffic k_decode_fused "):
+                if not line.startswith(f"traffic {entry_point} "):
                     continue
                 kv = dict(item.split("=", 1) for item in line.split()[2:])
                 if kv.get("workload") == workload and kv.get("source_sha256") == sha:
-                    return int(kv["bytes_per_launch"]), os.path.relpath(path, ROOT)
+                    return int(kv["bytes_per_call"]), os.path.relpath(path, ROOT)
     return None
 
 
-def other_workloads(torch, cgb, dev, skip):
+def other_workloads(torch, cgb, dev, skip, oracle_too):
     """Whole-blob encode and decode times of the other model-shaped workloads
     (one call each, inputs resident on the device, HIP events on the current
     stream): OPT-125m at 64 tokens (latency), Mistral-7B at 256 and 768
     tokens, GLM-4-9B at 16K tokens (its decode from a blob encoded before the
-    timed region). Medians over the repetitions."""
+    timed region). Medians over the repetitions. With oracle_too, the CPU
+    oracle is timed on each same input, on one thread and on all threads."""
     from kv_cache_compression_layer_amd.synth import WORKLOADS, generate_workload
 
     out = {}
@@ -111,7 +124,8 @@ def other_workloads(torch, cgb, dev, skip):
         if name == skip:
             continue
         w = WORKLOADS[name]
-        kv = torch.from_numpy(generate_workload(w).view(np.int16)).to(dev).view(torch.bfloat16)
+        kv_np = generate_workload(w)
+        kv = torch.from_numpy(kv_np.view(np.int16)).to(dev).view(torch.bfloat16)
         desc = cgb.Desc.for_kv(tuple(kv.shape))
         blob = torch.empty(cgb.cg_blob_bound(desc), dtype=torch.uint8, device=dev)
         size_dev = torch.zeros(1, dtype=torch.int64, device=dev)
@@ -150,41 +164,106 @@ def other_workloads(torch, cgb, dev, skip):
                      "compression_ratio": raw / nbytes, "encode_ms": enc_ms, "decode_ms": dec_ms,
                      "encode_GBps": raw / (enc_ms * 1e-3) / 1e9, "decode_GBps": raw / (dec_ms * 1e-3) / 1e9,
                      "reps": reps}
+        if oracle_too:
+            # The oracle on the same input, one thread and all threads.
+            bk_np, bv_np = np.asarray(desc.bins_k, np.uint8), np.asarray(desc.bins_v, np.uint8)
+            for threads in sorted({1, oracle_threads()}):
+                te, td, _, _ = time_oracle(kv_np, bk_np, bv_np, threads)
+                out[name][f"oracle_{threads}t"] = {"encode_GBps": raw / te / 1e9, "decode_GBps": raw / td / 1e9,
+                                                   "round_trip_GBps": raw / (te + td) / 1e9, "threads": threads}
         log(f"{name}: {json.dumps({k: v for k, v in out[name].items() if k != 'shape'})}")
-        del kv, blob, ws_e, ws_d, kv_out
+        del kv, kv_np, blob, ws_e, ws_d, kv_out
         torch.cuda.empty_cache()
     return out
 
 
-def cpu_baseline(w, layers):
-    """The oracle (scalar C, one thread) on layers [0, layers) of the workload."""
-    import oracle
-    from kv_cache_compression_layer_amd.synth import generate_kv
+def cpu_info():
+    """CPU model, SMT state and core counts of this host."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    smt = None
+    try:
+        with open("/sys/devices/system/cpu/smt/active") as f:
+            smt = "on" if f.read().strip() == "1" else "off"
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"cpu": model, "smt": smt, "nproc": os.cpu_count(), "affinity": affinity}
 
-    kv = generate_kv(layers, w.ntokens, w.nheads, w.head_size, rho=w.rho, innovations=w.innovations,
-                     outlier_frac=w.outlier_frac, outlier_scale=w.outlier_scale, seed=w.seed + 500)
-    bk, bv = oracle.default_bins(w.nlayers)
-    bk, bv = bk[:layers], bv[:layers]
+
+def oracle_threads():
+    """Host threads for the multi-threaded oracle: all the cores this process
+    may use, at most 16 (one GPU's share of a shared host)."""
+    info = cpu_info()
+    return max(1, min(16, info["affinity"] or 1))
+
+
+def time_oracle(kv_np, bk, bv, threads):
+    """to_bytes then from_bytes of the oracle on kv_np; seconds and outputs."""
+    import oracle
+
     t0 = time.perf_counter()
-    blob = oracle.to_bytes(kv, bk, bv)
+    blob = oracle.to_bytes(kv_np, bk, bv, threads=threads)
     t1 = time.perf_counter()
-    oracle.from_bytes(blob)
+    dec = oracle.from_bytes(blob, threads=threads)
     t2 = time.perf_counter()
-    raw = kv.nbytes
+    return t1 - t0, t2 - t1, blob, dec
+
+
+def cpu_baseline(w, kv_np, bk, bv, gpu_blob, gpu_out, slab_layers):
+    """The oracle (scalar C) on this host, on the benchmark's own input: all
+    layers on all threads (which also checks the GPU's blob and decode), and a
+    slab of the first `slab_layers` layers of the same tensor on one thread."""
+    import hashlib
+
+    threads = oracle_threads()
+    raw = kv_np.nbytes
+    log(f"cpu baseline: oracle on the whole input, {threads} threads")
+    te, td, blob, dec = time_oracle(kv_np, bk, bv, threads)
+    sha_o = hashlib.sha256(blob).hexdigest()
+    sha_g = hashlib.sha256(gpu_blob).hexdigest()
+    ndiff = int(np.count_nonzero(dec.reshape(-1) != gpu_out.reshape(-1)))
+    verified = {"blob_sha256_gpu": sha_g, "blob_sha256_oracle": sha_o, "blob_equal": sha_g == sha_o,
+                "decoded_values_differing": ndiff, "decoded_values": int(dec.size)}
+    log(f"verified: {json.dumps(verified)}")
+    del blob, dec
+    sub = np.ascontiguousarray(kv_np[:slab_layers])
+    sraw = sub.nbytes
+    log(f"cpu baseline: oracle on layers 0-{slab_layers - 1}, 1 thread")
+    te1, td1, _, _ = time_oracle(sub, bk[:slab_layers], bv[:slab_layers], 1)
+    info = cpu_info()
     return {
-        "value": raw / (t2 - t0) / 1e9,
+        "value": raw / (te + td) / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"layers 0-{layers - 1} of {w.name} ({layers}x2x{w.ntokens}x{w.nheads}x{w.head_size} bf16, "
-                  f"{raw / 2**20:.0f} MiB; same generator, seed {w.seed + 500}, bins of those layers); "
-                  f"to_bytes then from_bytes, single thread",
-        "encode_GBps": raw / (t1 - t0) / 1e9,
-        "decode_GBps": raw / (t2 - t1) / 1e9,
-        "seconds": t2 - t0,
-        "cpu": platform.processor() or platform.machine(),
-        "nproc": os.cpu_count(),
-    }
+        "sample": f"the whole benchmark input ({w.name}, seed {w.seed}, {raw / 2**30:.0f} GiB of bf16 KV): "
+                  f"to_bytes then from_bytes, {threads} threads over the layers",
+        "encode_GBps": raw / te / 1e9,
+        "decode_GBps": raw / td / 1e9,
+        "seconds": te + td,
+        "single_thread": {
+            "value": sraw / (te1 + td1) / 1e9,
+            "unit": "GB/s",
+            "cores": 1,
+            "sample": f"layers 0-{slab_layers - 1} of the same tensor as one {slab_layers}-layer call "
+                      f"({sraw / 2**20:.0f} MiB; their bins): to_bytes then from_bytes",
+            "encode_GBps": sraw / te1 / 1e9,
+            "decode_GBps": sraw / td1 / 1e9,
+            "seconds": te1 + td1,
+        },
+        **info,
+    }, verified
 
 
 def main():
@@ -213,7 +292,6 @@ def main():
     kv_np = generate_workload(w)
     log(f"generated in {time.perf_counter() - t0:.1f}s")
     kv = torch.from_numpy(kv_np.view(np.int16)).to(dev).view(torch.bfloat16)
-    del kv_np
 
     desc = cgb.Desc.for_kv(tuple(kv.shape))
     A = desc.alphabet
@@ -479,46 +557,34 @@ def main():
     del kv_copy
     log(f"copy {copy_ms:.3f} ms = {copy_GBps:.0f} GB/s")
 
-    # Algorithmic HBM bytes of the main kernel behind each entry point.
-    nstreams = desc.nstreams
-    len_bytes = 2 * nstreams
-    alg_bytes = {
-        # k_quantize: read bf16 KV, write u8 symbols and bf16 scales.
-        "quantize": 2 * N + N + 4 * L * T,
-        # k_histogram + k_cdf: read symbols, write int32 tables.
-        "build_cdf": N + 4 * 2 * L * C * (A + 1),
-        # k_encode: read symbols and tables, write payload, lengths, offsets.
-        "encode": N + 4 * 2 * L * C * (A + 1) + payload_bytes + len_bytes + 8 * (desc.nchunks + 1),
-        # k_decode (stage): read payload, lengths, tables; write symbols.
-        "decode": payload_bytes + len_bytes + 4 * 2 * L * C * (A + 1) + N,
-        # k_dequantize: read symbols + scales, write bf16.
-        "dequantize": N + 4 * L * T + 2 * N,
-        # k_lenscan + k_decode fused: read the blob, write bf16 KV.
-        "from_bytes": blob_size + 2 * N,
+    # Roofline of each direction: the algorithmic bytes of the metric (read the
+    # bf16 KV and write the blob, or read the blob and write the bf16 KV) over
+    # the whole entry point's time. Each call is a short sequence of kernels
+    # launched back to back on one stream; HIP events on that stream bracket
+    # the call, averaged over the timed steps. The kernel split of one call is
+    # in the rocprofv3 kernel trace under profiles/.
+    def direction(entry, kernels, ms):
+        alg = raw + blob_size
+        ach = alg / (ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+             "traffic": None, "kernel": f"{entry}: {kernels}", "entry_point": entry,
+             "algorithmic_bytes": alg, "avg_ms": ms,
+             "timing": "whole entry-point call; HIP events on the stream the library launches on, "
+                       "average over the timed steps",
+             "frac_of_copy": ach / copy_GBps}
+        rec = recorded_traffic(w.name, entry)
+        if rec is not None:
+            r["traffic"], r["traffic_source"] = rec
+            r["traffic_ratio"] = rec[0] / alg
+        return r
+
+    directions = {
+        "encode": direction("cg_to_bytes", "quantise + histogram (+ tables), range encode, offset scans, "
+                                           "compaction", enc_ms),
+        "decode": direction("cg_from_bytes", "length scan, range decode + dequantise", dec_ms),
     }
-    kernel_of = {"quantize": "k_quantize_vec", "build_cdf": "k_histogram4 + k_cdf", "encode": "k_encode",
-                 "decode": "k_decode (symbols out)", "dequantize": "k_dequantize",
-                 "from_bytes": "k_decode (fused dequantise, bf16 out)"}
-    path_stages = ["quantize", "build_cdf", "encode", "from_bytes"]
-    dom = max(path_stages, key=lambda k: stages_ms[k])
-    achieved = alg_bytes[dom] / (stages_ms[dom] * 1e-3) / 1e9
-    roofline = {
-        "bound": "hbm",
-        "achieved": achieved,
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": achieved / HBM_PEAK_GBPS,
-        "traffic": None,
-        "kernel": kernel_of[dom],
-        "entry_point": f"cg_{dom}" if dom != "from_bytes" else "cg_from_bytes",
-        "algorithmic_bytes": alg_bytes[dom],
-        "avg_ms": stages_ms[dom],
-        "frac_of_copy": achieved / copy_GBps,
-    }
-    rec = recorded_traffic(w.name) if dom == "from_bytes" else None
-    if rec is not None:
-        roofline["traffic"] = rec[0]
-        roofline["traffic_source"] = rec[1]
+    # The contract's single entry: the direction furthest from its roofline.
+    roofline = dict(min(directions.values(), key=lambda r: r["frac"]))
 
     enc_GBps = raw / (enc_ms * 1e-3) / 1e9
     dec_GBps = raw / (dec_ms * 1e-3) / 1e9
@@ -565,15 +631,21 @@ def main():
         "chunked_batch": batch,
         "streaming": streaming,
         "roofline": roofline,
+        "roofline_by_direction": directions,
         "cpu_baseline": None,
     }
 
     del sym, sym2, kv_out2, payload
     if not args.no_other_workloads:
-        result["other_workloads"] = other_workloads(torch, cgb, dev, w.name)
+        result["other_workloads"] = other_workloads(torch, cgb, dev, w.name, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_sample_layers} layers")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_layers)
+        gpu_blob = blob[:blob_size].cpu().numpy()
+        gpu_out = kv_out.view(torch.int16).cpu().numpy().view(np.uint16)
+        bk_np = np.asarray(desc.bins_k, np.uint8)
+        bv_np = np.asarray(desc.bins_v, np.uint8)
+        result["cpu_baseline"], result["verified"] = cpu_baseline(w, kv_np, bk_np, bv_np, gpu_blob, gpu_out,
+                                                                 args.cpu_slab_layers)
+        del gpu_blob, gpu_out
     line = json.dumps(result)
     print(line, flush=True)
     if args.json_out:

@@ -541,6 +541,458 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
         atomicOr(a.status, kStCorrupt);
 }
 
+// ------------------------------------------------------------------------
+// Two adjacent channels per lane (calls of eight chunks or more).
+//
+// A block of NW waves owns 128 consecutive channels of one (K|V, layer) and
+// NW chunks, one per wave; lane i decodes the streams of channels
+// 128 * cb2 + 2i and 2i + 1 of its wave's chunk, interleaved. Both streams of
+// a lane are at the same token, so one per-token scale serves both, their two
+// bf16 results leave in one 32-bit store, and the row address (of a paged
+// cache too) is computed once. The wave's 128 streams are the two adjacent
+// 64-stream tiles 2 * cb2 and 2 * cb2 + 1 of the chunk, one contiguous run of
+// payload bytes starting at the first tile's offset. Tables [symbol][stream]
+// [lane], start | freq << 16, shared by the block's waves.
+// Pool bytes per wave: four blocks of eight waves (32 waves) per CU fit the
+// 160 KiB of LDS with 16-entry tables (8 KiB per block) and 3840 bytes per
+// wave, or with 32-entry tables (16 KiB) and 2928 bytes per wave.
+__host__ __device__ constexpr uint32_t pool_per_wave2(int loga) { return loga <= 4 ? 3840u : 2928u; }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <bool FUSED, int LOGA, bool CLAMP, bool STAGED, bool HALF, bool PAGED, bool TAIL, bool FULL>
+__device__ __forceinline__ void decode_loop2(const DecArgs &a, DecStream (&st)[2], int n, uint32_t rowoff,
+                                             int pg_t0, int pg_b0, uint32_t pg_v, const uint32_t *tab,
+                                             const float *dq, uint32_t (&sc_v)[4], const uint8_t *pool,
+                                             __amdgpu_buffer_rsrc_t out_rsrc, uint32_t out_voff, int lane, int W,
+                                             int slab, const int (&cch)[2], uint64_t &bad_mask) {
+    constexpr int S = 2;
+    auto fetch = [&](int s) -> uint32_t {
+        DecStream &d = st[s];
+        if (STAGED) return pool[d.ptr++];
+        const uint32_t v = d.pos < d.len ? (uint32_t)d.gsrc[d.pos] : 0u;
+        ++d.pos;
+        return v;
+    };
+    uint32_t nx0[S], nx1[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        for (int i = 0; i < 4; ++i) st[s].code = (st[s].code << 8) | fetch(s);
+        nx0[s] = fetch(s);
+        nx1[s] = fetch(s);
+        if (STAGED) st[s].ptr -= 2;
+        else st[s].pos -= 2;
+    }
+
+    // Byte address in tab of (symbol q, stream s, this lane): q * RB + s * 256 + lane * 4.
+    constexpr uint32_t RB = 512u;
+    const uint8_t *tabb = reinterpret_cast<const uint8_t *>(tab);
+    uint32_t lane4[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) lane4[s] = (uint32_t)s * 256u + (uint32_t)lane * 4u;
+    auto start_at = [&](uint32_t ad) -> uint32_t { return *reinterpret_cast<const uint32_t *>(tabb + ad) & 0xFFFFu; };
+    const int WL = W < (1 << LOGA) ? W : (1 << LOGA);
+    constexpr int SD = HALF ? LOGA - 1 : LOGA;
+    constexpr uint32_t H1 = 1u << (SD - 1), H2 = 1u << (SD - 2);
+    uint32_t amax4[S], ltop4[S], top4[S], cdf_a[S], cdf_b[S], cdf_c[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        amax4[s] = ((uint32_t)WL - 1) * RB + lane4[s];
+        ltop4[s] = ((1u << LOGA) - 1) * RB + lane4[s];
+        top4[s] = ((1u << SD) - 1) * RB + lane4[s];
+        cdf_a[s] = start_at(H1 * RB + lane4[s]);
+        cdf_b[s] = start_at(H2 * RB + lane4[s]);
+        cdf_c[s] = start_at((H1 + H2) * RB + lane4[s]);
+    }
+    const bool tail_on = TAIL && W > (1 << LOGA);
+
+    // Output of the previous token, written one step late (token t - 1 while
+    // token t is searched; t is the wave-uniform loop counter).
+    float p_dq[S];
+    uint32_t p_sy[S], p_sc = 0;
+    auto row_off = [&](int t) -> uint32_t {
+        if constexpr (PAGED) {
+            const int tt = pg_t0 + t;
+            const uint32_t blk = (uint32_t)__builtin_amdgcn_readlane((int)pg_v, (tt >> a.paged.log2_bs) - pg_b0);
+            const uint32_t row = (blk << a.paged.log2_bs) | (uint32_t)(tt & ((1 << a.paged.log2_bs) - 1));
+            return row * (uint32_t)a.C * 2u;
+        } else {
+            return rowoff + (uint32_t)t * (uint32_t)a.C * (FUSED ? 2u : 1u);
+        }
+    };
+    auto store_all = [&](int t) {
+        // The token is wave-uniform; readfirstlane keeps its row offset in a
+        // scalar register (the buffer store's offset operand).
+        t = __builtin_amdgcn_readfirstlane(t);
+        if (t >= n) return;
+        const uint32_t off = row_off(t);
+        // Written once and not read back here: non-temporal stores (cache policy 2).
+        if constexpr (FUSED) {
+            const float sc = __uint_as_float(p_sc << 16);
+            // Both products rounded to bf16 (nearest even) by one packed
+            // conversion: channel c0 in the low half, c0 + 1 in the high.
+            const f32x2_t x = {__fmul_rn(p_dq[0], sc), __fmul_rn(p_dq[1], sc)};
+            const uint32_t hv = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+            if constexpr (FULL) {
+                __builtin_amdgcn_raw_buffer_store_b32(hv, out_rsrc, (int)out_voff, (int)off, 2);
+            } else {
+                // Channel counts that are not a multiple of 128: stores per
+                // channel, those of idle channels past the buffer (dropped).
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hv, out_rsrc, (int)out_voff, (int)off, 2);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hv >> 16), out_rsrc,
+                                                      (int)(cch[1] < a.C ? out_voff + 2u : 0x7FFFFFF0u), (int)off, 2);
+            }
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)p_sy[0], out_rsrc, (int)out_voff, (int)off, 2);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)p_sy[1], out_rsrc,
+                                                 (int)(cch[1] < a.C ? out_voff + 1u : 0x7FFFFFF0u), (int)off, 2);
+        }
+    };
+
+    for (int tb = 0; tb < n; tb += 64) {
+        const uint32_t cur_sc = sc_v[0];
+        const int tend = min(n, tb + 64);
+        for (int t = tb; t < tend; ++t) {
+            uint32_t r[S], ad[S];
+            // Levels 1 and 2 from registers.
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                r[s] = st[s].range >> 16;
+                const bool hi = __umul24(r[s], cdf_a[s]) <= st[s].code;
+                const uint32_t c2 = hi ? cdf_c[s] : cdf_b[s];
+                const bool hi2 = __umul24(r[s], c2) <= st[s].code;
+                ad[s] = lane4[s] | (hi ? H1 * RB : 0u) | (hi2 ? H2 * RB : 0u);
+            }
+            // Remaining levels: interleaved branch-free binary searches over LDS.
+#pragma unroll
+            for (int i = SD - 3; i >= 0; --i) {
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const uint32_t cand = ad[s] | (RB << i);
+                    ad[s] = __umul24(r[s], start_at(cand)) <= st[s].code ? cand : ad[s];
+                }
+            }
+            // The previous token's output, now that its LDS reads have landed.
+            if (t > 0) store_all(t - 1);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                DecStream &d = st[s];
+                if (HALF && __builtin_amdgcn_ballot_w64(ad[s] == top4[s])) {
+                    __asm__ volatile("" ::: "memory");
+                    if (ad[s] == top4[s]) {
+                        for (uint32_t cand = top4[s] + RB; cand < (1u << LOGA) * RB; cand += RB) {
+                            if (__umul24(r[s], start_at(cand)) > d.code) break;
+                            ad[s] = cand;
+                        }
+                    }
+                }
+                if (CLAMP) ad[s] = min(ad[s], amax4[s]);
+                uint32_t e = *reinterpret_cast<const uint32_t *>(tabb + ad[s]);
+                if (tail_on && __builtin_amdgcn_ballot_w64(ad[s] == ltop4[s])) {
+                    // The search stopped at the last LDS entry: the symbol may lie
+                    // above it (only in streams the quantiser did not make).
+                    // Continue upwards in global memory, every lane the same
+                    // number of steps (a per-lane exit from this loop would make
+                    // the token counter of the whole loop divergent).
+                    __asm__ volatile("" ::: "memory");
+                    bool bad = false;
+                    if (ad[s] == ltop4[s]) {
+                        bool up = true;
+                        for (int sy = 1 << LOGA; sy < W; ++sy) {
+                            uint32_t lo, hi;
+                            cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, min(cch[s], a.C - 1), a.A, W, sy, lo,
+                                       hi);
+                            up = up && __umul24(r[s], lo & 0xFFFFu) <= d.code;
+                            if (up) {
+                                bad |= hi <= lo || hi > kProbOne;
+                                ad[s] = (uint32_t)sy * RB + lane4[s];
+                                e = (lo & 0xFFFFu) | ((hi - lo) << 16);
+                            }
+                        }
+                        if (bad) e = (e & 0xFFFFu) | (1u << 16);
+                    }
+                    bad_mask |= __ballot(bad);
+                }
+                d.code -= __umul24(r[s], e & 0xFFFFu);
+                d.range = __umul24(r[s], e >> 16);
+                if (d.range < kTop) {
+                    // One byte in; a second one (range < 2^16 before: a rare
+                    // symbol) behind a wave-uniform test.
+                    d.code = (d.code << 8) | nx0[s];
+                    d.range <<= 8;
+                    if (STAGED) d.ptr += 1u;
+                    else d.pos += 1u;
+                    if (__builtin_amdgcn_ballot_w64(d.range < kTop)) {
+                        __asm__ volatile("" ::: "memory");  // a real branch, not selects
+                        if (d.range < kTop) {
+                            d.code = (d.code << 8) | nx1[s];
+                            d.range <<= 8;
+                            if (STAGED) d.ptr += 1u;
+                            else d.pos += 1u;
+                        }
+                    }
+                    if (STAGED) {
+                        nx0[s] = pool[d.ptr];
+                        nx1[s] = pool[d.ptr + 1];
+                    } else {
+                        nx0[s] = d.pos < d.len ? (uint32_t)d.gsrc[d.pos] : 0u;
+                        nx1[s] = d.pos + 1 < d.len ? (uint32_t)d.gsrc[d.pos + 1] : 0u;
+                    }
+                }
+                bad_mask |= __ballot(d.code >= d.range);
+                if (FUSED) {
+                    p_dq[s] = *reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(dq) +
+                                                               ((ad[s] >> 7) & ~3u));
+                } else {
+                    p_sy[s] = ad[s] >> 9;
+                }
+            }
+            if (FUSED) p_sc = (uint32_t)__builtin_amdgcn_readlane((int)cur_sc, t & 63);
+        }
+        sc_v[0] = sc_v[1];
+        sc_v[1] = sc_v[2];
+        sc_v[2] = sc_v[3];
+    }
+    if (n > 0) store_all(n - 1);
+}
+
+// At least eight waves per SIMD (at most 64 VGPRs): residency decides the
+// decoder's speed more than anything the registers would save.
+template <bool FUSED, int LOGA, bool CLAMP, int NW, bool PAGED, bool TAIL>
+__global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
+    constexpr int S = 2;
+    __shared__ uint32_t tab[(1 << LOGA) * 128];  // [symbol][stream][lane]
+    __shared__ float dq[128];
+    constexpr uint32_t kPoolBytes = NW * pool_per_wave2(LOGA);
+    __shared__ uint32_t pool_w[(kPoolBytes + kPoolSlack) / 4];  // staged payload
+    __shared__ uint32_t need_w[NW];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int A = a.A;
+    const int CB2 = (a.C + 127) >> 7;
+
+    const int bid = blockIdx.x;
+    const int cb2 = bid % CB2;
+    const int slab = (bid / CB2) % (2 * a.L);
+    const int g = bid / (CB2 * 2 * a.L);
+    const int kv = slab / a.L, l = slab - kv * a.L;
+    int cch[S];
+    bool act[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        cch[s] = cb2 * 128 + 2 * lane + s;
+        act[s] = cch[s] < a.C;
+    }
+    const int M = layer_m(a.mt, kv, l);
+    const int W = layer_w(a.mt, kv, l);
+    if (2 * M + 1 < a.nsym_lo || 2 * M + 1 > a.nsym_hi) return;  // block-uniform
+
+    // This wave's chunk and its 128 streams: lengths, offsets (the two tiles
+    // 2 cb2, 2 cb2 + 1 are adjacent in the payload) and the pool bytes they
+    // need (alignment head + bytes + four zero bytes after each stream).
+    const int jr = g * NW + wv, j = a.j0 + jr;
+    const int n = jr < a.NCr ? min(kChunk, a.T - j * kChunk) : 0;
+    const int t0 = (a.j0 + min(jr, a.NCr - 1)) * kChunk;
+    uint32_t len[S] = {0u, 0u}, excl = 0, total = 0;
+    uint64_t base = 0;
+    bool corrupt = false;
+    if (n) {
+        const uint16_t *lp = a.lengths + ((int64_t)j * 2 * a.L + slab) * a.C;
+#pragma unroll
+        for (int s = 0; s < S; ++s) len[s] = act[s] ? lp[cch[s]] : 0u;
+        const uint32_t pr = len[0] + len[1];
+        const uint32_t incl = wave_incl_scan_u32(pr, lane);
+        total = (uint32_t)__shfl((int)incl, 63, 64);
+        excl = incl - pr;
+        base = a.tile_off[((int64_t)j * 2 * a.L + slab) * a.CB + 2 * cb2];
+        if (base > a.payload_bytes || total > a.payload_bytes - base) {
+            corrupt = true;  // offsets point outside the payload: decode from nothing
+            len[0] = len[1] = excl = total = 0;
+            base = 0;
+        }
+    }
+    const uint32_t need_total = ((uint32_t)(base & 3u) + total + 4u * 128u + 4u + 3u) & ~3u;
+    if (lane == 0) need_w[wv] = need_total;
+    __syncthreads();
+    uint32_t woff = 0;
+    for (int i = 0; i < wv; ++i) woff += need_w[i];
+    const bool staged = woff + need_total <= kPoolBytes;
+
+    DecStream st[S];
+    uint8_t *pool = reinterpret_cast<uint8_t *>(pool_w);
+    uint32_t soff[S];  // offset of each stream from the wave's first payload byte
+    soff[0] = excl;
+    soff[1] = excl + len[0];
+    if (staged) {
+        for (uint32_t i = lane; i < need_total / 4; i += 64) pool_w[woff / 4 + i] = 0;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            // LDS start of this stream: congruent to its payload offset mod 4.
+            const uint64_t g0 = base + soff[s];
+            const uint32_t ls = woff + (uint32_t)(base & 3u) + soff[s] + 4u * (uint32_t)(2 * lane + s);
+            st[s].ptr = ls;
+            if (len[s]) {
+                const uint64_t gend = g0 + len[s];
+                const uint64_t ga = g0 & ~3ull, ge = (gend + 3) & ~3ull;
+                uint32_t la = ls - (uint32_t)(g0 - ga);
+#pragma unroll 4
+                for (uint64_t gw = ga; gw < ge; gw += 4, la += 4) {
+                    uint32_t v = load_word(a.payload, a.payload_bytes, gw);
+                    if (gw < g0) v &= 0xFFFFFFFFu << (8 * (uint32_t)(g0 - gw));
+                    if (gw + 4 > gend) v &= 0xFFFFFFFFu >> (8 * (uint32_t)(gw + 4 - gend));
+                    pool_w[la >> 2] = v;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        st[s].len = len[s];
+        st[s].pos = 0;
+        st[s].gsrc = a.payload + base + soff[s];
+        st[s].range = 0xFFFFFFFFu;
+        st[s].code = 0;
+        if (!staged) st[s].ptr = 0;
+    }
+
+    // Tables, built by the block's waves together: wave w writes symbols w,
+    // w + NW, ...; entries past the table's width W (up to 2^LOGA) have start
+    // 0xFFFF. Idle channels: code stays 0, so they always decode symbol 0,
+    // whose frequency 65535 never forces a renormalisation.
+    bool bad_table = false;
+    for (int q = wv; q < (1 << LOGA); q += NW) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            uint32_t entry = 0xFFFFu;
+            if (q < W && act[s]) {
+                uint32_t lo, hi;
+                cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, cch[s], A, W, q, lo, hi);
+                uint32_t f = hi - lo;
+                if (hi <= lo || hi > kProbOne || (q == 0 && lo != 0) || (q == W - 1 && hi != kProbOne)) {
+                    bad_table = true;
+                    f = 1;
+                }
+                entry = (lo & 0xFFFFu) | (f << 16);
+            } else if (q < W) {
+                entry = q == 0 ? 0xFFFFu << 16 : (uint32_t)q | (1u << 16);
+            }
+            tab[(q * 2 + s) * 64 + lane] = entry;
+        }
+    }
+    // Per-token scales of the chunk: lane i of sc_v[k] holds token 64k + i.
+    uint32_t sc_v[4];
+    {
+        const uint16_t *sp = a.scale + (int64_t)slab * a.T + t0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = 64 * k + lane;
+            sc_v[k] = FUSED && t < n ? (uint32_t)sp[t] : 0u;
+        }
+    }
+    if (FUSED && wv == 0) {
+        dq[lane] = __fdiv_rn((float)(lane - M), (float)M);
+        dq[lane + 64] = __fdiv_rn((float)(lane + 64 - M), (float)M);
+    }
+    __syncthreads();
+
+    // Output rows: a buffer over this (K|V, layer) slab; the row offset is
+    // wave-uniform, the lane offset constant; idle lanes point past the end.
+    const uint32_t esz = FUSED ? 2u : 1u;
+    const uint64_t slab_elems = (uint64_t)a.T * a.C;
+    const void *obase = FUSED ? (const void *)(a.kv + ((int64_t)l * 2 + kv) * (int64_t)slab_elems)
+                              : (const void *)(a.sym + (int64_t)slab * (int64_t)slab_elems);
+    __amdgpu_buffer_rsrc_t out_rsrc = make_rsrc(obase, (uint32_t)(slab_elems * esz));
+    int pg_t0 = 0, pg_b0 = 0;
+    uint32_t pg_v = 0;
+    if constexpr (PAGED) {
+        const uint32_t bs_log = (uint32_t)a.paged.log2_bs;
+        const uint32_t region = ((uint32_t)a.paged.num_blocks << bs_log) * (uint32_t)a.C * 2u;
+        out_rsrc = make_rsrc(a.paged.cache + (int64_t)l * a.paged.layer_stride + (int64_t)kv * a.paged.kv_stride,
+                             region);
+        const int nblk_total = (a.T + (1 << bs_log) - 1) >> bs_log;
+        bool bad_block = false;
+        pg_t0 = t0;
+        pg_b0 = t0 >> bs_log;
+        const int bi = pg_b0 + lane;
+        if (n && bi < nblk_total && bi <= ((t0 + n - 1) >> bs_log)) {
+            const int32_t e = a.paged.table[bi];
+            if (e < 0 || e >= a.paged.num_blocks) {
+                bad_block = true;
+                pg_v = (uint32_t)a.paged.num_blocks;
+            } else {
+                pg_v = (uint32_t)e;
+            }
+        }
+        if (__ballot(bad_block) && lane == 0) atomicOr(a.status, kStCorrupt);
+    }
+    const uint32_t out_voff = act[0] ? (uint32_t)cch[0] * esz : 0x7FFFFFF0u;
+    const uint32_t rowoff = (uint32_t)t0 * (uint32_t)a.C * esz;
+
+    uint64_t bad_mask = 0;
+    // The lower half of the table suffices when every symbol of the layer,
+    // 0..2M, lies below its top entry 2^(LOGA-1) - 1.
+    const bool half = LOGA >= 3 && M + 1 <= (1 << (LOGA - 2));
+    // Every lane's two channels exist and their bf16 pair is 4-byte aligned.
+    const bool full = FUSED && (a.C & 127) == 0;
+#define CG_DL2(ST, HF, FL)                                                                                        \
+    decode_loop2<FUSED, LOGA, CLAMP, ST, HF, PAGED, TAIL, FL>(a, st, n, rowoff, pg_t0, pg_b0, pg_v, tab, dq, sc_v, \
+                                                              pool, out_rsrc, out_voff, lane, W, slab, cch, bad_mask)
+    if (full) {
+        if (half) {
+            if (staged) CG_DL2(true, LOGA >= 3, true);
+            else CG_DL2(false, LOGA >= 3, true);
+        } else {
+            if (staged) CG_DL2(true, false, true);
+            else CG_DL2(false, false, true);
+        }
+    } else {
+        if (half) {
+            if (staged) CG_DL2(true, LOGA >= 3, false);
+            else CG_DL2(false, LOGA >= 3, false);
+        } else {
+            if (staged) CG_DL2(true, false, false);
+            else CG_DL2(false, false, false);
+        }
+    }
+#undef CG_DL2
+    const uint64_t act_mask = __ballot(act[0]) | __ballot(act[1]);
+    if ((__ballot((act[0] || act[1]) && (corrupt || bad_table)) | (bad_mask & act_mask)) && lane == 0)
+        atomicOr(a.status, kStCorrupt);
+}
+
+template <bool FUSED, int LOGA, int NW, bool PAGED, bool TAIL>
+static hipError_t launch_decode2_s(const Dims &d, const DecArgs &a, bool clamp, hipStream_t s) {
+    const int ngroups = (a.NCr + NW - 1) / NW;
+    const int CB2 = (d.C + 127) / 128;
+    const dim3 grid((unsigned)((int64_t)ngroups * 2 * d.L * CB2));
+    if (!clamp)
+        hipLaunchKernelGGL((k_decode2<FUSED, LOGA, false, NW, PAGED, TAIL>), grid, dim3(64 * NW), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_decode2<FUSED, LOGA, true, NW, PAGED, TAIL>), grid, dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+}
+
+// One launch of the paired decoder over every slab, with tables of the
+// call's width; the 16-bin slabs search the lower half. (A 16-entry launch
+// for those slabs needs the global-memory tail search for symbols above the
+// table, whose registers cost a quarter of the residency.)
+template <bool FUSED, int NW, bool PAGED>
+static hipError_t launch_decode2_f(const Dims &d, DecArgs a, hipStream_t s) {
+    int loga = 2;
+    while ((1 << loga) < d.A) ++loga;
+    a.nsym_lo = 0;
+    a.nsym_hi = 1 << 30;
+    const bool clamp = !(d.A == (1 << loga) && d.wmin == d.A);
+    switch (loga) {
+    case 2: return launch_decode2_s<FUSED, 2, NW, PAGED, false>(d, a, clamp, s);
+    case 3: return launch_decode2_s<FUSED, 3, NW, PAGED, false>(d, a, clamp, s);
+    case 4: return launch_decode2_s<FUSED, 4, NW, PAGED, false>(d, a, clamp, s);
+    case 5: return launch_decode2_s<FUSED, 5, NW, PAGED, false>(d, a, clamp, s);
+    case 6: return launch_decode2_s<FUSED, 6, NW, PAGED, false>(d, a, clamp, s);
+    default: return launch_decode2_s<FUSED, 7, NW, PAGED, false>(d, a, clamp, s);
+    }
+}
+
 template <int S, bool FUSED, int LOGA, int NW, bool PAGED, bool TAIL>
 static hipError_t launch_decode_s(const Dims &d, const DecArgs &a, bool clamp, hipStream_t s) {
     const int ngroups = (a.NCr + S * NW - 1) / (S * NW);
@@ -639,16 +1091,16 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     // Two streams per lane and eight (or four) waves per block when there are
     // enough chunks; otherwise one stream per lane and as few waves as chunks.
     if (out.paged.cache) {
-        if (ncr >= 16) return launch_decode_f<2, true, 8, true>(d, mt, a, s);
-        if (ncr >= 8) return launch_decode_f<2, true, 4, true>(d, mt, a, s);
+        if (ncr >= 16) return launch_decode2_f<true, 8, true>(d, a, s);
+        if (ncr >= 8) return launch_decode2_f<true, 4, true>(d, a, s);
         if (ncr >= 2) return launch_decode_f<1, true, 2, true>(d, mt, a, s);
         return launch_decode_f<1, true, 1, true>(d, mt, a, s);
     }
     const bool fused = out.kv != nullptr;
     if (ncr >= 16)
-        return fused ? launch_decode_f<2, true, 8>(d, mt, a, s) : launch_decode_f<2, false, 8>(d, mt, a, s);
+        return fused ? launch_decode2_f<true, 8, false>(d, a, s) : launch_decode2_f<false, 8, false>(d, a, s);
     if (ncr >= 8)
-        return fused ? launch_decode_f<2, true, 4>(d, mt, a, s) : launch_decode_f<2, false, 4>(d, mt, a, s);
+        return fused ? launch_decode2_f<true, 4, false>(d, a, s) : launch_decode2_f<false, 4, false>(d, a, s);
     if (ncr >= 2)
         return fused ? launch_decode_f<1, true, 2>(d, mt, a, s) : launch_decode_f<1, false, 2>(d, mt, a, s);
     return fused ? launch_decode_f<1, true, 1>(d, mt, a, s) : launch_decode_f<1, false, 1>(d, mt, a, s);

@@ -463,7 +463,7 @@ def main():
     if nb >= 2 and not args.no_chunked_batch:
         desc1 = cgb.Desc(L, ct, H, D, desc.bins_k, desc.bins_v)
         chunks = kv.view(L, 2, nb, ct, C).permute(2, 0, 1, 3, 4).contiguous()
-        stride = (cgb.cg_blob_bound(desc1) + 7) // 8 * 8
+        stride = (cgb.cg_blob_bound(desc1) + 15) // 16 * 16  # 16-byte multiple: tables written in place
         blobs = torch.empty(nb * stride, dtype=torch.uint8, device=dev)
         sizes = torch.zeros(nb, dtype=torch.int64, device=dev)
         ws_be = cgb.alloc_workspace_batch(desc1, nb, stride, cgb.CG_OP_TO_BYTES, dev)
@@ -524,7 +524,7 @@ def main():
         # The same batch with per-layer tables (every (K|V, layer) table has
         # its layer's bins): the tables are most of a 256-token blob.
         desc1p = cgb.Desc(L, ct, H, D, desc.bins_k, desc.bins_v, cgb.CG_TABLES_PER_LAYER)
-        stride_p = (cgb.cg_blob_bound(desc1p) + 7) // 8 * 8
+        stride_p = (cgb.cg_blob_bound(desc1p) + 15) // 16 * 16
         ws_pe = cgb.alloc_workspace_batch(desc1p, nb, stride_p, cgb.CG_OP_TO_BYTES, dev)
         ws_pd = cgb.alloc_workspace_batch(desc1p, nb, stride_p, cgb.CG_OP_FROM_BYTES, dev)
         sizes_p = torch.zeros(nb, dtype=torch.int64, device=dev)

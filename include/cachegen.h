@@ -275,14 +275,19 @@ int cg_from_bytes_chunks(const cg_desc *desc, const uint8_t *blob, size_t blob_s
  * blob_stride: a multiple of 8, >= the header and sections (cg_blob_layout's
  * off_payload); >= cg_blob_bound() can never overflow. With a smaller
  * stride a call that does not fit records CG_E_CAPACITY: blob_sizes_dev then
- * holds the size every call needs, and the blobs are not usable. The
- * workspace depends on the stride: cg_workspace_bytes_batch(desc, batch,
- * blob_stride, CG_OP_TO_BYTES / CG_OP_FROM_BYTES). batch * nlayers <= 32767.
+ * holds the size every call needs, and the blobs are not usable. Blobs
+ * 16-byte aligned with a stride that is a multiple of 16 are the fast case
+ * (the quantiser then writes the tables in place itself). Workspace:
+ * cg_workspace_bytes_batch(desc, batch, blob_stride, CG_OP_TO_BYTES /
+ * CG_OP_FROM_BYTES). batch * nlayers <= 32767.
  *
  * cg_from_bytes_batch decodes such a batch of blobs (all with this desc) to
  * kv_out [batch, L, 2, T, H, D]; blob_sizes_dev holds each blob's size. A
  * blob whose header, size or chunk offsets disagree with desc or with its
- * lengths records CG_E_CORRUPT (its tokens are decoded from nothing). */
+ * lengths records CG_E_CORRUPT; its tokens are then undefined, those of the
+ * other blobs are not affected, and no read leaves the blob's stride.
+ * Both calls read and write every blob's sections in place: the batch moves
+ * no blob bytes beyond those of the calls themselves. */
 int64_t cg_workspace_bytes_batch(const cg_desc *desc, int32_t batch, size_t blob_stride, int op);
 int cg_to_bytes_batch(const cg_desc *desc, int32_t batch, const void *kv, uint8_t *blobs, size_t blob_stride,
                       uint64_t *blob_sizes_dev, void *ws, size_t ws_bytes, void *stream);

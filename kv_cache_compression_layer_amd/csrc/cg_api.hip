@@ -43,6 +43,8 @@ int make_dims(const cg_desc *desc, Dims &d) {
     if (!bins_valid(desc->bins_k, desc->nlayers) || !bins_valid(desc->bins_v, desc->nlayers))
         return CG_E_INVAL;
     d.L = desc->nlayers;
+    d.Lc = d.L;
+    d.cstride = 0;
     d.T = desc->ntokens;
     d.H = desc->nheads;
     d.D = desc->head_size;
@@ -80,31 +82,18 @@ void make_max_table(const cg_desc *desc, const Dims &d, MaxTable &mt) {
     mt.A = d.A;
 }
 
-// The table of a batch of `batch` calls run as one call of batch * L layers:
-// the constants repeat with period L (written out when they fit the table).
-void make_max_table_batch(const cg_desc *desc, const Dims &d, int batch, MaxTable &mt) {
-    make_max_table(desc, d, mt);
-    const int L = desc->nlayers;
-    if ((int64_t)batch * L <= CG_MAX_LAYERS) {
-        for (int l = L; l < batch * L; ++l) {
-            mt.bins[0][l] = mt.bins[0][l % L];
-            mt.bins[1][l] = mt.bins[1][l % L];
-        }
-    } else {
-        mt.lper = (uint32_t)L;
-        mt.lmagic = (uint32_t)(((1ull << 32) + L - 1) / L);
-    }
-}
-
-// Sizes of a batch: one call (d) and the virtual call of batch * L layers (vd).
+// Sizes of a batch: one call (d) and the call of batch * L layers that runs
+// it (vd), whose blob sections lie stride bytes apart per call.
 constexpr int kMaxBatchLayers = 32767;  // grid y-dimension of the per-slab kernels is 2 * layers
 
-int make_dims_batch(const cg_desc *desc, int batch, Dims &d, Dims &vd) {
+int make_dims_batch(const cg_desc *desc, int batch, uint64_t stride, Dims &d, Dims &vd) {
     int rc = make_dims(desc, d);
     if (rc) return rc;
     if (batch < 1 || (int64_t)batch * d.L > kMaxBatchLayers) return CG_E_SHAPE;
     vd = d;
     vd.L = batch * d.L;
+    vd.Lc = d.L;
+    vd.cstride = stride;
     vd.tab_entries = (int64_t)batch * d.tab_entries;
     vd.N = 2LL * vd.L * vd.T * vd.C;
     vd.NS = (int64_t)vd.NC * 2 * vd.L * vd.C;
@@ -148,7 +137,7 @@ WsLayout ws_layout(const Dims &d, int op) {
     case CG_OP_ENCODE:
         w.tile_sum = take(4ull * d.tiles);
         w.tile_off = take(8ull * d.tiles);
-        w.chunk_total = take(8ull * d.NC);
+        w.chunk_total = take(8ull * d.NC * ncalls(d));
         w.overflow = take(4ull * d.tiles);
         w.staging = take(encode_staging_bytes(d));
         w.scan = take(tile_scan_tmp_bytes(d));
@@ -167,7 +156,7 @@ WsLayout ws_layout(const Dims &d, int op) {
         w.clear_end = off;
         w.tile_sum = take(4ull * d.tiles);
         w.tile_off = take(8ull * d.tiles);
-        w.chunk_total = take(8ull * d.NC);
+        w.chunk_total = take(8ull * d.NC * ncalls(d));
         w.overflow = take(4ull * d.tiles);
         w.staging = take(encode_staging_bytes(d));
         w.sym = take((uint64_t)d.N);
@@ -251,8 +240,8 @@ void fill_info(const Dims &d, const BlobLayout &b, cg_blob_info *out) {
     out->off_payload = b.off_payload;
 }
 
-// Quantise, tables and range coding of one call (or of the virtual call of
-// a batch) into the blob sections `scales`, `wire` and `o`; the workspace is
+// Quantise, tables and range coding of one call (or of a batch run as one
+// call) into the blob sections `scales`, `wire` and `o`; the workspace is
 // ws_layout(d, CG_OP_TO_BYTES). When one quantiser block covers a whole
 // (K|V, layer) slab it builds the tables itself (no counts to clear, no
 // k_cdf); the encoder reads the u16 tables from the blob.
@@ -282,50 +271,6 @@ int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *sca
                 at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging),
                 at<uint64_t>(ws, w.scan)};
     return hip_rc(launch_encode(d, mt, sym, nullptr, wire, wpre, o, ew, true, packed, s));
-}
-
-// Workspace of a batch: the virtual call's workspace, then the virtual blob
-// (payload capacity: the batch's blobs' payload capacity), the pieces and
-// the per-(call, chunk, K|V) payload sizes.
-struct BatchWs {
-    WsLayout w;
-    uint64_t vblob = 0, vcap = 0, pieces = 0, piece_len = 0, vsize = 0, total = 0;
-};
-
-BatchWs batch_ws(const Dims &d, const Dims &vd, int B, uint64_t stride, int op) {
-    BatchWs bw;
-    bw.w = ws_layout(vd, op);
-    uint64_t off = bw.w.total;
-    auto take = [&](uint64_t bytes) {
-        const uint64_t o = off;
-        off += align_up(bytes, kWsAlign);
-        return o;
-    };
-    const BlobLayout lay = blob_layout(d), vlay = blob_layout(vd);
-    bw.vcap = (uint64_t)B * (stride > lay.off_payload ? stride - lay.off_payload : 0);
-    bw.vblob = take(vlay.off_payload + bw.vcap);
-    bw.pieces = take((uint64_t)B * (4 + 4ull * d.NC) * sizeof(Piece));
-    bw.piece_len = take(16ull * B * d.NC);
-    bw.vsize = take(8);
-    bw.total = off;
-    return bw;
-}
-
-BatchGeom batch_geom(const cg_desc *desc, const Dims &d, const Dims &vd, int B, uint64_t stride) {
-    BatchGeom g;
-    g.d = d;
-    g.vd = vd;
-    g.lay = blob_layout(d);
-    g.vlay = blob_layout(vd);
-    g.B = B;
-    g.stride = stride;
-    g.npieces = 4 + 4 * d.NC;
-    g.wsum[0] = g.wsum[1] = 0;
-    for (int l = 0; l < d.L; ++l) {
-        g.wsum[0] += d.fmt ? desc->bins_k[l] : (uint64_t)d.A;
-        g.wsum[1] += d.fmt ? desc->bins_v[l] : (uint64_t)d.A;
-    }
-    return g;
 }
 
 // Device address of `scratch` on the current device, looked up once per
@@ -664,88 +609,74 @@ int cg_from_bytes_chunks(const cg_desc *desc, const uint8_t *blob, size_t blob_s
 
 int64_t cg_workspace_bytes_batch(const cg_desc *desc, int32_t batch, size_t blob_stride, int op) {
     Dims d, vd;
-    const int rc = make_dims_batch(desc, batch, d, vd);
+    const int rc = make_dims_batch(desc, batch, (uint64_t)blob_stride, d, vd);
     if (rc) return rc;
     if (op != CG_OP_TO_BYTES && op != CG_OP_FROM_BYTES) return CG_E_INVAL;
-    return (int64_t)batch_ws(d, vd, batch, (uint64_t)blob_stride, op).total;
+    return (int64_t)ws_layout(vd, op).total;
 }
 
+// A batch runs as one call of batch * L layers (vd) whose kernels write and
+// read each call's blob sections in place, blob_stride bytes apart.
 int cg_to_bytes_batch(const cg_desc *desc, int32_t batch, const void *kv, uint8_t *blobs, size_t blob_stride,
                       uint64_t *blob_sizes_dev, void *ws, size_t ws_bytes, void *stream) {
     Dims d, vd;
-    int rc = make_dims_batch(desc, batch, d, vd);
+    int rc = make_dims_batch(desc, batch, (uint64_t)blob_stride, d, vd);
     if (rc) return rc;
     if (!kv || !blobs || !blob_sizes_dev || !ws) return CG_E_INVAL;
     if ((uintptr_t)blobs % 8 || blob_stride % 8 || (uintptr_t)ws % kWsAlign) return CG_E_INVAL;
-    const BlobLayout lay = blob_layout(d), vlay = blob_layout(vd);
+    const BlobLayout lay = blob_layout(d);
     if ((uint64_t)blob_stride < lay.off_payload) return CG_E_CAPACITY;
-    const BatchWs bw = batch_ws(d, vd, batch, blob_stride, CG_OP_TO_BYTES);
-    if ((uint64_t)ws_bytes < bw.total) return CG_E_WORKSPACE;
-    const WsLayout &w = bw.w;
+    const WsLayout w = ws_layout(vd, CG_OP_TO_BYTES);
+    if ((uint64_t)ws_bytes < w.total) return CG_E_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
-    make_max_table_batch(desc, d, batch, mt);
+    make_max_table(desc, d, mt);
     HeaderBytes hb;
     make_header(desc, d, lay, hb);
-
-    uint32_t *status = at<uint32_t>(ws, 0);
-    uint8_t *vblob = at<uint8_t>(ws, bw.vblob);
     if ((rc = hip_rc(launch_blob_header(blobs, hb, lay, d, s, batch, blob_stride)))) return rc;
-    EncodeOut o{vblob + vlay.off_payload,
-                bw.vcap,
-                at<uint16_t>(vblob, vlay.off_lengths),
-                at<uint64_t>(vblob, vlay.off_chunk_off),
-                at<uint64_t>(ws, bw.vsize),
-                nullptr,
-                vlay.off_payload};
-    if ((rc = encode_call(vd, mt, kv, at<uint16_t>(vblob, vlay.off_scales), at<uint16_t>(vblob, vlay.off_cdf), o,
-                          ws, w, s)))
-        return rc;
-    const BatchGeom g = batch_geom(desc, d, vd, batch, blob_stride);
-    Piece *pieces = at<Piece>(ws, bw.pieces);
-    if ((rc = hip_rc(launch_split_plan(g, vblob, at<uint64_t>(ws, w.tile_off), blobs, blob_sizes_dev, pieces, status,
-                                       s))))
-        return rc;
-    return hip_rc(launch_copy_pieces(g, pieces, vblob, 0, blobs, blob_stride, s));
+    EncodeOut o{blobs + lay.off_payload,
+                (uint64_t)blob_stride - lay.off_payload,
+                at<uint16_t>(blobs, lay.off_lengths),
+                at<uint64_t>(blobs, lay.off_chunk_off),
+                blob_sizes_dev,
+                blobs + 40,
+                lay.off_payload};
+    return encode_call(vd, mt, kv, at<uint16_t>(blobs, lay.off_scales), at<uint16_t>(blobs, lay.off_cdf), o, ws, w,
+                       s);
 }
 
 int cg_from_bytes_batch(const cg_desc *desc, int32_t batch, const uint8_t *blobs, size_t blob_stride,
                         const uint64_t *blob_sizes_dev, void *kv_out, void *ws, size_t ws_bytes, void *stream) {
     Dims d, vd;
-    int rc = make_dims_batch(desc, batch, d, vd);
+    int rc = make_dims_batch(desc, batch, (uint64_t)blob_stride, d, vd);
     if (rc) return rc;
     if (!blobs || !blob_sizes_dev || !kv_out || !ws) return CG_E_INVAL;
     if ((uintptr_t)blobs % 8 || blob_stride % 8 || (uintptr_t)ws % kWsAlign) return CG_E_INVAL;
-    const BlobLayout lay = blob_layout(d), vlay = blob_layout(vd);
+    const BlobLayout lay = blob_layout(d);
     if ((uint64_t)blob_stride < lay.off_payload) return CG_E_INVAL;
-    const BatchWs bw = batch_ws(d, vd, batch, blob_stride, CG_OP_FROM_BYTES);
-    if ((uint64_t)ws_bytes < bw.total) return CG_E_WORKSPACE;
-    const WsLayout &w = bw.w;
+    const WsLayout w = ws_layout(vd, CG_OP_FROM_BYTES);
+    if ((uint64_t)ws_bytes < w.total) return CG_E_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
-    make_max_table_batch(desc, d, batch, mt);
+    make_max_table(desc, d, mt);
     HeaderBytes hb;
     make_header(desc, d, lay, hb);
     uint32_t *status = at<uint32_t>(ws, 0);
-    uint8_t *vblob = at<uint8_t>(ws, bw.vblob);
     if ((rc = clear_ws(ws, w, s))) return rc;
-    const BatchGeom g = batch_geom(desc, d, vd, batch, blob_stride);
-    Piece *pieces = at<Piece>(ws, bw.pieces);
-    if ((rc = hip_rc(launch_merge_plan(g, blobs, blob_sizes_dev, hb, vblob, at<uint64_t>(ws, bw.piece_len), pieces,
-                                       status, s))))
+    if ((rc = hip_rc(launch_batch_check(blobs, blob_stride, batch, blob_sizes_dev, hb, lay.off_payload, status, s))))
         return rc;
-    if ((rc = hip_rc(launch_copy_pieces(g, pieces, blobs, blob_stride, vblob, 0, s)))) return rc;
-    DecodeIn in{vblob + vlay.off_payload,
-                bw.vcap,
-                reinterpret_cast<const uint16_t *>(vblob + vlay.off_lengths),
-                reinterpret_cast<const uint64_t *>(vblob + vlay.off_chunk_off),
+    DecodeIn in{blobs + lay.off_payload,
+                (uint64_t)blob_stride - lay.off_payload,
+                reinterpret_cast<const uint16_t *>(blobs + lay.off_lengths),
+                reinterpret_cast<const uint64_t *>(blobs + lay.off_chunk_off),
                 nullptr,
-                reinterpret_cast<const uint16_t *>(vblob + vlay.off_cdf),
+                reinterpret_cast<const uint16_t *>(blobs + lay.off_cdf),
                 at<uint32_t>(ws, w.wpre)};
+    in.call_sizes = blob_sizes_dev;
+    in.payload_off = lay.off_payload;
     DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
-                  reinterpret_cast<const uint16_t *>(vblob + vlay.off_scales)};
-    return hip_rc(
-        launch_decode(vd, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan), status, s));
+                  reinterpret_cast<const uint16_t *>(blobs + lay.off_scales)};
+    return hip_rc(launch_decode(vd, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan), status, s));
 }
 
 int cg_from_bytes_paged(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_cache,

@@ -167,15 +167,15 @@ hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts,
 // entry k of the table (the first lane of a table also writes entry W). An
 // alphabet above 64 takes two rounds of 64, the second starting from the
 // first one's total. int32 tables are [2,L,C,A+1] with 2^16 past entry W; u16
-// wire tables hold entries 0..W-1 at wpre[slab] * C + c * W (wpre null: one
-// width A, slab * A).
+// wire tables hold entries 0..W-1 at wpre[ls] * C + c * W of their call's
+// section (wpre null: one width A, ls * A).
 template <int G>
 __global__ __launch_bounds__(256) void k_cdf(const uint32_t *__restrict__ counts,
                                              int32_t *__restrict__ cdf,
                                              uint16_t *__restrict__ wire,
                                              const uint32_t *__restrict__ wpre,
                                              uint32_t *__restrict__ status, int64_t ntab, int A,
-                                             int T, int L, int C, MaxTable mt) {
+                                             int T, int C, MaxTable mt, CallMap cm) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t tab = wave * (64 / G) + lane / G;
@@ -183,11 +183,12 @@ __global__ __launch_bounds__(256) void k_cdf(const uint32_t *__restrict__ counts
     const bool live = tab < ntab;
     const int slab = live ? (int)(tab / C) : 0;
     const int c = (int)(tab - (int64_t)slab * C);
-    const int kv = slab >= L ? 1 : 0;
-    const int W = layer_w(mt, kv, slab - kv * L);
+    const SlabLoc sl = slab_loc(cm, slab);
+    const int W = layer_w(mt, sl.kv, sl.l);
     const uint64_t S = kProbOne - (uint32_t)W;
     const double invT = 1.0 / (double)T;
-    uint16_t *wt = wire && live ? wire + (wpre ? (int64_t)wpre[slab] : (int64_t)slab * A) * C + (int64_t)c * W
+    uint16_t *wt = wire && live ? call_sec(wire, cm, sl.b) +
+                                      (wpre ? (int64_t)wpre[sl.ls] : (int64_t)sl.ls * A) * C + (int64_t)c * W
                                 : nullptr;
     uint64_t base = 0;
     bool bad = false;
@@ -223,7 +224,7 @@ hipError_t launch_cdf(const Dims &d, const MaxTable &mt, const uint32_t *counts,
     const int64_t ntab = 2LL * d.L * d.C;
 #define CG_CDF(GG)                                                                                      \
     hipLaunchKernelGGL(k_cdf<GG>, dim3((unsigned)((ntab + 4 * (64 / GG) - 1) / (4 * (64 / GG)))), dim3(256), \
-                       0, s, counts, cdf, cdf_wire, wpre, status, ntab, d.A, d.T, d.L, d.C, mt)
+                       0, s, counts, cdf, cdf_wire, wpre, status, ntab, d.A, d.T, d.C, mt, call_map(d))
     if (d.A <= 8) CG_CDF(8);
     else if (d.A <= 16) CG_CDF(16);
     else if (d.A <= 32) CG_CDF(32);
@@ -232,8 +233,9 @@ hipError_t launch_cdf(const Dims &d, const MaxTable &mt, const uint32_t *counts,
     return hipGetLastError();
 }
 
-// wpre[s] = the sum of the table widths of the (K|V, layer) slabs before s,
-// s = 0..2L (so wpre[2L] is the whole section's entries per channel).
+// wpre[s] = the sum of the table widths of the (K|V, layer) slabs of a call
+// before s, s = 0..2Lc (so wpre[2Lc] is the whole section's entries per
+// channel); every call of a batch places its tables alike.
 __global__ __launch_bounds__(1024) void k_table_prefix(MaxTable mt, int L, uint32_t *__restrict__ wpre) {
     __shared__ uint32_t wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(1024) void k_table_prefix(MaxTable mt, int L, uint3
 }
 
 hipError_t launch_table_prefix(const Dims &d, const MaxTable &mt, uint32_t *wpre, hipStream_t s) {
-    hipLaunchKernelGGL(k_table_prefix, dim3(1), dim3(1024), 0, s, mt, d.L, wpre);
+    hipLaunchKernelGGL(k_table_prefix, dim3(1), dim3(1024), 0, s, mt, d.Lc, wpre);
     return hipGetLastError();
 }
 

@@ -46,10 +46,26 @@ struct DecArgs {
     uint32_t *status;
     PagedOut paged;
     MaxTable mt;
+    CallMap cm;    // calls of a batch: blob sections per call
+    // Batches: call b's payload bound is min(call_sizes[b], stride) -
+    // payload_off (0 if below) instead of payload_bytes.
+    const uint64_t *call_sizes;
+    uint64_t payload_off;
     int L, T, C, A, NC, CB;
     int j0, NCr;   // the chunks decoded: [j0, j0 + NCr)
     int nsym_lo, nsym_hi;
 };
+
+// Payload of the call that slab location sl belongs to, and its size.
+__device__ __forceinline__ const uint8_t *call_payload(const DecArgs &a, const SlabLoc &sl, uint64_t &bytes) {
+    bytes = a.payload_bytes;
+    if (a.call_sizes) {
+        uint64_t sz = a.call_sizes[sl.b];
+        if (sz > a.cm.stride) sz = a.cm.stride;
+        bytes = sz > a.payload_off ? sz - a.payload_off : 0ull;
+    }
+    return call_sec(a.payload, a.cm, sl.b);
+}
 
 // Bytes of the LDS pool a block of NW waves shares for its tiles' payload,
 // and the slack after it: a stream is never read more than 4 + 2 * 256 + 2
@@ -103,7 +119,8 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
                                             const uint32_t *tab,
                                             const float *dq, uint32_t (&sc_v)[S][4], const uint8_t *pool,
                                             __amdgpu_buffer_rsrc_t out_rsrc, uint32_t out_voff,
-                                            int lane, int W, int slab, int c, uint64_t &bad_mask) {
+                                            int lane, int W, const uint16_t *c16, int slab, int c,
+                                            uint64_t &bad_mask) {
     auto fetch = [&](int s) -> uint32_t {
         DecStream &d = st[s];
         if (STAGED) return pool[d.ptr++];
@@ -244,7 +261,7 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
                     bool bad = false;
                     for (int sy = 1 << LOGA; sy < W; ++sy) {
                         uint32_t lo, hi;
-                        cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, c, a.A, W, sy, lo, hi);
+                        cdf_bounds(a.cdf32, c16, a.wpre, slab, a.C, c, a.A, W, sy, lo, hi);
                         if (__umul24(r[s], lo & 0xFFFFu) > st[s].code) break;
                         bad |= hi <= lo || hi > kProbOne;
                         ad[s] = (uint32_t)sy * RB + lane4;
@@ -337,7 +354,8 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     const int cb = bid % a.CB;
     const int slab = (bid / a.CB) % (2 * a.L);
     const int g = bid / (a.CB * 2 * a.L);
-    const int kv = slab / a.L, l = slab - kv * a.L;
+    const SlabLoc sl = slab_loc(a.cm, slab);
+    const int kv = sl.kv, l = sl.l;
     const int c = cb * 64 + lane;
     const bool active = c < a.C;
     const int M = layer_m(a.mt, kv, l);
@@ -345,6 +363,10 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // This launch decodes only the slabs whose quantiser symbol count 2M+1
     // lies in [nsym_lo, nsym_hi]; the other blocks return at once.
     if (2 * M + 1 < a.nsym_lo || 2 * M + 1 > a.nsym_hi) return;  // block-uniform
+    uint64_t payload_bytes;
+    const uint8_t *payload = call_payload(a, sl, payload_bytes);
+    const uint16_t *lengths = call_sec(a.lengths, a.cm, sl.b);
+    const uint16_t *cdf16 = call_sec(a.cdf16, a.cm, sl.b);
 
     // This wave's streams: lengths, offsets and the pool bytes they need
     // (alignment head + bytes + four zero bytes after each of the 64 streams).
@@ -362,12 +384,12 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
         len[s] = excl[s] = 0;
         base[s] = 0;
         if (n[s]) {
-            len[s] = active ? a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] : 0u;
+            len[s] = active ? lengths[((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C + c] : 0u;
             const uint32_t incl = wave_incl_scan_u32(len[s], lane);
             total = (uint32_t)__shfl((int)incl, 63, 64);
             excl[s] = incl - len[s];
             base[s] = a.tile_off[((int64_t)j * 2 * a.L + slab) * a.CB + cb];
-            if (base[s] > a.payload_bytes || total > a.payload_bytes - base[s]) {
+            if (base[s] > payload_bytes || total > payload_bytes - base[s]) {
                 corrupt = true;  // offsets point outside the payload: decode from nothing
                 len[s] = excl[s] = total = 0;
                 base[s] = 0;
@@ -399,7 +421,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
                 uint32_t la = ls - (uint32_t)(g0 - ga);
 #pragma unroll 4
                 for (uint64_t gw = ga; gw < ge; gw += 4, la += 4) {
-                    uint32_t v = load_word(a.payload, a.payload_bytes, gw);
+                    uint32_t v = load_word(payload, payload_bytes, gw);
                     if (gw < g0) v &= 0xFFFFFFFFu << (8 * (uint32_t)(g0 - gw));
                     if (gw + 4 > gend) v &= 0xFFFFFFFFu >> (8 * (uint32_t)(gw + 4 - gend));
                     pool_w[la >> 2] = v;
@@ -412,7 +434,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     for (int s = 0; s < S; ++s) {
         st[s].len = len[s];
         st[s].pos = 0;
-        st[s].gsrc = a.payload + base[s] + excl[s];
+        st[s].gsrc = payload + base[s] + excl[s];
         st[s].range = 0xFFFFFFFFu;
         st[s].code = 0;
         if (!staged) st[s].ptr = 0;
@@ -431,7 +453,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
             uint32_t v = 0xFFFFu;
             if (s < W && active) {
                 uint32_t lo, hi;
-                cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, c, A, W, s, lo, hi);
+                cdf_bounds(a.cdf32, cdf16, a.wpre, sl.ls, a.C, c, A, W, s, lo, hi);
                 if (s < (1 << LOGA) &&
                     (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)))
                     bad_table = true;
@@ -446,7 +468,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
         uint32_t entry = 0xFFFFu;
         if (s < W && active) {
             uint32_t lo, hi;
-            cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, c, A, W, s, lo, hi);
+            cdf_bounds(a.cdf32, cdf16, a.wpre, sl.ls, a.C, c, A, W, s, lo, hi);
             uint32_t f = hi - lo;
             if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)) {
                 bad_table = true;
@@ -463,7 +485,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     uint32_t sc_v[S][4];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const uint16_t *sp = a.scale + (int64_t)slab * a.T + t0[s];
+        const uint16_t *sp = call_sec(a.scale, a.cm, sl.b) + (int64_t)sl.ls * a.T + t0[s];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int t = 64 * k + lane;
@@ -480,7 +502,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // wave-uniform, the lane offset constant; idle lanes point past the end.
     const uint32_t esz = FUSED ? 2u : 1u;
     const uint64_t slab_elems = (uint64_t)a.T * a.C;
-    const void *obase = FUSED ? (const void *)(a.kv + ((int64_t)l * 2 + kv) * (int64_t)slab_elems)
+    const void *obase = FUSED ? (const void *)(a.kv + ((int64_t)sl.lv * 2 + kv) * (int64_t)slab_elems)
                               : (const void *)(a.sym + (int64_t)slab * (int64_t)slab_elems);
     __amdgpu_buffer_rsrc_t out_rsrc = make_rsrc(obase, (uint32_t)(slab_elems * esz));
     PagedRows<S> pg;
@@ -490,7 +512,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
         // so their stores are dropped (and the call reports corruption).
         const uint32_t bs_log = (uint32_t)a.paged.log2_bs;
         const uint32_t region = ((uint32_t)a.paged.num_blocks << bs_log) * (uint32_t)a.C * 2u;
-        out_rsrc = make_rsrc(a.paged.cache + (int64_t)l * a.paged.layer_stride + (int64_t)kv * a.paged.kv_stride,
+        out_rsrc = make_rsrc(a.paged.cache + (int64_t)sl.lv * a.paged.layer_stride + (int64_t)kv * a.paged.kv_stride,
                              region);
         const int nblk_total = (a.T + (1 << bs_log) - 1) >> bs_log;
         bool bad_block = false;
@@ -525,17 +547,17 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     if (half) {
         if (staged)
             decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                               out_voff, lane, W, slab, c, bad_mask);
+                                                               out_voff, lane, W, cdf16, sl.ls, c, bad_mask);
         else
             decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                                out_voff, lane, W, slab, c, bad_mask);
+                                                                out_voff, lane, W, cdf16, sl.ls, c, bad_mask);
     } else {
         if (staged)
             decode_loop<S, FUSED, LOGA, CLAMP, true, false, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                            out_voff, lane, W, slab, c, bad_mask);
+                                                            out_voff, lane, W, cdf16, sl.ls, c, bad_mask);
         else
             decode_loop<S, FUSED, LOGA, CLAMP, false, false, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
-                                                             out_voff, lane, W, slab, c, bad_mask);
+                                                             out_voff, lane, W, cdf16, sl.ls, c, bad_mask);
     }
     if ((__ballot(active && (corrupt || bad_table)) | (bad_mask & __ballot(active))) && lane == 0)
         atomicOr(a.status, kStCorrupt);
@@ -565,7 +587,8 @@ __device__ __forceinline__ void decode_loop2(const DecArgs &a, DecStream (&st)[2
                                              int pg_t0, int pg_b0, uint32_t pg_v, const uint32_t *tab,
                                              const float *dq, uint32_t (&sc_v)[4], const uint8_t *pool,
                                              __amdgpu_buffer_rsrc_t out_rsrc, uint32_t out_voff, int lane, int W,
-                                             int slab, const int (&cch)[2], uint64_t &bad_mask) {
+                                             const uint16_t *c16, int slab, const int (&cch)[2],
+                                             uint64_t &bad_mask) {
     constexpr int S = 2;
     auto fetch = [&](int s) -> uint32_t {
         DecStream &d = st[s];
@@ -700,7 +723,7 @@ __device__ __forceinline__ void decode_loop2(const DecArgs &a, DecStream (&st)[2
                         bool up = true;
                         for (int sy = 1 << LOGA; sy < W; ++sy) {
                             uint32_t lo, hi;
-                            cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, min(cch[s], a.C - 1), a.A, W, sy, lo,
+                            cdf_bounds(a.cdf32, c16, a.wpre, slab, a.C, min(cch[s], a.C - 1), a.A, W, sy, lo,
                                        hi);
                             up = up && __umul24(r[s], lo & 0xFFFFu) <= d.code;
                             if (up) {
@@ -775,7 +798,8 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
     const int cb2 = bid % CB2;
     const int slab = (bid / CB2) % (2 * a.L);
     const int g = bid / (CB2 * 2 * a.L);
-    const int kv = slab / a.L, l = slab - kv * a.L;
+    const SlabLoc sl = slab_loc(a.cm, slab);
+    const int kv = sl.kv, l = sl.l;
     int cch[S];
     bool act[S];
 #pragma unroll
@@ -786,6 +810,9 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
     const int M = layer_m(a.mt, kv, l);
     const int W = layer_w(a.mt, kv, l);
     if (2 * M + 1 < a.nsym_lo || 2 * M + 1 > a.nsym_hi) return;  // block-uniform
+    uint64_t payload_bytes;
+    const uint8_t *payload = call_payload(a, sl, payload_bytes);
+    const uint16_t *cdf16 = call_sec(a.cdf16, a.cm, sl.b);
 
     // This wave's chunk and its 128 streams: lengths, offsets (the two tiles
     // 2 cb2, 2 cb2 + 1 are adjacent in the payload) and the pool bytes they
@@ -797,7 +824,7 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
     uint64_t base = 0;
     bool corrupt = false;
     if (n) {
-        const uint16_t *lp = a.lengths + ((int64_t)j * 2 * a.L + slab) * a.C;
+        const uint16_t *lp = call_sec(a.lengths, a.cm, sl.b) + ((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C;
 #pragma unroll
         for (int s = 0; s < S; ++s) len[s] = act[s] ? lp[cch[s]] : 0u;
         const uint32_t pr = len[0] + len[1];
@@ -805,7 +832,7 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
         total = (uint32_t)__shfl((int)incl, 63, 64);
         excl = incl - pr;
         base = a.tile_off[((int64_t)j * 2 * a.L + slab) * a.CB + 2 * cb2];
-        if (base > a.payload_bytes || total > a.payload_bytes - base) {
+        if (base > payload_bytes || total > payload_bytes - base) {
             corrupt = true;  // offsets point outside the payload: decode from nothing
             len[0] = len[1] = excl = total = 0;
             base = 0;
@@ -837,7 +864,7 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
                 uint32_t la = ls - (uint32_t)(g0 - ga);
 #pragma unroll 4
                 for (uint64_t gw = ga; gw < ge; gw += 4, la += 4) {
-                    uint32_t v = load_word(a.payload, a.payload_bytes, gw);
+                    uint32_t v = load_word(payload, payload_bytes, gw);
                     if (gw < g0) v &= 0xFFFFFFFFu << (8 * (uint32_t)(g0 - gw));
                     if (gw + 4 > gend) v &= 0xFFFFFFFFu >> (8 * (uint32_t)(gw + 4 - gend));
                     pool_w[la >> 2] = v;
@@ -849,7 +876,7 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
     for (int s = 0; s < S; ++s) {
         st[s].len = len[s];
         st[s].pos = 0;
-        st[s].gsrc = a.payload + base + soff[s];
+        st[s].gsrc = payload + base + soff[s];
         st[s].range = 0xFFFFFFFFu;
         st[s].code = 0;
         if (!staged) st[s].ptr = 0;
@@ -866,7 +893,7 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
             uint32_t entry = 0xFFFFu;
             if (q < W && act[s]) {
                 uint32_t lo, hi;
-                cdf_bounds(a.cdf32, a.cdf16, a.wpre, slab, a.C, cch[s], A, W, q, lo, hi);
+                cdf_bounds(a.cdf32, cdf16, a.wpre, sl.ls, a.C, cch[s], A, W, q, lo, hi);
                 uint32_t f = hi - lo;
                 if (hi <= lo || hi > kProbOne || (q == 0 && lo != 0) || (q == W - 1 && hi != kProbOne)) {
                     bad_table = true;
@@ -882,7 +909,7 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
     // Per-token scales of the chunk: lane i of sc_v[k] holds token 64k + i.
     uint32_t sc_v[4];
     {
-        const uint16_t *sp = a.scale + (int64_t)slab * a.T + t0;
+        const uint16_t *sp = call_sec(a.scale, a.cm, sl.b) + (int64_t)sl.ls * a.T + t0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int t = 64 * k + lane;
@@ -899,7 +926,7 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
     // wave-uniform, the lane offset constant; idle lanes point past the end.
     const uint32_t esz = FUSED ? 2u : 1u;
     const uint64_t slab_elems = (uint64_t)a.T * a.C;
-    const void *obase = FUSED ? (const void *)(a.kv + ((int64_t)l * 2 + kv) * (int64_t)slab_elems)
+    const void *obase = FUSED ? (const void *)(a.kv + ((int64_t)sl.lv * 2 + kv) * (int64_t)slab_elems)
                               : (const void *)(a.sym + (int64_t)slab * (int64_t)slab_elems);
     __amdgpu_buffer_rsrc_t out_rsrc = make_rsrc(obase, (uint32_t)(slab_elems * esz));
     int pg_t0 = 0, pg_b0 = 0;
@@ -907,7 +934,7 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
     if constexpr (PAGED) {
         const uint32_t bs_log = (uint32_t)a.paged.log2_bs;
         const uint32_t region = ((uint32_t)a.paged.num_blocks << bs_log) * (uint32_t)a.C * 2u;
-        out_rsrc = make_rsrc(a.paged.cache + (int64_t)l * a.paged.layer_stride + (int64_t)kv * a.paged.kv_stride,
+        out_rsrc = make_rsrc(a.paged.cache + (int64_t)sl.lv * a.paged.layer_stride + (int64_t)kv * a.paged.kv_stride,
                              region);
         const int nblk_total = (a.T + (1 << bs_log) - 1) >> bs_log;
         bool bad_block = false;
@@ -936,7 +963,8 @@ __global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
     const bool full = FUSED && (a.C & 127) == 0;
 #define CG_DL2(ST, HF, FL)                                                                                        \
     decode_loop2<FUSED, LOGA, CLAMP, ST, HF, PAGED, TAIL, FL>(a, st, n, rowoff, pg_t0, pg_b0, pg_v, tab, dq, sc_v, \
-                                                              pool, out_rsrc, out_voff, lane, W, slab, cch, bad_mask)
+                                                              pool, out_rsrc, out_voff, lane, W, cdf16, sl.ls, cch, \
+                                                              bad_mask)
     if (full) {
         if (half) {
             if (staged) CG_DL2(true, LOGA >= 3, true);
@@ -1021,9 +1049,8 @@ static hipError_t launch_decode_f(const Dims &d, const MaxTable &mt, DecArgs a, 
         const int64_t blocks = (int64_t)((a.NCr + S * NW - 1) / (S * NW)) * 2 * d.L * d.CB;
         if (loga > 4) {
             bool small = false, large = false, small_narrow = false;
-            const int nl = mt.lper ? (int)mt.lper : (d.L < CG_MAX_LAYERS ? d.L : CG_MAX_LAYERS);
             for (int kv = 0; kv < 2; ++kv)
-                for (int l = 0; l < nl; ++l) {
+                for (int l = 0; l < d.Lc; ++l) {
                     const int b = mt.bins[kv][l], w = mt.per_layer ? b : d.A;
                     if (2 * (b / 2 - 1) + 1 <= 16) {
                         small = true;
@@ -1061,11 +1088,15 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
         hipError_t e0 = launch_table_prefix(d, mt, wpre, s);
         if (e0 != hipSuccess) return e0;
     }
-    TileScan ts{nullptr, in.lengths, tile_off, scan_tmp, nullptr, in.chunk_off, in.payload_bytes, status,
-                d.L, d.C, d.CB, d.NC, j0, j1 - j0};
+    if ((j0 != 0 || j1 != d.NC || out.paged.cache) && d.Lc != d.L) return hipErrorInvalidValue;  // one call only
+    TileScan ts{nullptr, in.lengths, tile_off, scan_tmp, nullptr, in.chunk_off, in.payload_bytes, in.call_sizes,
+                in.payload_off, status, d.L, d.C, d.CB, d.NC, call_map(d), j0, d.Lc == d.L ? j1 - j0 : -1};
     hipError_t e = launch_tile_scan(ts, s);
     if (e != hipSuccess) return e;
     DecArgs a;
+    a.cm = call_map(d);
+    a.call_sizes = in.call_sizes;
+    a.payload_off = in.payload_off;
     a.payload = in.payload;
     a.payload_bytes = in.payload_bytes;
     a.lengths = in.lengths;

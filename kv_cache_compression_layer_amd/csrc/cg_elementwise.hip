@@ -106,16 +106,17 @@ template <int NV, bool FULL>
 __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict__ kv,
                                                       uint8_t *__restrict__ sym,
                                                       uint16_t *__restrict__ scale,
-                                                      uint32_t *__restrict__ status, int L, int T,
-                                                      int C, MaxTable mt) {
+                                                      uint32_t *__restrict__ status, int T,
+                                                      int C, MaxTable mt, CallMap cm) {
     const int lane = threadIdx.x & 63;
     // The row is uniform across the wave; readfirstlane lets the compiler
     // keep the row arithmetic in scalar registers.
     const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     if (t >= T) return;
-    const int slab = blockIdx.y, k = slab >= L ? 1 : 0, l = slab - k * L;  // grid: (tokens/4, 2L)
+    const int slab = blockIdx.y;  // grid: (tokens/4, 2L)
+    const SlabLoc sl = slab_loc(cm, slab);
     const int64_t row = (int64_t)slab * T + t;
-    const uint16_t *src = kv + (((int64_t)l * 2 + k) * T + t) * C;
+    const uint16_t *src = kv + (((int64_t)sl.lv * 2 + sl.kv) * T + t) * C;
     uint8_t *dst = sym + row * C;
 
     uint4 v[NV];
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict
     uint32_t am = max(am2 & 0xFFFFu, am2 >> 16);
     am = wave_max_dpp(am);
     if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
-    const int M = layer_m(mt, k, l);
+    const int M = layer_m(mt, sl.kv, sl.l);
     const float Mf = (float)M;
     // m == 0 gives f == 0, so every symbol is exactly M.
     const float f = row_factor(am, Mf);
@@ -146,31 +147,32 @@ __global__ __launch_bounds__(256) void k_quantize_vec(const uint16_t *__restrict
             *reinterpret_cast<uint2 *>(dst + c0) = make_uint2(lo, hi);
         }
     }
-    if (lane == 0) scale[row] = (uint16_t)am;
+    if (lane == 0) call_sec(scale, cm, sl.b)[(int64_t)sl.ls * T + t] = (uint16_t)am;
 }
 
 // Any C and alignment: two passes over the row (the second hits the cache).
 __global__ __launch_bounds__(256) void k_quantize_any(const uint16_t *__restrict__ kv,
                                                       uint8_t *__restrict__ sym,
                                                       uint16_t *__restrict__ scale,
-                                                      uint32_t *__restrict__ status, int L, int T,
-                                                      int C, MaxTable mt) {
+                                                      uint32_t *__restrict__ status, int T,
+                                                      int C, MaxTable mt, CallMap cm) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const int slab = blockIdx.y, k = slab >= L ? 1 : 0, l = slab - k * L;  // grid: (tokens/4, 2L)
+    const int slab = blockIdx.y;  // grid: (tokens/4, 2L)
+    const SlabLoc sl = slab_loc(cm, slab);
     const int64_t row = (int64_t)slab * T + t;
-    const uint16_t *src = kv + (((int64_t)l * 2 + k) * T + t) * C;
+    const uint16_t *src = kv + (((int64_t)sl.lv * 2 + sl.kv) * T + t) * C;
     uint8_t *dst = sym + row * C;
     uint32_t am = 0;
     for (int c = lane; c < C; c += 64) am = max(am, (uint32_t)src[c] & 0x7FFFu);
     am = wave_max_u32(am);
     if (am >= 0x7F80u && lane == 0) atomicOr(status, kStNonfinite);
-    const int M = layer_m(mt, k, l);
+    const int M = layer_m(mt, sl.kv, sl.l);
     const float Mf = (float)M;
     const float f = row_factor(am, Mf);
     for (int c = lane; c < C; c += 64) dst[c] = (uint8_t)quant1(src[c], f, Mf);
-    if (lane == 0) scale[row] = (uint16_t)am;
+    if (lane == 0) call_sec(scale, cm, sl.b)[(int64_t)sl.ls * T + t] = (uint16_t)am;
 }
 
 hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
@@ -180,9 +182,10 @@ hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv
     if (aligned && d.C % 8 == 0 && d.C <= 2048) {
         const int nv = (d.C + 511) / 512;
         const bool full = d.C == nv * 512;
+    const CallMap cm = call_map(d);
 #define CG_QV(N)                                                                                      \
-    if (full) hipLaunchKernelGGL((k_quantize_vec<N, true>), grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt); \
-    else hipLaunchKernelGGL((k_quantize_vec<N, false>), grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt);
+    if (full) hipLaunchKernelGGL((k_quantize_vec<N, true>), grid, block, 0, s, kv, sym, scale, status, d.T, d.C, mt, cm); \
+    else hipLaunchKernelGGL((k_quantize_vec<N, false>), grid, block, 0, s, kv, sym, scale, status, d.T, d.C, mt, cm);
         switch (nv) {
         case 1: CG_QV(1) break;
         case 2: CG_QV(2) break;
@@ -191,7 +194,7 @@ hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv
         }
 #undef CG_QV
     } else {
-        hipLaunchKernelGGL(k_quantize_any, grid, block, 0, s, kv, sym, scale, status, d.L, d.T, d.C, mt);
+        hipLaunchKernelGGL(k_quantize_any, grid, block, 0, s, kv, sym, scale, status, d.T, d.C, mt, call_map(d));
     }
     return hipGetLastError();
 }
@@ -227,26 +230,28 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
                                                        uint32_t *__restrict__ counts,
                                                        uint16_t *__restrict__ wire,
                                                        const uint32_t *__restrict__ wpre,
-                                                       uint32_t *__restrict__ status, int L, int T,
-                                                       int C, int A, int TT, MaxTable mt) {
+                                                       uint32_t *__restrict__ status, int T,
+                                                       int C, int A, int TT, MaxTable mt, CallMap cm) {
     constexpr int NS = 1 << LOGA;
     constexpr int NWD = CW / 2;      // 32-bit words (two bf16) per load
     constexpr int NP = NV * NWD;     // channel pairs per lane
     __shared__ __attribute__((aligned(16))) uint32_t hist[NS * NP * 64];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int slab = blockIdx.y, k = slab >= L ? 1 : 0, l = slab - k * L;
+    const int slab = blockIdx.y;
+    const SlabLoc sl = slab_loc(cm, slab);
     const int t0 = blockIdx.x * TT, t1 = min(T, t0 + TT);
     uint4 *h4 = reinterpret_cast<uint4 *>(hist);
     for (int i = threadIdx.x; i < NS * NP * 64 / 4; i += 512) h4[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
-    const int M = layer_m(mt, k, l);
+    const int M = layer_m(mt, sl.kv, sl.l);
     const float Mf = (float)M;
     uint8_t *hb = reinterpret_cast<uint8_t *>(hist);
     const uint32_t lane4 = (uint32_t)lane * 4;
-    const uint16_t *kv_slab = kv + ((int64_t)l * 2 + k) * T * (int64_t)C;
+    const uint16_t *kv_slab = kv + ((int64_t)sl.lv * 2 + sl.kv) * T * (int64_t)C;
     uint8_t *sym_slab = sym + (int64_t)slab * T * (int64_t)C;
+    uint16_t *scale_slab = call_sec(scale, cm, sl.b) + (int64_t)sl.ls * T;
 
     auto count = [&](uint32_t bits, int pair, bool odd) {
         const uint32_t q = __builtin_amdgcn_ubfe(bits, 0, LOGA);
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
 #pragma unroll
             for (int e = 0; e < CW; ++e) count(qb[e], i * NWD + e / 2, (e & 1) != 0);
         }
-        if (lane == 0) scale[(int64_t)slab * T + t] = (uint16_t)am;
+        if (lane == 0) scale_slab[t] = (uint16_t)am;
     };
 
     if constexpr (PACK) {
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
         // W <= NS) for a coalesced copy to the slab's wire tables.
         constexpr int NCOL = NP * 64;
         const int col = threadIdx.x;
-        const int W = layer_w(mt, k, l);
+        const int W = layer_w(mt, sl.kv, sl.l);
         uint32_t tabv[NS];
         bool bad = false;
         if (col < NCOL) {
@@ -430,9 +435,10 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
         if (__ballot(bad) && lane == 0) atomicOr(status, kStCorrupt);
         __syncthreads();
         // C is a multiple of 256, so the slab's C * W entries and its offset
-        // wpre[slab] * C are whole 16-byte units.
+        // wpre[ls] * C are whole 16-byte units.
         const uint4 *src4 = reinterpret_cast<const uint4 *>(hist);
-        uint4 *dst4 = reinterpret_cast<uint4 *>(wire + (wpre ? (int64_t)wpre[slab] : (int64_t)slab * A) * C);
+        uint4 *dst4 = reinterpret_cast<uint4 *>(call_sec(wire, cm, sl.b) +
+                                                (wpre ? (int64_t)wpre[sl.ls] : (int64_t)sl.ls * A) * C);
         for (int i = threadIdx.x; i < C * W / 8; i += 512) dst4[i] = src4[i];
         return;
     }
@@ -473,7 +479,7 @@ bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym) {
 }
 
 bool quantize_hist_fuses_cdf(const Dims &d, const void *wire) {
-    return quantize_hist_rows(d) >= d.T && (uintptr_t)wire % 16 == 0;
+    return quantize_hist_rows(d) >= d.T && (uintptr_t)wire % 16 == 0 && d.cstride % 16 == 0;
 }
 
 hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
@@ -486,14 +492,15 @@ hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_
     int loga = 2;
     while ((1 << loga) < d.A) ++loga;
     const int tt = (int)TT;
+    const CallMap cm = call_map(d);
 #define CG_QH(NV, CW, LG)                                                                                   \
     do {                                                                                                    \
         if (packed)                                                                                         \
             hipLaunchKernelGGL((k_quantize_hist<NV, CW, LG, true>), grid, block, 0, s, kv, sym, scale, counts,  \
-                               wire, wpre, status, d.L, d.T, d.C, d.A, tt, mt);                             \
+                               wire, wpre, status, d.T, d.C, d.A, tt, mt, cm);                              \
         else                                                                                                \
             hipLaunchKernelGGL((k_quantize_hist<NV, CW, LG, false>), grid, block, 0, s, kv, sym, scale, counts, \
-                               wire, wpre, status, d.L, d.T, d.C, d.A, tt, mt);                             \
+                               wire, wpre, status, d.T, d.C, d.A, tt, mt, cm);                              \
     } while (0)
 #define CG_QH_A(NV, CW)                         \
     do {                                        \

@@ -131,6 +131,7 @@ struct EncArgs {
     uint32_t *overflow_list;   // [tiles]
     int L, T, C, A, NC, CB;
     MaxTable mt;               // table width of each (K|V, layer)
+    CallMap cm;                // calls of a batch (tables and lengths per call)
     // This launch codes only the slabs whose symbol count 2M+1 lies in
     // [nsym_lo, nsym_hi]; the other blocks return at once.
     int nsym_lo, nsym_hi;
@@ -300,9 +301,10 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     const int c = cb * 64 + lane;
     const bool active = c < a.C;
     const int lane_off = active ? lane : (a.C - 1 - cb * 64);  // in-bounds column for idle lanes
-    const int kvs = slab >= a.L ? 1 : 0, ls = slab - kvs * a.L;
-    const int nsym = 2 * layer_m(a.mt, kvs, ls) + 1;
+    const SlabLoc sl = slab_loc(a.cm, slab);
+    const int nsym = 2 * layer_m(a.mt, sl.kv, sl.l) + 1;
     if (nsym < a.nsym_lo || nsym > a.nsym_hi) return;  // block-uniform
+    const uint16_t *cdf16 = call_sec(a.cdf16, a.cm, sl.b);  // the call's wire tables
 
     // Symbols are read through a buffer over this (K|V, layer) slab: the row
     // offset is wave-uniform (scalar), the column the lane's constant offset.
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
 
     // Tables, built by the block's waves together: one per lane, packed
     // start | freq << 16, [symbol][lane]; W symbols (the slab's table width).
-    const int W = layer_w(a.mt, kvs, ls);
+    const int W = layer_w(a.mt, sl.kv, sl.l);
     bool bad = false;
     // A launch for slabs of at most 2^LOGA symbols holds only that many
     // entries of a wider table: the quantiser's symbols never reach the rest.
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
                 uint32_t v = 0;
                 if (s < W) {
                     uint32_t lo, hi;
-                    cdf_bounds(a.cdf, a.cdf16, a.wpre, slab, a.C, c, A, W, s, lo, hi);
+                    cdf_bounds(a.cdf, cdf16, a.wpre, sl.ls, a.C, c, A, W, s, lo, hi);
                     v = lo;
                     if (s < WT)
                         bad |= hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne);
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
         uint32_t entry;
         if (active) {
             uint32_t lo, hi;
-            cdf_bounds(a.cdf, a.cdf16, a.wpre, slab, a.C, c, A, W, s, lo, hi);
+            cdf_bounds(a.cdf, cdf16, a.wpre, sl.ls, a.C, c, A, W, s, lo, hi);
             uint32_t f = hi - lo;
             if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)) {
                 bad = true;
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
                                                       (int)(w * 4), 0, 0);
         }
         const int j = (g * NW + wv) * S + s;
-        if (active) a.lengths[((int64_t)j * 2 * a.L + slab) * a.C + c] = (uint16_t)len;
+        if (active) call_sec(a.lengths, a.cm, sl.b)[((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C + c] = (uint16_t)len;
         const int64_t tile = tile_index(j, slab, cb, a.L, a.CB);
         if (lane == 0) a.tile_sum[tile] = total;
         if (__ballot(len > (uint32_t)kStageBytes) && lane == 0)
@@ -552,24 +554,28 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
 // ------------------------------------------------------------ chunk scan
 
 struct ChunkScanArgs {
-    const uint64_t *chunk_total;
-    uint64_t *chunk_off;
-    uint64_t *size_dev;
-    uint8_t *header_size;
+    const uint64_t *chunk_total;  // [NC * B], (chunk j, call b) at j * B + b
+    uint64_t *chunk_off;          // call 0's
+    uint64_t *size_dev;           // [B] or null
+    uint8_t *header_size;         // call 0's, or null
     WsHeader *hdr;
     uint64_t payload_base;
-    uint64_t cap;
-    int NC;
+    uint64_t cap;                 // each call's payload capacity
+    int NC, B;
+    CallMap cm;
 };
 
-// Pass 2: one block scans the chunk totals into chunk offsets and the size.
+// Pass 2: block b scans the chunk totals of call b into its chunk offsets
+// and its size.
 __global__ __launch_bounds__(1024) void k_chunk_scan(ChunkScanArgs a) {
     __shared__ uint64_t wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int b = blockIdx.x;
+    uint64_t *chunk_off = call_sec(a.chunk_off, a.cm, b);
     uint64_t run = 0;
     for (int seg = 0; seg < a.NC; seg += 1024) {
         const int i = seg + tid;
-        const uint64_t v = i < a.NC ? a.chunk_total[i] : 0ull;
+        const uint64_t v = i < a.NC ? a.chunk_total[(int64_t)i * a.B + b] : 0ull;
         uint64_t incl = v;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -584,18 +590,19 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(ChunkScanArgs a) {
             if (k < wv) before += wsum[k];
             total += wsum[k];
         }
-        if (i < a.NC) a.chunk_off[i] = run + before + incl - v;
+        if (i < a.NC) chunk_off[i] = run + before + incl - v;
         run += total;
         __syncthreads();
     }
     if (tid == 0) {
-        a.chunk_off[a.NC] = run;
-        a.hdr->payload_total = run;
+        chunk_off[a.NC] = run;
         if (run > a.cap) atomicOr(&a.hdr->status, kStCapacity);
         const uint64_t size = a.payload_base + run;
-        if (a.size_dev) *a.size_dev = size;
-        if (a.header_size)
-            for (int i = 0; i < 8; ++i) a.header_size[i] = (uint8_t)(size >> (8 * i));
+        if (a.size_dev) a.size_dev[b] = size;
+        if (a.header_size) {
+            uint8_t *h = call_sec(a.header_size, a.cm, b);
+            for (int i = 0; i < 8; ++i) h[i] = (uint8_t)(size >> (8 * i));
+        }
     }
 }
 
@@ -612,11 +619,11 @@ struct CompactArgs {
     uint64_t cap;
     uint32_t *status;
     int L, C, CB;
-    int64_t tiles_per_chunk;
     // LDS stage rows the encoder used for slabs of at most 16 symbols and for
     // the others (they decide which tiles it gathered).
     int rows_small, rows_large;
     MaxTable mt;
+    CallMap cm;
 };
 
 __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
@@ -625,17 +632,20 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
     const int cb = (int)(tile % a.CB);
     const int64_t js = tile / a.CB;  // j * 2L + slab
     const int c = cb * 64 + lane;
-    const int slab = (int)(js % (2 * a.L)), kvs = slab >= a.L ? 1 : 0;
-    const uint32_t rows = 2 * layer_m(a.mt, kvs, slab - kvs * a.L) + 1 <= 16 ? a.rows_small : a.rows_large;
-    const uint32_t len = c < a.C ? a.lengths[js * a.C + c] : 0u;
+    const int slab = (int)(js % (2 * a.L)), j = (int)(js / (2 * a.L));
+    const SlabLoc sl = slab_loc(a.cm, slab);
+    const uint32_t rows = 2 * layer_m(a.mt, sl.kv, sl.l) + 1 <= 16 ? a.rows_small : a.rows_large;
+    const uint16_t *lengths = call_sec(a.lengths, a.cm, sl.b) + ((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C;
+    const uint32_t len = c < a.C ? lengths[c] : 0u;
     if (__ballot(len > (uint32_t)kStageBytes)) return;  // k_fixup writes this tile
     const uint32_t incl = wave_incl_scan_u32(len, lane);
     const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
     const uint32_t excl = incl - len;
-    const uint64_t base = a.chunk_off[tile / a.tiles_per_chunk] + a.tile_off[tile];
+    const uint64_t base = call_sec(a.chunk_off, a.cm, sl.b)[j] + a.tile_off[tile];
+    uint8_t *payload = call_sec(a.payload, a.cm, sl.b);
     const uint8_t *src = a.staging + tile * (kStageBytes * 64);
     bool over = base + total > a.cap;
-    if (total <= rows * 64 && !over && ((uintptr_t)a.payload & 3u) == 0) {
+    if (total <= rows * 64 && !over && ((uintptr_t)payload & 3u) == 0) {
         // The encoder left the tile's bytes contiguous: copy them, whole
         // destination dwords by dword stores (each assembled from the two
         // aligned source dwords it straddles; the slot is 16 KiB aligned and
@@ -646,12 +656,12 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
         const uint64_t wa = (base + 3) & ~3ull, we = end & ~3ull;
         const uint32_t *s32 = reinterpret_cast<const uint32_t *>(src);
         if (wa >= we) {
-            if ((uint32_t)lane < total) a.payload[base + lane] = src[lane];
+            if ((uint32_t)lane < total) payload[base + lane] = src[lane];
         } else {
             const uint32_t nhead = (uint32_t)(wa - base), ntail = (uint32_t)(end - we);
-            if ((uint32_t)lane < nhead) a.payload[base + lane] = src[lane];
-            if ((uint32_t)lane < ntail) a.payload[we + lane] = src[(uint32_t)(we - base) + lane];
-            uint32_t *d32 = reinterpret_cast<uint32_t *>(a.payload + wa);
+            if ((uint32_t)lane < nhead) payload[base + lane] = src[lane];
+            if ((uint32_t)lane < ntail) payload[we + lane] = src[(uint32_t)(we - base) + lane];
+            uint32_t *d32 = reinterpret_cast<uint32_t *>(payload + wa);
             const uint32_t nw = (uint32_t)((we - wa) >> 2);
             for (uint32_t w = lane; w < nw; w += 64) {
                 const uint32_t so = nhead + 4 * w;  // source byte of the word
@@ -667,10 +677,10 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
             for (int u = 0; u < 4; ++u) b[u] = src[p + 64 * u];
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                if (base + p + 64 * u < a.cap) a.payload[base + p + 64 * u] = (uint8_t)b[u];
+                if (base + p + 64 * u < a.cap) payload[base + p + 64 * u] = (uint8_t)b[u];
         }
         for (; p < total; p += 64)
-            if (base + p < a.cap) a.payload[base + p] = src[p];
+            if (base + p < a.cap) payload[base + p] = src[p];
     } else {
         // [byte][lane] rows: output byte p belongs to the last stream k with
         // excl_k <= p (binary search over the lanes' offsets; the loop is
@@ -687,7 +697,7 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
                     sk = sc;
                 }
             }
-            if (p < total && base + p < a.cap) a.payload[base + p] = src[(p - sk) * 64 + k];
+            if (p < total && base + p < a.cap) payload[base + p] = src[(p - sk) * 64 + k];
         }
     }
     if (__ballot(over) && lane == 0) atomicOr(a.status, kStCapacity);
@@ -709,6 +719,7 @@ struct FixupArgs {
     uint64_t cap;
     int L, T, C, A, CB;
     MaxTable mt;
+    CallMap cm;
     bool packed;  // symbols in the quantiser's packed layout (PK 1 or 2 by slab)
 };
 
@@ -724,17 +735,20 @@ __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
         const int c = cb * 64 + lane;
         const bool active = c < a.C;
         const int n = min(kChunk, a.T - j * kChunk);
-        const uint32_t len = active ? a.lengths[js * a.C + c] : 0u;
+        const SlabLoc sl = slab_loc(a.cm, slab);
+        const uint16_t *lengths = call_sec(a.lengths, a.cm, sl.b) + ((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C;
+        const uint32_t len = active ? lengths[c] : 0u;
         const uint32_t incl = wave_incl_scan_u32(len, lane);
         if (!active) continue;
-        const int kvs = slab >= a.L ? 1 : 0, ls = slab - kvs * a.L;
-        const int W = layer_w(a.mt, kvs, ls);
-        const bool nib = 2 * layer_m(a.mt, kvs, ls) + 1 <= 16;
+        const int W = layer_w(a.mt, sl.kv, sl.l);
+        const bool nib = 2 * layer_m(a.mt, sl.kv, sl.l) + 1 <= 16;
+        const uint16_t *cdf16 = call_sec(a.cdf16, a.cm, sl.b);
         const uint8_t *sp = a.sym + ((int64_t)slab * a.T + (int64_t)j * kChunk) * a.C + c;
         const uint8_t *slab_sym = a.sym + (int64_t)slab * a.T * a.C;
         RcEncHold enc;
         enc.init();
-        GlobalSink sink{a.payload, a.chunk_off[j] + a.tile_off[tile] + incl - len, a.cap, 0u, false};
+        GlobalSink sink{call_sec(a.payload, a.cm, sl.b),
+                        call_sec(a.chunk_off, a.cm, sl.b)[j] + a.tile_off[tile] + incl - len, a.cap, 0u, false};
         for (int t = 0; t < n; ++t) {
             uint32_t q;
             if (!a.packed) {
@@ -750,7 +764,7 @@ __global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
             }
             const uint32_t s = min(q, (uint32_t)W - 1);
             uint32_t lo, hi;
-            cdf_bounds(a.cdf, a.cdf16, a.wpre, slab, a.C, c, a.A, W, (int)s, lo, hi);
+            cdf_bounds(a.cdf, cdf16, a.wpre, sl.ls, a.C, c, a.A, W, (int)s, lo, hi);
             const uint32_t f = hi > lo ? hi - lo : 1u;
             enc.encode(lo & 0xFFFFu, f, sink);
         }
@@ -781,9 +795,8 @@ static EncPlan enc_plan(const Dims &d, const MaxTable &mt) {
     p.loga = 4;
     while ((1 << p.loga) < d.A) ++p.loga;
     p.small = p.large = false;
-    const int nl = mt.lper ? (int)mt.lper : (d.L < CG_MAX_LAYERS ? d.L : CG_MAX_LAYERS);
     for (int kv = 0; kv < 2; ++kv)
-        for (int l = 0; l < nl; ++l) (2 * (mt.bins[kv][l] / 2 - 1) + 1 <= 16 ? p.small : p.large) = true;
+        for (int l = 0; l < d.Lc; ++l) (2 * (mt.bins[kv][l] / 2 - 1) + 1 <= 16 ? p.small : p.large) = true;
     return p;
 }
 
@@ -819,6 +832,7 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     a.A = d.A;
     a.NC = d.NC;
     a.CB = d.CB;
+    a.cm = call_map(d);
     const int NW = plan.NW;
     const unsigned blocks = plan.blocks;
     const dim3 grid(blocks), block(64 * NW);
@@ -868,9 +882,8 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
 #undef CG_ENC_A
 #undef CG_ENC
 
-    const int64_t tpc = 2LL * d.L * d.CB;
-    TileScan ts{w.tile_sum, nullptr, w.tile_off, w.scan_tmp, w.chunk_total, nullptr, 0, &w.hdr->status,
-                d.L, d.C, d.CB, d.NC};
+    TileScan ts{w.tile_sum, nullptr, w.tile_off, w.scan_tmp, w.chunk_total, nullptr, 0, nullptr, 0,
+                &w.hdr->status, d.L, d.C, d.CB, d.NC, call_map(d)};
     if ((e = launch_tile_scan(ts, s)) != hipSuccess) return e;
     ChunkScanArgs sa;
     sa.chunk_total = w.chunk_total;
@@ -881,7 +894,9 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     sa.payload_base = o.payload_base;
     sa.cap = o.cap;
     sa.NC = d.NC;
-    hipLaunchKernelGGL(k_chunk_scan, dim3(1), dim3(1024), 0, s, sa);
+    sa.B = ncalls(d);
+    sa.cm = call_map(d);
+    hipLaunchKernelGGL(k_chunk_scan, dim3((unsigned)sa.B), dim3(1024), 0, s, sa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     CompactArgs ca;
@@ -897,7 +912,7 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     ca.L = d.L;
     ca.C = d.C;
     ca.CB = d.CB;
-    ca.tiles_per_chunk = tpc;
+    ca.cm = call_map(d);
     // The launches of the encoder above: with the split, slabs of at most 16
     // symbols took 16-entry tables; otherwise every slab took 2^loga.
     const bool split = trusted && enc_split(plan);
@@ -925,6 +940,7 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     fa.C = d.C;
     fa.A = d.A;
     fa.CB = d.CB;
+    fa.cm = call_map(d);
     fa.packed = packed;
     hipLaunchKernelGGL(k_fixup, dim3(256), dim3(64), 0, s, fa);
     return hipGetLastError();

@@ -27,32 +27,61 @@ constexpr uint32_t kStCapacity = 4u;
 // the table width W (the call's alphabet A, or with per-layer tables the
 // layer's bins) follow from them.
 struct MaxTable {
-    uint8_t bins[2][CG_MAX_LAYERS];
-    // Batched calls run as one call of batch * L layers: layer l then takes
-    // the bins of layer l mod lper (lper = 0: no period). lmagic =
-    // ceil(2^32 / lper) turns the modulo into a multiply-high, exact for
-    // l < 2^16 and lper <= 1024.
-    uint32_t lper, lmagic;
+    uint8_t bins[2][CG_MAX_LAYERS];  // [K|V][layer of a call]
     int32_t per_layer;  // table format: 0 = width A for all tables, 1 = width = the layer's bins
     int32_t A;
 };
 
-__device__ __forceinline__ int local_layer(const MaxTable &mt, int l) {
-    if (mt.lper == 0) return l;
-    if (mt.lper == 1) return 0;
-    return l - (int)mt.lper * (int)__umulhi((uint32_t)l, mt.lmagic);
-}
-__device__ __forceinline__ int layer_bins(const MaxTable &mt, int kv, int l) {
-    return mt.bins[kv][local_layer(mt, l)];
-}
+// l: the layer within its call (SlabLoc::l).
+__device__ __forceinline__ int layer_bins(const MaxTable &mt, int kv, int l) { return mt.bins[kv][l]; }
 __device__ __forceinline__ int layer_m(const MaxTable &mt, int kv, int l) { return (layer_bins(mt, kv, l) >> 1) - 1; }
 __device__ __forceinline__ int layer_w(const MaxTable &mt, int kv, int l) {
     return mt.per_layer ? layer_bins(mt, kv, l) : mt.A;
 }
 
+// A batch of B calls of one shape [Lc, 2, T, H, D] runs as one call of
+// L = B * Lc layers, whose KV is [B * Lc, 2, T, H, D]. Its (K|V, layer)
+// slabs are numbered call by call: slab vs = b * 2Lc + kv * Lc + l is (K|V
+// kv, layer l) of call b, which is layer b * Lc + l of the batch's KV. A
+// single call is the batch of one (Lc = L: vs = kv * L + l). Workspace
+// arrays (symbols, counts, tile sums and offsets, staging) are indexed by
+// vs, and the tiles of (chunk j, call b) are contiguous: tile (j * 2L + vs)
+// * CB + cb. The blob sections of call b (scales, tables, lengths, chunk
+// offsets, payload) lie b * stride bytes after those of call 0 and are
+// indexed as in a call of its own (slab ls = vs - b * 2Lc), so each call's
+// blob is the blob of that call alone.
+struct CallMap {
+    int Lc;           // layers per call
+    uint64_t stride;  // bytes between the blob sections of consecutive calls (one call: 0)
+};
+struct SlabLoc {
+    int b;   // call
+    int ls;  // slab within the call, kv * Lc + l
+    int kv;  // 0 = K, 1 = V
+    int l;   // layer within the call
+    int lv;  // layer within the batch, b * Lc + l
+};
+__host__ __device__ __forceinline__ SlabLoc slab_loc(const CallMap &m, int vs) {
+    SlabLoc s;
+    s.b = vs / (2 * m.Lc);
+    s.ls = vs - s.b * 2 * m.Lc;
+    s.kv = s.ls >= m.Lc ? 1 : 0;
+    s.l = s.ls - s.kv * m.Lc;
+    s.lv = s.b * m.Lc + s.l;
+    return s;
+}
+// Section pointer of call b (null stays null).
+template <class T>
+__host__ __device__ __forceinline__ T *call_sec(T *p, const CallMap &m, int b) {
+    if (!p) return p;
+    return reinterpret_cast<T *>(reinterpret_cast<uintptr_t>(p) + (uint64_t)b * m.stride);
+}
+
 // Derived sizes of one call.
 struct Dims {
     int L, T, H, D, C, A, NC;
+    int Lc;          // layers per call (a batch of L / Lc calls; one call: Lc = L)
+    uint64_t cstride;  // bytes between consecutive calls' blob sections (one call: 0)
     int fmt;         // table format (CG_TABLES_*)
     int wmin;        // narrowest table width of the call
     int64_t tab_entries;  // sum of the table widths over the 2L (K|V, layer) slabs
@@ -61,6 +90,8 @@ struct Dims {
     int64_t NS;      // NC*2*L*C streams
     int64_t tiles;   // NC*2*L*CB coder tiles (64 streams each)
 };
+inline CallMap call_map(const Dims &d) { return CallMap{d.Lc, d.cstride}; }
+inline int ncalls(const Dims &d) { return d.L / d.Lc; }
 
 // Header of every workspace (first 256 bytes).
 struct WsHeader {
@@ -114,30 +145,39 @@ hipError_t launch_cdf(const Dims &d, const MaxTable &mt, const uint32_t *counts,
                       uint16_t *cdf_wire, const uint32_t *wpre, uint32_t *status, hipStream_t s);
 
 // Tile offsets in stream order (three passes over blocks of 256 tiles). The
-// byte count of each tile is tile_sum[t], or, with tile_sum null, the sum of
-// its 64 lengths. Offsets are relative to the chunk, or, with chunk_off set,
-// absolute, each chunk then checked against chunk_off (kStCorrupt).
+// scan runs over segments of 2Lc * CB tiles, one per (chunk j, call b),
+// segment j * B + b. The byte count of each tile is tile_sum[t], or, with
+// tile_sum null, the sum of its 64 lengths. Offsets are relative to the
+// segment, or, with chunk_off set, absolute within the call's payload, each
+// segment then checked against the call's chunk offsets (kStCorrupt).
 struct TileScan {
     const uint32_t *tile_sum;    // [tiles] or null
-    const uint16_t *lengths;     // [NC,2,L,C] when tile_sum is null
+    const uint16_t *lengths;     // call 0's [NC,2,Lc,C] when tile_sum is null
     uint64_t *tile_off;          // out [tiles]
     uint64_t *tmp;               // tile_scan_tmp_bytes(d)
-    uint64_t *chunk_total;       // out [NC], or null
-    const uint64_t *chunk_off;   // [NC+1] or null
+    uint64_t *chunk_total;       // out [NC * B] (segment j * B + b), or null
+    const uint64_t *chunk_off;   // call 0's [NC+1], or null
     uint64_t payload_bytes;      // bound of chunk_off (with chunk_off)
+    // With call_sizes (device, [B]): call b's bound is min(call_sizes[b],
+    // stride) - payload_off instead (0 if below).
+    const uint64_t *call_sizes;
+    uint64_t payload_off;
     uint32_t *status;
     int L, C, CB, NC;
-    int j0 = 0, NCr = -1;        // chunks [j0, j0 + NCr) only (NCr < 0: all NC)
+    CallMap cm;
+    int j0 = 0, NCr = -1;        // chunks [j0, j0 + NCr) only (NCr < 0: all NC; one call only)
 };
 size_t tile_scan_tmp_bytes(const Dims &d);
 hipError_t launch_tile_scan(const TileScan &a, hipStream_t s);
 
+// Blob sections of call 0 (call b's lie b * stride bytes further, see
+// CallMap); cap is each call's payload capacity.
 struct EncodeOut {
     uint8_t *payload;
     uint64_t cap;
     uint16_t *lengths;
     uint64_t *chunk_off;
-    uint64_t *size_dev;       // optional: receives payload_base + total
+    uint64_t *size_dev;       // optional: [B], receives payload_base + each call's total
     uint8_t *header_size;     // optional: 8 bytes in the blob header for the size
     uint64_t payload_base;    // offset of the payload within the blob (0 for stage calls)
 };
@@ -179,6 +219,9 @@ struct DecodeIn {
     const uint16_t *cdf16;
     uint32_t *wpre;            // with cdf16: table offsets, filled by launch_decode
     int j0 = 0, j1 = -1;       // decode chunks [j0, j1) only (j1 < 0: all); their tokens are written
+    // Batches: each call's payload bound from its blob size (see TileScan).
+    const uint64_t *call_sizes = nullptr;
+    uint64_t payload_off = 0;
 };
 
 // Paged output of the fused decoder: element (l, kv, t, c) goes to
@@ -213,37 +256,11 @@ struct HeaderBytes {
 hipError_t launch_blob_header(uint8_t *blob, const HeaderBytes &h, const BlobLayout &lay,
                               const Dims &d, hipStream_t s, int nblobs = 1, uint64_t stride = 0);
 
-// ---------------------------------------------------------------- batches
-// A batch of B calls of the same shape runs as one virtual call of B * L
-// layers (Dims vd); these kernels move the virtual blob's sections to and
-// from the B per-call blobs (Dims d, blob b at blobs + b * stride).
-struct Piece {
-    uint64_t src, dst, len;  // byte offsets from the source / destination base
-};
-
-struct BatchGeom {
-    Dims d, vd;                 // one call / the virtual call
-    BlobLayout lay, vlay;       // their blob layouts
-    int B;
-    uint64_t stride;            // bytes between per-call blobs
-    int npieces;                // pieces per call: 2 scales + 2 cdf + 2*NC lengths + 2*NC payload
-    uint64_t wsum[2];           // table widths summed over one call's K (V) layers
-};
-
-// Split (to_bytes): plan the pieces of every call from the virtual blob's
-// chunk offsets and tile offsets, write each call's chunk offsets and size.
-hipError_t launch_split_plan(const BatchGeom &g, const uint8_t *vblob, const uint64_t *vtile_off,
-                             uint8_t *blobs, uint64_t *sizes_dev, Piece *pieces, uint32_t *status,
-                             hipStream_t s);
-// Merge (from_bytes): check each call's header against hdr, plan the pieces
-// into the virtual blob from the calls' lengths and chunk offsets, write the
-// virtual chunk offsets.
-hipError_t launch_merge_plan(const BatchGeom &g, const uint8_t *blobs, const uint64_t *sizes_dev,
-                             const HeaderBytes &hdr, uint8_t *vblob, uint64_t *piece_len, Piece *pieces,
-                             uint32_t *status, hipStream_t s);
-// Copies every piece: src_base + b * src_stride + src -> dst_base + b * dst_stride + dst.
-hipError_t launch_copy_pieces(const BatchGeom &g, const Piece *pieces, const uint8_t *src_base,
-                              uint64_t src_stride, uint8_t *dst_base, uint64_t dst_stride, hipStream_t s);
+// Batch decode: checks each call's blob header (all but the size field)
+// against hdr and its size against the header and the stride; a call that
+// fails records kStCorrupt.
+hipError_t launch_batch_check(const uint8_t *blobs, uint64_t stride, int B, const uint64_t *sizes_dev,
+                              const HeaderBytes &hdr, uint64_t off_payload, uint32_t *status, hipStream_t s);
 
 // ----------------------------------------------------------- device helpers
 

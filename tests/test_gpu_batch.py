@@ -7,8 +7,8 @@ alone, and the batch decode of those blobs must equal the per-call decode and th
 oracle's decode bit for bit.
 The cases cover ragged token counts, several chunks, channel counts that are
 not a multiple of 64, calls with constant or zero KV, layer counts that vary
-their bins, and batches of more than 1024 layers in total (where the layer
-constants are taken modulo the call's layer count on the device).
+their bins, and batches of more than 1024 layers in total (the device looks
+the layer constants up by the layer within its call).
 """
 
 from __future__ import annotations
@@ -39,16 +39,19 @@ def _batch_kv(B, L, T, H, D, seed, specials=True):
     return np.stack(calls)
 
 
-def _stride(desc):
-    return (cgb.cg_blob_bound(desc) + 7) // 8 * 8
+def _stride(desc, extra=0):
+    """A stride of a multiple of 16 bytes (plus `extra`): blobs whose stride
+    is not one take the path where the tables are built apart from the
+    quantiser."""
+    return (cgb.cg_blob_bound(desc) + 15) // 16 * 16 + extra
 
 
-def _to_bytes_batch(kv, bk, bv, stride=None, fmt=0):
+def _to_bytes_batch(kv, bk, bv, stride=None, fmt=0, extra=0):
     import torch
 
     B, L, _, T, H, D = kv.shape
     desc = cgb.Desc(L, T, H, D, bk, bv, fmt)
-    stride = _stride(desc) if stride is None else stride
+    stride = _stride(desc, extra) if stride is None else stride
     blobs = torch.zeros(B * stride, dtype=torch.uint8, device="cuda:0")
     sizes = torch.zeros(B, dtype=torch.int64, device="cuda:0")
     ws = cgb.alloc_workspace_batch(desc, B, stride, cgb.CG_OP_TO_BYTES)
@@ -77,22 +80,25 @@ def _per_call_decode(blob_bytes):
 
 
 @pytest.mark.parametrize(
-    "B,shape",
+    "B,shape,extra",
     [
-        (3, (2, 300, 1, 96)),   # ragged T over two chunks, C not a multiple of 64
-        (5, (3, 64, 2, 64)),    # one short chunk per call
-        (4, (1, 700, 1, 40)),   # three chunks, C < 64
-        (1, (2, 256, 1, 64)),   # a batch of one is the plain call
-        (3, (2, 256, 4, 128)),  # C = 512: the quantiser builds the tables (one block per slab)
-        (2, (3, 200, 8, 128)),  # C = 1024, ragged T, tables built by the quantiser
-        (2, (2, 300, 8, 128)),  # C = 1024, two chunks: tables from the counts
+        (3, (2, 300, 1, 96), 0),   # ragged T over two chunks, C not a multiple of 64
+        (5, (3, 64, 2, 64), 8),    # one short chunk per call
+        (4, (1, 700, 1, 40), 0),   # three chunks, C < 64
+        (1, (2, 256, 1, 64), 0),   # a batch of one is the plain call
+        (3, (2, 256, 4, 128), 0),  # C = 512: the quantiser builds the tables (one block per slab)
+        (3, (2, 256, 4, 128), 8),  # the same with a stride of 16k + 8: tables from the counts
+        (2, (3, 200, 8, 128), 0),  # C = 1024, ragged T, tables built by the quantiser
+        (2, (3, 200, 8, 128), 8),
+        (2, (2, 300, 8, 128), 0),  # C = 1024, two chunks: tables from the counts
+        (9, (2, 256, 8, 128), 0),  # 2L * 9 slabs of one chunk each, as LMCache's 256-token chunks
     ],
 )
-def test_batch_blobs_equal_oracle_per_call(B, shape):
+def test_batch_blobs_equal_oracle_per_call(B, shape, extra):
     L, T, H, D = shape
     kv = _batch_kv(B, L, T, H, D, seed=900 + B)
     bk, bv = oracle.default_bins(L)
-    desc, stride, blobs, sizes, status = _to_bytes_batch(kv, bk, bv)
+    desc, stride, blobs, sizes, status = _to_bytes_batch(kv, bk, bv, extra=extra)
     assert status == cgb.CG_OK
     blobs_np, sizes_np = to_np(blobs), to_np(sizes)
     for b in range(B):

@@ -115,8 +115,8 @@ BlobLayout blob_layout(const Dims &d) {
 
 // Workspace regions (byte offsets; 0 = unused). Region 0 is the WsHeader.
 struct WsLayout {
-    uint64_t counts = 0, tile_sum = 0, tile_off = 0, chunk_total = 0, overflow = 0, staging = 0, sym = 0,
-             scan = 0, wpre = 0;
+    uint64_t counts = 0, tile_sum = 0, tile_mode = 0, tile_off = 0, chunk_total = 0, overflow = 0, staging = 0,
+             sym = 0, scan = 0, wpre = 0;
     uint64_t clear_end = kWsAlign;  // bytes from 0 that must start zeroed
     uint64_t total = kWsAlign;
 };
@@ -136,6 +136,7 @@ WsLayout ws_layout(const Dims &d, int op) {
         break;
     case CG_OP_ENCODE:
         w.tile_sum = take(4ull * d.tiles);
+        w.tile_mode = take((uint64_t)d.tiles);
         w.tile_off = take(8ull * d.tiles);
         w.chunk_total = take(8ull * d.NC * ncalls(d));
         w.overflow = take(4ull * d.tiles);
@@ -155,6 +156,7 @@ WsLayout ws_layout(const Dims &d, int op) {
         w.counts = take(4ull * 2 * d.L * d.C * d.A);
         w.clear_end = off;
         w.tile_sum = take(4ull * d.tiles);
+        w.tile_mode = take((uint64_t)d.tiles);
         w.tile_off = take(8ull * d.tiles);
         w.chunk_total = take(8ull * d.NC * ncalls(d));
         w.overflow = take(4ull * d.tiles);
@@ -267,9 +269,9 @@ int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *sca
         if ((rc = hip_rc(launch_histogram(d, sym, counts, status, s)))) return rc;
     }
     if (!fused && (rc = hip_rc(launch_cdf(d, mt, counts, nullptr, wire, wpre, status, s)))) return rc;
-    EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
-                at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging),
-                at<uint64_t>(ws, w.scan)};
+    EncodeWs ew{at<WsHeader>(ws, 0),         at<uint32_t>(ws, w.tile_sum), at<uint8_t>(ws, w.tile_mode),
+                at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow),
+                at<uint8_t>(ws, w.staging),   at<uint64_t>(ws, w.scan)};
     return hip_rc(launch_encode(d, mt, sym, nullptr, wire, wpre, o, ew, true, packed, s));
 }
 
@@ -446,9 +448,9 @@ int cg_encode(const cg_desc *desc, const uint8_t *sym, const int32_t *cdf, uint8
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if ((rc = clear_ws(ws, w, s))) return rc;
     EncodeOut o{payload, (uint64_t)cap, lengths, chunk_off, nullptr, nullptr, 0};
-    EncodeWs ew{at<WsHeader>(ws, 0), at<uint32_t>(ws, w.tile_sum), at<uint64_t>(ws, w.tile_off),
-                at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow), at<uint8_t>(ws, w.staging),
-                at<uint64_t>(ws, w.scan)};
+    EncodeWs ew{at<WsHeader>(ws, 0),         at<uint32_t>(ws, w.tile_sum), at<uint8_t>(ws, w.tile_mode),
+                at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow),
+                at<uint8_t>(ws, w.staging),   at<uint64_t>(ws, w.scan)};
     MaxTable mt;
     make_max_table(desc, d, mt);
     return hip_rc(launch_encode(d, mt, sym, cdf, nullptr, nullptr, o, ew, false, false, s));

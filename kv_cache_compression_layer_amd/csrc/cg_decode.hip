@@ -76,6 +76,7 @@ __device__ __forceinline__ const uint8_t *call_payload(const DecArgs &a, const S
 // wave (~39 KiB per block) four blocks, 32 waves, fit a CU; the few tiles
 // that do not fit read global memory.
 constexpr uint32_t kPoolPerWave = 3840;
+constexpr uint32_t kPoolPerWaveSmall = 1536;  // blocks of one or two waves
 constexpr uint32_t kPoolSlack = 528;
 
 // One stream's decoder state. Staged streams read pool bytes at `ptr` (each
@@ -336,13 +337,16 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     constexpr bool T16 = NW <= 2;
     __shared__ uint32_t tab[T16 ? ((1 << LOGA) + 1) * 32 : (1 << LOGA) * 64];  // [symbol][lane]
     __shared__ float dq[128];
-    // Blocks of one or two waves (calls of fewer than eight chunks) keep no
-    // pool: what limits them is residency, and at a few bits per symbol a
-    // stream fetches a byte only every several symbols, which the look-ahead
-    // reads hide. Larger blocks share their tables across more waves and the
-    // pool pays for itself (measured: 1.79 vs 2.14 ms on 32K tokens).
-    constexpr uint32_t kPoolBytes = NW <= 2 ? 0u : NW * kPoolPerWave;
-    __shared__ uint32_t pool_w[kPoolBytes ? (kPoolBytes + kPoolSlack) / 4 : 1];  // staged payload
+    // Blocks of one or two waves (calls of fewer than eight chunks) keep a
+    // small pool: what limits them is residency, so it holds only the tiles
+    // of short streams (a 16-bin slab's 64 streams of a 256-token chunk at
+    // about 12 bytes each), whose bytes then come from LDS instead of
+    // bounds-checked global reads (128 calls of 256 tokens: 2.55 ms with no
+    // pool, 2.42 / 2.39 / 2.49 ms with 1024 / 1536 / 2560 bytes per wave).
+    // Larger blocks share their tables across more waves and a full pool
+    // pays for itself (measured: 1.79 vs 2.14 ms on 32K tokens).
+    constexpr uint32_t kPoolBytes = NW * (NW <= 2 ? kPoolPerWaveSmall : kPoolPerWave);
+    __shared__ uint32_t pool_w[(kPoolBytes + kPoolSlack) / 4];  // staged payload
     __shared__ uint32_t need_w[NW];
     const int lane = threadIdx.x & 63;
     // The wave index is uniform across the wave; readfirstlane tells the compiler so,
@@ -779,10 +783,21 @@ __device__ __forceinline__ void decode_loop2(const DecArgs &a, DecStream (&st)[2
     if (n > 0) store_all(n - 1);
 }
 
-// At least eight waves per SIMD (at most 64 VGPRs): residency decides the
-// decoder's speed more than anything the registers would save.
+// Waves per SIMD that the LDS of a block allows (160 KiB per CU, four
+// SIMDs), at most eight: the register budget is set to match, so the
+// registers never hold residency below what the LDS allows (eight waves
+// means at most 64 VGPRs): residency decides the decoder's speed more than
+// anything the registers would save.
+__host__ __device__ constexpr uint32_t dec2_lds_bytes(int loga, int nw) {
+    return (1u << loga) * 128u * 4u + 128u * 4u + (uint32_t)nw * pool_per_wave2(loga) + kPoolSlack + 4u * nw;
+}
+__host__ __device__ constexpr int dec2_waves_per_simd(int loga, int nw) {
+    return (int)(163840u / dec2_lds_bytes(loga, nw)) * nw / 4 > 8 ? 8 : (int)(163840u / dec2_lds_bytes(loga, nw)) * nw / 4;
+}
+static_assert(dec2_waves_per_simd(5, 8) == 8 && dec2_waves_per_simd(4, 8) == 8, "32-wave residency of the 32K path");
+
 template <bool FUSED, int LOGA, bool CLAMP, int NW, bool PAGED, bool TAIL>
-__global__ __launch_bounds__(64 * NW, 8) void k_decode2(DecArgs a) {
+__global__ __launch_bounds__(64 * NW, dec2_waves_per_simd(LOGA, NW)) void k_decode2(DecArgs a) {
     constexpr int S = 2;
     __shared__ uint32_t tab[(1 << LOGA) * 128];  // [symbol][stream][lane]
     __shared__ float dq[128];

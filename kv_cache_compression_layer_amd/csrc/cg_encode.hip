@@ -46,6 +46,12 @@ namespace cg {
 constexpr int kStageBytes = 256;  // staging slot bytes per stream (5 bits/symbol fit)
 constexpr int kRing = 16;         // symbol prefetch depth
 
+// What k_encode left in a tile's staging slot: the tile's bytes in stream
+// order at slot bytes [0, total) (gathered), each stream's bytes in slot rows
+// [row][lane] (rows), or a stream too long for the slot, re-coded by k_fixup
+// (overflow).
+constexpr uint8_t kTileGathered = 0, kTileRows = 1, kTileOverflow = 2;
+
 // ----------------------------------------------------------- fix-up coder
 
 struct RcEncHold {
@@ -126,6 +132,7 @@ struct EncArgs {
     const uint32_t *wpre;
     uint8_t *staging;          // [tiles][kStageBytes][64] bytes
     uint32_t *tile_sum;        // [tiles]
+    uint8_t *tile_mode;        // [tiles] kTileGathered / kTileRows / kTileOverflow
     uint16_t *lengths;         // [NC, 2L, C]
     WsHeader *hdr;
     uint32_t *overflow_list;   // [tiles]
@@ -503,7 +510,9 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
         const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
         const uint32_t excl = incl - len;
         const uint8_t *lst = stage + (wv * S + s) * (R + 2) * kRowPitch;
-        if (total <= (uint32_t)(R * 64) && !__ballot(len > (uint32_t)kStageBytes)) {
+        const bool ovf = __ballot(len > (uint32_t)kStageBytes) != 0;
+        const bool gathered = total <= (uint32_t)(R * 64) && !ovf;
+        if (gathered) {
             // Compact tile: gather the streams' bytes in stream order into
             // slot bytes [0, total) (64 consecutive bytes per store). Output
             // byte p belongs to the last stream k with excl_k <= p, found by a
@@ -544,9 +553,11 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
         const int j = (g * NW + wv) * S + s;
         if (active) call_sec(a.lengths, a.cm, sl.b)[((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C + c] = (uint16_t)len;
         const int64_t tile = tile_index(j, slab, cb, a.L, a.CB);
-        if (lane == 0) a.tile_sum[tile] = total;
-        if (__ballot(len > (uint32_t)kStageBytes) && lane == 0)
-            a.overflow_list[atomicAdd(&a.hdr->overflow_count, 1u)] = (uint32_t)tile;
+        if (lane == 0) {
+            a.tile_sum[tile] = total;
+            a.tile_mode[tile] = gathered ? kTileGathered : ovf ? kTileOverflow : kTileRows;
+        }
+        if (ovf && lane == 0) a.overflow_list[atomicAdd(&a.hdr->overflow_count, 1u)] = (uint32_t)tile;
     }
     if (__ballot((active && (qmax > amax || bad))) && lane == 0) atomicOr(&a.hdr->status, kStCorrupt);
 }
@@ -611,41 +622,37 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(ChunkScanArgs a) {
 struct CompactArgs {
     const uint8_t *staging;
     const uint16_t *lengths;
+    const uint32_t *tile_sum;
+    const uint8_t *tile_mode;
     const uint64_t *tile_off;   // relative to the chunk
     const uint64_t *chunk_off;
-    const uint32_t *overflow_list;
-    const WsHeader *hdr;
     uint8_t *payload;
     uint64_t cap;
     uint32_t *status;
+    int64_t tiles;
     int L, C, CB;
-    // LDS stage rows the encoder used for slabs of at most 16 symbols and for
-    // the others (they decide which tiles it gathered).
-    int rows_small, rows_large;
-    MaxTable mt;
     CallMap cm;
 };
 
+// One wave per tile. Every load a tile's copy depends on (its mode, byte
+// count and offsets) is issued at once, so the copy waits for one round
+// trip.
 __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
     const int lane = threadIdx.x;
     const int64_t tile = blockIdx.x;
     const int cb = (int)(tile % a.CB);
     const int64_t js = tile / a.CB;  // j * 2L + slab
-    const int c = cb * 64 + lane;
     const int slab = (int)(js % (2 * a.L)), j = (int)(js / (2 * a.L));
     const SlabLoc sl = slab_loc(a.cm, slab);
-    const uint32_t rows = 2 * layer_m(a.mt, sl.kv, sl.l) + 1 <= 16 ? a.rows_small : a.rows_large;
-    const uint16_t *lengths = call_sec(a.lengths, a.cm, sl.b) + ((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C;
-    const uint32_t len = c < a.C ? lengths[c] : 0u;
-    if (__ballot(len > (uint32_t)kStageBytes)) return;  // k_fixup writes this tile
-    const uint32_t incl = wave_incl_scan_u32(len, lane);
-    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
-    const uint32_t excl = incl - len;
+    const uint32_t mode = a.tile_mode[tile];
+    const uint32_t total = a.tile_sum[tile];
     const uint64_t base = call_sec(a.chunk_off, a.cm, sl.b)[j] + a.tile_off[tile];
+    if (mode == kTileOverflow) return;  // k_fixup writes this tile
     uint8_t *payload = call_sec(a.payload, a.cm, sl.b);
+    const bool gathered = mode == kTileGathered;
     const uint8_t *src = a.staging + tile * (kStageBytes * 64);
     bool over = base + total > a.cap;
-    if (total <= rows * 64 && !over && ((uintptr_t)payload & 3u) == 0) {
+    if (gathered && !over && ((uintptr_t)payload & 3u) == 0) {
         // The encoder left the tile's bytes contiguous: copy them, whole
         // destination dwords by dword stores (each assembled from the two
         // aligned source dwords it straddles; the slot is 16 KiB aligned and
@@ -663,12 +670,34 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
             if ((uint32_t)lane < ntail) payload[we + lane] = src[(uint32_t)(we - base) + lane];
             uint32_t *d32 = reinterpret_cast<uint32_t *>(payload + wa);
             const uint32_t nw = (uint32_t)((we - wa) >> 2);
-            for (uint32_t w = lane; w < nw; w += 64) {
-                const uint32_t so = nhead + 4 * w;  // source byte of the word
-                d32[w] = __builtin_amdgcn_alignbyte(s32[(so >> 2) + 1], s32[so >> 2], so & 3u);
+            const uint32_t sh = nhead & 3u;  // source byte offset of every word
+            constexpr int U = 12;            // words per lane in one round trip (a gathered tile has <= 2816 bytes)
+            if (nw <= U * 64) {
+                // Every load first, then every store: one round trip.
+                uint32_t v0[U], v1[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t w = (uint32_t)lane + 64u * u;
+                    const uint32_t si = (nhead >> 2) + w;  // aligned source word below the word's first byte
+                    v0[u] = v1[u] = 0;
+                    if (w < nw) {
+                        v0[u] = s32[si];
+                        v1[u] = s32[si + 1];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t w = (uint32_t)lane + 64u * u;
+                    if (w < nw) d32[w] = __builtin_amdgcn_alignbyte(v1[u], v0[u], sh);
+                }
+            } else {
+                for (uint32_t w = lane; w < nw; w += 64) {
+                    const uint32_t so = nhead + 4 * w;  // source byte of the word
+                    d32[w] = __builtin_amdgcn_alignbyte(s32[(so >> 2) + 1], s32[so >> 2], sh);
+                }
             }
         }
-    } else if (total <= rows * 64) {
+    } else if (gathered) {
         // The same copy a byte at a time (capacity overflow, unaligned payload).
         uint32_t p = lane;
         for (; p + 192 < total; p += 256) {
@@ -685,6 +714,10 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
         // [byte][lane] rows: output byte p belongs to the last stream k with
         // excl_k <= p (binary search over the lanes' offsets; the loop is
         // wave-uniform because the search reads other lanes).
+        const int c = cb * 64 + lane;
+        const uint16_t *lengths = call_sec(a.lengths, a.cm, sl.b) + ((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C;
+        const uint32_t len = c < a.C ? lengths[c] : 0u;
+        const uint32_t excl = wave_incl_scan_u32(len, lane) - len;
         for (uint32_t p0 = 0; p0 < total; p0 += 64) {
             const uint32_t p = p0 + (uint32_t)lane;
             int k = 0;
@@ -823,6 +856,7 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     a.mt = mt;
     a.staging = w.staging;
     a.tile_sum = w.tile_sum;
+    a.tile_mode = w.tile_mode;
     a.lengths = o.lengths;
     a.hdr = w.hdr;
     a.overflow_list = w.overflow_list;
@@ -902,23 +936,18 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     CompactArgs ca;
     ca.staging = w.staging;
     ca.lengths = o.lengths;
+    ca.tile_sum = w.tile_sum;
+    ca.tile_mode = w.tile_mode;
     ca.tile_off = w.tile_off;
     ca.chunk_off = o.chunk_off;
-    ca.overflow_list = w.overflow_list;
-    ca.hdr = w.hdr;
     ca.payload = o.payload;
     ca.cap = o.cap;
     ca.status = &w.hdr->status;
+    ca.tiles = d.tiles;
     ca.L = d.L;
     ca.C = d.C;
     ca.CB = d.CB;
     ca.cm = call_map(d);
-    // The launches of the encoder above: with the split, slabs of at most 16
-    // symbols took 16-entry tables; otherwise every slab took 2^loga.
-    const bool split = trusted && enc_split(plan);
-    ca.rows_small = split ? enc_rows(4, NW) : enc_rows(loga, NW);
-    ca.rows_large = enc_rows(loga, NW);
-    ca.mt = mt;
     hipLaunchKernelGGL(k_compact, dim3((unsigned)d.tiles), dim3(64), 0, s, ca);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 

@@ -185,6 +185,7 @@ struct EncodeOut {
 struct EncodeWs {
     WsHeader *hdr;
     uint32_t *tile_sum;       // [tiles] bytes of each 64-stream tile
+    uint8_t *tile_mode;       // [tiles] how the tile's bytes were left in its staging slot
     uint64_t *tile_off;       // [tiles] offset of each tile within its chunk
     uint64_t *chunk_total;    // [NC] bytes of each chunk
     uint32_t *overflow_list;  // [tiles] tiles with a stream beyond the LDS stage

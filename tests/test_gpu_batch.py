@@ -119,11 +119,11 @@ def test_batch_blobs_equal_oracle_per_call(B, shape, extra):
 @pytest.mark.parametrize(
     "B,L,H,D,fmt",
     [
-        (1100, 1, 1, 64, 0),   # 1100 layers: every virtual layer takes call layer 0
+        (1100, 1, 1, 64, 0),   # 1100 layers in total: every call has one layer
         (150, 7, 1, 64, 0),    # 1050 layers, period 7
         (100, 12, 1, 64, 0),   # 1200 layers, bins differ across a call's layers
         (40, 32, 8, 128, 0),   # 1280 layers of C = 1024 (tables built by the quantiser)
-        (100, 12, 1, 64, 1),   # the same with per-layer tables (widths taken modulo L)
+        (100, 12, 1, 64, 1),   # the same with per-layer tables (widths of the layer within its call)
         (40, 32, 8, 128, 1),
     ],
 )

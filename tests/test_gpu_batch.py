@@ -92,6 +92,8 @@ def _per_call_decode(blob_bytes):
         (2, (3, 200, 8, 128), 8),
         (2, (2, 300, 8, 128), 0),  # C = 1024, two chunks: tables from the counts
         (9, (2, 256, 8, 128), 0),  # 2L * 9 slabs of one chunk each, as LMCache's 256-token chunks
+        (4, (2, 256, 2, 128), 0),  # C = 256: tables built by the quantiser eight entries at a time
+        (3, (2, 256, 6, 128), 0),  # C = 768
     ],
 )
 def test_batch_blobs_equal_oracle_per_call(B, shape, extra):

@@ -38,6 +38,9 @@ CASES = [
     ((32, 256, 8, 128), "default"),  # C = 1024, one chunk: the quantiser builds the tables
     ((4, 700, 8, 128), "default"),   # C = 1024, three chunks: tables from the counts
     ((3, 256, 4, 128), "odd"),       # C = 512, quantiser-built tables, odd widths
+    ((4, 256, 8, 128), "odd"),       # C = 1024, quantiser-built tables held whole, odd widths
+    ((4, 264, 2, 128), "odd"),       # C = 256, quantiser-built tables, eight entries at a time
+    ((3, 200, 6, 128), "default"),   # C = 768, quantiser-built tables
     ((2, 300, 1, 64), "wide"),       # alphabet above 32
 ]
 

@@ -749,6 +749,12 @@ __device__ __forceinline__ void decode_loop2(const DecArgs &a, DecStream (&st)[2
                     d.range <<= 8;
                     if (STAGED) d.ptr += 1u;
                     else d.pos += 1u;
+                    // Keep the shifted state in its registers: otherwise the
+                    // second shift is rebuilt from the unshifted values
+                    // (range << 16, ptr + 2) and both paths merge through
+                    // register copies on every step.
+                    if (STAGED) __asm__ volatile("" : "+v"(d.code), "+v"(d.range), "+v"(d.ptr));
+                    else __asm__ volatile("" : "+v"(d.code), "+v"(d.range), "+v"(d.pos));
                     if (__builtin_amdgcn_ballot_w64(d.range < kTop)) {
                         __asm__ volatile("" ::: "memory");  // a real branch, not selects
                         if (d.range < kTop) {

@@ -548,6 +548,45 @@ def main():
         }
         log(f"batch of {nb} x {ct} tokens: {json.dumps(batch)}")
         del chunks, chunks_out, out_p, blobs, ws_be, ws_bd, ws_pe, ws_pd
+        torch.cuda.empty_cache()
+        # The pages' chunk-size sweep: the same KV cut into calls of 64, 128
+        # and 768 tokens (768 takes the first 42 * 768 tokens), one batch call
+        # each way.
+        sweep = []
+        for ct2 in (64, 128, 768):
+            nb2 = T // ct2
+            if nb2 < 2 or nb2 * L > 32767:
+                continue
+            d2 = cgb.Desc(L, ct2, H, D, desc.bins_k, desc.bins_v)
+            ch2 = kv.view(L, 2, T, C)[:, :, : nb2 * ct2].reshape(L, 2, nb2, ct2, C).permute(2, 0, 1, 3, 4).contiguous()
+            st2 = (cgb.cg_blob_bound(d2) + 15) // 16 * 16
+            bl2 = torch.empty(nb2 * st2, dtype=torch.uint8, device=dev)
+            sz2 = torch.zeros(nb2, dtype=torch.int64, device=dev)
+            we2 = cgb.alloc_workspace_batch(d2, nb2, st2, cgb.CG_OP_TO_BYTES, dev)
+            wd2 = cgb.alloc_workspace_batch(d2, nb2, st2, cgb.CG_OP_FROM_BYTES, dev)
+            out2 = torch.empty_like(ch2)
+
+            def e2():
+                cgb.cg_to_bytes_batch(d2, nb2, ch2, bl2, st2, sz2, we2)
+
+            def d2f():
+                cgb.cg_from_bytes_batch(d2, nb2, bl2, st2, sz2, out2, wd2)
+
+            e2()
+            cgb.check_status(we2, what=f"cg_to_bytes_batch ({ct2}-token calls)")
+            d2f()
+            cgb.check_status(wd2, what=f"cg_from_bytes_batch ({ct2}-token calls)")
+            r2 = ch2.numel() * 2
+            te2 = time_events(e2, args.stage_reps, torch)
+            td2 = time_events(d2f, args.stage_reps, torch)
+            row = {"tokens_per_call": ct2, "calls": nb2, "to_bytes_ms": te2, "from_bytes_ms": td2,
+                   "to_bytes_GBps": r2 / (te2 * 1e-3) / 1e9, "from_bytes_GBps": r2 / (td2 * 1e-3) / 1e9,
+                   "compression_ratio": r2 / int(sz2.sum().item())}
+            log(f"batch of {nb2} x {ct2} tokens: {json.dumps(row)}")
+            sweep.append(row)
+            del ch2, bl2, sz2, we2, wd2, out2
+            torch.cuda.empty_cache()
+        batch["chunk_size_sweep"] = sweep
 
     # Achievable copy bandwidth: a device-to-device copy of the raw KV
     # (read + write of 4 GiB), the practical ceiling beside the 8 TB/s spec.

@@ -99,7 +99,7 @@ struct WsHeader {
     uint32_t reserved0;
     uint32_t overflow_count;   // tiles whose streams did not fit in LDS
     uint32_t pad0;
-    uint64_t payload_total;    // sum of all stream lengths (encode)
+    uint64_t reserved1;
     uint32_t pad[58];
 };
 static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");

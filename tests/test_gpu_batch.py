@@ -158,6 +158,34 @@ def test_batch_many_layers(B, L, H, D, fmt):
                                       _per_call_decode(_blob(blobs_np, stride, sizes_np, b)))
 
 
+def test_batch_at_the_layer_limit():
+    """32767 one-layer calls: 65534 (K|V, layer) slabs, the largest grid
+    dimension the per-slab kernels take. Every call equals the plain GPU
+    call; a sample also equals the oracle."""
+    import torch
+
+    B, L, T, H, D = 32767, 1, 8, 1, 64
+    rng = np.random.default_rng(32767)
+    kv = (rng.standard_normal((B, L, 2, T, H, D)).astype(np.float32)
+          * rng.lognormal(0.0, 1.0, (B, 1, 1, 1, 1, 1)).astype(np.float32))
+    u = kv.view(np.uint32)
+    kv = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)  # bf16, nearest even
+    bk, bv = oracle.default_bins(L)
+    desc, stride, blobs, sizes, status = _to_bytes_batch(kv, bk, bv)
+    assert status == cgb.CG_OK
+    blobs_np, sizes_np = to_np(blobs), to_np(sizes)
+    got, st = _from_bytes_batch(desc, B, blobs, stride, sizes)
+    assert st == cgb.CG_OK
+    n = 2 * L * T * H * D
+    kv_d = to_dev(kv).view(torch.bfloat16)
+    for b in list(range(0, B, 4099)) + [B - 1]:
+        one = to_np(cgb.to_bytes(kv_d[b], bk, bv)).tobytes()
+        assert _blob(blobs_np, stride, sizes_np, b) == one, f"call {b}"
+        assert one == oracle.to_bytes(kv[b], bk, bv), f"call {b}"
+        ref = np.asarray(oracle.from_bytes(one)).view(np.uint16).reshape(-1)
+        assert_bf16_equal(got[b * n : (b + 1) * n], ref)
+
+
 def test_batch_corrupt_call_is_reported_and_isolated():
     import torch
 

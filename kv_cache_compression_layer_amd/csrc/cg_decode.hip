@@ -448,16 +448,17 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // w + NW, ...; entries past the table's width W (up to 2^LOGA) have start
     // 0xFFFF.
     bool bad_table = false;
+    // Loads read an in-bounds column (the lane's own for active lanes).
+    const LaneTable lt = lane_table(a.cdf32, cdf16, a.wpre, sl.ls, a.C, min(c, a.C - 1), A, W);
     if constexpr (T16) {
         // Starts 0..2^LOGA: the symbol's lower bound below W, 0xFFFF from W
         // on; idle lanes: 0 then 0xFFFF (code 0 always decodes symbol 0 with
         // frequency 0xFFFF, which never forces a renormalisation).
         uint16_t *tab16 = reinterpret_cast<uint16_t *>(tab);
-        for (int s = wv; s <= (1 << LOGA); s += NW) {
+        for_lane_bounds<((1 << LOGA) + NW) / NW, kTabGroup>(lt, wv, NW, (1 << LOGA) + 1,
+                                                            [&](int s, uint32_t lo, uint32_t hi) {
             uint32_t v = 0xFFFFu;
             if (s < W && active) {
-                uint32_t lo, hi;
-                cdf_bounds(a.cdf32, cdf16, a.wpre, sl.ls, a.C, c, A, W, s, lo, hi);
                 if (s < (1 << LOGA) &&
                     (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)))
                     bad_table = true;
@@ -466,25 +467,24 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
                 v = 0;
             }
             tab16[s * 64 + lane] = (uint16_t)v;
-        }
-    } else
-    for (int s = wv; s < (1 << LOGA); s += NW) {
-        uint32_t entry = 0xFFFFu;
-        if (s < W && active) {
-            uint32_t lo, hi;
-            cdf_bounds(a.cdf32, cdf16, a.wpre, sl.ls, a.C, c, A, W, s, lo, hi);
-            uint32_t f = hi - lo;
-            if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)) {
-                bad_table = true;
-                f = 1;
+        });
+    } else {
+        for_lane_bounds<((1 << LOGA) + NW - 1) / NW, kTabGroup>(lt, wv, NW, 1 << LOGA, [&](int s, uint32_t lo, uint32_t hi) {
+            uint32_t entry = 0xFFFFu;
+            if (s < W && active) {
+                uint32_t f = hi - lo;
+                if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)) {
+                    bad_table = true;
+                    f = 1;
+                }
+                entry = (lo & 0xFFFFu) | (f << 16);
+            } else if (s < W) {
+                // Idle lanes: code stays 0, so they always decode symbol 0,
+                // whose frequency 65535 never forces a renormalisation.
+                entry = s == 0 ? 0xFFFFu << 16 : (uint32_t)s | (1u << 16);
             }
-            entry = (lo & 0xFFFFu) | (f << 16);
-        } else if (s < W) {
-            // Idle lanes: code stays 0, so they always decode symbol 0, whose
-            // frequency 65535 never forces a renormalisation.
-            entry = s == 0 ? 0xFFFFu << 16 : (uint32_t)s | (1u << 16);
-        }
-        tab[s * 64 + lane] = entry;
+            tab[s * 64 + lane] = entry;
+        });
     }
     uint32_t sc_v[S][4];
 #pragma unroll
@@ -908,13 +908,12 @@ __global__ __launch_bounds__(64 * NW, dec2_waves_per_simd(LOGA, NW)) void k_deco
     // 0xFFFF. Idle channels: code stays 0, so they always decode symbol 0,
     // whose frequency 65535 never forces a renormalisation.
     bool bad_table = false;
-    for (int q = wv; q < (1 << LOGA); q += NW) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
+    for (int s = 0; s < S; ++s) {
+        const LaneTable lt = lane_table(a.cdf32, cdf16, a.wpre, sl.ls, a.C, min(cch[s], a.C - 1), A, W);
+        for_lane_bounds<((1 << LOGA) + NW - 1) / NW, kTabGroup>(lt, wv, NW, 1 << LOGA, [&](int q, uint32_t lo, uint32_t hi) {
             uint32_t entry = 0xFFFFu;
             if (q < W && act[s]) {
-                uint32_t lo, hi;
-                cdf_bounds(a.cdf32, cdf16, a.wpre, sl.ls, a.C, cch[s], A, W, q, lo, hi);
                 uint32_t f = hi - lo;
                 if (hi <= lo || hi > kProbOne || (q == 0 && lo != 0) || (q == W - 1 && hi != kProbOne)) {
                     bad_table = true;
@@ -925,7 +924,7 @@ __global__ __launch_bounds__(64 * NW, dec2_waves_per_simd(LOGA, NW)) void k_deco
                 entry = q == 0 ? 0xFFFFu << 16 : (uint32_t)q | (1u << 16);
             }
             tab[(q * 2 + s) * 64 + lane] = entry;
-        }
+        });
     }
     // Per-token scales of the chunk: lane i of sc_v[k] holds token 64k + i.
     uint32_t sc_v[4];

@@ -367,41 +367,39 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
     // A launch for slabs of at most 2^LOGA symbols holds only that many
     // entries of a wider table: the quantiser's symbols never reach the rest.
     const int WT = min(W, 1 << LOGA);
+    // Loads use the in-bounds column col (the lane's own for active lanes).
+    const LaneTable lt = lane_table(a.cdf, cdf16, a.wpre, sl.ls, a.C, col, A, W);
     if constexpr (T16) {
         // Starts 0..WT (start WT is 2^16, stored as 0, when WT == W). Idle
         // lanes write nothing and read the table of an active column.
         uint16_t *tab16 = reinterpret_cast<uint16_t *>(tab);
-        if (active) {
-            for (int s = 0; s <= WT; ++s) {
-                uint32_t v = 0;
-                if (s < W) {
-                    uint32_t lo, hi;
-                    cdf_bounds(a.cdf, cdf16, a.wpre, sl.ls, a.C, c, A, W, s, lo, hi);
-                    v = lo;
-                    if (s < WT)
-                        bad |= hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne);
+        for_lane_bounds<(1 << LOGA) + 1, kTabGroup>(lt, 0, 1, WT + 1, [&](int s, uint32_t lo, uint32_t hi) {
+            if (!active) return;
+            uint32_t v = 0;
+            if (s < W) {
+                v = lo;
+                if (s < WT) bad |= hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne);
+            }
+            tab16[s * 64 + lane] = (uint16_t)v;
+        });
+    } else {
+        // Wave wv writes symbols wv, wv + NW, ...
+        for_lane_bounds<((1 << LOGA) + NW - 1) / NW, kTabGroup>(lt, wv, NW, WT, [&](int s, uint32_t lo, uint32_t hi) {
+            uint32_t entry;
+            if (active) {
+                uint32_t f = hi - lo;
+                if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)) {
+                    bad = true;
+                    f = 1;
                 }
-                tab16[s * 64 + lane] = (uint16_t)v;
+                entry = (lo & 0xFFFFu) | (f << 16);
+            } else {
+                // Idle lanes code with frequency 65535 whatever their symbol:
+                // they never shift a byte out.
+                entry = 0xFFFFu << 16;
             }
-        }
-    } else
-    for (int s = wv; s < WT; s += NW) {
-        uint32_t entry;
-        if (active) {
-            uint32_t lo, hi;
-            cdf_bounds(a.cdf, cdf16, a.wpre, sl.ls, a.C, c, A, W, s, lo, hi);
-            uint32_t f = hi - lo;
-            if (hi <= lo || hi > kProbOne || (s == 0 && lo != 0) || (s == W - 1 && hi != kProbOne)) {
-                bad = true;
-                f = 1;
-            }
-            entry = (lo & 0xFFFFu) | (f << 16);
-        } else {
-            // Idle lanes code with frequency 65535 whatever their symbol: they
-            // never shift a byte out.
-            entry = 0xFFFFu << 16;
-        }
-        tab[s * 64 + lane] = entry;
+            tab[s * 64 + lane] = entry;
+        });
     }
     __syncthreads();
 

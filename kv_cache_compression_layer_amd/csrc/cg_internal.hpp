@@ -313,6 +313,74 @@ __device__ __forceinline__ void cdf_bounds(const int32_t *c32, const uint16_t *c
     }
 }
 
+// One lane's table, as cdf_bounds reads it: the wire table w (u16, W
+// entries, entry W being 2^16) when p is null, else the int32 table p.
+struct LaneTable {
+    const int32_t *p;
+    const uint16_t *w;
+    int W;
+};
+
+__device__ __forceinline__ LaneTable lane_table(const int32_t *c32, const uint16_t *c16, const uint32_t *wpre,
+                                                int slab, int C, int c, int A, int W) {
+    LaneTable t;
+    t.W = W;
+    t.p = c16 ? nullptr : c32 + ((int64_t)slab * C + c) * (A + 1);
+    t.w = c16 ? c16 + (wpre ? (int64_t)wpre[slab] : (int64_t)slab * A) * C + (int64_t)c * W : nullptr;
+    return t;
+}
+
+// Bounds of symbols first + k * step, k < N, with every load issued before
+// the first result is used. Indexes are clamped into the table, so symbols
+// at or past W get meaningless values that callers must not use.
+template <int N>
+__device__ __forceinline__ void lane_bounds_n(const LaneTable &t, int first, int step, uint32_t (&lo)[N],
+                                              uint32_t (&hi)[N]) {
+    const int W = t.W;
+    if (!t.p) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const int s = first + k * step;
+            lo[k] = t.w[min(s, W - 1)];
+            hi[k] = t.w[min(s + 1, W - 1)];
+        }
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            if (first + k * step + 1 >= W) hi[k] = kProbOne;
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const int s = first + k * step;
+            lo[k] = (uint32_t)t.p[min(s, W)];
+            hi[k] = (uint32_t)t.p[min(s + 1, W)];
+        }
+    }
+}
+
+// Calls f(s, lo, hi) for the symbols s = first + k * step < limit, k < N,
+// with cdf_bounds' lo and hi (meaningless for s >= W). The loads go out G
+// symbols at a time, one memory round trip per group instead of one per
+// symbol (which short calls, one wave per SIMD, cannot hide); the compiler
+// barrier after each group keeps the next group's loads behind this one's
+// uses, so no more than G symbols' values are live. limit is wave-uniform.
+constexpr int kTabGroup = 8;  // table symbols per load group
+
+template <int N, int G, class F>
+__device__ __forceinline__ void for_lane_bounds(const LaneTable &t, int first, int step, int limit, F &&f) {
+#pragma unroll
+    for (int k0 = 0; k0 < N; k0 += G) {
+        if (first + k0 * step >= limit) break;
+        uint32_t lo[G], hi[G];
+        lane_bounds_n<G>(t, first + k0 * step, step, lo, hi);
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int s = first + (k0 + k) * step;
+            if (k0 + k < N && s < limit) f(s, lo[k], hi[k]);
+        }
+        __asm__ volatile("" ::: "memory");
+    }
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }

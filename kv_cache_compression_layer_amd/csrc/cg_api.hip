@@ -115,7 +115,7 @@ BlobLayout blob_layout(const Dims &d) {
 
 // Workspace regions (byte offsets; 0 = unused). Region 0 is the WsHeader.
 struct WsLayout {
-    uint64_t counts = 0, tile_sum = 0, tile_mode = 0, tile_off = 0, chunk_total = 0, overflow = 0, staging = 0,
+    uint64_t counts = 0, tile_sum = 0, tile_mode = 0, tile_off = 0, chunk_total = 0, staging = 0,
              sym = 0, scan = 0, wpre = 0;
     uint64_t clear_end = kWsAlign;  // bytes from 0 that must start zeroed
     uint64_t total = kWsAlign;
@@ -139,7 +139,6 @@ WsLayout ws_layout(const Dims &d, int op) {
         w.tile_mode = take((uint64_t)d.tiles);
         w.tile_off = take(8ull * d.tiles);
         w.chunk_total = take(8ull * d.NC * ncalls(d));
-        w.overflow = take(4ull * d.tiles);
         w.staging = take(encode_staging_bytes(d));
         w.scan = take(tile_scan_tmp_bytes(d));
         break;
@@ -159,7 +158,6 @@ WsLayout ws_layout(const Dims &d, int op) {
         w.tile_mode = take((uint64_t)d.tiles);
         w.tile_off = take(8ull * d.tiles);
         w.chunk_total = take(8ull * d.NC * ncalls(d));
-        w.overflow = take(4ull * d.tiles);
         w.staging = take(encode_staging_bytes(d));
         w.sym = take((uint64_t)d.N);
         w.scan = take(tile_scan_tmp_bytes(d));
@@ -246,9 +244,11 @@ void fill_info(const Dims &d, const BlobLayout &b, cg_blob_info *out) {
 // call) into the blob sections `scales`, `wire` and `o`; the workspace is
 // ws_layout(d, CG_OP_TO_BYTES). When one quantiser block covers a whole
 // (K|V, layer) slab it builds the tables itself (no counts to clear, no
-// k_cdf); the encoder reads the u16 tables from the blob.
+// k_cdf); the encoder reads the u16 tables from the blob. status_zeroed:
+// the status word has been zeroed on the stream already (by the blob
+// header's kernel), so only the counts, if used, need clearing.
 int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *scales, uint16_t *wire,
-                const EncodeOut &o, void *ws, const WsLayout &w, hipStream_t s) {
+                const EncodeOut &o, void *ws, const WsLayout &w, hipStream_t s, bool status_zeroed) {
     uint32_t *status = at<uint32_t>(ws, 0);
     uint32_t *counts = at<uint32_t>(ws, w.counts);
     uint32_t *wpre = d.fmt == CG_TABLES_PER_LAYER ? at<uint32_t>(ws, w.wpre) : nullptr;
@@ -257,8 +257,10 @@ int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *sca
     const bool qh = quantize_hist_fits(d, kv, sym);
     const bool fused = qh && quantize_hist_fuses_cdf(d, wire);
     const bool packed = qh && encode_packs(d, mt);
-    int rc = hip_rc(launch_fill_u32(status, 0u, (int64_t)((fused ? kWsAlign : w.clear_end) / 4), s));
-    if (rc) return rc;
+    int rc = CG_OK;
+    if (!(fused && status_zeroed) &&
+        (rc = hip_rc(launch_fill_u32(status, 0u, (int64_t)((fused ? kWsAlign : w.clear_end) / 4), s))))
+        return rc;
     if (wpre && (rc = hip_rc(launch_table_prefix(d, mt, wpre, s)))) return rc;
     if (qh) {
         rc = hip_rc(
@@ -270,7 +272,7 @@ int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *sca
     }
     if (!fused && (rc = hip_rc(launch_cdf(d, mt, counts, nullptr, wire, wpre, status, s)))) return rc;
     EncodeWs ew{at<WsHeader>(ws, 0),         at<uint32_t>(ws, w.tile_sum), at<uint8_t>(ws, w.tile_mode),
-                at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow),
+                at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.chunk_total),
                 at<uint8_t>(ws, w.staging),   at<uint64_t>(ws, w.scan)};
     return hip_rc(launch_encode(d, mt, sym, nullptr, wire, wpre, o, ew, true, packed, s));
 }
@@ -449,7 +451,7 @@ int cg_encode(const cg_desc *desc, const uint8_t *sym, const int32_t *cdf, uint8
     if ((rc = clear_ws(ws, w, s))) return rc;
     EncodeOut o{payload, (uint64_t)cap, lengths, chunk_off, nullptr, nullptr, 0};
     EncodeWs ew{at<WsHeader>(ws, 0),         at<uint32_t>(ws, w.tile_sum), at<uint8_t>(ws, w.tile_mode),
-                at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.chunk_total), at<uint32_t>(ws, w.overflow),
+                at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.chunk_total),
                 at<uint8_t>(ws, w.staging),   at<uint64_t>(ws, w.scan)};
     MaxTable mt;
     make_max_table(desc, d, mt);
@@ -467,8 +469,8 @@ int cg_decode(const cg_desc *desc, const uint8_t *payload, size_t payload_bytes,
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
     make_max_table(desc, d, mt);
-    if ((rc = clear_ws(ws, w, s))) return rc;
     DecodeIn in{payload, (uint64_t)payload_bytes, lengths, chunk_off, cdf, nullptr, nullptr};
+    in.zero_status = true;
     DecodeOut out{sym, nullptr, nullptr};
     return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
                                 at<uint32_t>(ws, 0), s));
@@ -508,7 +510,7 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
     HeaderBytes hb;
     make_header(desc, d, b, hb);
 
-    if ((rc = hip_rc(launch_blob_header(blob, hb, b, d, s)))) return rc;
+    if ((rc = hip_rc(launch_blob_header(blob, hb, b, d, s, 1, 0, at<uint32_t>(ws, 0))))) return rc;
     EncodeOut o{blob + b.off_payload,
                 (uint64_t)cap - b.off_payload,
                 at<uint16_t>(blob, b.off_lengths),
@@ -516,7 +518,8 @@ int cg_to_bytes(const cg_desc *desc, const void *kv, uint8_t *blob, size_t cap,
                 blob_size_dev,
                 blob + 40,
                 b.off_payload};
-    return encode_call(d, mt, kv, at<uint16_t>(blob, b.off_scales), at<uint16_t>(blob, b.off_cdf), o, ws, w, s);
+    return encode_call(d, mt, kv, at<uint16_t>(blob, b.off_scales), at<uint16_t>(blob, b.off_cdf), o, ws, w, s,
+                       true);
 }
 
 int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, void *kv_out,
@@ -532,7 +535,6 @@ int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, vo
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
     make_max_table(desc, d, mt);
-    if ((rc = clear_ws(ws, w, s))) return rc;
     DecodeIn in{blob + b.off_payload,
                 (uint64_t)blob_size - b.off_payload,
                 reinterpret_cast<const uint16_t *>(blob + b.off_lengths),
@@ -540,6 +542,7 @@ int cg_from_bytes(const cg_desc *desc, const uint8_t *blob, size_t blob_size, vo
                 nullptr,
                 reinterpret_cast<const uint16_t *>(blob + b.off_cdf),
                 at<uint32_t>(ws, w.wpre)};
+    in.zero_status = true;
     DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
                   reinterpret_cast<const uint16_t *>(blob + b.off_scales)};
     return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
@@ -562,10 +565,6 @@ int cg_from_bytes_noalloc(const cg_desc *desc, const uint8_t *blob, size_t blob_
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
     make_max_table(desc, d, mt);
-    // The status word is the caller's; nothing else in the scratch needs to
-    // start at zero (tile offsets and scan partials are written before they
-    // are read).
-    if ((rc = hip_rc(launch_fill_u32(status_dev, 0u, 1, s)))) return rc;
     DecodeIn in{blob + b.off_payload,
                 (uint64_t)blob_size - b.off_payload,
                 reinterpret_cast<const uint16_t *>(blob + b.off_lengths),
@@ -573,6 +572,10 @@ int cg_from_bytes_noalloc(const cg_desc *desc, const uint8_t *blob, size_t blob_
                 nullptr,
                 reinterpret_cast<const uint16_t *>(blob + b.off_cdf),
                 at<uint32_t>(ws, w.wpre)};
+    // The status word is the caller's; nothing in the scratch needs to start
+    // at zero (tile offsets and scan partials are written before they are
+    // read).
+    in.zero_status = true;
     DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
                   reinterpret_cast<const uint16_t *>(blob + b.off_scales)};
     return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
@@ -593,7 +596,6 @@ int cg_from_bytes_chunks(const cg_desc *desc, const uint8_t *blob, size_t blob_s
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
     make_max_table(desc, d, mt);
-    if ((rc = clear_ws(ws, w, s))) return rc;
     DecodeIn in{blob + b.off_payload,
                 (uint64_t)blob_size - b.off_payload,
                 reinterpret_cast<const uint16_t *>(blob + b.off_lengths),
@@ -603,6 +605,7 @@ int cg_from_bytes_chunks(const cg_desc *desc, const uint8_t *blob, size_t blob_s
                 at<uint32_t>(ws, w.wpre),
                 chunk_begin,
                 chunk_end};
+    in.zero_status = true;
     DecodeOut out{nullptr, reinterpret_cast<uint16_t *>(kv_out),
                   reinterpret_cast<const uint16_t *>(blob + b.off_scales)};
     return hip_rc(launch_decode(d, mt, in, out, at<uint64_t>(ws, w.tile_off), at<uint64_t>(ws, w.scan),
@@ -635,7 +638,7 @@ int cg_to_bytes_batch(const cg_desc *desc, int32_t batch, const void *kv, uint8_
     make_max_table(desc, d, mt);
     HeaderBytes hb;
     make_header(desc, d, lay, hb);
-    if ((rc = hip_rc(launch_blob_header(blobs, hb, lay, d, s, batch, blob_stride)))) return rc;
+    if ((rc = hip_rc(launch_blob_header(blobs, hb, lay, d, s, batch, blob_stride, at<uint32_t>(ws, 0))))) return rc;
     EncodeOut o{blobs + lay.off_payload,
                 (uint64_t)blob_stride - lay.off_payload,
                 at<uint16_t>(blobs, lay.off_lengths),
@@ -644,7 +647,7 @@ int cg_to_bytes_batch(const cg_desc *desc, int32_t batch, const void *kv, uint8_
                 blobs + 40,
                 lay.off_payload};
     return encode_call(vd, mt, kv, at<uint16_t>(blobs, lay.off_scales), at<uint16_t>(blobs, lay.off_cdf), o, ws, w,
-                       s);
+                       s, true);
 }
 
 int cg_from_bytes_batch(const cg_desc *desc, int32_t batch, const uint8_t *blobs, size_t blob_stride,
@@ -701,7 +704,6 @@ int cg_from_bytes_paged(const cg_desc *desc, const uint8_t *blob, size_t blob_si
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     MaxTable mt;
     make_max_table(desc, d, mt);
-    if ((rc = clear_ws(ws, w, s))) return rc;
     DecodeIn in{blob + b.off_payload,
                 (uint64_t)blob_size - b.off_payload,
                 reinterpret_cast<const uint16_t *>(blob + b.off_lengths),
@@ -709,6 +711,7 @@ int cg_from_bytes_paged(const cg_desc *desc, const uint8_t *blob, size_t blob_si
                 nullptr,
                 reinterpret_cast<const uint16_t *>(blob + b.off_cdf),
                 at<uint32_t>(ws, w.wpre)};
+    in.zero_status = true;
     int log2_bs = 0;
     while ((1 << log2_bs) < block_size) ++log2_bs;
     DecodeOut out{nullptr, nullptr, reinterpret_cast<const uint16_t *>(blob + b.off_scales),

@@ -77,6 +77,7 @@ __device__ __forceinline__ const uint8_t *call_payload(const DecArgs &a, const S
 // that do not fit read global memory.
 constexpr uint32_t kPoolPerWave = 3840;
 constexpr uint32_t kPoolPerWaveSmall = 1536;  // blocks of one or two waves
+constexpr uint32_t kPoolPerWaveLat = 12288;   // the same, in a launch of few waves (LAT)
 constexpr uint32_t kPoolSlack = 528;
 
 // One stream's decoder state. Staged streams read pool bytes at `ptr` (each
@@ -329,7 +330,9 @@ __device__ __forceinline__ uint32_t load_word(const uint8_t *payload, uint64_t p
 // Block of NW waves for one (K|V, layer, 64-channel block): wave w decodes
 // the S chunks (group * NW + w) * S + s, lane = channel. The waves share the
 // channel tables, the dequantisation table and an LDS pool for the payload.
-template <int S, bool FUSED, int LOGA, bool CLAMP, int NW, bool PAGED, bool TAIL>
+// LAT: a launch of few waves (a short call alone), whose time is one
+// stream's latency; see kPoolBytes.
+template <int S, bool FUSED, int LOGA, bool CLAMP, int NW, bool PAGED, bool TAIL, bool LAT>
 __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // Static LDS sized by the template, so every address folds to an immediate.
     // Blocks of one or two waves (short calls) are as many per CU as their
@@ -344,8 +347,12 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // bounds-checked global reads (128 calls of 256 tokens: 2.55 ms with no
     // pool, 2.42 / 2.39 / 2.49 ms with 1024 / 1536 / 2560 bytes per wave).
     // Larger blocks share their tables across more waves and a full pool
-    // pays for itself (measured: 1.79 vs 2.14 ms on 32K tokens).
-    constexpr uint32_t kPoolBytes = NW * (NW <= 2 ? kPoolPerWaveSmall : kPoolPerWave);
+    // pays for itself (measured: 1.79 vs 2.14 ms on 32K tokens). A launch of
+    // few waves (LAT) is not held back by residency at all: with a pool
+    // that holds whole tiles of long streams (a 32-bin slab's 64 streams of a
+    // 256-token chunk take about 5 KB) no renormalisation waits for a
+    // global read.
+    constexpr uint32_t kPoolBytes = NW * (LAT ? kPoolPerWaveLat : NW <= 2 ? kPoolPerWaveSmall : kPoolPerWave);
     __shared__ uint32_t pool_w[(kPoolBytes + kPoolSlack) / 4];  // staged payload
     __shared__ uint32_t need_w[NW];
     const int lane = threadIdx.x & 63;
@@ -423,7 +430,9 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
                 const uint64_t gend = g0 + len[s];
                 const uint64_t ga = g0 & ~3ull, ge = (gend + 3) & ~3ull;
                 uint32_t la = ls - (uint32_t)(g0 - ga);
-#pragma unroll 4
+                // LAT: the copy is on the call's critical path: more loads in flight.
+                constexpr int kCopyUnroll = LAT ? 16 : 4;
+#pragma unroll kCopyUnroll
                 for (uint64_t gw = ga; gw < ge; gw += 4, la += 4) {
                     uint32_t v = load_word(payload, payload_bytes, gw);
                     if (gw < g0) v &= 0xFFFFFFFFu << (8 * (uint32_t)(g0 - gw));
@@ -1041,14 +1050,28 @@ static hipError_t launch_decode2_f(const Dims &d, DecArgs a, hipStream_t s) {
     }
 }
 
+// Waves (over the chip) up to which a launch of one- or two-wave blocks
+// takes the large pool (LAT): eight per CU, whose LDS then still fits.
+constexpr int64_t kLatWaves = 8 * 256;
+
 template <int S, bool FUSED, int LOGA, int NW, bool PAGED, bool TAIL>
 static hipError_t launch_decode_s(const Dims &d, const DecArgs &a, bool clamp, hipStream_t s) {
     const int ngroups = (a.NCr + S * NW - 1) / (S * NW);
     const dim3 grid((unsigned)((int64_t)ngroups * 2 * d.L * d.CB));
-    if (!clamp)  // every table fills the 2^LOGA entries: no clamp
-        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, false, NW, PAGED, TAIL>), grid, dim3(64 * NW), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, true, NW, PAGED, TAIL>), grid, dim3(64 * NW), 0, s, a);
+    constexpr bool kLat = NW <= 2;
+    const bool lat = kLat && (int64_t)grid.x * NW <= kLatWaves;
+#define CG_DEC(CL, LT) hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, CL, NW, PAGED, TAIL, LT>), grid, dim3(64 * NW), 0, s, a)
+    // clamp: some table is narrower than the 2^LOGA entries.
+    if (lat) {
+        if constexpr (kLat) {
+            if (!clamp) CG_DEC(false, true);
+            else CG_DEC(true, true);
+        }
+    } else {
+        if (!clamp) CG_DEC(false, false);
+        else CG_DEC(true, false);
+    }
+#undef CG_DEC
     return hipGetLastError();
 }
 
@@ -1111,7 +1134,10 @@ hipError_t launch_decode(const Dims &d, const MaxTable &mt, const DecodeIn &in, 
     if ((j0 != 0 || j1 != d.NC || out.paged.cache) && d.Lc != d.L) return hipErrorInvalidValue;  // one call only
     TileScan ts{nullptr, in.lengths, tile_off, scan_tmp, nullptr, in.chunk_off, in.payload_bytes, in.call_sizes,
                 in.payload_off, status, d.L, d.C, d.CB, d.NC, call_map(d), j0, d.Lc == d.L ? j1 - j0 : -1};
-    hipError_t e = launch_tile_scan(ts, s);
+    const bool one_block = call_scan_fits(ts) && d.Lc == d.L;
+    hipError_t e;
+    if (in.zero_status && !one_block && (e = launch_fill_u32(status, 0u, 1, s)) != hipSuccess) return e;
+    e = call_scan_fits(ts) ? launch_call_scan(ts, nullptr, s, in.zero_status && one_block) : launch_tile_scan(ts, s);
     if (e != hipSuccess) return e;
     DecArgs a;
     a.cm = call_map(d);

@@ -624,11 +624,14 @@ hipError_t launch_dequantize(const Dims &d, const MaxTable &mt, const uint8_t *s
 
 // ------------------------------------------------------------ blob header
 
-// One block per blob (blob b at blob + b * stride).
+// One block per blob (blob b at blob + b * stride). Block 0 also zeroes the
+// workspace status word when given one: this kernel runs first, so the call
+// needs no launch of its own for that.
 __global__ __launch_bounds__(256) void k_blob_header(uint8_t *__restrict__ blob, uint64_t stride, HeaderBytes h,
                                                      BlobLayout lay, uint64_t end_scales,
                                                      uint64_t end_cdf, uint64_t end_off,
-                                                     uint64_t end_len) {
+                                                     uint64_t end_len, uint32_t *__restrict__ status) {
+    if (status && blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
     blob += (uint64_t)blockIdx.x * stride;
     for (uint32_t i = threadIdx.x; i < h.n; i += blockDim.x) blob[i] = h.b[i];
     // Zero the gaps between the end of each section and the next one.
@@ -639,13 +642,13 @@ __global__ __launch_bounds__(256) void k_blob_header(uint8_t *__restrict__ blob,
 }
 
 hipError_t launch_blob_header(uint8_t *blob, const HeaderBytes &h, const BlobLayout &lay,
-                              const Dims &d, hipStream_t s, int nblobs, uint64_t stride) {
+                              const Dims &d, hipStream_t s, int nblobs, uint64_t stride, uint32_t *status) {
     const uint64_t end_scales = lay.off_scales + 4ull * d.L * d.T;
     const uint64_t end_cdf = lay.off_cdf + 2ull * d.C * (uint64_t)d.tab_entries;
     const uint64_t end_off = lay.off_chunk_off + 8ull * (d.NC + 1);
     const uint64_t end_len = lay.off_lengths + 4ull * d.NC * d.L * d.C;
     hipLaunchKernelGGL(k_blob_header, dim3((unsigned)nblobs), dim3(256), 0, s, blob, stride, h, lay, end_scales,
-                       end_cdf, end_off, end_len);
+                       end_cdf, end_off, end_len, status);
     return hipGetLastError();
 }
 

@@ -27,18 +27,17 @@
 // in global memory. At the end the wave gathers the tile's streams in
 // stream order into the slot, contiguously, and writes the stream lengths
 // and the tile's byte total. A stream longer than the slot (256 bytes)
-// marks the tile for k_fixup.
+// marks the tile as an overflow tile.
 //
-// launch_tile_scan + k_chunk_scan: exclusive scan of the tile totals in
-// stream order (per chunk, then over the chunk totals) -> tile offsets, chunk
-// offsets and the payload size.
+// launch_call_scan, or launch_tile_scan + k_chunk_scan: exclusive scan of
+// the tile totals in stream order (per chunk, then over the chunk totals)
+// -> tile offsets, chunk offsets and the payload size.
 //
 // k_compact: one wave per tile copies the gathered tile to its offset (a
-// tile too large for the LDS gather is gathered here from the slot's rows).
-//
-// k_fixup: re-encodes every stream of a marked tile straight to its final
+// tile too large for the LDS gather is gathered here from the slot's rows),
+// and re-encodes every stream of an overflow tile straight to its final
 // offset with a byte-at-a-time coder that holds back the last byte and the
-// run of 0xFF after it until no carry can reach them.
+// run of 0xFF after it until no carry can reach them (fixup_tile).
 #include "cg_internal.hpp"
 
 namespace cg {
@@ -48,7 +47,7 @@ constexpr int kRing = 16;         // symbol prefetch depth
 
 // What k_encode left in a tile's staging slot: the tile's bytes in stream
 // order at slot bytes [0, total) (gathered), each stream's bytes in slot rows
-// [row][lane] (rows), or a stream too long for the slot, re-coded by k_fixup
+// [row][lane] (rows), or a stream too long for the slot, re-coded by fixup_tile
 // (overflow).
 constexpr uint8_t kTileGathered = 0, kTileRows = 1, kTileOverflow = 2;
 
@@ -135,7 +134,6 @@ struct EncArgs {
     uint8_t *tile_mode;        // [tiles] kTileGathered / kTileRows / kTileOverflow
     uint16_t *lengths;         // [NC, 2L, C]
     WsHeader *hdr;
-    uint32_t *overflow_list;   // [tiles]
     int L, T, C, A, NC, CB;
     MaxTable mt;               // table width of each (K|V, layer)
     CallMap cm;                // calls of a batch (tables and lengths per call)
@@ -161,7 +159,7 @@ __device__ __forceinline__ int64_t tile_index(int j, int slab, int cb, int L, in
 // is a spare that takes the LDS writes of rows past R); bytes past row R also
 // go to the tile's staging slot in global memory, row pos - 1, through a
 // buffer whose range is the slot (bytes past the slot are dropped; such a
-// stream is re-coded by k_fixup).
+// stream is re-coded by fixup_tile).
 // The coder tracks the LDS address of its next row, `la`, rather than the row
 // number (row = (la - lrow0) / kRowPitch), so a byte costs one min (clamp to
 // the spare row) and one compare (spill test) besides the write.
@@ -555,7 +553,6 @@ __global__ __launch_bounds__(64 * NW) void k_encode(EncArgs a) {
             a.tile_sum[tile] = total;
             a.tile_mode[tile] = gathered ? kTileGathered : ovf ? kTileOverflow : kTileRows;
         }
-        if (ovf && lane == 0) a.overflow_list[atomicAdd(&a.hdr->overflow_count, 1u)] = (uint32_t)tile;
     }
     if (__ballot((active && (qmax > amax || bad))) && lane == 0) atomicOr(&a.hdr->status, kStCorrupt);
 }
@@ -630,11 +627,62 @@ struct CompactArgs {
     int64_t tiles;
     int L, C, CB;
     CallMap cm;
+    // What the fix-up coder re-reads for an overflow tile.
+    const uint8_t *sym;
+    const int32_t *cdf;
+    const uint16_t *cdf16;
+    const uint32_t *wpre;
+    int T, A;
+    bool packed;  // symbols in the quantiser's packed layout (PK 1 or 2 by slab)
+    MaxTable mt;
 };
+
+// Fix-up of a tile with a stream longer than its staging slot: lane = stream
+// re-encodes its symbols with the byte-at-a-time coder straight to the
+// stream's final offset (base = the tile's).
+__device__ void fixup_tile(const CompactArgs &a, int j, int slab, int cb, const SlabLoc &sl, uint64_t base,
+                           int lane) {
+    const int c = cb * 64 + lane;
+    const bool active = c < a.C;
+    const int n = min(kChunk, a.T - j * kChunk);
+    const uint16_t *lengths = call_sec(a.lengths, a.cm, sl.b) + ((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C;
+    const uint32_t len = active ? lengths[c] : 0u;
+    const uint32_t incl = wave_incl_scan_u32(len, lane);
+    if (!active) return;
+    const int W = layer_w(a.mt, sl.kv, sl.l);
+    const bool nib = 2 * layer_m(a.mt, sl.kv, sl.l) + 1 <= 16;
+    const uint16_t *cdf16 = call_sec(a.cdf16, a.cm, sl.b);
+    const uint8_t *sp = a.sym + ((int64_t)slab * a.T + (int64_t)j * kChunk) * a.C + c;
+    const uint8_t *slab_sym = a.sym + (int64_t)slab * a.T * a.C;
+    RcEncHold enc;
+    enc.init();
+    GlobalSink sink{call_sec(a.payload, a.cm, sl.b), base + incl - len, a.cap, 0u, false};
+    for (int t = 0; t < n; ++t) {
+        uint32_t q;
+        if (!a.packed) {
+            q = sp[(int64_t)t * a.C];
+        } else {
+            const int tt = j * kChunk + t;
+            if (nib) {
+                const uint8_t b = slab_sym[((int64_t)(tt >> 3) * a.C + c) * 4 + (tt & 3)];
+                q = (tt & 4) ? b >> 4 : b & 0xFu;
+            } else {
+                q = slab_sym[((int64_t)(tt >> 2) * a.C + c) * 4 + (tt & 3)];
+            }
+        }
+        const uint32_t s = min(q, (uint32_t)W - 1);
+        uint32_t lo, hi;
+        cdf_bounds(a.cdf, cdf16, a.wpre, sl.ls, a.C, c, a.A, W, (int)s, lo, hi);
+        const uint32_t f = hi > lo ? hi - lo : 1u;
+        enc.encode(lo & 0xFFFFu, f, sink);
+    }
+    enc.flush(sink);
+    if (sink.overflow) atomicOr(a.status, kStCapacity);
+}
 
 // One wave per tile. Every load a tile's copy depends on (its mode, byte
 // count and offsets) is issued at once, so the copy waits for one round
-// trip.
+// trip. Overflow tiles are re-encoded here by fixup_tile.
 __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
     const int lane = threadIdx.x;
     const int64_t tile = blockIdx.x;
@@ -645,7 +693,10 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
     const uint32_t mode = a.tile_mode[tile];
     const uint32_t total = a.tile_sum[tile];
     const uint64_t base = call_sec(a.chunk_off, a.cm, sl.b)[j] + a.tile_off[tile];
-    if (mode == kTileOverflow) return;  // k_fixup writes this tile
+    if (mode == kTileOverflow) {
+        fixup_tile(a, j, slab, cb, sl, base, lane);
+        return;
+    }
     uint8_t *payload = call_sec(a.payload, a.cm, sl.b);
     const bool gathered = mode == kTileGathered;
     const uint8_t *src = a.staging + tile * (kStageBytes * 64);
@@ -734,76 +785,6 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
     if (__ballot(over) && lane == 0) atomicOr(a.status, kStCapacity);
 }
 
-// ----------------------------------------------------------------- fix-up
-
-struct FixupArgs {
-    const uint8_t *sym;
-    const int32_t *cdf;
-    const uint16_t *cdf16;
-    const uint32_t *wpre;
-    const uint16_t *lengths;
-    const uint64_t *tile_off;   // relative to the chunk
-    const uint64_t *chunk_off;
-    const uint32_t *overflow_list;
-    WsHeader *hdr;
-    uint8_t *payload;
-    uint64_t cap;
-    int L, T, C, A, CB;
-    MaxTable mt;
-    CallMap cm;
-    bool packed;  // symbols in the quantiser's packed layout (PK 1 or 2 by slab)
-};
-
-__global__ __launch_bounds__(64) void k_fixup(FixupArgs a) {
-    const int lane = threadIdx.x;
-    const uint32_t count = a.hdr->overflow_count;
-    for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
-        const int64_t tile = a.overflow_list[i];
-        const int cb = (int)(tile % a.CB);
-        const int64_t js = tile / a.CB;
-        const int slab = (int)(js % (2 * a.L));
-        const int j = (int)(js / (2 * a.L));
-        const int c = cb * 64 + lane;
-        const bool active = c < a.C;
-        const int n = min(kChunk, a.T - j * kChunk);
-        const SlabLoc sl = slab_loc(a.cm, slab);
-        const uint16_t *lengths = call_sec(a.lengths, a.cm, sl.b) + ((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C;
-        const uint32_t len = active ? lengths[c] : 0u;
-        const uint32_t incl = wave_incl_scan_u32(len, lane);
-        if (!active) continue;
-        const int W = layer_w(a.mt, sl.kv, sl.l);
-        const bool nib = 2 * layer_m(a.mt, sl.kv, sl.l) + 1 <= 16;
-        const uint16_t *cdf16 = call_sec(a.cdf16, a.cm, sl.b);
-        const uint8_t *sp = a.sym + ((int64_t)slab * a.T + (int64_t)j * kChunk) * a.C + c;
-        const uint8_t *slab_sym = a.sym + (int64_t)slab * a.T * a.C;
-        RcEncHold enc;
-        enc.init();
-        GlobalSink sink{call_sec(a.payload, a.cm, sl.b),
-                        call_sec(a.chunk_off, a.cm, sl.b)[j] + a.tile_off[tile] + incl - len, a.cap, 0u, false};
-        for (int t = 0; t < n; ++t) {
-            uint32_t q;
-            if (!a.packed) {
-                q = sp[(int64_t)t * a.C];
-            } else {
-                const int tt = j * kChunk + t;
-                if (nib) {
-                    const uint8_t b = slab_sym[((int64_t)(tt >> 3) * a.C + c) * 4 + (tt & 3)];
-                    q = (tt & 4) ? b >> 4 : b & 0xFu;
-                } else {
-                    q = slab_sym[((int64_t)(tt >> 2) * a.C + c) * 4 + (tt & 3)];
-                }
-            }
-            const uint32_t s = min(q, (uint32_t)W - 1);
-            uint32_t lo, hi;
-            cdf_bounds(a.cdf, cdf16, a.wpre, sl.ls, a.C, c, a.A, W, (int)s, lo, hi);
-            const uint32_t f = hi > lo ? hi - lo : 1u;
-            enc.encode(lo & 0xFFFFu, f, sink);
-        }
-        enc.flush(sink);
-        if (sink.overflow) atomicOr(&a.hdr->status, kStCapacity);
-    }
-}
-
 // ---------------------------------------------------------------- launch
 
 size_t encode_staging_bytes(const Dims &d) { return (size_t)d.tiles * kStageBytes * 64; }
@@ -857,7 +838,6 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     a.tile_mode = w.tile_mode;
     a.lengths = o.lengths;
     a.hdr = w.hdr;
-    a.overflow_list = w.overflow_list;
     a.L = d.L;
     a.T = d.T;
     a.C = d.C;
@@ -916,20 +896,30 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
 
     TileScan ts{w.tile_sum, nullptr, w.tile_off, w.scan_tmp, w.chunk_total, nullptr, 0, nullptr, 0,
                 &w.hdr->status, d.L, d.C, d.CB, d.NC, call_map(d)};
-    if ((e = launch_tile_scan(ts, s)) != hipSuccess) return e;
-    ChunkScanArgs sa;
-    sa.chunk_total = w.chunk_total;
-    sa.chunk_off = o.chunk_off;
-    sa.size_dev = o.size_dev;
-    sa.header_size = o.header_size;
-    sa.hdr = w.hdr;
-    sa.payload_base = o.payload_base;
-    sa.cap = o.cap;
-    sa.NC = d.NC;
-    sa.B = ncalls(d);
-    sa.cm = call_map(d);
-    hipLaunchKernelGGL(k_chunk_scan, dim3((unsigned)sa.B), dim3(1024), 0, s, sa);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (call_scan_fits(ts)) {
+        ChunkOut co;
+        co.chunk_off = o.chunk_off;
+        co.size_dev = o.size_dev;
+        co.header_size = o.header_size;
+        co.payload_base = o.payload_base;
+        co.cap = o.cap;
+        if ((e = launch_call_scan(ts, &co, s)) != hipSuccess) return e;
+    } else {
+        if ((e = launch_tile_scan(ts, s)) != hipSuccess) return e;
+        ChunkScanArgs sa;
+        sa.chunk_total = w.chunk_total;
+        sa.chunk_off = o.chunk_off;
+        sa.size_dev = o.size_dev;
+        sa.header_size = o.header_size;
+        sa.hdr = w.hdr;
+        sa.payload_base = o.payload_base;
+        sa.cap = o.cap;
+        sa.NC = d.NC;
+        sa.B = ncalls(d);
+        sa.cm = call_map(d);
+        hipLaunchKernelGGL(k_chunk_scan, dim3((unsigned)sa.B), dim3(1024), 0, s, sa);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
 
     CompactArgs ca;
     ca.staging = w.staging;
@@ -946,30 +936,15 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     ca.C = d.C;
     ca.CB = d.CB;
     ca.cm = call_map(d);
+    ca.sym = sym;
+    ca.cdf = cdf;
+    ca.cdf16 = cdf16;
+    ca.wpre = wpre;
+    ca.T = d.T;
+    ca.A = d.A;
+    ca.packed = packed;
+    ca.mt = mt;
     hipLaunchKernelGGL(k_compact, dim3((unsigned)d.tiles), dim3(64), 0, s, ca);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-
-    FixupArgs fa;
-    fa.sym = sym;
-    fa.cdf = cdf;
-    fa.cdf16 = cdf16;
-    fa.wpre = wpre;
-    fa.mt = mt;
-    fa.lengths = o.lengths;
-    fa.tile_off = w.tile_off;
-    fa.chunk_off = o.chunk_off;
-    fa.overflow_list = w.overflow_list;
-    fa.hdr = w.hdr;
-    fa.payload = o.payload;
-    fa.cap = o.cap;
-    fa.L = d.L;
-    fa.T = d.T;
-    fa.C = d.C;
-    fa.A = d.A;
-    fa.CB = d.CB;
-    fa.cm = call_map(d);
-    fa.packed = packed;
-    hipLaunchKernelGGL(k_fixup, dim3(256), dim3(64), 0, s, fa);
     return hipGetLastError();
 }
 

@@ -96,11 +96,7 @@ inline int ncalls(const Dims &d) { return d.L / d.Lc; }
 // Header of every workspace (first 256 bytes).
 struct WsHeader {
     uint32_t status;
-    uint32_t reserved0;
-    uint32_t overflow_count;   // tiles whose streams did not fit in LDS
-    uint32_t pad0;
-    uint64_t reserved1;
-    uint32_t pad[58];
+    uint32_t pad[63];
 };
 static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
 
@@ -170,6 +166,21 @@ struct TileScan {
 size_t tile_scan_tmp_bytes(const Dims &d);
 hipError_t launch_tile_scan(const TileScan &a, hipStream_t s);
 
+// The encoder's chunk offsets (call 0's [NC+1]), sizes ([B] or null), the
+// header's size field (call 0's or null), the payload's offset in the blob
+// and each call's payload capacity.
+struct ChunkOut {
+    uint64_t *chunk_off = nullptr;
+    uint64_t *size_dev = nullptr;
+    uint8_t *header_size = nullptr;
+    uint64_t payload_base = 0, cap = 0;
+};
+// One launch for the tile scan of calls of a few chunks (and, with co, the
+// encoder's chunk offsets and sizes); call_scan_fits says which calls.
+// zero_status (one call only): the kernel zeroes the status word first.
+bool call_scan_fits(const TileScan &a);
+hipError_t launch_call_scan(const TileScan &a, const ChunkOut *co, hipStream_t s, bool zero_status = false);
+
 // Blob sections of call 0 (call b's lie b * stride bytes further, see
 // CallMap); cap is each call's payload capacity.
 struct EncodeOut {
@@ -188,7 +199,6 @@ struct EncodeWs {
     uint8_t *tile_mode;       // [tiles] how the tile's bytes were left in its staging slot
     uint64_t *tile_off;       // [tiles] offset of each tile within its chunk
     uint64_t *chunk_total;    // [NC] bytes of each chunk
-    uint32_t *overflow_list;  // [tiles] tiles with a stream beyond the LDS stage
     uint8_t *staging;         // encode_staging_bytes(d)
     uint64_t *scan_tmp;       // tile_scan_tmp_bytes(d)
 };
@@ -223,6 +233,9 @@ struct DecodeIn {
     // Batches: each call's payload bound from its blob size (see TileScan).
     const uint64_t *call_sizes = nullptr;
     uint64_t payload_off = 0;
+    // The status word still has to be zeroed: launch_decode does it before
+    // any kernel can set a bit (in the scan kernel when that is one block).
+    bool zero_status = false;
 };
 
 // Paged output of the fused decoder: element (l, kv, t, c) goes to
@@ -254,8 +267,10 @@ struct HeaderBytes {
     uint8_t b[2048 + 64];
     uint32_t n;
 };
+// With status, also zeroes that workspace status word.
 hipError_t launch_blob_header(uint8_t *blob, const HeaderBytes &h, const BlobLayout &lay,
-                              const Dims &d, hipStream_t s, int nblobs = 1, uint64_t stride = 0);
+                              const Dims &d, hipStream_t s, int nblobs = 1, uint64_t stride = 0,
+                              uint32_t *status = nullptr);
 
 // Batch decode: checks each call's blob header (all but the size field)
 // against hdr and its size against the header and the stride; a call that
@@ -369,15 +384,16 @@ template <int N, int G, class F>
 __device__ __forceinline__ void for_lane_bounds(const LaneTable &t, int first, int step, int limit, F &&f) {
 #pragma unroll
     for (int k0 = 0; k0 < N; k0 += G) {
-        if (first + k0 * step >= limit) break;
-        uint32_t lo[G], hi[G];
-        lane_bounds_n<G>(t, first + k0 * step, step, lo, hi);
+        if (first + k0 * step < limit) {
+            uint32_t lo[G], hi[G];
+            lane_bounds_n<G>(t, first + k0 * step, step, lo, hi);
 #pragma unroll
-        for (int k = 0; k < G; ++k) {
-            const int s = first + (k0 + k) * step;
-            if (k0 + k < N && s < limit) f(s, lo[k], hi[k]);
+            for (int k = 0; k < G; ++k) {
+                const int s = first + (k0 + k) * step;
+                if (k0 + k < N && s < limit) f(s, lo[k], hi[k]);
+            }
+            __asm__ volatile("" ::: "memory");
         }
-        __asm__ volatile("" ::: "memory");
     }
 }
 

@@ -24,6 +24,13 @@
 // A range of chunks [j0, j0 + NCr) of one call can be scanned alone (the
 // decoder of a blob whose payload has arrived up to some chunk): only those
 // chunks' tiles are written and only those chunks are checked.
+//
+// Calls of at most 1024 tiles per chunk and few chunks (the 256-token
+// calls LMCache makes, alone or batched: one chunk; the encoder takes up to
+// four) use k_call_scan instead: one launch, one block per call, which does
+// the three passes (and the encoder's chunk pass) in order within the block.
+// Each of those kernels costs a few microseconds however little it does, a
+// large share of a short call.
 #include "cg_internal.hpp"
 
 namespace cg {
@@ -51,6 +58,43 @@ __device__ __forceinline__ uint64_t call_payload_bytes(const TileScan &a, int b)
     return sz > a.payload_off ? sz - a.payload_off : 0ull;
 }
 
+// Byte count of tile tl of segment js: given (tile_sum), or the sum of its
+// 64 stream lengths.
+__device__ __forceinline__ uint32_t tile_bytes(const TileScan &a, int64_t js, int64_t tps, int64_t tl) {
+    if (a.tile_sum) return a.tile_sum[js * tps + tl];
+    int j, b;
+    seg_call(a, js, j, b);
+    const int64_t ls = tl / a.CB;
+    const int cb = (int)(tl - ls * a.CB);
+    const uint16_t *lb = call_sec(a.lengths, a.cm, b);
+    const uint16_t *p = lb + ((int64_t)j * 2 * a.cm.Lc + ls) * a.C + cb * 64;
+    const int nch = min(64, a.C - cb * 64);
+    uint32_t v = 0;
+    if (nch == 64 && a.C % 8 == 0 && ((uintptr_t)lb & 15) == 0) {
+        // A full tile's 64 lengths are 128 aligned bytes: eight 16-byte
+        // loads, each word holding two lengths.
+        const uint4 *p4 = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 w = p4[i];
+            v += (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) + (w.z & 0xFFFFu) + (w.z >> 16) +
+                 (w.w & 0xFFFFu) + (w.w >> 16);
+        }
+    } else {
+        for (int i = 0; i < nch; ++i) v += p[i];
+    }
+    return v;
+}
+
+// Checks chunk j of call b (decoder): its stored offsets against the bytes
+// of its tiles and the call's payload.
+__device__ __forceinline__ void check_chunk(const TileScan &a, int j, int b, uint64_t bytes) {
+    const uint64_t *co = call_sec(a.chunk_off, a.cm, b);
+    const uint64_t c0 = co[j], c1 = co[j + 1];
+    const bool bad = (j == 0 && c0 != 0) || c1 < c0 || c1 - c0 != bytes || c1 > call_payload_bytes(a, b);
+    if (bad) atomicOr(a.status, kStCorrupt);
+}
+
 }  // namespace
 
 size_t tile_scan_tmp_bytes(const Dims &d) {
@@ -64,33 +108,7 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_local(TileScan a, int64_t t
     const int64_t bid = blockIdx.x;
     const int64_t jr = bid / nbps, blk = bid - jr * nbps, js = a.j0 + jr;
     const int64_t tl = blk * kScanBlock + tid;
-    uint32_t v = 0;
-    if (tl < tps) {
-        if (a.tile_sum) {
-            v = a.tile_sum[js * tps + tl];
-        } else {
-            int j, b;
-            seg_call(a, js, j, b);
-            const int64_t ls = tl / a.CB;
-            const int cb = (int)(tl - ls * a.CB);
-            const uint16_t *lb = call_sec(a.lengths, a.cm, b);
-            const uint16_t *p = lb + ((int64_t)j * 2 * a.cm.Lc + ls) * a.C + cb * 64;
-            const int nch = min(64, a.C - cb * 64);
-            if (nch == 64 && a.C % 8 == 0 && ((uintptr_t)lb & 15) == 0) {
-                // A full tile's 64 lengths are 128 aligned bytes: eight
-                // 16-byte loads, each word holding two lengths.
-                const uint4 *p4 = reinterpret_cast<const uint4 *>(p);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint4 w = p4[i];
-                    v += (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) + (w.z & 0xFFFFu) +
-                         (w.z >> 16) + (w.w & 0xFFFFu) + (w.w >> 16);
-                }
-            } else {
-                for (int i = 0; i < nch; ++i) v += p[i];
-            }
-        }
-    }
+    const uint32_t v = tl < tps ? tile_bytes(a, js, tps, tl) : 0u;
     const uint32_t incl = wave_incl_scan_u32(v, lane);
     if (lane == 63) wsum[wv] = incl;
     __syncthreads();
@@ -137,11 +155,7 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_blocks(TileScan a, int64_t 
         if (a.chunk_off) {
             int j, b;
             seg_call(a, js, j, b);
-            const uint64_t *co = call_sec(a.chunk_off, a.cm, b);
-            const uint64_t c0 = co[j], c1 = co[j + 1];
-            const bool bad =
-                (j == 0 && c0 != 0) || c1 < c0 || c1 - c0 != run || c1 > call_payload_bytes(a, b);
-            if (bad) atomicOr(a.status, kStCorrupt);
+            check_chunk(a, j, b, run);
         }
     }
 }
@@ -171,6 +185,108 @@ hipError_t launch_tile_scan(const TileScan &a, hipStream_t s) {
     hipLaunchKernelGGL(k_scan_blocks, dim3((unsigned)nseg), dim3(kScanBlock), 0, s, a, nbps);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_scan_add, dim3(nblk), dim3(kScanBlock), 0, s, a, tps, nbps);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------ one block per call
+
+// Calls of a few chunks, and batches of such calls, scan in one launch
+// instead of three (or four, with the encoder's chunk pass): block b takes
+// call b's chunks in order, kCallScanThreads tiles at a time, loads all of
+// their byte counts up front (one round trip), and carries the chunk
+// offsets from one chunk to the next. The decoder's form adds the stored
+// chunk offset to every tile and checks each chunk, as k_scan_add and
+// k_scan_blocks do; the encoder's form leaves the tile offsets relative to
+// their chunk and writes what k_chunk_scan would: the chunk offsets, the
+// size and the capacity check. Sums within a step fit 32 bits: 1024 tiles
+// of 64 lengths below 2^16.
+constexpr int kCallScanThreads = 1024, kCallScanSteps = 4;
+
+template <bool ENC>
+__global__ __launch_bounds__(kCallScanThreads) void k_call_scan(TileScan a, ChunkOut co, int64_t tps, int parts,
+                                                                int nch, bool zero_status) {
+    __shared__ uint32_t wsum[kCallScanThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // A one-block launch that runs before anything else sets a status bit
+    // zeroes the word itself (thread 0, which alone sets bits here, and by an
+    // atomic, so its later atomicOr is ordered after it).
+    if (zero_status && tid == 0) atomicExch(a.status, 0u);
+    const int b = blockIdx.x;
+    const int B = a.L / a.cm.Lc;
+    const int steps = nch * parts;
+    uint32_t v[kCallScanSteps];
+#pragma unroll
+    for (int i = 0; i < kCallScanSteps; ++i) {
+        v[i] = 0;
+        const int64_t tl = (int64_t)(i % parts) * kCallScanThreads + tid;
+        if (i < steps && tl < tps) v[i] = tile_bytes(a, (int64_t)(a.j0 + i / parts) * B + b, tps, tl);
+    }
+    uint64_t run = 0, chunk = 0;  // bytes of the call's earlier chunks; of this chunk's earlier steps
+#pragma unroll
+    for (int i = 0; i < kCallScanSteps; ++i) {
+        if (i >= steps) break;
+        const int j = a.j0 + i / parts, part = i % parts;
+        const int64_t tl = (int64_t)part * kCallScanThreads + tid;
+        const uint32_t incl = wave_incl_scan_u32(v[i], lane);
+        if (lane == 63) wsum[wv] = incl;
+        __syncthreads();
+        uint32_t before = 0, total = 0;
+#pragma unroll
+        for (int k = 0; k < kCallScanThreads / 64; ++k) {
+            if (k < wv) before += wsum[k];
+            total += wsum[k];
+        }
+        __syncthreads();
+        if (part == 0) chunk = 0;
+        if (tl < tps) {
+            uint64_t off = chunk + before + incl - v[i];
+            if (!ENC) off += call_sec(a.chunk_off, a.cm, b)[j];
+            a.tile_off[((int64_t)j * B + b) * tps + tl] = off;
+        }
+        chunk += total;
+        if (part == parts - 1) {
+            if (tid == 0) {
+                if (ENC) call_sec(co.chunk_off, a.cm, b)[j] = run;
+                else check_chunk(a, j, b, chunk);
+            }
+            run += chunk;
+        }
+    }
+    if (ENC && tid == 0) {
+        call_sec(co.chunk_off, a.cm, b)[a.j0 + nch] = run;
+        if (run > co.cap) atomicOr(a.status, kStCapacity);
+        const uint64_t size = co.payload_base + run;
+        if (co.size_dev) co.size_dev[b] = size;
+        if (co.header_size) {
+            uint8_t *h = call_sec(co.header_size, a.cm, b);
+            for (int i = 0; i < 8; ++i) h[i] = (uint8_t)(size >> (8 * i));
+        }
+    }
+}
+
+// The decoder's form reads each tile's 64 lengths (128 bytes), so it takes
+// one step: a block summing more is slower than the three passes spread
+// over the chip (3 x 1024 tiles: +5 us on a 768-token call).
+bool call_scan_fits(const TileScan &a) {
+    const int64_t parts = (tiles_per_seg(a) + kCallScanThreads - 1) / kCallScanThreads;
+    const int64_t nch = a.NCr < 0 ? a.NC : a.NCr;
+    return nch * parts <= (a.tile_sum ? kCallScanSteps : 1);
+}
+
+hipError_t launch_call_scan(const TileScan &a, const ChunkOut *co, hipStream_t s, bool zero_status) {
+    if (!call_scan_fits(a) || (a.NCr >= 0 && a.cm.Lc != a.L)) return hipErrorInvalidValue;
+    if (zero_status && a.cm.Lc != a.L) return hipErrorInvalidValue;  // one block only
+    if (co && (a.j0 != 0 || a.NCr >= 0)) return hipErrorInvalidValue;  // the encoder scans every chunk
+    const int64_t tps = tiles_per_seg(a);
+    const int parts = (int)((tps + kCallScanThreads - 1) / kCallScanThreads);
+    const int nch = a.NCr < 0 ? a.NC : a.NCr;
+    const unsigned B = (unsigned)(a.L / a.cm.Lc);
+    if (co)
+        hipLaunchKernelGGL(k_call_scan<true>, dim3(B), dim3(kCallScanThreads), 0, s, a, *co, tps, parts, nch,
+                           zero_status);
+    else
+        hipLaunchKernelGGL(k_call_scan<false>, dim3(B), dim3(kCallScanThreads), 0, s, a, ChunkOut{}, tps, parts, nch,
+                           zero_status);
     return hipGetLastError();
 }
 

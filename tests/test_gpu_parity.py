@@ -203,6 +203,43 @@ def test_corrupt_blob_is_reported():
         cgb.from_bytes(to_dev(np.frombuffer(bytes(blob2), np.uint8).copy()))
 
 
+@pytest.mark.parametrize("T", [200, 600])
+def test_status_is_cleared_by_the_next_call(T):
+    """A workspace whose status word reports a fault is zeroed by the next
+    call before any kernel can set a bit: a corrupt blob and then the good
+    one, decoded with one workspace; an encode into a blob too small for the
+    payload and then one into a blob large enough. With 200 tokens (one
+    chunk) the tile scan runs as one block that zeroes the word itself (the
+    encoder's first kernel, the header's, zeroes it in every call); with 600
+    tokens (three chunks) the decoder's scan takes three passes after a fill."""
+    import torch
+
+    kv = generate_kv(2, T, 1, 64, seed=21)
+    want = oracle.to_bytes(kv, *oracle.default_bins(2))
+    desc = cgb.Desc.for_kv(kv.shape)
+    out = torch.empty(kv.shape, dtype=torch.int16, device="cuda:0")
+    ws = cgb.alloc_workspace(desc, cgb.CG_OP_FROM_BYTES)
+    bad = bytearray(want)
+    info, _, _ = cgb.cg_blob_peek(bytes(bad[:52]))
+    off = info["off_lengths"] + 2 * 5
+    bad[off] = (bad[off] + 1) & 0xFF
+    cgb.cg_from_bytes(desc, to_dev(np.frombuffer(bytes(bad), np.uint8).copy()), len(bad), out, ws)
+    assert cgb.cg_read_status(ws) == cgb.CG_E_CORRUPT
+    cgb.cg_from_bytes(desc, to_dev(np.frombuffer(want, np.uint8).copy()), len(want), out, ws)
+    assert cgb.cg_read_status(ws) == cgb.CG_OK
+    assert_bf16_equal(to_np(out, np.uint16), oracle.from_bytes(want))
+
+    wse = cgb.alloc_workspace(desc, cgb.CG_OP_TO_BYTES)
+    size = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    small = torch.zeros(info["off_payload"] + 16, dtype=torch.uint8, device="cuda:0")
+    cgb.cg_to_bytes(desc, to_dev(kv), small, size, wse)
+    assert cgb.cg_read_status(wse) == cgb.CG_E_CAPACITY
+    blob = torch.zeros(cgb.cg_blob_bound(desc), dtype=torch.uint8, device="cuda:0")
+    cgb.cg_to_bytes(desc, to_dev(kv), blob, size, wse)
+    assert cgb.cg_read_status(wse) == cgb.CG_OK
+    assert to_np(blob[: int(size.item())]).tobytes() == want
+
+
 def test_bad_arguments_launch_nothing():
     import torch
 

@@ -683,6 +683,11 @@ __device__ void fixup_tile(const CompactArgs &a, int j, int slab, int cb, const 
 // One wave per tile. Every load a tile's copy depends on (its mode, byte
 // count and offsets) is issued at once, so the copy waits for one round
 // trip. Overflow tiles are re-encoded here by fixup_tile.
+// LDS_ROWS: rows tiles are put in order in LDS (16 KiB per block) and leave
+// as dwords; otherwise a byte at a time. The LDS costs residency, which a
+// large grid needs (32K tokens: 2.31 vs 2.50 ms per call) and a small one
+// does not (256 tokens: 120 vs 131 us).
+template <bool LDS_ROWS>
 __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
     const int lane = threadIdx.x;
     const int64_t tile = blockIdx.x;
@@ -759,10 +764,67 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
         }
         for (; p < total; p += 64)
             if (base + p < a.cap) payload[base + p] = src[p];
+    } else if (LDS_ROWS && !over && ((uintptr_t)payload & 3u) == 0) {
+        // [byte][lane] rows: byte i of stream k at slot byte i * 64 + k (no
+        // stream is longer than the slot's 256 rows, or the tile would be an
+        // overflow tile). Lane l reads the dwords of rows l / 16 + 4m, each
+        // holding byte i of streams 4q .. 4q + 3 (q = l % 16), all of a group
+        // of rows in one round trip, and puts every byte at its place in the
+        // tile in LDS, offset by base % 4 so that the payload's aligned
+        // dwords are aligned LDS words; the wave then stores those dwords
+        // (and the bytes at either end) as the gathered copy does.
+        __shared__ uint32_t gat_w[LDS_ROWS ? (kStageBytes * 64 + 8) / 4 : 1];
+        uint8_t *gat = reinterpret_cast<uint8_t *>(gat_w);
+        const int c = cb * 64 + lane;
+        const uint16_t *lengths = call_sec(a.lengths, a.cm, sl.b) + ((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C;
+        const uint32_t len = c < a.C ? lengths[c] : 0u;
+        const uint32_t excl = wave_incl_scan_u32(len, lane) - len;
+        const uint32_t rows = wave_max_u32(len);
+        const uint32_t h = (uint32_t)(base & 3u);
+        const int q = lane & 15, r0 = lane >> 4;
+        uint32_t qlen[4], qoff[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            qlen[cc] = (uint32_t)__shfl((int)len, 4 * q + cc, 64);
+            qoff[cc] = (uint32_t)__shfl((int)excl, 4 * q + cc, 64) + h;
+        }
+        // Rows are read through a buffer over the slot; past its 256 rows a
+        // read returns 0 (and its bytes are not used).
+        const __amdgpu_buffer_rsrc_t srsrc = make_rsrc(src, kStageBytes * 64);
+        constexpr int U = 16;  // rows per lane per round trip (64 rows per wave)
+        for (uint32_t i0 = 0; i0 < rows; i0 += 4 * U) {
+            uint32_t v[U];
+            const int voff = (int)(((i0 + (uint32_t)r0) * 16 + (uint32_t)q) * 4);
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, voff + 256 * u, 0, 0);
+            const uint32_t ir = i0 + (uint32_t)r0;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                uint8_t *g = gat + qoff[cc] + ir;  // row u's byte at g[4u]
+                const uint32_t left = qlen[cc] > ir ? qlen[cc] - ir : 0u;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (4u * u < left) g[4 * u] = (uint8_t)(v[u] >> (8 * cc));
+            }
+        }
+        __syncthreads();
+        const uint64_t end = base + total;
+        const uint64_t wa = (base + 3) & ~3ull, we = end & ~3ull;
+        if (wa >= we) {
+            if ((uint32_t)lane < total) payload[base + lane] = gat[h + lane];
+        } else {
+            const uint32_t nhead = (uint32_t)(wa - base), ntail = (uint32_t)(end - we);
+            if ((uint32_t)lane < nhead) payload[base + lane] = gat[h + lane];
+            if ((uint32_t)lane < ntail) payload[we + lane] = gat[h + (uint32_t)(we - base) + lane];
+            uint32_t *d32 = reinterpret_cast<uint32_t *>(payload + wa);
+            const uint32_t nw = (uint32_t)((we - wa) >> 2), w0 = (h + nhead) >> 2;
+            for (uint32_t w = lane; w < nw; w += 64) d32[w] = gat_w[w0 + w];
+        }
     } else {
-        // [byte][lane] rows: output byte p belongs to the last stream k with
-        // excl_k <= p (binary search over the lanes' offsets; the loop is
-        // wave-uniform because the search reads other lanes).
+        // [byte][lane] rows, a byte at a time (capacity overflow, unaligned
+        // payload): output byte p belongs to the last stream k with excl_k <=
+        // p (binary search over the lanes' offsets; the loop is wave-uniform
+        // because the search reads other lanes).
         const int c = cb * 64 + lane;
         const uint16_t *lengths = call_sec(a.lengths, a.cm, sl.b) + ((int64_t)j * 2 * a.cm.Lc + sl.ls) * a.C;
         const uint32_t len = c < a.C ? lengths[c] : 0u;
@@ -788,6 +850,10 @@ __global__ __launch_bounds__(64) void k_compact(CompactArgs a) {
 // ---------------------------------------------------------------- launch
 
 size_t encode_staging_bytes(const Dims &d) { return (size_t)d.tiles * kStageBytes * 64; }
+
+// Grids of compaction blocks up to which rows tiles are ordered in LDS
+// (k_compact's LDS_ROWS): sixteen per CU.
+constexpr int64_t kCompactLdsTiles = 16 * 256;
 
 // Launch shape of k_encode: S chunks per lane, NW waves per block, and
 // whether the call has slabs of at most 16 symbols (small) and others (large).
@@ -944,7 +1010,8 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     ca.A = d.A;
     ca.packed = packed;
     ca.mt = mt;
-    hipLaunchKernelGGL(k_compact, dim3((unsigned)d.tiles), dim3(64), 0, s, ca);
+    if (d.tiles <= kCompactLdsTiles) hipLaunchKernelGGL(k_compact<true>, dim3((unsigned)d.tiles), dim3(64), 0, s, ca);
+    else hipLaunchKernelGGL(k_compact<false>, dim3((unsigned)d.tiles), dim3(64), 0, s, ca);
     return hipGetLastError();
 }
 

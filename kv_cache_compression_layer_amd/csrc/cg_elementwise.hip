@@ -202,8 +202,9 @@ hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv
 // ------------------------------------------------- quantise + histogram
 
 // The to_bytes path quantises and counts in one pass, so the symbols are
-// not read back for the histogram. A block of 8 waves owns a tile of TT
-// rows (tokens) of one (K|V, layer); each wave quantises two rows at a time
+// not read back for the histogram. A block of NT / 64 waves (8, or 16 when
+// the grid has fewer blocks than the chip has CUs) owns a tile of TT rows
+// (tokens) of one (K|V, layer); each wave quantises four rows at a time
 // exactly as k_quantize_vec does. Lane l always holds the same CW*NV channels
 // ((i*64 + l)*CW + e), so the block keeps lane-column counters in LDS,
 // uint32 [symbol][pair][lane] with the counts of channels e and e+1 of a
@@ -223,8 +224,8 @@ hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv
 // CW: channels per lane and load (8: 16-byte loads, C = 512 or 1024; 4:
 // 8-byte loads, C = 256 or 768); a lane holds channels (i*64 + lane)*CW + e,
 // i < NV, e < CW.
-template <int NV, int CW, int LOGA, bool PACK>
-__global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restrict__ kv,
+template <int NV, int CW, int LOGA, bool PACK, int NT>
+__global__ __launch_bounds__(NT) void k_quantize_hist(const uint16_t *__restrict__ kv,
                                                        uint8_t *__restrict__ sym,
                                                        uint16_t *__restrict__ scale,
                                                        uint32_t *__restrict__ counts,
@@ -233,6 +234,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
                                                        uint32_t *__restrict__ status, int T,
                                                        int C, int A, int TT, MaxTable mt, CallMap cm) {
     constexpr int NS = 1 << LOGA;
+    constexpr int NWV = NT / 64;     // waves per block
     constexpr int NWD = CW / 2;      // 32-bit words (two bf16) per load
     constexpr int NP = NV * NWD;     // channel pairs per lane
     __shared__ __attribute__((aligned(16))) uint32_t hist[NS * NP * 64];
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
     const SlabLoc sl = slab_loc(cm, slab);
     const int t0 = blockIdx.x * TT, t1 = min(T, t0 + TT);
     uint4 *h4 = reinterpret_cast<uint4 *>(hist);
-    for (int i = threadIdx.x; i < NS * NP * 64 / 4; i += 512) h4[i] = make_uint4(0, 0, 0, 0);
+    for (int i = threadIdx.x; i < NS * NP * 64 / 4; i += NT) h4[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
     const int M = layer_m(mt, sl.kv, sl.l);
@@ -329,12 +331,12 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
     };
 
     if constexpr (PACK) {
-        // Wave wv takes the 8-row groups t0 + 8*(wv + 8k) (t0 and t1 are
+        // Wave wv takes the 8-row groups t0 + 8*(wv + NWV k) (t0 and t1 are
         // multiples of 8).
         const bool nib = 2 * M + 1 <= 16;
 #pragma unroll
         for (int e = 0; e < NV * CW; ++e) pw[0][e] = pw[1][e] = 0;  // every byte is overwritten per group
-        for (int g0 = t0 + 8 * wv; g0 < t1; g0 += 64) {
+        for (int g0 = t0 + 8 * wv; g0 < t1; g0 += 8 * NWV) {
             // Four rows in flight at a time.
 #pragma unroll
             for (int r = 0; r < 8; r += 4) {
@@ -372,15 +374,20 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
             }
         }
     } else {
+        // Wave wv takes rows t0 + wv + NWV k, four in flight at a time.
         int t = t0 + wv;
-        for (; t + 8 < t1; t += 16) {
-            uint32_t va[NV][NWD], vb[NV][NWD];
+        for (; t + 3 * NWV < t1; t += 4 * NWV) {
+            uint32_t va[NV][NWD], vb[NV][NWD], vc[NV][NWD], vd[NV][NWD];
             load_row(t, va);
-            load_row(t + 8, vb);
+            load_row(t + NWV, vb);
+            load_row(t + 2 * NWV, vc);
+            load_row(t + 3 * NWV, vd);
             do_row(t, va, 0);
-            do_row(t + 8, vb, 0);
+            do_row(t + NWV, vb, 0);
+            do_row(t + 2 * NWV, vc, 0);
+            do_row(t + 3 * NWV, vd, 0);
         }
-        if (t < t1) {
+        for (; t < t1; t += NWV) {
             uint32_t va[NV][NWD];
             load_row(t, va);
             do_row(t, va, 0);
@@ -489,7 +496,7 @@ __global__ __launch_bounds__(512) void k_quantize_hist(const uint16_t *__restric
     }
 
     // Flush: word (s, pair, lane) holds channels c and c + 1 of symbol s.
-    for (int wi = threadIdx.x; wi < NS * NP * 64; wi += 512) {
+    for (int wi = threadIdx.x; wi < NS * NP * 64; wi += NT) {
         const uint32_t v = hist[wi];
         if (!v) continue;
         const int s = wi / (NP * 64), pr = (wi / 64) % NP, ln = wi % 64;
@@ -533,19 +540,26 @@ hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_
     const int64_t TT = quantize_hist_rows(d);
     if (wire && !quantize_hist_fuses_cdf(d, wire)) return hipErrorInvalidValue;
     if (packed && d.T % 8 != 0) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((d.T + TT - 1) / TT), (unsigned)(2 * d.L)), block(512);
+    const dim3 grid((unsigned)((d.T + TT - 1) / TT), (unsigned)(2 * d.L));
+    // A grid with fewer blocks than the chip has CUs (a short call) gives
+    // each block 16 waves: twice the rows in flight per CU.
+    const bool wide = (int64_t)grid.x * grid.y < 256;
     int loga = 2;
     while ((1 << loga) < d.A) ++loga;
     const int tt = (int)TT;
     const CallMap cm = call_map(d);
-#define CG_QH(NV, CW, LG)                                                                                   \
-    do {                                                                                                    \
-        if (packed)                                                                                         \
-            hipLaunchKernelGGL((k_quantize_hist<NV, CW, LG, true>), grid, block, 0, s, kv, sym, scale, counts,  \
-                               wire, wpre, status, d.T, d.C, d.A, tt, mt, cm);                              \
-        else                                                                                                \
-            hipLaunchKernelGGL((k_quantize_hist<NV, CW, LG, false>), grid, block, 0, s, kv, sym, scale, counts, \
-                               wire, wpre, status, d.T, d.C, d.A, tt, mt, cm);                              \
+#define CG_QH_T(NV, CW, LG, PK, NT)                                                                              \
+    hipLaunchKernelGGL((k_quantize_hist<NV, CW, LG, PK, NT>), grid, dim3(NT), 0, s, kv, sym, scale, counts, wire, \
+                       wpre, status, d.T, d.C, d.A, tt, mt, cm)
+#define CG_QH(NV, CW, LG)                                  \
+    do {                                                   \
+        if (packed) {                                      \
+            if (wide) CG_QH_T(NV, CW, LG, true, 1024);     \
+            else CG_QH_T(NV, CW, LG, true, 512);           \
+        } else {                                           \
+            if (wide) CG_QH_T(NV, CW, LG, false, 1024);    \
+            else CG_QH_T(NV, CW, LG, false, 512);          \
+        }                                                  \
     } while (0)
 #define CG_QH_A(NV, CW)                         \
     do {                                        \
@@ -564,7 +578,7 @@ hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_
     }
 #undef CG_QH_A
 #undef CG_QH
-    return hipGetLastError();
+#undef CG_QH_T
     return hipGetLastError();
 }
 

@@ -460,6 +460,14 @@ def main():
     ct = 256
     nb = T // ct
     batch = None
+
+    # Batch calls (a few ms each) are averaged over at least 20 calls, after
+    # two untimed ones.
+    def time_batch(fn):
+        fn()
+        fn()
+        return time_events(fn, max(args.stage_reps, 20), torch)
+
     if nb >= 2 and not args.no_chunked_batch:
         desc1 = cgb.Desc(L, ct, H, D, desc.bins_k, desc.bins_v)
         chunks = kv.view(L, 2, nb, ct, C).permute(2, 0, 1, 3, 4).contiguous()
@@ -480,8 +488,8 @@ def main():
         cgb.check_status(ws_be, what="cg_to_bytes_batch")
         b_dec()
         cgb.check_status(ws_bd, what="cg_from_bytes_batch")
-        b_enc_ms = time_events(b_enc, args.stage_reps, torch)
-        b_dec_ms = time_events(b_dec, args.stage_reps, torch)
+        b_enc_ms = time_batch(b_enc)
+        b_dec_ms = time_batch(b_dec)
         sizes_h = [int(x) for x in sizes.cpu()]
         # One call per chunk (views prepared outside the timed region).
         ws1e = cgb.alloc_workspace(desc1, cgb.CG_OP_TO_BYTES, dev)
@@ -542,8 +550,8 @@ def main():
         cgb.check_status(ws_pd, what="cg_from_bytes_batch (per-layer tables)")
         assert torch.equal(out_p, chunks_out), "per-layer tables decode differently"
         batch["per_layer_tables"] = {
-            "to_bytes_ms": time_events(p_enc, args.stage_reps, torch),
-            "from_bytes_ms": time_events(p_dec, args.stage_reps, torch),
+            "to_bytes_ms": time_batch(p_enc),
+            "from_bytes_ms": time_batch(p_dec),
             "compression_ratio": craw / int(sizes_p.sum().item()),
         }
         log(f"batch of {nb} x {ct} tokens: {json.dumps(batch)}")
@@ -577,8 +585,8 @@ def main():
             d2f()
             cgb.check_status(wd2, what=f"cg_from_bytes_batch ({ct2}-token calls)")
             r2 = ch2.numel() * 2
-            te2 = time_events(e2, args.stage_reps, torch)
-            td2 = time_events(d2f, args.stage_reps, torch)
+            te2 = time_batch(e2)
+            td2 = time_batch(d2f)
             row = {"tokens_per_call": ct2, "calls": nb2, "to_bytes_ms": te2, "from_bytes_ms": td2,
                    "to_bytes_GBps": r2 / (te2 * 1e-3) / 1e9, "from_bytes_GBps": r2 / (td2 * 1e-3) / 1e9,
                    "compression_ratio": r2 / int(sz2.sum().item())}

@@ -15,7 +15,9 @@
 //
 // k_encode: a block of four waves owns 64 consecutive channels (lane =
 // channel) of one (K|V, layer) and eight 256-token chunks; each wave codes
-// two chunks per lane interleaved (independent dependency chains). The
+// two chunks per lane interleaved (independent dependency chains; one, in
+// four-chunk blocks, for the wider tables when they have a launch of their
+// own). The
 // waves share one table per lane in LDS, start | freq << 16 laid out
 // [symbol][lane] (no bank conflicts whatever the symbols). Symbols come
 // straight from global memory into a register ring of prefetches, so the
@@ -913,7 +915,8 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     a.cm = call_map(d);
     const int NW = plan.NW;
     const unsigned blocks = plan.blocks;
-    const dim3 grid(blocks), block(64 * NW);
+    dim3 grid(blocks);
+    const dim3 block(64 * NW);
     const int loga = plan.loga;
     // Packed symbols: nibbles in the 16-entry launch (slabs of at most 16
     // symbols), bytes in the wider one.
@@ -930,10 +933,25 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
         else if (LOGA_ == 6) CG_ENC(SS, 6, W);    \
         else CG_ENC(SS, 7, W);                    \
     } while (0)
-    auto launch = [&](int lg) {
-        if (NW == 4) CG_ENC_A(2, 4, lg);
-        else if (S == 2) CG_ENC_A(2, 1, lg);
-        else CG_ENC_A(1, 1, lg);
+    // wide1: the wider launch of a split with four-wave blocks codes one
+    // chunk per lane, in twice the blocks: its 32-entry tables and 44-row
+    // stages fit five two-chunk blocks per CU but eight one-chunk blocks,
+    // and its few slabs (12 of 64 on the benchmark call) leave the chip
+    // half idle in the tail of a two-chunk launch (2.38 -> 2.31 ms per
+    // call; one chunk per lane in the 16-entry launch too, or a 60-row
+    // stage, measured slower).
+    auto launch = [&](int lg, bool wide1) {
+        if (NW == 4 && wide1) {
+            grid.x = (unsigned)((int64_t)((d.NC + 3) / 4) * 2 * d.L * d.CB);
+            CG_ENC_A(1, 4, lg);
+            grid.x = blocks;
+        } else if (NW == 4) {
+            CG_ENC_A(2, 4, lg);
+        } else if (S == 2) {
+            CG_ENC_A(2, 1, lg);
+        } else {
+            CG_ENC_A(1, 1, lg);
+        }
         return hipGetLastError();
     };
     // The quantiser's symbols of a slab stay below 2M + 1, so with trusted
@@ -946,16 +964,16 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     if (trusted && enc_split(plan)) {
         a.nsym_lo = 0;
         a.nsym_hi = 16;
-        if ((e = launch(4)) != hipSuccess) return e;
+        if ((e = launch(4, false)) != hipSuccess) return e;
         if (large) {
             a.nsym_lo = 17;
             a.nsym_hi = 1 << 30;
-            if ((e = launch(loga)) != hipSuccess) return e;
+            if ((e = launch(loga, true)) != hipSuccess) return e;
         }
     } else {
         a.nsym_lo = 0;
         a.nsym_hi = 1 << 30;
-        if ((e = launch(loga)) != hipSuccess) return e;
+        if ((e = launch(loga, false)) != hipSuccess) return e;
     }
 #undef CG_ENC_A
 #undef CG_ENC

@@ -264,7 +264,8 @@ int encode_call(const Dims &d, const MaxTable &mt, const void *kv, uint16_t *sca
     if (wpre && (rc = hip_rc(launch_table_prefix(d, mt, wpre, s)))) return rc;
     if (qh) {
         rc = hip_rc(
-            launch_quantize_hist(d, mt, kv16, sym, scales, counts, fused ? wire : nullptr, wpre, status, packed, s));
+            launch_quantize_hist(d, mt, kv16, sym, scales, counts, fused ? wire : nullptr, wpre, status, packed,
+                                 packed && encode_nibbles(d, mt), s));
         if (rc) return rc;
     } else {
         if ((rc = hip_rc(launch_quantize(d, mt, kv16, sym, scales, status, s)))) return rc;

@@ -214,11 +214,12 @@ hipError_t launch_quantize(const Dims &d, const MaxTable &mt, const uint16_t *kv
 // below A by construction.
 //
 // PACK: the symbols are written for the encoder in token groups instead of
-// [T][C] rows (T % 8 == 0). A slab whose symbols fit four bits (2M + 1 <= 16)
-// holds one dword per (8-token group g, channel c) at byte (g*C + c)*4, byte
-// j of which carries token 8g + j in its low nibble and token 8g + 4 + j in
-// its high nibble; the other slabs hold one dword per (4-token group, c), byte
-// j = token 4g + j. Each wave then quantises 8 consecutive rows per group and
+// [T][C] rows (T % 8 == 0). With `nibbles`, a slab whose symbols fit four
+// bits (2M + 1 <= 16) holds one dword per (8-token group g, channel c) at
+// byte (g*C + c)*4, byte j of which carries token 8g + j in its low nibble
+// and token 8g + 4 + j in its high nibble; the other slabs (all of them
+// without `nibbles`) hold one dword per (4-token group, c), byte j = token
+// 4g + j. Each wave then quantises 8 consecutive rows per group and
 // assembles the dwords in registers.
 //
 // CW: channels per lane and load (8: 16-byte loads, C = 512 or 1024; 4:
@@ -232,7 +233,8 @@ __global__ __launch_bounds__(NT) void k_quantize_hist(const uint16_t *__restrict
                                                        uint16_t *__restrict__ wire,
                                                        const uint32_t *__restrict__ wpre,
                                                        uint32_t *__restrict__ status, int T,
-                                                       int C, int A, int TT, MaxTable mt, CallMap cm) {
+                                                       int C, int A, int TT, MaxTable mt, CallMap cm,
+                                                       bool nibbles) {
     constexpr int NS = 1 << LOGA;
     constexpr int NWV = NT / 64;     // waves per block
     constexpr int NWD = CW / 2;      // 32-bit words (two bf16) per load
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(NT) void k_quantize_hist(const uint16_t *__restrict
     if constexpr (PACK) {
         // Wave wv takes the 8-row groups t0 + 8*(wv + NWV k) (t0 and t1 are
         // multiples of 8).
-        const bool nib = 2 * M + 1 <= 16;
+        const bool nib = nibbles && 2 * M + 1 <= 16;
 #pragma unroll
         for (int e = 0; e < NV * CW; ++e) pw[0][e] = pw[1][e] = 0;  // every byte is overwritten per group
         for (int g0 = t0 + 8 * wv; g0 < t1; g0 += 8 * NWV) {
@@ -536,7 +538,7 @@ bool quantize_hist_fuses_cdf(const Dims &d, const void *wire) {
 
 hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
                                 uint16_t *scale, uint32_t *counts, uint16_t *wire, const uint32_t *wpre,
-                                uint32_t *status, bool packed, hipStream_t s) {
+                                uint32_t *status, bool packed, bool nibbles, hipStream_t s) {
     const int64_t TT = quantize_hist_rows(d);
     if (wire && !quantize_hist_fuses_cdf(d, wire)) return hipErrorInvalidValue;
     if (packed && d.T % 8 != 0) return hipErrorInvalidValue;
@@ -550,7 +552,7 @@ hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_
     const CallMap cm = call_map(d);
 #define CG_QH_T(NV, CW, LG, PK, NT)                                                                              \
     hipLaunchKernelGGL((k_quantize_hist<NV, CW, LG, PK, NT>), grid, dim3(NT), 0, s, kv, sym, scale, counts, wire, \
-                       wpre, status, d.T, d.C, d.A, tt, mt, cm)
+                       wpre, status, d.T, d.C, d.A, tt, mt, cm, nibbles)
 #define CG_QH(NV, CW, LG)                                  \
     do {                                                   \
         if (packed) {                                      \

@@ -635,7 +635,8 @@ struct CompactArgs {
     const uint16_t *cdf16;
     const uint32_t *wpre;
     int T, A;
-    bool packed;  // symbols in the quantiser's packed layout (PK 1 or 2 by slab)
+    bool packed;   // symbols in the quantiser's packed layout
+    bool nibbles;  // packed: slabs of at most 16 symbols as nibbles (PK 1), else bytes (PK 2)
     MaxTable mt;
 };
 
@@ -652,7 +653,7 @@ __device__ void fixup_tile(const CompactArgs &a, int j, int slab, int cb, const 
     const uint32_t incl = wave_incl_scan_u32(len, lane);
     if (!active) return;
     const int W = layer_w(a.mt, sl.kv, sl.l);
-    const bool nib = 2 * layer_m(a.mt, sl.kv, sl.l) + 1 <= 16;
+    const bool nib = a.nibbles && 2 * layer_m(a.mt, sl.kv, sl.l) + 1 <= 16;
     const uint16_t *cdf16 = call_sec(a.cdf16, a.cm, sl.b);
     const uint8_t *sp = a.sym + ((int64_t)slab * a.T + (int64_t)j * kChunk) * a.C + c;
     const uint8_t *slab_sym = a.sym + (int64_t)slab * a.T * a.C;
@@ -884,9 +885,13 @@ static EncPlan enc_plan(const Dims &d, const MaxTable &mt) {
 // trusted launch sees one kind, so one packed layout.
 static bool enc_split(const EncPlan &p) { return p.loga > 4 && p.small && (!p.large || p.blocks >= 16384); }
 
-bool encode_packs(const Dims &d, const MaxTable &mt) {
+// A launch that sees both kinds of slabs (a small grid) reads bytes for all
+// of them; nibbles need a launch of 16-entry tables.
+bool encode_packs(const Dims &d, const MaxTable &) { return d.T % 8 == 0; }
+
+bool encode_nibbles(const Dims &d, const MaxTable &mt) {
     const EncPlan p = enc_plan(d, mt);
-    return d.T % 8 == 0 && (!(p.small && p.large) || enc_split(p));
+    return enc_split(p) || p.loga <= 4;
 }
 
 hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, const int32_t *cdf,
@@ -918,8 +923,9 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     dim3 grid(blocks);
     const dim3 block(64 * NW);
     const int loga = plan.loga;
-    // Packed symbols: nibbles in the 16-entry launch (slabs of at most 16
-    // symbols), bytes in the wider one.
+    // Packed symbols: nibbles in a launch of 16-entry tables (slabs of at
+    // most 16 symbols), bytes in a wider one (whose slabs may be of both
+    // kinds).
 #define CG_ENC(SS, LG, W)                                                                           \
     do {                                                                                            \
         if (!trusted) hipLaunchKernelGGL((k_encode<SS, LG, W, false, 0>), grid, block, 0, s, a);    \
@@ -1027,6 +1033,7 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
     ca.T = d.T;
     ca.A = d.A;
     ca.packed = packed;
+    ca.nibbles = packed && encode_nibbles(d, mt);
     ca.mt = mt;
     if (d.tiles <= kCompactLdsTiles) hipLaunchKernelGGL(k_compact<true>, dim3((unsigned)d.tiles), dim3(64), 0, s, ca);
     else hipLaunchKernelGGL(k_compact<false>, dim3((unsigned)d.tiles), dim3(64), 0, s, ca);

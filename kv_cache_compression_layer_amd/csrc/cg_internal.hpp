@@ -123,10 +123,11 @@ hipError_t launch_histogram(const Dims &d, const uint8_t *sym, uint32_t *counts,
 bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym);
 bool quantize_hist_fuses_cdf(const Dims &d, const void *wire);
 // packed: write the symbols in the encoder's packed layout (T % 8 == 0; see
-// k_quantize_hist), as encode_packs() decides.
+// k_quantize_hist), as encode_packs() decides; nibbles: the slabs of at most
+// 16 symbols as nibbles, as encode_nibbles() decides (else bytes).
 hipError_t launch_quantize_hist(const Dims &d, const MaxTable &mt, const uint16_t *kv, uint8_t *sym,
                                 uint16_t *scale, uint32_t *counts, uint16_t *wire, const uint32_t *wpre,
-                                uint32_t *status, bool packed, hipStream_t s);
+                                uint32_t *status, bool packed, bool nibbles, hipStream_t s);
 
 // Table placement: table (slab, c) of width W = layer_w starts at entry
 // wpre[slab] * C + c * W of the u16 wire section; wpre[2L] = the section's
@@ -216,9 +217,12 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
                          const uint16_t *cdf16, const uint32_t *wpre, const EncodeOut &o, const EncodeWs &w,
                          bool trusted, bool packed, hipStream_t s);
 
-// Whether the trusted encoder can read packed symbols for this call: every
-// launch sees slabs of one kind (at most 16 symbols, or more) and T % 8 == 0.
+// Whether the trusted encoder can read packed symbols for this call (T % 8
+// == 0), and whether its slabs of at most 16 symbols are read as nibbles:
+// only when they have a launch of 16-entry tables of their own (bytes when
+// one launch sees both kinds of slabs).
 bool encode_packs(const Dims &d, const MaxTable &mt);
+bool encode_nibbles(const Dims &d, const MaxTable &mt);
 
 // Decoder table source: int32 [2,L,C,A+1] or the u16 wire form [2,L,C,A].
 struct DecodeIn {

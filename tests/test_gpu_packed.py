@@ -2,10 +2,11 @@
 
 For C = 256, 512, 768 or 1024 and a token count that is a multiple of 8, the fused
 quantiser hands the encoder its symbols packed per token group: 8 tokens per
-dword as nibbles for the slabs of at most 16 symbols (16-bin layers), 4 tokens
-per dword as bytes for the others, provided every encoder launch sees slabs of
-one kind (calls whose layers all have 16 bins or all more, or grids large
-enough that the two kinds take separate launches). The layout is internal:
+dword as nibbles for the slabs of at most 16 symbols (16-bin layers) when they
+have an encoder launch of 16-entry tables of their own (calls whose layers all
+have 16 bins, or grids large enough that the two kinds take separate
+launches), 4 tokens per dword as bytes otherwise (so in a launch that sees both
+kinds, every slab is bytes). The layout is internal:
 the blob must still be the oracle's byte for byte, including streams long
 enough to be re-coded by the fix-up kernel, which reads the packed symbols.
 (The fused quantiser takes alphabets of at most 32 symbols, so so does the

@@ -25,6 +25,10 @@
 // decoder of a blob whose payload has arrived up to some chunk): only those
 // chunks' tiles are written and only those chunks are checked.
 //
+// Segments of at most 1024 tiles (2L * ceil(C / 64) of them per chunk of a
+// call: 32 layers of 1024 channels, or fewer) take one launch instead,
+// k_scan_seg, a block of 1024 threads per segment.
+//
 // Calls of at most 1024 tiles per chunk and few chunks (the 256-token
 // calls LMCache makes, alone or batched: one chunk; the encoder takes up to
 // four) use k_call_scan instead: one launch, one block per call, which does
@@ -174,10 +178,43 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_add(TileScan a, int64_t tps
     a.tile_off[js * tps + tl] += add;
 }
 
+// Segments of at most kSegThreads tiles: one block per segment does the
+// three passes at once (its block scan is the segment's scan), as their
+// last two would for a segment of one block.
+constexpr int kSegThreads = 1024;
+
+__global__ __launch_bounds__(kSegThreads) void k_scan_seg(TileScan a, int64_t tps) {
+    __shared__ uint32_t wsum[kSegThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t js = a.j0 + (int64_t)blockIdx.x;
+    int j, b;
+    seg_call(a, js, j, b);
+    const uint32_t v = tid < tps ? tile_bytes(a, js, tps, tid) : 0u;
+    const uint64_t add = a.chunk_off ? call_sec(a.chunk_off, a.cm, b)[j] : 0ull;
+    const uint32_t incl = wave_incl_scan_u32(v, lane);
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < kSegThreads / 64; ++k) {
+        if (k < wv) before += wsum[k];
+        total += wsum[k];
+    }
+    if (tid < tps) a.tile_off[js * tps + tid] = add + before + incl - v;
+    if (tid == 0) {
+        if (a.chunk_total) a.chunk_total[js] = total;
+        if (a.chunk_off) check_chunk(a, j, b, total);
+    }
+}
+
 hipError_t launch_tile_scan(const TileScan &a, hipStream_t s) {
     if (a.NCr >= 0 && a.cm.Lc != a.L) return hipErrorInvalidValue;  // chunk ranges: one call only
     const int64_t tps = tiles_per_seg(a), nbps = blocks_per_seg(a);
     const int nseg = segs_in_range(a);
+    if (tps <= kSegThreads) {
+        hipLaunchKernelGGL(k_scan_seg, dim3((unsigned)nseg), dim3(kSegThreads), 0, s, a, tps);
+        return hipGetLastError();
+    }
     const unsigned nblk = (unsigned)(nseg * nbps);
     hipLaunchKernelGGL(k_scan_local, dim3(nblk), dim3(kScanBlock), 0, s, a, tps, nbps);
     hipError_t e = hipGetLastError();

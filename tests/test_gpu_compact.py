@@ -1,4 +1,5 @@
-"""Compaction of tiles whose streams outgrew the encoder's LDS stage.
+"""Compaction of tiles whose streams outgrew the encoder's LDS stage, and the
+forms of the tile-offset scan.
 
 Such a tile leaves the encoder in rows (byte i of every stream at row i of
 its staging slot) and is put in stream order by the compaction kernel: in
@@ -44,6 +45,29 @@ def test_rows_tiles_match_oracle(L, T, H, why):
     blob = cgb.to_bytes(to_dev(kv).view(torch.bfloat16), bins, bins)
     got = to_np(blob).tobytes()
     assert len(got) == len(want), why
+    assert got == want, why
+    out = to_np(cgb.from_bytes(blob).view(torch.int16), np.uint16)
+    assert_bf16_equal(out.reshape(-1), oracle.from_bytes(want).reshape(-1))
+
+
+@pytest.mark.parametrize(
+    "L,T,why",
+    [
+        (2, 256, "one chunk: one block per call scans it (and the chunk pass)"),
+        (2, 1500, "six chunks of 64 tiles: a block per chunk, then the chunk pass"),
+        (33, 600, "1056 tiles per chunk: the three-pass scan"),
+    ],
+)
+def test_scan_forms_match_oracle(L, T, why):
+    """The tile-offset scan takes one of three forms by the tiles per chunk
+    and the chunks per call; each must give the oracle's blob and decode it."""
+    import torch
+
+    kv = generate_kv(L, T, 8, 128, outlier_frac=0.02, outlier_scale=8.0, seed=950 + L + T)
+    bk, bv = oracle.default_bins(L)
+    want = oracle.to_bytes(kv, bk, bv)
+    blob = cgb.to_bytes(to_dev(kv).view(torch.bfloat16), bk, bv)
+    got = to_np(blob).tobytes()
     assert got == want, why
     out = to_np(cgb.from_bytes(blob).view(torch.int16), np.uint16)
     assert_bf16_equal(out.reshape(-1), oracle.from_bytes(want).reshape(-1))

@@ -77,7 +77,8 @@ __device__ __forceinline__ const uint8_t *call_payload(const DecArgs &a, const S
 // that do not fit read global memory.
 constexpr uint32_t kPoolPerWave = 3840;
 constexpr uint32_t kPoolPerWaveSmall = 1536;  // blocks of one or two waves
-constexpr uint32_t kPoolPerWaveLat = 12288;   // the same, in a launch of few waves (LAT)
+constexpr uint32_t kPoolPerWaveLat = 12288;   // the same, in a launch of few waves (LAT 1)
+constexpr uint32_t kPoolPerWaveLat2 = 6144;   // ... of somewhat more waves (LAT 2)
 constexpr uint32_t kPoolSlack = 528;
 
 // One stream's decoder state. Staged streams read pool bytes at `ptr` (each
@@ -330,9 +331,9 @@ __device__ __forceinline__ uint32_t load_word(const uint8_t *payload, uint64_t p
 // Block of NW waves for one (K|V, layer, 64-channel block): wave w decodes
 // the S chunks (group * NW + w) * S + s, lane = channel. The waves share the
 // channel tables, the dequantisation table and an LDS pool for the payload.
-// LAT: a launch of few waves (a short call alone), whose time is one
+// LAT (1, 2): a launch of few waves (a short call alone), whose time is one
 // stream's latency; see kPoolBytes.
-template <int S, bool FUSED, int LOGA, bool CLAMP, int NW, bool PAGED, bool TAIL, bool LAT>
+template <int S, bool FUSED, int LOGA, bool CLAMP, int NW, bool PAGED, bool TAIL, int LAT>
 __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // Static LDS sized by the template, so every address folds to an immediate.
     // Blocks of one or two waves (short calls) are as many per CU as their
@@ -351,8 +352,10 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     // few waves (LAT) is not held back by residency at all: with a pool
     // that holds whole tiles of long streams (a 32-bin slab's 64 streams of a
     // 256-token chunk take about 5 KB) no renormalisation waits for a
-    // global read.
-    constexpr uint32_t kPoolBytes = NW * (LAT ? kPoolPerWaveLat : NW <= 2 ? kPoolPerWaveSmall : kPoolPerWave);
+    // global read; 12 KiB per wave up to 8 waves per CU (LAT 1), 6 KiB up
+    // to 16 (LAT 2), which still fit the CU's LDS.
+    constexpr uint32_t kPoolBytes =
+        NW * (LAT == 1 ? kPoolPerWaveLat : LAT == 2 ? kPoolPerWaveLat2 : NW <= 2 ? kPoolPerWaveSmall : kPoolPerWave);
     __shared__ uint32_t pool_w[(kPoolBytes + kPoolSlack) / 4];  // staged payload
     __shared__ uint32_t need_w[NW];
     const int lane = threadIdx.x & 63;
@@ -1051,25 +1054,31 @@ static hipError_t launch_decode2_f(const Dims &d, DecArgs a, hipStream_t s) {
 }
 
 // Waves (over the chip) up to which a launch of one- or two-wave blocks
-// takes the large pool (LAT): eight per CU, whose LDS then still fits.
-constexpr int64_t kLatWaves = 8 * 256;
+// takes a large pool: eight per CU (LAT 1), sixteen (LAT 2).
+constexpr int64_t kLatWaves = 8 * 256, kLat2Waves = 16 * 256;
 
 template <int S, bool FUSED, int LOGA, int NW, bool PAGED, bool TAIL>
 static hipError_t launch_decode_s(const Dims &d, const DecArgs &a, bool clamp, hipStream_t s) {
     const int ngroups = (a.NCr + S * NW - 1) / (S * NW);
     const dim3 grid((unsigned)((int64_t)ngroups * 2 * d.L * d.CB));
     constexpr bool kLat = NW <= 2;
-    const bool lat = kLat && (int64_t)grid.x * NW <= kLatWaves;
+    const int64_t waves = (int64_t)grid.x * NW;
+    const int lat = !kLat ? 0 : waves <= kLatWaves ? 1 : waves <= kLat2Waves ? 2 : 0;
 #define CG_DEC(CL, LT) hipLaunchKernelGGL((k_decode<S, FUSED, LOGA, CL, NW, PAGED, TAIL, LT>), grid, dim3(64 * NW), 0, s, a)
     // clamp: some table is narrower than the 2^LOGA entries.
-    if (lat) {
+    if (lat == 1) {
         if constexpr (kLat) {
-            if (!clamp) CG_DEC(false, true);
-            else CG_DEC(true, true);
+            if (!clamp) CG_DEC(false, 1);
+            else CG_DEC(true, 1);
+        }
+    } else if (lat == 2) {
+        if constexpr (kLat) {
+            if (!clamp) CG_DEC(false, 2);
+            else CG_DEC(true, 2);
         }
     } else {
-        if (!clamp) CG_DEC(false, false);
-        else CG_DEC(true, false);
+        if (!clamp) CG_DEC(false, 0);
+        else CG_DEC(true, 0);
     }
 #undef CG_DEC
     return hipGetLastError();

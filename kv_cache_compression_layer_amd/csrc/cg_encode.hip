@@ -858,6 +858,8 @@ size_t encode_staging_bytes(const Dims &d) { return (size_t)d.tiles * kStageByte
 // (k_compact's LDS_ROWS): sixteen per CU.
 constexpr int64_t kCompactLdsTiles = 16 * 256;
 
+constexpr int64_t kEncOneChunkWaves = 4 * 1024;
+
 // Launch shape of k_encode: S chunks per lane, NW waves per block, and
 // whether the call has slabs of at most 16 symbols (small) and others (large).
 struct EncPlan {
@@ -871,6 +873,12 @@ static EncPlan enc_plan(const Dims &d, const MaxTable &mt) {
     p.S = d.NC >= 2 ? 2 : 1;
     // Four waves per block share a table when there are enough chunks.
     p.NW = d.NC >= 8 ? 4 : 1;
+    // A grid of at most four one-chunk waves per SIMD (a call of a few
+    // chunks) codes one chunk per lane: with the SIMD nearly to itself a
+    // wave's time is its chain's latency, and two chains interleaved in one
+    // wave take almost twice one (768 tokens of 32 x 1024 channels: 106 us
+    // for the two-chunk launch against 57 for a one-chunk call's).
+    if (p.NW == 1 && (int64_t)d.NC * 2 * d.L * d.CB <= kEncOneChunkWaves) p.S = 1;
     const int ngroups = (d.NC + p.S * p.NW - 1) / (p.S * p.NW);
     p.blocks = (unsigned)((int64_t)ngroups * 2 * d.L * d.CB);
     p.loga = 4;

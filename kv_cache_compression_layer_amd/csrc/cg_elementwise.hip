@@ -523,13 +523,16 @@ static int64_t quantize_hist_rows(const Dims &d) {
     return TT;
 }
 
-// Calls too small to give the fused kernel 64 blocks (a few layers of a
+// Calls too small to give the fused kernel 16 blocks (a few layers of a
 // few tokens) run faster as one wave per row in k_quantize_vec plus the
-// separate histogram (OPT-125m at 64 tokens: 73 vs 83 us).
+// separate histogram. (With eight-wave blocks the bar was 64 blocks: the
+// OPT-125m shape at 64 tokens, 24 slabs, took 83 us fused against 73
+// unfused per to_bytes call; with the sixteen-wave blocks of small grids it
+// takes 59 fused against 62.)
 bool quantize_hist_fits(const Dims &d, const void *kv, const void *sym) {
     const int64_t TT = quantize_hist_rows(d);
     return (d.C == 256 || d.C == 512 || d.C == 768 || d.C == 1024) && d.A <= 32 && (uintptr_t)kv % 16 == 0 &&
-           (uintptr_t)sym % 16 == 0 && 2 * (int64_t)d.L * ((d.T + TT - 1) / TT) >= 64;
+           (uintptr_t)sym % 16 == 0 && 2 * (int64_t)d.L * ((d.T + TT - 1) / TT) >= 16;
 }
 
 bool quantize_hist_fuses_cdf(const Dims &d, const void *wire) {

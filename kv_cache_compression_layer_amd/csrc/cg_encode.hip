@@ -13,11 +13,12 @@
 //
 // Kernels:
 //
-// k_encode: a block of four waves owns 64 consecutive channels (lane =
-// channel) of one (K|V, layer) and eight 256-token chunks; each wave codes
-// two chunks per lane interleaved (independent dependency chains; one, in
-// four-chunk blocks, for the wider tables when they have a launch of their
-// own). The
+// k_encode: a block of NW waves (four for calls of eight 256-token chunks
+// or more, else one) owns 64 consecutive channels (lane = channel) of one
+// (K|V, layer) and NW * S chunks; each wave codes S chunks per lane: two
+// interleaved (independent dependency chains), or one (calls of one chunk;
+// grids small enough that a wave has its SIMD nearly to itself; the wider
+// launch of a split, see enc_plan and launch_encode). The
 // waves share one table per lane in LDS, start | freq << 16 laid out
 // [symbol][lane] (no bank conflicts whatever the symbols). Symbols come
 // straight from global memory into a register ring of prefetches, so the
@@ -859,6 +860,7 @@ size_t encode_staging_bytes(const Dims &d) { return (size_t)d.tiles * kStageByte
 constexpr int64_t kCompactLdsTiles = 16 * 256;
 
 constexpr int64_t kEncOneChunkWaves = 4 * 1024;
+constexpr int64_t kEncOneChunkWaves4 = 256 * 256;
 
 // Launch shape of k_encode: S chunks per lane, NW waves per block, and
 // whether the call has slabs of at most 16 symbols (small) and others (large).
@@ -877,8 +879,13 @@ static EncPlan enc_plan(const Dims &d, const MaxTable &mt) {
     // chunks) codes one chunk per lane: with the SIMD nearly to itself a
     // wave's time is its chain's latency, and two chains interleaved in one
     // wave take almost twice one (768 tokens of 32 x 1024 channels: 106 us
-    // for the two-chunk launch against 57 for a one-chunk call's).
+    // for the two-chunk launch against 57 for a one-chunk call's). Four-wave
+    // blocks do the same up to 256 one-chunk waves per CU: a few rounds of
+    // blocks, whose tail the smaller one-chunk blocks shorten (GLM-4-9B shape
+    // at 16K tokens, 80 per CU: 0.53 -> 0.51 ms; the 32K-token call, 512
+    // per CU, keeps two chunks per lane but in its wider launch).
     if (p.NW == 1 && (int64_t)d.NC * 2 * d.L * d.CB <= kEncOneChunkWaves) p.S = 1;
+    if (p.NW == 4 && (int64_t)d.NC * 2 * d.L * d.CB <= kEncOneChunkWaves4) p.S = 1;
     const int ngroups = (d.NC + p.S * p.NW - 1) / (p.S * p.NW);
     p.blocks = (unsigned)((int64_t)ngroups * 2 * d.L * d.CB);
     p.loga = 4;
@@ -960,7 +967,8 @@ hipError_t launch_encode(const Dims &d, const MaxTable &mt, const uint8_t *sym, 
             CG_ENC_A(1, 4, lg);
             grid.x = blocks;
         } else if (NW == 4) {
-            CG_ENC_A(2, 4, lg);
+            if (S == 2) CG_ENC_A(2, 4, lg);
+            else CG_ENC_A(1, 4, lg);
         } else if (S == 2) {
             CG_ENC_A(2, 1, lg);
         } else {

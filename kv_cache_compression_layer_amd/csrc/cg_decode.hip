@@ -116,7 +116,9 @@ struct PagedRows {
 // is wider than the LDS part), and a symbol's frequency is the difference of
 // two starts, plus one for the last symbol W - 1 (whose upper bound 2^16 is
 // stored as 0xFFFF so that the search never passes it).
-template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED, bool HALF, bool PAGED, bool TAIL, bool T16>
+// BL: renormalise without a branch (launches of few waves, where a wave's
+// branches and exec-mask updates sit on its chain with nothing to hide them).
+template <int S, bool FUSED, int LOGA, bool CLAMP, bool STAGED, bool HALF, bool PAGED, bool TAIL, bool T16, bool BL>
 __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S], const int (&n)[S],
                                             const uint32_t (&rowoff)[S], const PagedRows<S> &pg,
                                             const uint32_t *tab,
@@ -276,7 +278,21 @@ __device__ __forceinline__ void decode_loop(const DecArgs &a, DecStream (&st)[S]
             }
             d.code -= __umul24(r[s], e & 0xFFFFu);
             d.range = __umul24(r[s], e >> 16);
-            if (d.range < kTop) {
+            if (BL && STAGED) {
+                // The same renormalisation without a branch: selects, and the
+                // look-ahead bytes read again at the same place when nothing
+                // shifted.
+                const bool one = d.range < kTop, two = d.range < (1u << 16);
+                d.code = one ? (d.code << 8) | nx0[s] : d.code;
+                d.range = two ? d.range << 16 : one ? d.range << 8 : d.range;
+                d.ptr += (uint32_t)one + (uint32_t)two;
+                if (__builtin_amdgcn_ballot_w64(two)) {
+                    __asm__ volatile("" ::: "memory");
+                    if (two) d.code = (d.code << 8) | nx1[s];
+                }
+                nx0[s] = pool[d.ptr];
+                nx1[s] = pool[d.ptr + 1];
+            } else if (d.range < kTop) {
                 // A second shift (range < 2^16) needs a rare symbol (freq <
                 // 2^16 / r); the wave-uniform test keeps its code out of the
                 // common path.
@@ -562,17 +578,17 @@ __global__ __launch_bounds__(64 * NW) void k_decode(DecArgs a) {
     const bool half = LOGA >= 3 && M + 1 <= (1 << (LOGA - 2));
     if (half) {
         if (staged)
-            decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, true, LOGA >= 3, PAGED, TAIL, T16, (LAT == 1)>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                                out_voff, lane, W, cdf16, sl.ls, c, bad_mask);
         else
-            decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, false, LOGA >= 3, PAGED, TAIL, T16, (LAT == 1)>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                                 out_voff, lane, W, cdf16, sl.ls, c, bad_mask);
     } else {
         if (staged)
-            decode_loop<S, FUSED, LOGA, CLAMP, true, false, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, true, false, PAGED, TAIL, T16, (LAT == 1)>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                             out_voff, lane, W, cdf16, sl.ls, c, bad_mask);
         else
-            decode_loop<S, FUSED, LOGA, CLAMP, false, false, PAGED, TAIL, T16>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
+            decode_loop<S, FUSED, LOGA, CLAMP, false, false, PAGED, TAIL, T16, (LAT == 1)>(a, st, n, rowoff, pg, tab, dq, sc_v, pool, out_rsrc,
                                                              out_voff, lane, W, cdf16, sl.ls, c, bad_mask);
     }
     if ((__ballot(active && (corrupt || bad_table)) | (bad_mask & __ballot(active))) && lane == 0)

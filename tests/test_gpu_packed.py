@@ -44,7 +44,8 @@ def _roundtrip(kv, bk, bv, fmt=0):
 @pytest.mark.parametrize("H,D", [(2, 128), (4, 128), (6, 128), (8, 128)])
 def test_nibble_layout(T, H, D):
     """Every layer at 16 bins: all slabs in the 16-entry launch, nibbles.
-    (32 layers give the fused quantiser its minimum of 64 blocks.)"""
+    (32 layers, 64 slabs, are well above the fused quantiser's minimum of
+    16 blocks.)"""
     L = 32
     kv = generate_kv(L, T, H, D, outlier_frac=0.01, outlier_scale=20.0, seed=700 + T + H)
     bins = np.full(L, 16, np.uint8)

@@ -8,7 +8,8 @@ have 16 bins, or grids large enough that the two kinds take separate
 launches), 4 tokens per dword as bytes otherwise (so in a launch that sees both
 kinds, every slab is bytes). The layout is internal:
 the blob must still be the oracle's byte for byte, including streams long
-enough to be re-coded by the fix-up kernel, which reads the packed symbols.
+enough to be re-coded by the fix-up coder in compaction, which reads the
+packed symbols.
 (The fused quantiser takes alphabets of at most 32 symbols, so so does the
 packed layout.)
 """

@@ -132,8 +132,11 @@ def test_tiny_rows():
 
 
 def test_long_streams_leave_the_stage():
-    """White noise at 128 bins: streams of ~200 bytes exceed the 128-byte
-    on-chip stage and go through the fix-up kernel."""
+    """White noise at 128 bins: streams of ~200 bytes outgrow the encoder's
+    LDS stage (28 bytes per lane at this table width) and leave through the
+    workspace slot's rows, which compaction gathers. (Streams longer than
+    the 256-byte slot itself, re-coded by the fix-up coder in compaction,
+    are covered in test_gpu_packed.py.)"""
     L, T, C = 1, 512, 128
     rng = np.random.default_rng(5)
     x = rng.uniform(-1, 1, (L, 2, T, C)).astype(np.float32)

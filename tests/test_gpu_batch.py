@@ -158,6 +158,35 @@ def test_batch_many_layers(B, L, H, D, fmt):
                                       _per_call_decode(_blob(blobs_np, stride, sizes_np, b)))
 
 
+def test_batch_whole_slab_tiles_of_hundreds_of_tokens():
+    """150 calls of 2 layers, 520 tokens, C = 512: 600 (K|V, layer) slabs in
+    all, so the quantiser gives each slab one block over all its 520 tokens
+    and builds the tables itself (packed symbols, three chunks with a ragged
+    tail), while one such call alone takes three blocks per slab and the
+    counts + k_cdf path. Every call equals the plain GPU call; a sample also
+    equals the oracle, and decodes to the oracle's KV."""
+    import torch
+
+    B, L, T, H, D = 150, 2, 520, 4, 128
+    kv = _batch_kv(B, L, T, H, D, seed=1500)
+    bk, bv = oracle.default_bins(L)
+    desc, stride, blobs, sizes, status = _to_bytes_batch(kv, bk, bv)
+    assert status == cgb.CG_OK
+    blobs_np, sizes_np = to_np(blobs), to_np(sizes)
+    kv_d = to_dev(kv).view(torch.bfloat16)
+    for b in range(B):
+        one = to_np(cgb.to_bytes(kv_d[b], bk, bv)).tobytes()
+        assert _blob(blobs_np, stride, sizes_np, b) == one, f"call {b}"
+    got, st = _from_bytes_batch(desc, B, blobs, stride, sizes)
+    assert st == cgb.CG_OK
+    n = 2 * L * T * H * D
+    for b in (0, 1, 2, 77, B - 1):
+        blob_b = _blob(blobs_np, stride, sizes_np, b)
+        assert blob_b == oracle.to_bytes(kv[b], bk, bv), f"call {b}"
+        ref = np.asarray(oracle.from_bytes(blob_b)).view(np.uint16).reshape(-1)
+        assert_bf16_equal(got[b * n : (b + 1) * n], ref)
+
+
 def test_batch_at_the_layer_limit():
     """32767 one-layer calls: 65534 (K|V, layer) slabs, the largest grid
     dimension the per-slab kernels take. Every call equals the plain GPU

@@ -6,6 +6,9 @@ Llama-3.1-8B-shaped long context (32 layers x 1024 channels x 32768 tokens,
 
 - cg_to_bytes: the whole blob equals the oracle's byte for byte.
 - cg_from_bytes: the whole decoded KV equals the oracle's decode bit for bit.
+- cg_from_bytes_paged (16-token blocks, a shuffled table with spare blocks,
+  as the benchmark times it): gathered back through the table, equal to
+  cg_from_bytes bit for bit.
 - The stage calls at the same size (cg_quantize, cg_build_cdf, cg_encode,
   cg_decode, cg_dequantize) each equal the oracle's stage output, or the
   corresponding section of its blob.
@@ -77,7 +80,25 @@ def test_full_size_whole_outputs(name):
     _say(name, f"oracle from_bytes on {THREADS} threads")
     ref = oracle.from_bytes(want, threads=THREADS).reshape(-1)
     assert_bf16_equal(to_np(out.view(torch.int16), np.uint16).reshape(-1), ref, "cg_from_bytes")
-    del out
+
+    # The paged decode at the same size, into 16-token blocks through a
+    # shuffled table with spare blocks, gathered back on the device: equal to
+    # cg_from_bytes (itself equal to the oracle above) bit for bit.
+    _say(name, "cg_from_bytes_paged on the GPU")
+    desc = cgb.Desc(L, T, H, D, bk, bv)
+    bs = 16
+    nblk = (T + bs - 1) // bs
+    num_blocks = nblk + nblk // 100 + 1
+    table = np.random.default_rng(1234).permutation(num_blocks)[:nblk].astype(np.int32)
+    cache = torch.full((L, 2, num_blocks, bs, C), 0x7F7F, dtype=torch.int16, device=kv_d.device)
+    ws = cgb.alloc_workspace(desc, cgb.CG_OP_FROM_BYTES)
+    cgb.cg_from_bytes_paged(desc, to_dev(blob_np), blob_np.size, cache, 2 * num_blocks * bs * C,
+                            num_blocks * bs * C, bs, to_dev(table), num_blocks, ws)
+    assert cgb.cg_read_status(ws) == cgb.CG_OK
+    rows = torch.from_numpy(table.astype(np.int64)).to(kv_d.device)
+    got = cache[:, :, rows].reshape(L, 2, nblk * bs, C)[:, :, :T]
+    assert torch.equal(got, out.view(torch.int16).view(L, 2, T, C)), "cg_from_bytes_paged differs"
+    del out, cache, got, ws
     torch.cuda.empty_cache()
 
     # The stage calls, at the same size.

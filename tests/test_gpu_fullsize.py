@@ -9,6 +9,8 @@ Llama-3.1-8B-shaped long context (32 layers x 1024 channels x 32768 tokens,
 - cg_from_bytes_paged (16-token blocks, a shuffled table with spare blocks,
   as the benchmark times it): gathered back through the table, equal to
   cg_from_bytes bit for bit.
+- The pipelined load (pieces of 16 chunks copied from pinned host memory
+  and decoded as they land, on two streams): equal to cg_from_bytes.
 - The stage calls at the same size (cg_quantize, cg_build_cdf, cg_encode,
   cg_decode, cg_dequantize) each equal the oracle's stage output, or the
   corresponding section of its blob.
@@ -29,6 +31,7 @@ import oracle
 from blob_format import parse
 from gpu_util import assert_bf16_equal, to_dev, to_np
 from kv_cache_compression_layer_amd import cachegen as cgb
+from kv_cache_compression_layer_amd import streaming
 from kv_cache_compression_layer_amd.synth import WORKLOADS, generate_workload
 
 pytestmark = pytest.mark.gpu
@@ -98,7 +101,26 @@ def test_full_size_whole_outputs(name):
     rows = torch.from_numpy(table.astype(np.int64)).to(kv_d.device)
     got = cache[:, :, rows].reshape(L, 2, nblk * bs, C)[:, :, :T]
     assert torch.equal(got, out.view(torch.int16).view(L, 2, T, C)), "cg_from_bytes_paged differs"
-    del out, cache, got, ws
+    del cache, got, ws
+
+    # The pipelined load the benchmark times: the blob copied from pinned host
+    # memory in pieces of 16 chunks on one stream, each piece's chunk range
+    # decoded on another as it lands; equal to cg_from_bytes bit for bit.
+    _say(name, "pipelined load on the GPU")
+    lay = cgb.cg_blob_layout(desc)
+    host = torch.empty(blob_np.size, dtype=torch.uint8, pin_memory=True)
+    host.copy_(torch.from_numpy(blob_np))
+    dev_blob = torch.zeros(blob_np.size, dtype=torch.uint8, device=kv_d.device)
+    out2 = torch.empty(L * 2 * T * C, dtype=torch.int16, device=kv_d.device)
+    ws = cgb.alloc_workspace(desc, cgb.CG_OP_FROM_BYTES)
+    pieces = streaming.plan_pieces(int(lay["off_payload"]), p["chunk_off"], 16)
+    assert pieces[-1].byte_end == blob_np.size
+    copy_s, dec_s = torch.cuda.Stream(), torch.cuda.Stream()
+    streaming.enqueue_pipelined_load(desc, host, dev_blob, out2, ws, pieces, copy_s, dec_s)
+    torch.cuda.synchronize()
+    assert cgb.cg_read_status(ws) == cgb.CG_OK
+    assert torch.equal(out2, out.view(torch.int16).reshape(-1)), "pipelined load differs"
+    del out, out2, dev_blob, host, ws
     torch.cuda.empty_cache()
 
     # The stage calls, at the same size.
